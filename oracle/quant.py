@@ -1,0 +1,139 @@
+"""Canonical quantizers and dequantizers (numpy; test infrastructure only).
+
+int8 b32 (symmetric absmax, block of 32 along K)
+    Source: Qwen3-VL 4B/8B Core AI cards, Files table ("int8 per-block-32 body
+    + untied absmax int8 head"); zoo Qwen3-VL page, Measured paragraph (int8hu
+    = int8lin per-block-32 body + untied absmax int8 head); zoo Qwen3.8-27B
+    page, Numerics paragraph ("absmax symmetric per-block-32 head rule",
+    clipping not used).  The same rule serves body and head.
+
+    Per block of 32 weights w (fp32) of one row:
+      a   = max |w|                         exact in fp32
+      s32 = fl32(a / 127)                   IEEE fp32 division, RNE
+      s   = fp16_RNE(s32)                   the stored scale
+      q   = 0                               if s == 0
+          = clamp(rint(fl32(w / s)), -127, 127)   otherwise (ties to even)
+      w^  = q * s                           (exact in fp64)
+
+    Readings (the pages give only the names): divisor 127, code -128 unused;
+    the quotient uses the STORED fp16 scale so codes and dequantization agree;
+    rounding is half-to-even; an all-zero block has scale 0 and codes 0;
+    non-finite input or a scale beyond fp16 range is refused.
+
+int4 g64 (affine min/max, group of 64 along K)
+    Source: CoreML-LLM handoff page, Architecture paragraph ("INT4
+    per-grouped-channel (group_size 64, matching the MLX *-4bit builds)").
+    The affine form is the workload definition, not the pages' (parity
+    unpinned by the pages).
+
+    Per group of 64 weights w (fp32):
+      mn, mx = min w, max w                 exact
+      s = fp16_RNE(fl32(fl32(mx - mn) / 15)),  m = fp16_RNE(mn)
+      q = 0                                 if s == 0
+        = clamp(rint(fl32(fl32(w - m) / s)), 0, 15)
+      w^ = m + q * s                        (exact in fp64)
+    Canonical packing: uint32 word j of a row holds codes 8j..8j+7, code 8j+i
+    in bits [4i, 4i+4) (low nibble = lowest k).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK8 = 32
+GROUP4 = 64
+QMAX8 = 127
+QMAX4 = 15
+
+
+def _check_input(w: np.ndarray, mult: int) -> np.ndarray:
+    w = np.asarray(w)
+    if w.dtype != np.float32:
+        raise TypeError("weights must be float32")
+    if w.ndim != 2:
+        raise ValueError("weights must be [N, K]")
+    if w.shape[1] % mult:
+        raise ValueError(f"K={w.shape[1]} is not a multiple of {mult}")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    return w
+
+
+def quantize_int8_b32(w: np.ndarray):
+    """fp32 [N, K] -> (codes int8 [N, K], scales fp16 [N, K/32])."""
+    w = _check_input(w, BLOCK8)
+    n, k = w.shape
+    blocks = w.reshape(n, k // BLOCK8, BLOCK8)
+    a = np.max(np.abs(blocks), axis=2) if k else np.zeros((n, 0), np.float32)
+    s32 = (a / np.float32(QMAX8)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    if np.any(np.isinf(s16)):
+        raise ValueError("scale overflows fp16")
+    sf = s16.astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = (blocks / sf).astype(np.float32)
+    qf = np.rint(quot)
+    qf = np.where(sf == 0, np.float32(0), qf)
+    q = np.clip(qf, -QMAX8, QMAX8).astype(np.int8)
+    return q.reshape(n, k), s16
+
+
+def dequantize_int8_b32(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """(int8 [N, K], fp16 [N, K/32]) -> fp64 [N, K], w^ = q * s."""
+    return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), BLOCK8, axis=1)
+
+
+def quantize_int4_g64(w: np.ndarray):
+    """fp32 [N, K] -> (codes uint8 [N, K] in 0..15, scales fp16 [N, K/64],
+    mins fp16 [N, K/64])."""
+    w = _check_input(w, GROUP4)
+    n, k = w.shape
+    groups = w.reshape(n, k // GROUP4, GROUP4)
+    if k:
+        mn = np.min(groups, axis=2)
+        mx = np.max(groups, axis=2)
+    else:
+        mn = mx = np.zeros((n, 0), np.float32)
+    rng = (mx - mn).astype(np.float32)
+    s32 = (rng / np.float32(QMAX4)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+        m16 = mn.astype(np.float16)
+    if np.any(np.isinf(s16)) or np.any(np.isinf(m16)):
+        raise ValueError("scale or min overflows fp16")
+    sf = s16.astype(np.float32)[:, :, None]
+    mf = m16.astype(np.float32)[:, :, None]
+    shifted = (groups - mf).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = (shifted / sf).astype(np.float32)
+    qf = np.rint(quot)
+    qf = np.where(sf == 0, np.float32(0), qf)
+    q = np.clip(qf, 0, QMAX4).astype(np.uint8)
+    return q.reshape(n, k), s16, m16
+
+
+def dequantize_int4_g64(codes: np.ndarray, scales: np.ndarray, mins: np.ndarray) -> np.ndarray:
+    """(uint8 codes [N, K], fp16 [N, K/64] x2) -> fp64 [N, K], w^ = m + q * s."""
+    s = np.repeat(scales.astype(np.float64), GROUP4, axis=1)
+    m = np.repeat(mins.astype(np.float64), GROUP4, axis=1)
+    return m + codes.astype(np.float64) * s
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes [N, K] (0..15) -> canonical uint32 words [N, K/8];
+    code 8j+i sits in bits [4i, 4i+4) of word j."""
+    n, k = codes.shape
+    c = codes.astype(np.uint32).reshape(n, k // 8, 8)
+    words = np.zeros((n, k // 8), np.uint32)
+    for i in range(8):
+        words |= c[:, :, i] << np.uint32(4 * i)
+    return words
+
+
+def unpack_nibbles(words: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_nibbles``."""
+    n, kw = words.shape
+    out = np.empty((n, kw, 8), np.uint8)
+    for i in range(8):
+        out[:, :, i] = (words >> np.uint32(4 * i)) & np.uint32(0xF)
+    return out.reshape(n, kw * 8)
