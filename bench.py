@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark one decode step's quantized linear stack on one MI355X.
+
+A step is one pass over every projection of a Qwen3-8B-shaped decoder (36
+layers x [q|k|v] -> o -> [gate|up] -> down, then the 151 936-row head) with
+int8 b32 weights and one fp16 activation vector per group, all resident in HBM
+before timing starts.  The metric is the algorithmic bytes a step must move
+(packed weights + activations + outputs) divided by the time per step.
+
+Prints one JSON line.  Run with no flags for the default workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+METRIC = "achieved HBM GB/s and us per decode step (8B-shaped int8 b32 stack, M=1)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b-int8-m1")
+    ap.add_argument("--path", choices=["plan", "launches"], default="plan",
+                    help="plan: persistent stack plan; launches: one launch per group")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-mb", type=int, default=1024,
+                    help="single-GEMV workload: weight copies cycled to exceed the caches")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_stack(qd, si, torch, workload, dev):
+    wl = si.WORKLOADS[workload]
+    m = wl.m
+    if wl.single is not None:
+        n, k = wl.single
+        groups, model = [("gemv", [("W", n, k)])], "single"
+    else:
+        groups, model = wl.decoder.groups(), wl.decoder.name
+    pack = qd.qpack_int8_b32 if wl.fmt == "int8_b32" else qd.qpack_int4_g64
+    ops, alg_bytes, weight_bytes = [], 0, 0
+    for gi, (gname, members) in enumerate(groups):
+        k = members[0][2]
+        x = si.activations(si.activation_seed(workload, gname), m, k)
+        x_gpu = torch.from_numpy(x if m > 1 else x[0]).to(dev)
+        alg_bytes += m * k * 2
+        for pname, n, kk in members:
+            w = si.weights_torch(si.matrix_seed(model, pname), n, kk, dev)
+            pw = pack(w)
+            del w
+            y = torch.empty((m, n) if m > 1 else (n,), dtype=torch.float16, device=dev)
+            ops.append(qd.LinearOp(pw, x_gpu, y, gi))
+            alg_bytes += pw.blob.numel() + m * n * 2
+            weight_bytes += pw.blob.numel()
+    torch.cuda.synchronize()
+    return ops, alg_bytes, weight_bytes, m
+
+
+def cpu_baseline(si, workload, alg_bytes_step, dev, torch):
+    """The oracle as it stands, timed on host cores over a bounded sample:
+    layer 0's projections of the same workload (same weights, regenerated on
+    the device and copied over), scaled to a full step."""
+    import numpy as np
+    from oracle import linear, quant
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    wl = si.WORKLOADS[workload]
+    if wl.single is not None:
+        n, k = wl.single
+        sample = [("gemv", [("W", n, k)])]
+        model = "single"
+    else:
+        sample = wl.decoder.groups()[:4]          # layer 0: qkv, o, gate_up, down
+        model = wl.decoder.name
+    qz = quant.quantize_int8_b32 if wl.fmt == "int8_b32" else quant.quantize_int4_g64
+    t_total, sample_bytes = 0.0, 0
+    for gname, members in sample:
+        k = members[0][2]
+        x = si.activations(si.activation_seed(workload, gname), wl.m, k)
+        xin = x if wl.m > 1 else x[0]
+        sample_bytes += wl.m * k * 2
+        for pname, n, kk in members:
+            w = si.weights_torch(si.matrix_seed(model, pname), n, kk, dev).cpu().numpy()
+            parts = qz(w)                                  # untimed: packing is offline
+            del w
+            t0 = time.perf_counter()
+            linear.ref_linear(wl.fmt, parts, xin)
+            t_total += time.perf_counter() - t0
+            sample_bytes += sum(p.nbytes for p in parts) + wl.m * n * 2
+    gbs = sample_bytes / t_total / 1e9
+    us_step = t_total * 1e6 * alg_bytes_step / sample_bytes
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_step": round(us_step, 1),
+            "sample": f"layer 0 of {workload} ({len(sample)} groups, {sample_bytes / 1e6:.1f} MB "
+                      f"of quantized weights + activations), fp64 dequantize-then-multiply, "
+                      f"{t_total:.2f} s; scaled to a full step by bytes"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import int4_quantized_decode_amd as qd
+    import synthetic_inputs as si
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"building {args.workload} (weights generated and packed on the device)")
+    ops, alg_bytes, weight_bytes, m = build_stack(qd, si, torch, args.workload, dev)
+    log(f"{len(ops)} projections, {weight_bytes / 1e9:.3f} GB packed weights, "
+        f"{alg_bytes / 1e9:.4f} GB per step")
+
+    plans = []
+    wl = si.WORKLOADS[args.workload]
+    if wl.single is not None:
+        # Cycle copies of the one matrix so successive steps miss the caches.
+        copies = max(1, (args.rotate_mb << 20) // max(1, weight_bytes))
+        op = ops[0]
+        rot = [op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
+                                  op.x, op.y, 0) for _ in range(copies - 1)]
+        step_ops = [[r] for r in rot]
+    else:
+        step_ops = [ops]
+    if args.path == "plan":
+        plans = [qd.StackPlan(o, m) for o in step_ops]
+        runners = [p.run for p in plans]
+    else:
+        runners = [(lambda o=o: qd.decode_linear_stack(o, m)) for o in step_ops]
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        runners[i % len(runners)]()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    step_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        a, b = step_events[i]
+        a.record(stream)
+        runners[i % len(runners)]()
+        b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_events)
+    med_ms = step_ms[len(step_ms) // 2]
+    for p in plans:
+        if p.error():
+            raise RuntimeError("stack plan reported a timed-out wait")
+    log(f"wall {wall_ms * 1e3:.1f} us/step, event median {med_ms * 1e3:.1f} us "
+        f"(p10 {step_ms[len(step_ms) // 10] * 1e3:.1f}, p90 {step_ms[(9 * len(step_ms)) // 10] * 1e3:.1f})")
+
+    value = alg_bytes / (wall_ms * 1e-3) / 1e9
+    kernel_gbs = alg_bytes / (med_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "us_per_step": round(wall_ms * 1e3, 2),
+        "tok_per_s_equiv": round(m * 1e3 / wall_ms, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if wl.fmt == "int8_b32" else "int4",
+        "data": "synthetic (W ~ N(0,0.02) fp32 quantized on the device; x ~ N(0,1) fp16)",
+        "config": {"workload": args.workload, "m": m, "path": args.path,
+                   "bytes_per_step": alg_bytes, "weight_bytes": weight_bytes,
+                   "projections": len(ops), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "stack step (HIP events on the launch stream, median)"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(si, args.workload, alg_bytes, dev, torch)
+    for p in plans:
+        p.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * qdecode -- weight-only quantized linear layers for LLM decoding on
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What is computed
+ *   y = W^ x for an fp16 activation vector x (one decoded token), or
+ *   Y = X W^T for up to 16 token rows (a static chunked-prefill step), where
+ *   W^ is a weight matrix stored quantized:
+ *
+ *   int8 b32  -- int8 codes, symmetric absmax per block of 32 consecutive
+ *                weights along K, one fp16 scale per block: s = fp16(fl32(
+ *                max|w| / 127)), q = clamp(rint(fl32(w / s)), -127, 127),
+ *                w^ = q s.  The pages call this the "int8 per-block-32 body +
+ *                untied absmax int8 head" ship config (Qwen3-VL 4B/8B Core AI
+ *                cards, Files table; zoo Qwen3-VL page, Measured paragraph) and
+ *                apply the same absmax rule to the LM head without clipping
+ *                (zoo Qwen3.8-27B page, Numerics paragraph).
+ *   int4 g64  -- 4-bit codes per group of 64 along K (CoreML-LLM Qwen3-VL
+ *                4B/8B handoff page, Architecture paragraph), in affine form:
+ *                s = fp16(fl32(fl32(max - min) / 15)), m = fp16(min),
+ *                q = clamp(rint(fl32(fl32(w - m) / s)), 0, 15), w^ = m + q s.
+ *   A zero scale gives zero codes.  Rounding is IEEE round-to-nearest-even
+ *   throughout.
+ *
+ *   Decode is bandwidth-bound: each step streams every quantized weight once
+ *   (Core AI 4B/8B cards, Measured paragraph).  The kernels read each packed
+ *   byte exactly once per call and dequantize in registers.
+ *
+ * Conventions
+ *   - Matrices are [N, K] row-major in the PyTorch Linear sense: y[n] =
+ *     sum_k W[n,k] x[k].  fp16 values travel as uint16_t bit patterns.
+ *   - Every data pointer is a DEVICE pointer unless marked "host".  The caller
+ *     owns every buffer; the library never allocates on the compute path
+ *     (only qd_stack_plan_create allocates, once).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate
+ *     their arguments on the host and return synchronously; on success the
+ *     work is enqueued on `stream` and runs asynchronously.  On any error
+ *     nothing is enqueued.  Errors raised while a kernel runs surface at the
+ *     next synchronizing HIP call.
+ *   - Outputs must not overlap inputs.
+ *   - The functions hold no global mutable state and are thread-safe, except
+ *     that one qd_stack_plan must not run on two streams at once.
+ *
+ * Packed layout ("tiled blob")
+ *   Rows are padded to Np = 16 ceil(N/16), K to Kp = 256 ceil(K/256), with
+ *   zero codes, scales and mins.  Row-group r = rows 16r..16r+15; super-block
+ *   j = k in [256j, 256j+256).  Tile (r, j) starts at byte (r (Kp/256) + j) T.
+ *   In each 1024-byte chunk of a tile, lane l = 16g + rho (0..63) owns bytes
+ *   16l..16l+15 for row 16r + rho and K-quarter g.
+ *   int8 b32, T = 4352: chunk s = 0..3; lane bytes 0..7 = codes at k = 256j +
+ *     64s + 8g + i, bytes 8..15 = codes at k = 256j + 64s + 32 + 8g + i
+ *     (i = 0..7); then 16 rows x 8 fp16 scales (blocks 8j..8j+7) at 4096 +
+ *     16 rho.
+ *   int4 g64, T = 2304: chunk s = 0..1; lane bytes 0..7 = codes of group
+ *     4j+2s, in-group offsets 16g..16g+15; bytes 8..15 = same for group
+ *     4j+2s+1; each little-endian uint32 holds 8 consecutive codes k0..k0+7
+ *     with nibble p holding code k0 + (0,2,4,6,1,3,5,7)[p]; then per row rho
+ *     at 2048 + 16 rho: 4 fp16 scales, 4 fp16 mins (groups 4j..4j+3).
+ *   With N % 16 == 0 and K % 256 == 0 the blob holds exactly N K (1 + 2/32)
+ *   (int8) or N K (1/2 + 4/64) (int4) bytes.
+ */
+#ifndef QDECODE_H
+#define QDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QD_OK = 0,
+  QD_EINVAL = 1,   /* null pointer, unknown enum, overlapping buffers, bad plan */
+  QD_ESHAPE = 2,   /* K not a multiple of 32 (int8) / 64 (int4), N or K < 0,
+                      K > QD_MAX_K, M outside 1..16, blob smaller than needed */
+  QD_EALIGN = 3,   /* blob, x or W not 16-byte aligned */
+  QD_ERANGE = 4,   /* (reported through the packer's device flag, see below) */
+  QD_ELAUNCH = 5,  /* a HIP launch or runtime call failed */
+  QD_EFORMAT = 6,  /* weight format not supported by this entry point */
+  QD_EDEVICE = 7   /* no usable device, or the plan belongs to another device */
+} qd_status;
+
+typedef enum { QD_FMT_INT8_B32 = 1, QD_FMT_INT4_G64 = 2 } qd_format;
+
+enum { QD_MAX_K = 24576, QD_MAX_M = 16 };
+
+/* A packed weight.  `data` is a device pointer to the tiled blob (16-byte
+ * aligned, at least qd_packed_bytes(fmt, n, k) bytes), owned by the caller. */
+typedef struct {
+  int32_t fmt;        /* qd_format */
+  int32_t reserved;   /* 0 */
+  int64_t n, k;       /* logical shape [N, K] */
+  const void* data;
+  uint64_t bytes;     /* size of the buffer at `data` */
+} qd_weight;
+
+/* Bytes of the tiled blob for an [n, k] matrix; 0 if the shape is invalid.
+ * Host only, pure. */
+uint64_t qd_packed_bytes(int32_t fmt, int64_t n, int64_t k);
+
+/* Static description of a status code (host, never NULL). */
+const char* qd_status_string(int32_t status);
+
+/*
+ * Quantize and pack an fp32 matrix (device, [n, k] row-major, 16-byte
+ * aligned) into `out` (device, out_bytes >= qd_packed_bytes).  Bit-exact with
+ * the definitions above, including the padding.  A block/group holding a
+ * non-finite weight sets bit 1 of *err_flag, one whose scale or min overflows
+ * fp16 sets bit 2 (err_flag: device int32, may be NULL; bits are OR-ed in,
+ * never cleared); such a block/group is written as zero codes, zero scale.
+ * int8: k % 32 == 0.  int4: k % 64 == 0.
+ */
+qd_status qpack_int8_b32(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
+                         int32_t* err_flag, void* stream);
+qd_status qpack_int4_g64(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
+                         int32_t* err_flag, void* stream);
+
+/*
+ * One decoded token: y[n] = fp16_RNE(sum_k w^[n,k] x[k]) with fp32
+ * accumulation.  `w` is a host pointer to the descriptor; x (device, fp16
+ * [K], 16-byte aligned) and y (device, fp16 [N]).  N == 0 is a no-op; K == 0
+ * writes zeros.  The format must match the entry point (else QD_EFORMAT).
+ */
+qd_status qgemv_int8_b32(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream);
+qd_status qgemv_int4_g64(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream);
+
+/*
+ * A static chunk of m tokens (1 <= m <= 16, the pages' S=16 chunked-prefill
+ * function, zoo Qwen3.8-27B page, vision path section): Y[i, n] =
+ * fp16_RNE(sum_k X[i,k] w^[n,k]), X fp16 [m, K] row-major (16-byte aligned),
+ * Y fp16 [m, N] row-major.  The contraction runs on the matrix cores.
+ * Formats: int8 b32.
+ */
+qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_t* y, int64_t m, void* stream);
+
+/*
+ * One decode step's linear layers, issued back to back on one stream.
+ * ops[i] computes ops[i].y = W^_i ops[i].x (m token rows).  Consecutive ops
+ * with equal `group` form one group: they must share x, K and format and are
+ * fused into one launch.  Group g+1 starts only after group g has written all
+ * its outputs, so a later op's x may be an earlier group's y (a dependent
+ * chain).  All ops use the same m (1..16; m > 1 needs int8 b32).
+ */
+typedef struct {
+  qd_weight w;
+  const uint16_t* x;
+  uint16_t* y;
+  int32_t group;
+  int32_t reserved;
+} qd_linear_op;
+
+qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m, void* stream);
+
+/*
+ * The same step as a persistent plan: one kernel launch per step that walks
+ * every group in order, keeping the weight stream going across group
+ * boundaries (weights of the next group are fetched while the previous group
+ * completes; a group's activations are read only after the group before it
+ * has finished).  qd_stack_plan_create validates `ops` exactly as
+ * decode_linear_stack does, copies the descriptors to the device and
+ * allocates the plan's scratch (counters, partial sums) once; the pointers in
+ * `ops` must stay valid while the plan lives.  qd_stack_plan_run enqueues one
+ * step on `stream` and allocates nothing.  A plan may be run repeatedly but
+ * not concurrently.  m == 1 only.
+ */
+typedef struct qd_stack_plan qd_stack_plan;
+
+qd_status qd_stack_plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out);
+qd_status qd_stack_plan_run(qd_stack_plan* plan, void* stream);
+/* Device error word of the last completed run (host reads it with a blocking
+ * copy): 0 = fine, 1 = a wait timed out (the step's outputs are incomplete). */
+qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error);
+void qd_stack_plan_destroy(qd_stack_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDECODE_H */

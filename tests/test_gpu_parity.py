@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Packing is compared byte for byte; products within the acceptance bound of
+tests/numerics.py.  Sizes span several tiles plus ragged row and K tails; the
+full 8B-shaped matrices are checked on sampled rows."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from oracle import layout, linear, quant
+from tests.numerics import check_vector
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def qd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_quantized_decode_amd as qd
+    return qd
+
+
+def _gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _oracle_parts(fmt, w):
+    return quant.quantize_int8_b32(w) if fmt == "int8_b32" else quant.quantize_int4_g64(w)
+
+
+def _oracle_blob(fmt, parts):
+    return layout.tile_int8_b32(*parts) if fmt == "int8_b32" else layout.tile_int4_g64(*parts)
+
+
+def _pack(qd, fmt, w_gpu):
+    return qd.qpack_int8_b32(w_gpu) if fmt == "int8_b32" else qd.qpack_int4_g64(w_gpu)
+
+
+SHAPES = [(16, 256), (200, 1056), (200, 1088), (37, 576), (1, 64), (48, 2048), (2048, 2048),
+          (100, 4096)]
+
+
+def _skip_bad_k(fmt, k):
+    if fmt == "int4_g64" and k % 64:
+        pytest.skip("int4 g64 needs K % 64 == 0")
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_pack_bit_exact(qd, fmt, n, k):
+    _skip_bad_k(fmt, k)
+    w = si.weights(si.seed_for("pack", fmt, n, k), n, k)
+    pw = _pack(qd, fmt, _gpu(w))
+    got = _host(pw.blob)
+    want = _oracle_blob(fmt, _oracle_parts(fmt, w))
+    assert got.size == want.size
+    diff = np.flatnonzero(got != want)
+    assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
+
+
+def _adversarial(fmt, n=32, k=512):
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0                                          # zero blocks / groups
+    s = np.float32(2.0 ** -7)
+    w[1, :32] = (np.arange(32, dtype=np.float32) - 15.5) * s  # halves: exact ties
+    w[1, 0] = np.float32(127) * s
+    w[2, :] = (rng.standard_normal(k) * 1e-7).astype(np.float32)   # fp16-subnormal scales
+    w[3, :] = (rng.standard_normal(k) * 50).astype(np.float32)     # large values
+    w[4, :] = np.float32(0.3)                                       # constant groups
+    w[5, 64:128] = -np.abs(w[5, 64:128])                           # one-signed groups
+    w[6, :] = (rng.integers(-127, 128, k) * 2.0 ** -9).astype(np.float32)  # on-grid values
+    for c in range(16):                                             # near-ties around x.5
+        w[7, c] = np.float32((c + 0.5) * 2.0 ** -7 * (1 + (-1) ** c * 2.0 ** -20))
+    w[7, 31] = np.float32(127 * 2.0 ** -7)
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_pack_adversarial_bit_exact(qd, fmt):
+    w = _adversarial(fmt)
+    pw = _pack(qd, fmt, _gpu(w))
+    got = _host(pw.blob)
+    want = _oracle_blob(fmt, _oracle_parts(fmt, w))
+    diff = np.flatnonzero(got != want)
+    assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_pack_error_flags(qd, fmt):
+    w = np.zeros((16, 256), np.float32)
+    w[3, 7] = np.nan
+    with pytest.raises(qd.QDError):
+        _pack(qd, fmt, _gpu(w))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pack = qd.qpack_int8_b32 if fmt == "int8_b32" else qd.qpack_int4_g64
+    pack(_gpu(w), err=err)
+    assert int(err.item()) & 1
+    # int8: max|w| / 127 beyond fp16; int4: the group min beyond fp16
+    w[3, 7] = 1e9 if fmt == "int8_b32" else -70000.0
+    err.zero_()
+    pack(_gpu(w), err=err)
+    assert int(err.item()) & 2
+
+
+# ------------------------------------------------------------------ M = 1
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("n,k", SHAPES + [(16, 24576)])
+def test_gemv_parity(qd, fmt, n, k):
+    _skip_bad_k(fmt, k)
+    w = si.weights(si.seed_for("gemv", fmt, n, k), n, k)
+    x = si.activations(si.seed_for("gemv-x", fmt, n, k), 1, k)[0]
+    pw = _pack(qd, fmt, _gpu(w))
+    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    y = _host(fn(pw, _gpu(x)))
+    parts = _oracle_parts(fmt, w)
+    y_ref = linear.ref_linear(fmt, parts, x)
+    check_vector(y, y_ref, linear.row_max_abs(fmt, parts), x, f"{fmt} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_gemv_edge_cases(qd, fmt):
+    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    # K = 0: y = 0
+    pw0 = _pack(qd, fmt, torch.zeros((20, 0), dtype=torch.float32, device=DEV))
+    y0 = fn(pw0, torch.zeros(0, dtype=torch.float16, device=DEV),
+            torch.full((20,), 7.0, dtype=torch.float16, device=DEV))
+    assert not _host(y0).any()
+    # N = 0: no-op
+    pwn = _pack(qd, fmt, torch.zeros((0, 256), dtype=torch.float32, device=DEV))
+    assert fn(pwn, torch.zeros(256, dtype=torch.float16, device=DEV)).numel() == 0
+    # all-zero weights give exact zeros; adversarial rows stay in bound
+    w = _adversarial(fmt)
+    x = si.activations(99, 1, w.shape[1])[0]
+    y = _host(fn(_pack(qd, fmt, _gpu(w)), _gpu(x)))
+    parts = _oracle_parts(fmt, w)
+    check_vector(y, linear.ref_linear(fmt, parts, x), linear.row_max_abs(fmt, parts), x, "adv")
+
+
+# ------------------------------------------------------------------ M <= 16
+
+@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("n,k", [(16, 256), (200, 1056), (48, 2048), (100, 4096), (64, 12288)])
+def test_small_m_parity(qd, m, n, k):
+    w = si.weights(si.seed_for("sm", n, k), n, k)
+    X = si.activations(si.seed_for("sm-x", m, n, k), m, k)
+    pw = qd.qpack_int8_b32(_gpu(w))
+    Y = _host(qd.qgemm_small_m(pw, _gpu(X)))
+    parts = quant.quantize_int8_b32(w)
+    Y_ref = linear.ref_linear("int8_b32", parts, X)
+    rmax = linear.row_max_abs("int8_b32", parts)
+    for i in range(m):
+        check_vector(Y[i], Y_ref[i], rmax, X[i], f"m={m} row {i}")
+
+
+def test_small_m_rows_match_gemv(qd):
+    """Each token row of the 16-row chunk agrees with the one-token GEMV on
+    that row (the pages' chunked-vs-S=1 consistency idea)."""
+    n, k = 512, 4096
+    w = si.weights(5, n, k)
+    X = si.activations(6, 16, k)
+    pw = qd.qpack_int8_b32(_gpu(w))
+    Y = _host(qd.qgemm_small_m(pw, _gpu(X)))
+    parts = quant.quantize_int8_b32(w)
+    rmax = linear.row_max_abs("int8_b32", parts)
+    for i in range(16):
+        y1 = _host(qd.qgemv_int8_b32(pw, _gpu(X[i])))
+        check_vector(Y[i], y1.astype(np.float64), 2 * rmax, X[i], f"row {i}")
+
+
+# ------------------------------------------------------------------ stack
+
+def _tiny_decoder_ops(qd, fmt, m, layers=2, chained=False):
+    d = si.Decoder("tiny", layers=layers, hidden=512, q_heads=4, mlp=1280, vocab=1000,
+                   kv_heads=2, head_dim=64)
+    ops, meta = [], []
+    gid = 0
+    for gname, members in d.groups():
+        k = members[0][2]
+        x = si.activations(si.seed_for("stack-x", gname, m), m, k)
+        x_gpu = _gpu(x if m > 1 else x[0])
+        for pname, n, kk in members:
+            w = si.weights(si.seed_for("stack-w", pname), n, kk)
+            pw = _pack(qd, fmt, _gpu(w))
+            y = torch.full((m, n) if m > 1 else (n,), float("nan"), dtype=torch.float16, device=DEV)
+            ops.append(qd.LinearOp(pw, x_gpu, y, gid))
+            meta.append((pname, w, x))
+        gid += 1
+    return ops, meta
+
+
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("int8_b32", 16)])
+def test_stack_parity(qd, fmt, m):
+    ops, meta = _tiny_decoder_ops(qd, fmt, m)
+    qd.decode_linear_stack(ops, m)
+    for op, (pname, w, x) in zip(ops, meta):
+        y = _host(op.y)
+        parts = _oracle_parts(fmt, w)
+        y_ref = linear.ref_linear(fmt, parts, x)
+        rmax = linear.row_max_abs(fmt, parts)
+        if m == 1:
+            check_vector(y, y_ref[0] if y_ref.ndim == 2 else y_ref, rmax, x[0], pname)
+        else:
+            for i in range(m):
+                check_vector(y[i], y_ref[i], rmax, x[i], f"{pname} row {i}")
+
+
+def test_stack_chain_respects_order(qd):
+    """A chain where each op reads the previous op's output: correct only if
+    every group starts after the one before it has finished.  Outputs are
+    poisoned with NaN first, so reading too early cannot pass."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 1024
+    ws = [si.weights(si.seed_for("chain", i), k, k) for i in range(4)]
+    x0 = si.activations(si.seed_for("chain-x"), 1, k)[0]
+    pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
+    bufs = [_gpu(x0)] + [torch.full((k,), float("nan"), dtype=torch.float16, device=DEV)
+                         for _ in ws]
+    ops = [LinearOp(pws[i], bufs[i], bufs[i + 1], i) for i in range(len(ws))]
+    for rep in range(3):
+        for b in bufs[1:]:
+            b.fill_(float("nan"))
+        qd.decode_linear_stack(ops, 1)
+        oracle_ops = [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[0]), "x": x0}]
+        oracle_ops += [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[i]), "x_from": i - 1}
+                       for i in range(1, len(ws))]
+        refs = linear.ref_stack(oracle_ops)
+        x_in = x0.astype(np.float64)
+        for i, ref in enumerate(refs):
+            y = _host(bufs[i + 1])
+            parts = oracle_ops[i]["parts"]
+            rmax = linear.row_max_abs("int8_b32", parts)
+            # depth i inherits the fp16 rounding of i earlier outputs: bound grows linearly
+            check_vector(y, ref, (i + 1) * rmax, x_in, f"chain step {i}")
+            x_in = ref.astype(np.float16)
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+FULL = [("q", 4096, 4096), ("down", 4096, 12288), ("head", 151936, 4096)]
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("name,n,k", FULL)
+def test_full_size_sampled(qd, fmt, name, n, k):
+    """8B-shaped matrices at full size, in the launch configuration the bench
+    uses; packing and outputs checked on sampled row-groups."""
+    seed = si.matrix_seed("qwen3-8b", f"L0.{name}" if name != "head" else "head")
+    w_gpu = si.weights_torch(seed, n, k, DEV)
+    pw = _pack(qd, fmt, w_gpu)
+    x = si.activations(si.seed_for("full-x", name), 1, k)[0]
+    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    y = _host(fn(pw, _gpu(x)))
+    rng = np.random.default_rng(3)
+    R = -(-n // 16)
+    rgs = sorted(set([0, R - 1] + list(rng.choice(R, 6, replace=False))))
+    for r in rgs:
+        rows = np.arange(16 * r, min(n, 16 * r + 16))
+        w_rows = w_gpu[rows[0]:rows[-1] + 1].cpu().numpy()
+        parts = _oracle_parts(fmt, w_rows)
+        want = _oracle_blob(fmt, parts)
+        got = _host(pw.blob[layout.row_group_slice(fmt, n, k, r)])
+        assert np.array_equal(got, want), f"row-group {r} bytes differ"
+        y_ref = linear.ref_linear(fmt, parts, x)
+        check_vector(y[rows], y_ref, linear.row_max_abs(fmt, parts), x, f"{name} rg {r}")
+    del w_gpu
+    torch.cuda.empty_cache()
