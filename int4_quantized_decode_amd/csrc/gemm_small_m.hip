@@ -13,32 +13,10 @@
 // waves in LDS.  The path stays bound by the weight stream: at m = 16 each
 // weight byte feeds 32 flops.
 #include "qd_internal.h"
+#include "tiles.h"
 
 namespace qd {
 namespace {
-
-constexpr int kDescWord3 = 0x00020000;
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kDescWord3);
-}
-
-__device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-__device__ inline half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-// 8 int8 codes (k order) -> 8 exact fp16 values.
-__device__ inline half8_t codes_to_half8(uint32_t d0, uint32_t d1) {
-  const uint32_t u0 = d0 ^ 0x80808080u, u1 = d1 ^ 0x80808080u;
-  const half2_t bias = {(half_t)-1152.0f, (half_t)-1152.0f};
-  const half2_t q01 = as_h2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) + bias;
-  const half2_t q23 = as_h2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) + bias;
-  const half2_t q45 = as_h2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) + bias;
-  const half2_t q67 = as_h2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) + bias;
-  return (half8_t){q01[0], q01[1], q23[0], q23[1], q45[0], q45[1], q67[0], q67[1]};
-}
 
 struct Owner {
   const uint8_t* blob;

@@ -19,121 +19,10 @@
 //   * per-row partial sums are reduced across the 4 lanes of a row with lane
 //     shuffles, then across waves through LDS, and rounded once to fp16.
 #include "qd_internal.h"
+#include "tiles.h"
 
 namespace qd {
 namespace {
-
-constexpr int kDescWord3 = 0x00020000;   // raw buffer, gfx9-family data format
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kDescWord3);
-}
-
-__device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-__device__ inline half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-// sum_{i<8} q_i x_i for 8 int8 codes in (d0, d1) (k order) and 8 fp16 x.
-// Each code byte b is biased to b ^ 0x80 = q + 128 and permuted under the
-// fp16 exponent byte 0x64, giving the exact fp16 value 1024 + 128 + q; one
-// packed subtraction of 1152 leaves q exactly.
-__device__ inline float dot8_int8(uint32_t d0, uint32_t d1, half8_t x, float acc) {
-  const uint32_t u0 = d0 ^ 0x80808080u, u1 = d1 ^ 0x80808080u;
-  const half2_t bias = {(half_t)-1152.0f, (half_t)-1152.0f};
-  const half2_t q01 = as_h2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) + bias;
-  const half2_t q23 = as_h2(__builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) + bias;
-  const half2_t q45 = as_h2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) + bias;
-  const half2_t q67 = as_h2(__builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) + bias;
-  acc = __builtin_amdgcn_fdot2(q01, (half2_t){x[0], x[1]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(q23, (half2_t){x[2], x[3]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(q45, (half2_t){x[4], x[5]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(q67, (half2_t){x[6], x[7]}, acc, false);
-  return acc;
-}
-
-// sum_{i<8} (1024 + c_i) x_i for one int4 word (nibble p holds code
-// k0 + (0,2,4,6,1,3,5,7)[p]), so each and-or yields the pair (k0+2t, k0+2t+1).
-__device__ inline float dot8_int4_biased(uint32_t w, half8_t x, float acc) {
-  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
-  const half2_t c01 = as_h2((w & m) | e);
-  const half2_t c23 = as_h2(((w >> 4) & m) | e);
-  const half2_t c45 = as_h2(((w >> 8) & m) | e);
-  const half2_t c67 = as_h2(((w >> 12) & m) | e);
-  acc = __builtin_amdgcn_fdot2(c01, (half2_t){x[0], x[1]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c23, (half2_t){x[2], x[3]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c45, (half2_t){x[4], x[5]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c67, (half2_t){x[6], x[7]}, acc, false);
-  return acc;
-}
-
-struct Tile8 {
-  u32x4 c[4];
-  u32x4 sc;
-};
-
-struct Tile4 {
-  u32x4 c[2];
-  u32x4 meta;
-};
-
-__device__ inline Tile8 load_tile8(__amdgpu_buffer_rsrc_t r, int j, int lane) {
-  const uint32_t t = (uint32_t)j * kTileBytes8;
-  Tile8 T;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) T.c[s] = bload16(r, t + 1024 * s + 16 * lane);
-  T.sc = bload16(r, t + kMetaOffset8 + 16 * (lane & 15));
-  return T;
-}
-
-__device__ inline Tile4 load_tile4(__amdgpu_buffer_rsrc_t r, int j, int lane) {
-  const uint32_t t = (uint32_t)j * kTileBytes4;
-  Tile4 T;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) T.c[s] = bload16(r, t + 1024 * s + 16 * lane);
-  T.meta = bload16(r, t + kMetaOffset4 + 16 * (lane & 15));
-  return T;
-}
-
-// Lane (g, rho)'s share of one int8 tile: row rho, K quarter g, 8 blocks.
-__device__ inline float tile_dot8(const Tile8& T, const half_t* xs_j, int g, float acc) {
-  const half8_t scales = __builtin_bit_cast(half8_t, T.sc);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const half8_t xv = *reinterpret_cast<const half8_t*>(xs_j + 64 * s + 32 * h + 8 * g);
-      const float p = dot8_int8(T.c[s][2 * h], T.c[s][2 * h + 1], xv, 0.0f);
-      acc = __builtin_fmaf((float)scales[2 * s + h], p, acc);
-    }
-  }
-  return acc;
-}
-
-// Lane (g, rho)'s share of one int4 tile: 4 groups x 16 codes.
-// y += s * sum (1024 + c) x + (m - 1024 s) * sum x  ==  sum (m + c s) x.
-__device__ inline float tile_dot4(const Tile4& T, const half_t* xs_j, const float* xsum_j, int g,
-                                  float acc) {
-  const half8_t meta = __builtin_bit_cast(half8_t, T.meta);
-  const float4_t xsum = *reinterpret_cast<const float4_t*>(xsum_j + 4 * g);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int gam = 2 * s + h;
-      const half_t* xp = xs_j + 64 * gam + 16 * g;
-      const half8_t xa = *reinterpret_cast<const half8_t*>(xp);
-      const half8_t xb = *reinterpret_cast<const half8_t*>(xp + 8);
-      float p = dot8_int4_biased(T.c[s][2 * h], xa, 0.0f);
-      p = dot8_int4_biased(T.c[s][2 * h + 1], xb, p);
-      const float sc = (float)meta[gam], mn = (float)meta[4 + gam];
-      acc = __builtin_fmaf(sc, p, acc);
-      acc = __builtin_fmaf(__builtin_fmaf(-1024.0f, sc, mn), xsum[gam], acc);
-    }
-  }
-  return acc;
-}
 
 // Resolve which member matrix owns row-group `rg` (selects, no indexing).
 struct Owner {

@@ -88,40 +88,3 @@ hipError_t launch_groups(const std::vector<StackGroup>& groups, hipStream_t s) {
 
 }  // namespace qd
 
-// Plan: the validated group list, replayed on each run.
-struct qd_stack_plan {
-  std::vector<qd::StackGroup> groups;
-  int device;
-};
-
-namespace qd {
-
-qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out) {
-  std::vector<StackGroup> groups;
-  qd_status st = build_groups(ops, n_ops, m, &groups);
-  if (st != QD_OK) return st;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return QD_EDEVICE;
-  qd_stack_plan* p = new (std::nothrow) qd_stack_plan;
-  if (!p) return QD_ELAUNCH;
-  p->groups = std::move(groups);
-  p->device = dev;
-  *out = p;
-  return QD_OK;
-}
-
-qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return QD_EDEVICE;
-  return launch_groups(plan->groups, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
-}
-
-qd_status plan_error(qd_stack_plan* plan, int32_t* out_error) {
-  (void)plan;
-  *out_error = 0;
-  return QD_OK;
-}
-
-void plan_destroy(qd_stack_plan* plan) { delete plan; }
-
-}  // namespace qd

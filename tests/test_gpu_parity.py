@@ -277,3 +277,127 @@ def test_full_size_sampled(qd, fmt, name, n, k):
         check_vector(y[rows], y_ref, linear.row_max_abs(fmt, parts), x, f"{name} rg {r}")
     del w_gpu
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ persistent plan
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_plan_parity_and_determinism(qd, fmt):
+    """The persistent one-launch step: oracle parity on every output, repeated
+    runs (outputs poisoned in between) are bit-identical, no wait timed out."""
+    ops, meta = _tiny_decoder_ops(qd, fmt, 1, layers=3)
+    plan = qd.StackPlan(ops, 1)
+    first = None
+    for rep in range(3):
+        for op in ops:
+            op.y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        outs = [_host(op.y).copy() for op in ops]
+        if first is None:
+            first = outs
+            for y, (pname, w, x) in zip(outs, meta):
+                parts = _oracle_parts(fmt, w)
+                y_ref = linear.ref_linear(fmt, parts, x)[0]
+                check_vector(y, y_ref, linear.row_max_abs(fmt, parts), x[0], f"plan {pname}")
+        else:
+            for a, b in zip(first, outs):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    plan.close()
+
+
+def test_plan_chain_respects_order(qd):
+    """Each op reads the previous op's output inside one persistent launch."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 1024
+    depth = 6
+    ws = [si.weights(si.seed_for("pchain", i), k, k) for i in range(depth)]
+    x0 = si.activations(si.seed_for("pchain-x"), 1, k)[0]
+    pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
+    bufs = [_gpu(x0)] + [torch.full((k,), float("nan"), dtype=torch.float16, device=DEV)
+                         for _ in ws]
+    ops = [LinearOp(pws[i], bufs[i], bufs[i + 1], i) for i in range(depth)]
+    plan = qd.StackPlan(ops, 1)
+    oracle_ops = [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[0]), "x": x0}]
+    oracle_ops += [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[i]), "x_from": i - 1}
+                   for i in range(1, depth)]
+    refs = linear.ref_stack(oracle_ops)
+    for rep in range(3):
+        for b in bufs[1:]:
+            b.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        x_in = x0.astype(np.float64)
+        for i, ref in enumerate(refs):
+            y = _host(bufs[i + 1])
+            rmax = linear.row_max_abs("int8_b32", oracle_ops[i]["parts"])
+            check_vector(y, ref, (i + 1) * rmax, x_in, f"plan chain step {i} rep {rep}")
+            x_in = ref.astype(np.float16)
+    plan.close()
+
+
+def test_plan_ragged_and_split_groups(qd):
+    """Groups whose row-groups split across many workgroups (few rows, long K),
+    ragged tails, and groups with more row-groups than workgroups whose
+    ranges straddle member boundaries."""
+    from int4_quantized_decode_amd import LinearOp
+    shapes = [[(24, 12288)], [(37, 2048), (5, 2048), (100, 2048)], [(4000, 512)], [(16, 256)],
+              [(9, 4096)],
+              # at least one row-group per workgroup: whole-row-group ranges, several of
+              # which straddle a boundary between members
+              [(4096, 256), (1024, 256), (1024, 256)], [(2000, 512), (1000, 512), (1200, 512)]]
+    ops, meta = [], []
+    for gi, members in enumerate(shapes):
+        k = members[0][1]
+        x = si.activations(si.seed_for("ragged-x", gi), 1, k)[0]
+        xg = _gpu(x)
+        for mi, (n, kk) in enumerate(members):
+            w = si.weights(si.seed_for("ragged-w", gi, mi), n, kk)
+            y = torch.full((n,), float("nan"), dtype=torch.float16, device=DEV)
+            ops.append(LinearOp(qd.qpack_int8_b32(_gpu(w)), xg, y, gi))
+            meta.append((w, x))
+    plan = qd.StackPlan(ops, 1)
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    for op, (w, x) in zip(ops, meta):
+        parts = quant.quantize_int8_b32(w)
+        check_vector(_host(op.y), linear.ref_linear("int8_b32", parts, x),
+                     linear.row_max_abs("int8_b32", parts), x, f"ragged {w.shape}")
+    plan.close()
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1"])
+def test_plan_full_size_sampled(qd, workload):
+    """The full 8B-shaped step in the launch configuration the bench times:
+    every output finite, sampled rows of sampled projections match the oracle."""
+    import bench
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
+    plan = qd.StackPlan(ops, 1)
+    for op in ops:
+        op.y.fill_(float("nan"))
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    wl = si.WORKLOADS[workload]
+    names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
+    for op in ops:
+        assert torch.isfinite(op.y).all()
+    picks = ["L0.q", "L0.k", "L17.gate", "L17.up", "L35.down", "L35.o", "head"]
+    rng = np.random.default_rng(11)
+    for name in picks:
+        i = names.index(name)
+        op = ops[i]
+        n, k = op.w.n, op.w.k
+        rows = np.sort(rng.choice(n, 24, replace=False))
+        w_rows = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)[rows].cpu().numpy()
+        x = op.x.cpu().numpy()
+        parts = _oracle_parts(wl.fmt, w_rows)
+        y_ref = linear.ref_linear(wl.fmt, parts, x)
+        check_vector(_host(op.y)[rows], y_ref, linear.row_max_abs(wl.fmt, parts), x, name)
+    plan.close()
+    del ops
+    torch.cuda.empty_cache()
