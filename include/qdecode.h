@@ -155,22 +155,29 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
 /*
  * The same step as a persistent plan: one kernel launch per step that walks
  * every group in order, keeping the weight stream going across group
- * boundaries (weights of the next group are fetched while the previous group
- * completes; a group's activations are read only after the group before it
- * has finished).  qd_stack_plan_create validates `ops` exactly as
- * decode_linear_stack does, copies the descriptors to the device and
- * allocates the plan's scratch (counters, partial sums) once; the pointers in
- * `ops` must stay valid while the plan lives.  qd_stack_plan_run enqueues one
- * step on `stream` and allocates nothing.  A plan may be run repeatedly but
- * not concurrently.  m == 1 only.
+ * boundaries (weights of later groups are fetched while a group completes; a
+ * group's activations are read only after every op of the group before it
+ * has finished, so an op may consume an earlier op's output).
+ * qd_stack_plan_create validates `ops` exactly as decode_linear_stack does,
+ * copies the descriptors to the device and allocates the plan's scratch
+ * (completion stamps, an error word) once; the pointers in `ops` must stay
+ * valid while the plan lives.  qd_stack_plan_run enqueues one step on
+ * `stream` and allocates nothing.  A plan may be run repeatedly but not
+ * concurrently.  Steps the persistent kernel does not take (m > 1, mixed
+ * formats, a schedule larger than one CU's LDS) are replayed as the same
+ * per-group launches decode_linear_stack makes, with the same results;
+ * qd_stack_plan_is_persistent tells which.
  */
 typedef struct qd_stack_plan qd_stack_plan;
 
 qd_status qd_stack_plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out);
 qd_status qd_stack_plan_run(qd_stack_plan* plan, void* stream);
 /* Device error word of the last completed run (host reads it with a blocking
- * copy): 0 = fine, 1 = a wait timed out (the step's outputs are incomplete). */
+ * copy): 0 = fine, nonzero = a bounded wait timed out (the step's outputs are
+ * incomplete; the plan resets its scratch and can be run again). */
 qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error);
+/* *out = 1 if runs use the persistent kernel, 0 if they replay launches. */
+qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out);
 void qd_stack_plan_destroy(qd_stack_plan* plan);
 
 #ifdef __cplusplus

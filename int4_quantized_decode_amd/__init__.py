@@ -182,6 +182,14 @@ class StackPlan:
         check(lib.qd_stack_plan_error(self._h, ctypes.byref(e)), "qd_stack_plan_error")
         return e.value
 
+    @property
+    def persistent(self) -> bool:
+        """True if runs use the one-launch persistent kernel, False if they
+        replay per-group launches."""
+        v = ctypes.c_int32(0)
+        check(lib.qd_stack_plan_is_persistent(self._h, ctypes.byref(v)), "qd_stack_plan_is_persistent")
+        return bool(v.value)
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             lib.qd_stack_plan_destroy(self._h)

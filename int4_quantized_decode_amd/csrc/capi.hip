@@ -181,6 +181,12 @@ QD_EXPORT qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error)
   return plan_error(plan, out_error);
 }
 
+QD_EXPORT qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out) {
+  if (!plan || !out) return QD_EINVAL;
+  *out = plan_is_persistent(plan) ? 1 : 0;
+  return QD_OK;
+}
+
 QD_EXPORT void qd_stack_plan_destroy(qd_stack_plan* plan) { plan_destroy(plan); }
 
 // ---- validation helpers shared with stack.hip --------------------------------

@@ -7,25 +7,28 @@
 // weight stream keeps going across group boundaries:
 //
 //   * one workgroup per CU (cooperative launch, all co-resident), 16 waves:
-//     15 compute waves and 1 control wave.  The workgroup's share of every
-//     group's schedule lives in LDS, so no wave waits on a memory round trip
-//     to find its next tiles;
+//     streaming compute waves, reserve compute waves and 1 control wave.  The
+//     workgroup's share of every group's schedule lives in LDS, so no wave
+//     waits on a memory round trip to find its next tiles;
 //   * a group's tiles (row-group major) are split into one range per
 //     workgroup, on row-group boundaries whenever the group has at least one
-//     row-group per workgroup; each compute wave takes a contiguous part of
-//     the range;
-//   * each compute wave keeps a ring of D tiles in registers, reloading a
-//     slot as soon as it is consumed and following its tile sequence across
-//     group boundaries, so weights of the next groups are in flight while the
-//     current group completes;
-//   * a group's activation vector is read only after every workgroup has
-//     published that it finished the group before (one completion stamp per
-//     workgroup, polled with a single 2 KiB read), so an op may consume an
-//     earlier op's output;
-//   * compute waves issue no global stores or atomics.  Per-wave row partial
-//     sums go to LDS; the control wave reduces them, writes outputs, combines
-//     row-groups split across workgroups (fixed-order sums: deterministic),
-//     publishes completion and stages the next activation vector.
+//     row-group per workgroup; compute waves take tiles of the workgroup's
+//     sequence from an LDS counter, in order, across group boundaries;
+//   * a streaming wave keeps a ring of tiles in registers and refills a slot
+//     as soon as it is consumed.  Its loads are accepted only as fast as
+//     memory delivers, so at a group boundary its ring holds landed data and
+//     it has nothing more to issue; reserve waves hold no tiles until the
+//     workgroup has computed every tile of a group and then issue the next
+//     tiles while the device synchronises, so memory keeps streaming;
+//   * compute waves write each tile's row partials to their own LDS slot and
+//     count the tile against its row-group; the control wave reduces and
+//     stores each row-group as soon as it is complete (fixed-order sums:
+//     deterministic), publishes that the workgroup has finished the group
+//     (one completion stamp per workgroup), waits until every workgroup has
+//     published it, then stages the next activation vector straight into LDS
+//     and releases the compute waves (one barrier per group), so an op may
+//     consume an earlier op's output;
+//   * compute waves issue no global stores or atomics.
 //
 // Data another workgroup reads (outputs, split-row-group partials, stamps) is
 // written with device-coherent stores and read with device-coherent loads,
@@ -48,8 +51,27 @@ namespace qd {
 namespace {
 
 constexpr int kWaves = 16;
-constexpr int kWc = 15;                 // compute waves
+#ifndef QD_PLAN_RESERVE_WAVES8
+#define QD_PLAN_RESERVE_WAVES8 7
+#endif
+#ifndef QD_PLAN_RESERVE_WAVES4
+#define QD_PLAN_RESERVE_WAVES4 0
+#endif
+#ifndef QD_PLAN_RESERVE_SLOTS8
+#define QD_PLAN_RESERVE_SLOTS8 5
+#endif
+#ifndef QD_PLAN_RESERVE_SLOTS4
+#define QD_PLAN_RESERVE_SLOTS4 4
+#endif
 constexpr int kCtl = 15;                // the control wave
+// Compute waves that load only while the workgroup stalls (the rest stream
+// continuously).  int4 tiles cost twice the arithmetic per byte, and there
+// the streaming waves need every slot.
+template <int FMT>
+constexpr int kReserve = FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_WAVES8 : QD_PLAN_RESERVE_WAVES4;
+template <int FMT>
+constexpr int kMain = kCtl - kReserve<FMT>;
+static_assert(kMain<QD_FMT_INT8_B32> >= 1 && kMain<QD_FMT_INT4_G64> >= 1, "wave roles");
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
 
 struct PGroup {         // 32 bytes
@@ -69,15 +91,13 @@ struct PMember {        // 32 bytes
   int32_t pad;
 };
 
-struct PSched {         // 32 bytes: one workgroup's part of one group
-  int32_t a, b;         // tile range [a, b)
-  int32_t wf0, nc0;     // first row-group: first contributing workgroup, contributors
-  int32_t wf1, nc1;     // last row-group: same
+struct PSched {         // 16 bytes: one workgroup's part of one group
+  int32_t a, b;         // tile range [a, b): whole row-groups
   int32_t off;          // tiles of this workgroup in the groups before this one
-  int32_t rg0;          // a / J: first row-group touched
+  int32_t rg0;          // a / J: first row-group
 };
 
-static_assert(sizeof(PGroup) == 32 && sizeof(PMember) == 32 && sizeof(PSched) == 32,
+static_assert(sizeof(PGroup) == 32 && sizeof(PMember) == 32 && sizeof(PSched) == 16,
               "schedule records are copied to LDS in 16-byte units");
 
 struct PlanArgs {
@@ -85,15 +105,15 @@ struct PlanArgs {
   const PMember* members;     // [nmem]
   const PSched* sched;        // [ngroups][G]
   unsigned long long* flags;  // [G] completion stamps
-  unsigned long long* slots;  // [G][2][16] split-row-group partials: (stamp << 32) | float bits
   uint32_t* err;
   unsigned long long epoch;   // runs so far, including this one
   int32_t ngroups;
   int32_t nmem;
   int32_t G;
-  int32_t x_bytes;            // LDS layout: x | xsum | red | groups | members | sched
+  int32_t x_bytes;            // LDS layout: x | xsum | red | cnt | groups | members | sched
   int32_t xsum_bytes;
   int32_t red_bytes;
+  int32_t cnt_bytes;
   int32_t tab_bytes;
 };
 
@@ -158,6 +178,7 @@ struct TileRef {
   int g;      // group (ngroups: no tile)
   int j;      // super-block within the row
   int rel;    // tile index relative to the first row-group of the range (t - rg0 J)
+  int seg;    // row-group relative to the first row-group of the range
 };
 
 struct IssueCursor {
@@ -171,10 +192,12 @@ struct IssueCursor {
 template <int FMT>
 __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngroups, int total,
                                                          uint32_t* next, IssueCursor& c,
-                                                         TileRef& ref, int lane) {
+                                                         TileRef& ref, int lane, bool take = true) {
   constexpr int T = Fmt<FMT>::kT;
-  uint32_t got = 0;
-  if (lane == 0) got = atomicAdd(next, 1u);
+  // take == false: claim nothing; the load below then reads an empty buffer
+  // (zeros, no memory traffic), which keeps the caller's control flow uniform.
+  uint32_t got = (uint32_t)total;
+  if (take && lane == 0) got = atomicAdd(next, 1u);
   const int idx = uni((int)got);
   const uint8_t* base = nullptr;
   uint32_t nbytes = 0;
@@ -205,8 +228,20 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
     ref.g = c.g;
     ref.j = c.j;
     ref.rel = t - c.rg0 * c.J;
+    ref.seg = c.rg - c.rg0;
   }
   return Fmt<FMT>::load(make_rsrc(base, nbytes), lane);
+}
+
+// Reserve-wave pacing, in ticks of the 100 MHz real-time counter per tile:
+// kT / 256 ticks per tile is 25.6 GB/s per CU, about one CU's share of the
+// HBM bandwidth; QD_PLAN_PACE_PCT scales that rate.
+#ifndef QD_PLAN_PACE_PCT
+#define QD_PLAN_PACE_PCT 250
+#endif
+template <int FMT>
+__device__ __forceinline__ uint32_t pace_ticks(int k) {
+  return (uint32_t)(((int64_t)k * Fmt<FMT>::kT * 100) / (256 * QD_PLAN_PACE_PCT));
 }
 
 template <int FMT>
@@ -232,47 +267,102 @@ __device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const
     asm volatile("" ::: "memory");      \
   } while (0)
 
-template <int FMT, int D>
+// Compute waves come in two kinds.
+//
+// A streaming wave keeps a ring of D tiles and refills a slot as soon as it is
+// consumed, following the workgroup's tile sequence across group boundaries.
+// Its loads are accepted by the memory pipeline only as fast as memory
+// delivers, so when the workgroup stalls at a group boundary (the next
+// group's activations need every workgroup to finish), its ring already holds
+// landed data and it has nothing more to issue: on its own the weight stream
+// would idle for the length of the stall.
+//
+// A reserve wave holds no tiles while the stream runs.  When the workgroup has
+// computed every tile of a group (the control wave says so through `stalled`),
+// it takes the next S tiles of the sequence and issues them, so memory keeps
+// streaming while the workgroup synchronises; it computes them once their
+// group's activations are staged, then waits for the next stall.
+//
+// Both wait for "activations of group g staged" (one workgroup barrier per
+// group).  After each tile a wave writes the tile's 16 row partials to their
+// own LDS slot and counts the tile against its row-group, so the control wave
+// can finish a row-group as soon as its last tile is in.
+template <int FMT, int D, bool RESERVE>
 __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint32_t* next,
-                             int lane, const half_t* xs, const float* xsum, float* red) {
-  (void)p;
+                             int lane, const half_t* xs, const float* xsum, float* red,
+                             uint32_t* cnt, const int* stalled, const int* staged) {
   using Tile = typename Fmt<FMT>::Tile;
   const int ng = p.ngroups;
   const int g4 = lane >> 4;
   IssueCursor ic{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0};
   Tile ring[D];
   TileRef ref[D];
-#pragma unroll
-  for (int s = 0; s < D; ++s) {
-    ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane);
-    QD_PIN_ISSUE();
-  }
-  // Barriers: "activations staged" on entering a group, "group done" on
-  // leaving it; every wave passes both for every group, in order.
-  int cg = -1;
+  int cg = -1;                      // last group whose activations this wave has waited for
   auto settle_to = [&](int g) {
     while (cg < g) {
-      if (cg >= 0) wg_barrier();
       ++cg;
       if (cg < ng) wg_barrier();
     }
   };
-  // Each tile's row partials go to their own LDS slot: the sum over tiles is
-  // then taken in a fixed order, whichever wave computed which tile.
-  // The ring is consumed and refilled in slot order with a single loop exit,
-  // so each compute waits only for its own slot's loads.
-  for (;;) {
+  auto compute = [&](const Tile& t, const TileRef& r) {
+    settle_to(r.g);
+    const float part = quad_reduce(tile_dot<FMT>(t, xs, xsum, r.j, g4, 0.0f));
+    if (lane < 16) red[r.rel * 16 + lane] = part;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_fetch_add(cnt + r.seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  if (!RESERVE) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      if (ref[s].g < ng) {
-        settle_to(ref[s].g);
-        const float part = quad_reduce(tile_dot<FMT>(ring[s], xs, xsum, ref[s].j, g4, 0.0f));
-        if (lane < 16) red[ref[s].rel * 16 + lane] = part;
-      }
       ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane);
       QD_PIN_ISSUE();
     }
-    if (ref[0].g >= ng) break;     // slot 0 was refilled first: nothing left for later slots
+    // The ring is consumed and refilled in slot order with a single loop
+    // exit, so each compute waits only for its own slot's loads.
+    for (;;) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        if (ref[s].g < ng) compute(ring[s], ref[s]);
+        ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane);
+        QD_PIN_ISSUE();
+      }
+      if (ref[0].g >= ng) break;   // slot 0 was refilled first: nothing left for later slots
+    }
+  } else {
+    const volatile int* st = stalled;
+    const volatile int* sg = staged;
+    const int r = uni((int)(threadIdx.x >> 6)) - kMain<FMT>;   // rank among reserve waves
+    int trig = 0;                   // issue at the stall that ends group `trig`
+    for (;;) {
+      // Pass the barrier of group `trig` first: the control wave reaches the
+      // next barrier only after the stall of `trig`, so this wait holds up
+      // no barrier.
+      settle_to(trig);
+      for (uint32_t spins = 0; *st < trig && spins < kSpinLimit; ++spins) __builtin_amdgcn_s_sleep(1);
+      // Issue at a bounded rate rather than all at once (the control wave's
+      // stores and loads on the boundary's critical path queue behind what
+      // the CU has in flight), and only while the stall lasts: once the next
+      // activations are staged the streaming waves are loading again.
+      const uint32_t t0 = (uint32_t)__builtin_amdgcn_s_memrealtime();
+      bool stop = false, exhausted = false;
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        const uint32_t due = t0 + pace_ticks<FMT>(s * kReserve<FMT> + r);
+        while (!stop && (int32_t)((uint32_t)__builtin_amdgcn_s_memrealtime() - due) < 0) {
+          stop = *sg > trig;
+          if (!stop) __builtin_amdgcn_s_sleep(2);
+        }
+        stop = stop || *sg > trig;
+        ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane, !stop);
+        exhausted = exhausted || (!stop && ref[s].g >= ng);
+        QD_PIN_ISSUE();
+      }
+#pragma unroll
+      for (int s = 0; s < D; ++s)
+        if (ref[s].g < ng) compute(ring[s], ref[s]);
+      if (exhausted) break;         // the sequence is used up
+      trig = cg > trig ? cg : trig + 1;
+    }
   }
   settle_to(ng);
 }
@@ -286,36 +376,30 @@ __device__ __forceinline__ unsigned long long stamp(const PlanArgs& p, int g) {
 }
 
 // Stage a group's activation vector (and, for int4, its 16-value run sums) in
-// LDS.  All loads of a batch are issued before any is consumed, so staging
-// costs about one memory round trip per 8 KiB.
+// LDS.  Each load moves 64 lanes x 16 bytes straight from memory into LDS (no
+// registers), all issued before the single wait, so staging costs one memory
+// round trip whatever K is; past K the buffer reads zeros.
 template <int FMT>
-__device__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs, float* xsum) {
-  constexpr int kBatch = 8;
+__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
+                                              float* xsum) {
   const int Kp = S.J(g) * kSuperK;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), (uint32_t)(S.k(g) * 2));
-  for (int i0 = 0; i0 < Kp; i0 += 64 * 8 * kBatch) {
-    u32x4 v[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int i = i0 + (b * 64 + lane) * 8;
-      v[b] = bload16_coherent(rx, (uint32_t)min(i, Kp) * 2);   // past K: zeros
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int i = i0 + (b * 64 + lane) * 8;
+  for (int i = 0; i < Kp; i += 512)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rx, (__attribute__((address_space(3))) void*)(xs + i), 16, (uint32_t)(i * 2 + lane * 16), 0,
+        0, kPolicyCoherent);
+  wait_stores();                                   // vmcnt(0): the data is in LDS
+  if (FMT == QD_FMT_INT4_G64) {
+    for (int i0 = 0; i0 < Kp; i0 += 512) {
+      const int i = i0 + lane * 8;
+      const half8_t h = *reinterpret_cast<const half8_t*>(xs + i);
       float sum = 0.0f;
-      if (FMT == QD_FMT_INT4_G64) {
-        const half8_t h = __builtin_bit_cast(half8_t, v[b]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += (float)h[e];
-        sum += __shfl_xor(sum, 1);        // lanes 2q, 2q+1 hold one 16-value run
-      }
-      if (i < Kp) {
-        *reinterpret_cast<u32x4*>(xs + i) = v[b];
-        if (FMT == QD_FMT_INT4_G64 && (lane & 1) == 0) {
-          const int t = i >> 4, jj = t >> 4, within = t & 15;
-          xsum[16 * jj + 4 * (within & 3) + (within >> 2)] = sum;
-        }
+      for (int e = 0; e < 8; ++e) sum += (float)h[e];
+      sum += __shfl_xor(sum, 1);                   // lanes 2q, 2q+1 hold one 16-value run
+      if ((lane & 1) == 0 && i < Kp) {
+        const int t = i >> 4, jj = t >> 4, within = t & 15;
+        xsum[16 * jj + 4 * (within & 3) + (within >> 2)] = sum;
       }
     }
   }
@@ -333,79 +417,45 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Reduce the compute waves' partials of group g, write finished rows, and
-// combine row-groups split across workgroups.  A split row-group's partial
-// travels as one 8-byte word per row holding the partial and the group's
-// stamp, so it needs no separate flag: the last contributor of the row-group
-// polls the others' words until every stamp is current, then adds them in
-// workgroup order (deterministic) to its own partial and writes the rows.
-__device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, int lane,
-                             const float* red) {
-  const int a = S.a(g), b = S.b(g);
-  if (a >= b) return;
-  const int J = S.J(g);
-  const int rg0 = a / J, nseg = (b - 1) / J - rg0 + 1;
-  const int row = lane & 15;
-  const bool first_split = (a != rg0 * J) || (b < (rg0 + 1) * J);
-  const int rgl = rg0 + nseg - 1;
-  const bool last_split = nseg > 1 && (b != (rgl + 1) * J);
-  const uint32_t st = (uint32_t)stamp(p, g);
-  float own[2] = {0.0f, 0.0f};                 // this workgroup's partials of split row-groups
-  for (int s0 = 0; s0 < nseg; s0 += 4) {
-    const int s = s0 + (lane >> 4);
-    float sum = 0.0f;
-    bool split = false;
-    if (s < nseg) {
-      // Tiles of row-group rg0 + s inside [a, b), summed in tile order.
-      const int rg = rg0 + s;
-      const int r0 = max(a, rg * J) - rg0 * J, r1 = min(b, (rg + 1) * J) - rg0 * J;
-      for (int r = r0; r < r1; ++r) sum += red[r * 16 + row];
-      split = (s == 0 && first_split) || (s == nseg - 1 && s > 0 && last_split);
-      if (!split) store_row(S, g, rg, row, sum);
+// Spin (bounded) until the compute waves have counted `want` tiles against
+// row-group slot `seg`.  After one timed-out wait (an error) later waits are
+// skipped.
+__device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cnt, int seg,
+                                           uint32_t want, bool& dead) {
+  const volatile uint32_t* c = cnt + seg;
+  for (uint32_t spins = 0; !dead && *c < want; ++spins) {
+    if (spins > kSpinLimit) {
+      atomicOr(p.err, 2u);
+      dead = true;
     }
-    // Bring the split partials (lanes 0..15 for the first segment, the lanes
-    // of segment nseg-1 for the last) to lanes 0..15.
-    if (s0 == 0) own[0] = first_split ? sum : 0.0f;
-    const int last_lane0 = ((nseg - 1) - s0) * 16;
-    if (last_split && last_lane0 >= 0 && last_lane0 < 64) own[1] = __shfl(sum, last_lane0 + row);
+    __builtin_amdgcn_s_sleep(1);
   }
-  const PSched* ms = S.s + g;
-  for (int side = 0; side < 2; ++side) {
-    if (side == 0 ? !first_split : !last_split) continue;
-    const int wf = uni(side == 0 ? ms->wf0 : ms->wf1), nc = uni(side == 0 ? ms->nc0 : ms->nc1);
-    const int wl = wf + nc - 1;
-    const int rg = side == 0 ? rg0 : rgl;
-    if (w != wl) {
-      // Hand the partial to the last contributor.
-      if (lane < 16) {
-        const unsigned long long word =
-            ((unsigned long long)st << 32) | __builtin_bit_cast(uint32_t, own[side]);
-        __hip_atomic_store(p.slots + ((size_t)w * 2 + side) * 16 + row, word, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-      continue;
-    }
-    float sum = 0.0f;
-    for (int c = wf; c < wl; ++c) {
-      const int ca = p.sched[(size_t)g * p.G + c].a;        // contributor's first tile
-      const int cside = (rg == ca / J) ? 0 : 1;
-      const unsigned long long* src = p.slots + ((size_t)c * 2 + cside) * 16 + row;
-      unsigned long long word = 0;
-      uint32_t spins = 0;
-      for (;;) {
-        word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool ready = (uint32_t)(word >> 32) == st || lane >= 16;
-        if (__ballot(!ready) == 0ull) break;
-        if (++spins > kSpinLimit ||
-            __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-          if (lane == 0) atomicOr(p.err, 1u);
-          break;
-        }
-      }
-      sum += __builtin_bit_cast(float, (uint32_t)word);
-    }
-    sum += own[side];
-    if (lane < 16) store_row(S, g, rg, row, sum);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Reduce the compute waves' partials of group g row-group by row-group, as
+// each row-group's last tile is counted, and write its rows.  The sum over a
+// row-group's tiles is taken in a fixed order (tiles t = q mod 4 per
+// quarter-wave, then the four quarters), whichever wave computed which tile,
+// so results are deterministic.
+__device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
+                             uint32_t* cnt, int* stalled, bool& dead) {
+  const int a = S.a(g), b = S.b(g);
+  if (a >= b) {
+    if (lane == 0) *reinterpret_cast<volatile int*>(stalled) = g;
+    return;
+  }
+  const int J = S.J(g);
+  const int rg0 = a / J, nseg = (b - a) / J;
+  const int row = lane & 15, q = lane >> 4;
+  for (int s = 0; s < nseg; ++s) {
+    wait_count(p, cnt, s, (uint32_t)J, dead);
+    if (s == nseg - 1 && lane == 0) *reinterpret_cast<volatile int*>(stalled) = g;   // every tile of g is in
+    float part = 0.0f;
+    for (int r = s * J + q; r < (s + 1) * J; r += 4) part += red[r * 16 + row];
+    const float sum = quad_reduce(part);
+    if (lane == 0) cnt[s] = 0u;                // ready for the next group
+    if (lane < 16) store_row(S, g, rg0 + s, row, sum);
   }
 }
 
@@ -443,19 +493,22 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
 
 template <int FMT>
 __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane, half_t* xs,
-                             float* xsum, float* red) {
+                             float* xsum, const float* red, uint32_t* cnt, int* stalled,
+                             int* staged) {
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
   stage_group_x<FMT>(S, 0, lane, xs, xsum);
+  wg_barrier();                   // activations of group 0 staged
+  bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
-    wg_barrier();                 // activations of g staged
-    wg_barrier();                 // compute waves finished g
-    finish_group(p, S, g, w, lane, red);
+    finish_group(p, S, g, lane, red, cnt, stalled, dead);
     publish(p, g, w, lane);
     if (g + 1 < p.ngroups) {
       wait_group(p, g, lane);
       stage_group_x<FMT>(S, g + 1, lane, xs, xsum);
+      if (lane == 0) *reinterpret_cast<volatile int*>(staged) = g + 1;
+      wg_barrier();               // activations of g + 1 staged
     }
   }
 }
@@ -466,8 +519,11 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   half_t* xs = reinterpret_cast<half_t*>(smem);
   float* xsum = reinterpret_cast<float*>(smem + p.x_bytes);
   float* red = reinterpret_cast<float*>(smem + p.x_bytes + p.xsum_bytes);
-  uint8_t* tab = smem + p.x_bytes + p.xsum_bytes + p.red_bytes;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + p.x_bytes + p.xsum_bytes + p.red_bytes);
+  uint8_t* tab = smem + p.x_bytes + p.xsum_bytes + p.red_bytes + p.cnt_bytes;
   uint32_t* next = reinterpret_cast<uint32_t*>(tab + p.tab_bytes);   // tile hand-out counter
+  int* stalled = reinterpret_cast<int*>(next + 1);   // last group whose tiles are all computed
+  int* staged = reinterpret_cast<int*>(next + 2);    // last group whose activations are staged
   const int w = blockIdx.x;
   const int wave = uni(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -484,32 +540,44 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
     const u32x4* gsrc = reinterpret_cast<const u32x4*>(p.groups);
     const u32x4* msrc = reinterpret_cast<const u32x4*>(p.members);
     const int ng16 = p.ngroups * 2, nm16 = p.nmem * 2;     // 16-byte units
-    for (int i = threadIdx.x; i < ng16 + nm16 + ng16; i += kWaves * 64) {
+    for (int i = threadIdx.x; i < ng16 + nm16 + p.ngroups; i += kWaves * 64) {
       u32x4 val;
       if (i < ng16) val = gsrc[i];
       else if (i < ng16 + nm16) val = msrc[i - ng16];
-      else {
-        const int q = i - ng16 - nm16, gi = q >> 1, half = q & 1;
-        val = reinterpret_cast<const u32x4*>(p.sched + (size_t)gi * p.G + w)[half];
-      }
+      else val = *reinterpret_cast<const u32x4*>(p.sched + (size_t)(i - ng16 - nm16) * p.G + w);
       dst[i] = val;
     }
-    if (threadIdx.x == 0) *next = 0u;
+    if (threadIdx.x == 0) {
+      *next = 0u;
+      *stalled = -1;
+      *staged = 0;
+    }
+    for (int i = threadIdx.x; i < p.cnt_bytes / 4; i += kWaves * 64) cnt[i] = 0u;
   }
   __syncthreads();
 
   if (wave == kCtl) {
-    control_wave<FMT>(p, S, w, lane, xs, xsum, red);
+    control_wave<FMT>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
   } else {
     const int last = p.ngroups - 1;
     const int total = S.off(last) + S.b(last) - S.a(last);
-    compute_wave<FMT, D>(p, S, total, next, lane, xs, xsum, red);
+    if (wave < kMain<FMT>)
+      compute_wave<FMT, D, false>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+    else
+      compute_wave<FMT, FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_SLOTS8 : QD_PLAN_RESERVE_SLOTS4, true>(
+          p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-constexpr int kRing8 = 3;
-constexpr int kRing4 = 4;
+#ifndef QD_PLAN_RING8
+#define QD_PLAN_RING8 3
+#endif
+#ifndef QD_PLAN_RING4
+#define QD_PLAN_RING4 4
+#endif
+constexpr int kRing8 = QD_PLAN_RING8;
+constexpr int kRing4 = QD_PLAN_RING4;
 
 }  // namespace
 
@@ -603,58 +671,43 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   std::vector<PMember> pm;
   std::vector<PSched> ps((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
-  int maxJ = 1, maxRel = 1;
-  std::vector<int64_t> s(G + 1);
+  int maxJ = 1, maxRel = 1, maxSeg = 1;
+  // A step the persistent walker cannot hold (tile counts past int32, LDS
+  // beyond one CU's) replays per-group launches instead.
+  auto fallback = [&]() {
+    plan->replay = std::move(replay);
+    *out = plan;
+    return QD_OK;
+  };
   for (int g = 0; g < ng; ++g) {
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
-    if (T > (int64_t)INT32_MAX / 2) {
-      delete plan;
-      return QD_ESHAPE;
-    }
+    if (T > (int64_t)INT32_MAX / 2) return fallback();
     pg[g] = PGroup{hg.x, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size()};
     for (const PMember& mm : hg.mem) pm.push_back(mm);
     maxJ = std::max(maxJ, hg.J);
-    // Tile ranges per workgroup: whole row-groups when that splits the group
-    // evenly to within 5% (no cross-workgroup combine), else an even split of
-    // tiles.
-    if (R >= G && (R + G - 1) / G * G * 20 <= R * 21) {
-      for (int w = 0; w <= G; ++w) s[w] = (int64_t)w * R / G * J;
-    } else {
-      const int64_t Gg = std::min<int64_t>(G, T);
-      for (int w = 0; w <= G; ++w) s[w] = w <= Gg ? (int64_t)w * T / Gg : T;
-    }
-    auto owner = [&](int64_t t) {   // workgroup whose (non-empty) range holds tile t
-      int lo = 0, hi = G - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (s[mid] <= t) lo = mid;
-        else hi = mid - 1;
-      }
-      return lo;
-    };
+    // Tile ranges per workgroup: whole row-groups, spread evenly; when the
+    // group has fewer row-groups than workgroups some get none (their waves
+    // go on prefetching the next groups).  Splitting a row-group across
+    // workgroups would put a cross-workgroup combine, one more device-wide
+    // round trip, on the group's critical path; measured, that costs more
+    // than the uneven split.
     for (int w = 0; w < G; ++w) {
-      PSched& e = ps[(size_t)g * G + w];
-      const int64_t a = s[w], b = s[w + 1];
-      e = PSched{(int32_t)a, (int32_t)b, 0, 1, 0, 1, off[w], (int32_t)(a / J)};
+      const int64_t a = (int64_t)w * R / G * J, b = (int64_t)(w + 1) * R / G * J;
+      ps[(size_t)g * G + w] = PSched{(int32_t)a, (int32_t)b, off[w], (int32_t)(a / J)};
       if (a >= b) continue;
       off[w] += (int32_t)(b - a);
-      const int64_t rg0 = a / J, rgl = (b - 1) / J;
-      maxRel = std::max<int>(maxRel, (int)(b - rg0 * J));
-      const int f0 = owner(rg0 * J), l0 = owner(rg0 * J + J - 1);
-      const int f1 = owner(rgl * J), l1 = owner(rgl * J + J - 1);
-      e.wf0 = f0;
-      e.nc0 = l0 - f0 + 1;
-      e.wf1 = f1;
-      e.nc1 = l1 - f1 + 1;
+      maxRel = std::max<int>(maxRel, (int)(b - a));
+      maxSeg = std::max<int>(maxSeg, (int)((b - a) / J));
     }
   }
-  const size_t x_bytes = align_up((size_t)maxJ * kSuperK * 2, 16);
+  const size_t x_bytes = align_up((size_t)maxJ * kSuperK * 2, 1024);
   const size_t xsum_bytes = fmt == QD_FMT_INT4_G64 ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
   const size_t red_bytes = align_up((size_t)maxRel * 16 * 4, 16);
+  const size_t cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   const size_t tab_bytes = (size_t)ng * sizeof(PGroup) + pm.size() * sizeof(PMember) +
                            (size_t)ng * sizeof(PSched);
-  const size_t lds = x_bytes + xsum_bytes + red_bytes + tab_bytes + 16;
+  const size_t lds = x_bytes + xsum_bytes + red_bytes + cnt_bytes + tab_bytes + 16;   // + counter, stall flag
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
     delete plan;
@@ -662,20 +715,17 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   }
   const void* kfn = kernel_ptr(fmt);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
-  if (lds > lds_max) {
-    delete plan;
-    return QD_ESHAPE;
-  }
+  if (lds > lds_max) return fallback();
   if (lds > 65536 &&
       hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-    delete plan;
-    return QD_ESHAPE;
+    (void)hipGetLastError();
+    return fallback();
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kWaves * 64, lds) != hipSuccess ||
       per_cu < 1) {
-    delete plan;
-    return QD_ESHAPE;
+    (void)hipGetLastError();
+    return fallback();
   }
 
   // Device tables, then scratch.
@@ -684,8 +734,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   const size_t o_sched = align_up(o_mem + sizeof(PMember) * pm.size(), 256);
   const size_t t_bytes = align_up(o_sched + sizeof(PSched) * ps.size(), 256);
   const size_t s_flags = 0;
-  const size_t s_slots = align_up(sizeof(unsigned long long) * G, 256);
-  const size_t s_err = align_up(s_slots + sizeof(unsigned long long) * G * 2 * 16, 256);
+  const size_t s_err = align_up(sizeof(unsigned long long) * G, 256);
   const size_t s_bytes = s_err + 256;
   std::vector<uint8_t> host(t_bytes, 0);
   memcpy(host.data() + o_groups, pg.data(), sizeof(PGroup) * ng);
@@ -707,7 +756,6 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.members = reinterpret_cast<const PMember*>(tb + o_mem);
   a.sched = reinterpret_cast<const PSched*>(tb + o_sched);
   a.flags = reinterpret_cast<unsigned long long*>(sb + s_flags);
-  a.slots = reinterpret_cast<unsigned long long*>(sb + s_slots);
   a.err = reinterpret_cast<uint32_t*>(sb + s_err);
   a.ngroups = ng;
   a.nmem = (int32_t)pm.size();
@@ -715,6 +763,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.x_bytes = (int32_t)x_bytes;
   a.xsum_bytes = (int32_t)xsum_bytes;
   a.red_bytes = (int32_t)red_bytes;
+  a.cnt_bytes = (int32_t)cnt_bytes;
   a.tab_bytes = (int32_t)tab_bytes;
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
@@ -755,6 +804,8 @@ qd_status plan_error(qd_stack_plan* plan, int32_t* out_error) {
   }
   return QD_OK;
 }
+
+bool plan_is_persistent(const qd_stack_plan* plan) { return plan->persistent; }
 
 void plan_destroy(qd_stack_plan* plan) {
   if (!plan) return;

@@ -22,6 +22,7 @@ hipError_t launch_groups(const std::vector<StackGroup>& groups, hipStream_t s);
 qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out);
 qd_status plan_run(qd_stack_plan* plan, hipStream_t s);
 qd_status plan_error(qd_stack_plan* plan, int32_t* out_error);
+bool plan_is_persistent(const qd_stack_plan* plan);
 void plan_destroy(qd_stack_plan* plan);
 
 }  // namespace qd

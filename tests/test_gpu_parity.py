@@ -287,6 +287,7 @@ def test_plan_parity_and_determinism(qd, fmt):
     runs (outputs poisoned in between) are bit-identical, no wait timed out."""
     ops, meta = _tiny_decoder_ops(qd, fmt, 1, layers=3)
     plan = qd.StackPlan(ops, 1)
+    assert plan.persistent
     first = None
     for rep in range(3):
         for op in ops:
@@ -338,13 +339,15 @@ def test_plan_chain_respects_order(qd):
     plan.close()
 
 
-def test_plan_ragged_and_split_groups(qd):
-    """Groups whose row-groups split across many workgroups (few rows, long K),
-    ragged tails, and groups with more row-groups than workgroups whose
-    ranges straddle member boundaries."""
+def test_plan_ragged_and_uneven_groups(qd):
+    """Groups with fewer row-groups than workgroups (most workgroups get none),
+    long K (activations staged in many 1 KiB blocks), K that is not a multiple
+    of 256 or gives an odd number of 256-wide blocks, ragged row tails, and
+    groups with more row-groups than workgroups whose ranges straddle member
+    boundaries."""
     from int4_quantized_decode_amd import LinearOp
     shapes = [[(24, 12288)], [(37, 2048), (5, 2048), (100, 2048)], [(4000, 512)], [(16, 256)],
-              [(9, 4096)],
+              [(9, 4096)], [(40, 768)], [(33, 1056)],
               # at least one row-group per workgroup: whole-row-group ranges, several of
               # which straddle a boundary between members
               [(4096, 256), (1024, 256), (1024, 256)], [(2000, 512), (1000, 512), (1200, 512)]]
@@ -359,6 +362,7 @@ def test_plan_ragged_and_split_groups(qd):
             ops.append(LinearOp(qd.qpack_int8_b32(_gpu(w)), xg, y, gi))
             meta.append((w, x))
     plan = qd.StackPlan(ops, 1)
+    assert plan.persistent
     plan.run()
     torch.cuda.synchronize()
     assert plan.error() == 0
@@ -366,6 +370,30 @@ def test_plan_ragged_and_split_groups(qd):
         parts = quant.quantize_int8_b32(w)
         check_vector(_host(op.y), linear.ref_linear("int8_b32", parts, x),
                      linear.row_max_abs("int8_b32", parts), x, f"ragged {w.shape}")
+    plan.close()
+
+
+def test_plan_replays_launches_when_schedule_exceeds_lds(qd):
+    """A step with more groups than one CU's LDS can hold the schedule of is
+    replayed as per-group launches: same results, reported as not persistent."""
+    from int4_quantized_decode_amd import LinearOp
+    n_groups, n, k = 2600, 16, 256
+    w_all = si.weights(si.seed_for("many-groups-w"), n_groups * n, k)
+    x_all = si.activations(si.seed_for("many-groups-x"), n_groups, k)
+    pw_all = [qd.qpack_int8_b32(_gpu(w_all[i * n:(i + 1) * n])) for i in range(n_groups)]
+    xg = _gpu(x_all)
+    y = torch.full((n_groups, n), float("nan"), dtype=torch.float16, device=DEV)
+    ops = [LinearOp(pw_all[i], xg[i], y[i], i) for i in range(n_groups)]
+    plan = qd.StackPlan(ops, 1)
+    assert not plan.persistent
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    yh = _host(y)
+    for i in range(0, n_groups, 97):
+        parts = quant.quantize_int8_b32(w_all[i * n:(i + 1) * n])
+        check_vector(yh[i], linear.ref_linear("int8_b32", parts, x_all[i]),
+                     linear.row_max_abs("int8_b32", parts), x_all[i], f"replayed group {i}")
     plan.close()
 
 
