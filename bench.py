@@ -31,8 +31,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b-int8-m1")
-    ap.add_argument("--path", choices=["plan", "launches"], default="launches",
-                    help="launches: one fused launch per group; plan: persistent one-launch step")
+    ap.add_argument("--path", choices=["plan", "launches"], default="plan",
+                    help="plan: persistent one-launch step (default); launches: one fused launch per group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-mb", type=int, default=1024,
                     help="single-GEMV workload: weight copies cycled to exceed the caches")
@@ -70,6 +70,35 @@ def build_stack(qd, si, torch, workload, dev):
             weight_bytes += pw.blob.numel()
     torch.cuda.synchronize()
     return ops, alg_bytes, weight_bytes, m
+
+
+def recorded_traffic(kernel_tag, workload):
+    """HBM bytes per launch of the timed kernel as last measured with
+    rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by the same
+    counter's reading for a plain copy of known size), from the committed
+    summary under profiles/.  None when there is no summary, or when the
+    kernel's source has changed since the counters were taken (the summary
+    records a hash of the sources)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    srcs = fields.get("sources", "").split()
+    h = hashlib.sha256()
+    for rel in srcs:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if not srcs or h.hexdigest()[:16] != fields.get("sources_sha256_16"):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def kernel_time(torch, runner, reps=9):
@@ -215,9 +244,13 @@ def main():
     ksec = kernel_time(torch, runners[0])
     kernel_gbs = alg_bytes / ksec / 1e9
     ngroups = len({op.group for op in step_ops[0]})
-    kname = ("stack_kernel (persistent, one launch per step)" if args.path == "plan" else
+    persistent = args.path == "plan" and all(p.persistent for p in plans)
+    if args.path == "plan" and not persistent:
+        log("the plan replays per-group launches for this workload")
+    kname = ("stack_kernel (persistent, one launch per step)" if persistent else
              f"gemv_int{8 if wl.fmt == 'int8_b32' else 4}_kernel family, {ngroups} fused launches "
              f"per step (kernels plus launch gaps)")
+    traffic = recorded_traffic("stack_kernel" if persistent else "gemv_launches", args.workload)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -238,7 +271,7 @@ def main():
                    "projections": len(ops), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": kname,
+                     "traffic": traffic, "kernel": kname,
                      "kernel_us_per_step": round(ksec * 1e6, 2)},
     }
     if not args.no_cpu_baseline:
