@@ -101,21 +101,26 @@ def recorded_traffic(kernel_tag, workload):
         return None
 
 
-def kernel_time(torch, runner, reps=9):
-    """Median duration of one step's kernels, timed with HIP events on the
-    launch stream (the stream the library launches on) outside the timed
-    steps.  For the plan path this is the one persistent kernel; for the
-    launch path it spans the step's per-group kernels and the gaps between
-    them."""
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        runner()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in evs)[reps // 2] * 1e-3
+def read_probe_gbs(qd, torch, dev, gib=2, reps=7):
+    """Best-of-grid median bandwidth of a plain streaming read of `gib` GiB
+    (the library's read probe), measured in this run."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = 0.0
+    for grid in (256, 512, 1024):
+        qd.read_probe(buf, sink, grid)                 # warm
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            qd.read_probe(buf, sink, grid)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+        best = max(best, buf.numel() / (ms * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def cpu_baseline(si, workload, alg_bytes_step, dev, torch, min_seconds=10.0):
@@ -241,15 +246,22 @@ def main():
         f"(p10 {step_ms[len(step_ms) // 10] * 1e3:.1f}, p90 {step_ms[(9 * len(step_ms)) // 10] * 1e3:.1f})")
 
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
-    ksec = kernel_time(torch, runners[0])
+    probe = read_probe_gbs(qd, torch, dev)
+    log(f"read probe {probe:.0f} GB/s")
+    # The timed kernel's average launch duration over the timed region: each
+    # step's HIP-event pair on the launch stream brackets exactly one launch
+    # of the persistent kernel (for the launch path: the step's launches and
+    # the gaps between them).
+    ksec = sum(a.elapsed_time(b) for a, b in step_events) / len(step_events) * 1e-3
     kernel_gbs = alg_bytes / ksec / 1e9
     ngroups = len({op.group for op in step_ops[0]})
     persistent = args.path == "plan" and all(p.persistent for p in plans)
     if args.path == "plan" and not persistent:
         log("the plan replays per-group launches for this workload")
+    family = ("small_m_int8_kernel" if m > 1 else f"gemv_int{8 if wl.fmt == 'int8_b32' else 4}_kernel")
     kname = ("stack_kernel (persistent, one launch per step)" if persistent else
-             f"gemv_int{8 if wl.fmt == 'int8_b32' else 4}_kernel family, {ngroups} fused launches "
-             f"per step (kernels plus launch gaps)")
+             f"{family} family, {ngroups} fused launch{'es' if ngroups > 1 else ''} per step "
+             f"(kernels plus launch gaps)")
     traffic = recorded_traffic("stack_kernel" if persistent else "gemv_launches", args.workload)
     out = {
         "metric": METRIC,
@@ -268,7 +280,11 @@ def main():
         "data": "synthetic (W ~ N(0,0.02) fp32 quantized on the device; x ~ N(0,1) fp16)",
         "config": {"workload": args.workload, "m": m, "path": args.path,
                    "bytes_per_step": alg_bytes, "weight_bytes": weight_bytes,
-                   "projections": len(ops), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+                   "projections": len(ops), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "read_probe_gbs": round(probe, 1), "frac_of_read_probe": round(value / probe, 4),
+                   "us_p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
+                   "us_p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2),
+                   "tok_per_s_note": "linear stack only; excludes attention, norms and embedding"},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname,

@@ -180,6 +180,18 @@ qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error);
 qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out);
 void qd_stack_plan_destroy(qd_stack_plan* plan);
 
+/*
+ * Measurement helper (not part of the method): read every byte of the device
+ * buffer `buf` (16-byte aligned, `bytes` > 0) once with a plain streaming
+ * kernel of `grid` workgroups (1..65535) x 256 threads, so a run can quote
+ * the step's bandwidth as a fraction of what a bare read reaches on this
+ * device.  `sink` (device, 4 bytes, 4-byte aligned) is written only if an
+ * impossible value turns up; it keeps the loads from being optimised away.
+ * Errors: QD_EINVAL (null), QD_EALIGN, QD_ESHAPE (bytes == 0 or grid out of
+ * range), QD_ELAUNCH.
+ */
+qd_status qd_read_probe(const void* buf, uint64_t bytes, void* sink, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -200,3 +200,14 @@ class StackPlan:
             self.close()
         except Exception:
             pass
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int = 512) -> None:
+    """Enqueue one plain streaming read of every byte of `buf` (a measurement
+    helper: the bandwidth a bare read reaches, to quote a step against).
+    `sink` is a 4-byte int32 device tensor the kernel writes only if an
+    impossible value turns up."""
+    if not (buf.is_cuda and sink.is_cuda and sink.dtype == torch.int32 and sink.numel() >= 1):
+        raise ValueError("read_probe needs a CUDA buffer and an int32 CUDA sink")
+    nbytes = buf.numel() * buf.element_size()
+    check(lib.qd_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, _stream()), "qd_read_probe")

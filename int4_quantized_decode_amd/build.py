@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqdecode.so")
-SOURCES = ["pack.hip", "gemv.hip", "gemm_small_m.hip", "stack.hip", "persist.hip", "capi.hip"]
+SOURCES = ["pack.hip", "gemv.hip", "gemm_small_m.hip", "stack.hip", "persist.hip", "probe.hip", "capi.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

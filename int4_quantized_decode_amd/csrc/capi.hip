@@ -181,6 +181,17 @@ QD_EXPORT qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error)
   return plan_error(plan, out_error);
 }
 
+QD_EXPORT qd_status qd_read_probe(const void* buf, uint64_t bytes, void* sink, int32_t grid,
+                                  void* stream) {
+  if (!buf || !sink) return QD_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3)) return QD_EALIGN;
+  if (bytes == 0 || grid < 1 || grid > 65535) return QD_ESHAPE;
+  if (qd::launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink), grid,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return QD_ELAUNCH;
+  return QD_OK;
+}
+
 QD_EXPORT qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out) {
   if (!plan || !out) return QD_EINVAL;
   *out = plan_is_persistent(plan) ? 1 : 0;

@@ -56,5 +56,6 @@ hipError_t launch_pack_int4(const float* w, int64_t n, int64_t k, uint8_t* out, 
 hipError_t launch_gemv(int fmt, const LinearArgs& a, hipStream_t s);
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(uint16_t* y, int64_t count, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int grid, hipStream_t s);
 
 }  // namespace qd

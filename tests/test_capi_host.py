@@ -111,3 +111,17 @@ def test_stack_validation_errors(L):
     assert lib.qd_stack_plan_create(ops, 2, 0, ctypes.byref(h)) == 2
     assert lib.qd_stack_plan_create(ops, 2, 1, None) == 1
     assert lib.qd_stack_plan_run(None, None) == 1
+    v = ctypes.c_int32(5)
+    assert lib.qd_stack_plan_is_persistent(None, ctypes.byref(v)) == 1
+
+
+def test_read_probe_validation_errors(L):
+    lib = L.lib
+    buf, sink = 1 << 20, 1 << 24
+    assert lib.qd_read_probe(None, 64, sink, 4, None) == 1                    # EINVAL
+    assert lib.qd_read_probe(buf, 64, None, 4, None) == 1
+    assert lib.qd_read_probe(buf + 8, 64, sink, 4, None) == 3                 # EALIGN
+    assert lib.qd_read_probe(buf, 64, sink + 2, 4, None) == 3
+    assert lib.qd_read_probe(buf, 0, sink, 4, None) == 2                      # ESHAPE
+    assert lib.qd_read_probe(buf, 64, sink, 0, None) == 2
+    assert lib.qd_read_probe(buf, 64, sink, 65536, None) == 2
