@@ -51,12 +51,6 @@ namespace qd {
 namespace {
 
 constexpr int kWaves = 16;
-#ifndef QD_PLAN_RESERVE_WAVES8
-#define QD_PLAN_RESERVE_WAVES8 7
-#endif
-#ifndef QD_PLAN_RESERVE_WAVES4
-#define QD_PLAN_RESERVE_WAVES4 0
-#endif
 #ifndef QD_PLAN_RESERVE_SLOTS8
 #define QD_PLAN_RESERVE_SLOTS8 5
 #endif
@@ -64,14 +58,9 @@ constexpr int kWaves = 16;
 #define QD_PLAN_RESERVE_SLOTS4 4
 #endif
 constexpr int kCtl = 15;                // the control wave
-// Compute waves that load only while the workgroup stalls (the rest stream
-// continuously).  int4 tiles cost twice the arithmetic per byte, and there
-// the streaming waves need every slot.
-template <int FMT>
-constexpr int kReserve = FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_WAVES8 : QD_PLAN_RESERVE_WAVES4;
-template <int FMT>
-constexpr int kMain = kCtl - kReserve<FMT>;
-static_assert(kMain<QD_FMT_INT8_B32> >= 1 && kMain<QD_FMT_INT4_G64> >= 1, "wave roles");
+// Compute waves are waves 0 .. 14: the first kCtl - R stream continuously,
+// the last R (a kernel template parameter) load only while the workgroup
+// stalls.  The plan picks R from the step's shape (see plan_create).
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
 
 struct PGroup {         // 32 bytes
@@ -136,6 +125,20 @@ __device__ __forceinline__ void wg_barrier() {
 }
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Flags and counters other waves of the workgroup update, in LDS.  Relaxed
+// workgroup-scope atomics compile to plain LDS reads and writes; a volatile
+// access through a generic pointer would become a flat access, which also
+// counts against the wave's vector-memory counter and so waits for the
+// wave's weight loads in flight.
+template <typename T>
+__device__ __forceinline__ T lds_get(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+template <typename T>
+__device__ __forceinline__ void lds_put(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 template <typename T>
 __device__ __forceinline__ T* uni_ptr(T* ptr) {
@@ -237,7 +240,7 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
 // kT / 256 ticks per tile is 25.6 GB/s per CU, about one CU's share of the
 // HBM bandwidth; QD_PLAN_PACE_PCT scales that rate.
 #ifndef QD_PLAN_PACE_PCT
-#define QD_PLAN_PACE_PCT 250
+#define QD_PLAN_PACE_PCT 100
 #endif
 template <int FMT>
 __device__ __forceinline__ uint32_t pace_ticks(int k) {
@@ -287,7 +290,7 @@ __device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const
 // group).  After each tile a wave writes the tile's 16 row partials to their
 // own LDS slot and counts the tile against its row-group, so the control wave
 // can finish a row-group as soon as its last tile is in.
-template <int FMT, int D, bool RESERVE>
+template <int FMT, int D, bool RESERVE, int R>
 __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint32_t* next,
                              int lane, const half_t* xs, const float* xsum, float* red,
                              uint32_t* cnt, const int* stalled, const int* staged) {
@@ -329,16 +332,15 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       if (ref[0].g >= ng) break;   // slot 0 was refilled first: nothing left for later slots
     }
   } else {
-    const volatile int* st = stalled;
-    const volatile int* sg = staged;
-    const int r = uni((int)(threadIdx.x >> 6)) - kMain<FMT>;   // rank among reserve waves
+    const int r = uni((int)(threadIdx.x >> 6)) - (kCtl - R);   // rank among reserve waves
     int trig = 0;                   // issue at the stall that ends group `trig`
     for (;;) {
       // Pass the barrier of group `trig` first: the control wave reaches the
       // next barrier only after the stall of `trig`, so this wait holds up
       // no barrier.
       settle_to(trig);
-      for (uint32_t spins = 0; *st < trig && spins < kSpinLimit; ++spins) __builtin_amdgcn_s_sleep(1);
+      for (uint32_t spins = 0; lds_get(stalled) < trig && spins < kSpinLimit; ++spins)
+        __builtin_amdgcn_s_sleep(1);
       // Issue at a bounded rate rather than all at once (the control wave's
       // stores and loads on the boundary's critical path queue behind what
       // the CU has in flight), and only while the stall lasts: once the next
@@ -347,12 +349,12 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       bool stop = false, exhausted = false;
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        const uint32_t due = t0 + pace_ticks<FMT>(s * kReserve<FMT> + r);
+        const uint32_t due = t0 + pace_ticks<FMT>(s * R + r);
         while (!stop && (int32_t)((uint32_t)__builtin_amdgcn_s_memrealtime() - due) < 0) {
-          stop = *sg > trig;
+          stop = lds_get(staged) > trig;
           if (!stop) __builtin_amdgcn_s_sleep(2);
         }
-        stop = stop || *sg > trig;
+        stop = stop || lds_get(staged) > trig;
         ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane, !stop);
         exhausted = exhausted || (!stop && ref[s].g >= ng);
         QD_PIN_ISSUE();
@@ -413,7 +415,10 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
   while (mi < last && rg >= S.rg_begin_l(mi + 1)) ++mi;
   const int64_t n = (int64_t)(rg - S.rg_begin_l(mi)) * kTileRows + row;
   if (n < S.n_l(mi))
-    __hip_atomic_store(S.y_l(mi) + n, __builtin_bit_cast(uint16_t, (half_t)v), __ATOMIC_RELAXED,
+    // Through a global pointer: a flat store would also count against the LDS
+    // counter, making the next LDS wait wait for this store's acknowledgement.
+    __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(S.y_l(mi) + n),
+                       __builtin_bit_cast(uint16_t, (half_t)v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -422,8 +427,7 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
 // skipped.
 __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cnt, int seg,
                                            uint32_t want, bool& dead) {
-  const volatile uint32_t* c = cnt + seg;
-  for (uint32_t spins = 0; !dead && *c < want; ++spins) {
+  for (uint32_t spins = 0; !dead && lds_get(cnt + seg) < want; ++spins) {
     if (spins > kSpinLimit) {
       atomicOr(p.err, 2u);
       dead = true;
@@ -442,7 +446,7 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
                              uint32_t* cnt, int* stalled, bool& dead) {
   const int a = S.a(g), b = S.b(g);
   if (a >= b) {
-    if (lane == 0) *reinterpret_cast<volatile int*>(stalled) = g;
+    if (lane == 0) lds_put(stalled, g);
     return;
   }
   const int J = S.J(g);
@@ -450,7 +454,7 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
   const int row = lane & 15, q = lane >> 4;
   for (int s = 0; s < nseg; ++s) {
     wait_count(p, cnt, s, (uint32_t)J, dead);
-    if (s == nseg - 1 && lane == 0) *reinterpret_cast<volatile int*>(stalled) = g;   // every tile of g is in
+    if (s == nseg - 1 && lane == 0) lds_put(stalled, g);   // every tile of g is in
     float part = 0.0f;
     for (int r = s * J + q; r < (s + 1) * J; r += 4) part += red[r * 16 + row];
     const float sum = quad_reduce(part);
@@ -466,28 +470,52 @@ __device__ __forceinline__ void publish(const PlanArgs& p, int g, int w, int lan
     __hip_atomic_store(&p.flags[w], stamp(p, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until every workgroup has published group g (one coherent read of all
-// stamps per poll).
+// Wait until every workgroup has published group g.  One poll is a single
+// coherent read of all stamps (4 loads per lane cover up to 512 workgroups);
+// polls are kept two deep, so a stamp that lands while one poll is in flight
+// is seen by the next one, already on its way.
+constexpr int kMaxWorkgroups = 512;
+
+__device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4]) {
+  // The clobbers keep the compiler from merging two polls of the same
+  // addresses into one load or hoisting a poll out of the loop.
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int b = 0; b < 4; ++b) v[b] = bload16_coherent(rf, (uint32_t)(128 * b + 2 * lane) * 8);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int lane,
+                                               unsigned long long target) {
+  bool ok = true;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = 128 * b + 2 * lane;
+    const unsigned long long s0 = ((unsigned long long)v[b][1] << 32) | v[b][0];
+    const unsigned long long s1 = ((unsigned long long)v[b][3] << 32) | v[b][2];
+    ok = ok && (i >= G || s0 >= target) && (i + 1 >= G || s1 >= target);
+  }
+  return __ballot(!ok) == 0ull;
+}
+
 __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   const unsigned long long target = stamp(p, g);
+  // Past the G stamps the buffer reads zeros, which the check ignores.
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(p.flags, (uint32_t)p.G * 8);
-  uint32_t spins = 0;
-  for (;;) {
-    bool ok = true;
-    for (int base = 0; base < p.G; base += 128) {           // 2 stamps per lane per load
-      const int i = base + 2 * lane;
-      const u32x4 v = bload16_coherent(rf, (uint32_t)i * 8);
-      const unsigned long long s0 = ((unsigned long long)v[1] << 32) | v[0];
-      const unsigned long long s1 = ((unsigned long long)v[3] << 32) | v[2];
-      ok = ok && (i >= p.G || s0 >= target) && (i + 1 >= p.G || s1 >= target);
-    }
-    if (__ballot(!ok) == 0ull) break;
-    if (++spins > kSpinLimit) {
+  u32x4 a[4], b[4];
+  poll_stamps(rf, lane, a);
+  for (uint32_t spins = 0;; spins += 2) {
+    poll_stamps(rf, lane, b);
+    if (stamps_reached(a, p.G, lane, target)) break;
+    poll_stamps(rf, lane, a);
+    if (stamps_reached(b, p.G, lane, target)) break;
+    if (spins > kSpinLimit) {
       if (lane == 0) atomicOr(p.err, 1u);
       break;
     }
   }
+  wait_stores();                  // no poll left in flight
   asm volatile("" ::: "memory");
 }
 
@@ -507,14 +535,15 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
     if (g + 1 < p.ngroups) {
       wait_group(p, g, lane);
       stage_group_x<FMT>(S, g + 1, lane, xs, xsum);
-      if (lane == 0) *reinterpret_cast<volatile int*>(staged) = g + 1;
+      if (lane == 0) lds_put(staged, g + 1);
       wg_barrier();               // activations of g + 1 staged
     }
   }
 }
 
-template <int FMT, int D>
+template <int FMT, int D, int R>
 __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
+  static_assert(R >= 0 && R < kCtl, "at least one streaming wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);
   float* xsum = reinterpret_cast<float*>(smem + p.x_bytes);
@@ -561,10 +590,10 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   } else {
     const int last = p.ngroups - 1;
     const int total = S.off(last) + S.b(last) - S.a(last);
-    if (wave < kMain<FMT>)
-      compute_wave<FMT, D, false>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+    if (wave < kCtl - R)
+      compute_wave<FMT, D, false, R>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
     else
-      compute_wave<FMT, FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_SLOTS8 : QD_PLAN_RESERVE_SLOTS4, true>(
+      compute_wave<FMT, FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_SLOTS8 : QD_PLAN_RESERVE_SLOTS4, true, R>(
           p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -590,6 +619,7 @@ struct qd_stack_plan {
   int device = 0;
   bool persistent = false;
   int fmt = 0;
+  int reserve = 0;                       // reserve waves of the persistent kernel
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (m > 1, K = 0, mixed formats)
   void* tables = nullptr;
   void* scratch = nullptr;
@@ -613,10 +643,20 @@ struct HostGroup {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-const void* kernel_ptr(int fmt) {
-  return fmt == QD_FMT_INT8_B32
-             ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8>)
-             : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4>);
+// Reserve waves per format and step shape (measured on MI355X): int4 tiles
+// carry twice the arithmetic per byte and there every streaming slot is
+// needed; int8 steps whose groups give each workgroup many tiles (8B-shaped:
+// ~50 per group) gain up to 7 reserve waves, while steps with smaller groups
+// (2B/4B-shaped: 15-26) do best with 4, where more reserve tiles run several
+// groups ahead and are then not free for the next stall.
+constexpr int kReserveBig = 7, kReserveSmall = 4;
+constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
+
+const void* kernel_ptr(int fmt, int reserve) {
+  if (fmt == QD_FMT_INT4_G64) return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, 0>);
+  return reserve == kReserveBig
+             ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveBig>)
+             : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveSmall>);
 }
 
 }  // namespace
@@ -654,7 +694,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   int cus = 0;
   if (ok && !groups.empty()) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
+        cus <= 0 || cus > kMaxWorkgroups)
       ok = false;
   } else {
     ok = false;
@@ -713,7 +753,12 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     delete plan;
     return QD_EDEVICE;
   }
-  const void* kfn = kernel_ptr(fmt);
+  int64_t total_tiles = 0;
+  for (int g = 0; g < ng; ++g) total_tiles += (int64_t)pg[g].R * pg[g].J;
+  const int reserve = fmt == QD_FMT_INT4_G64 ? 0
+                      : total_tiles >= (int64_t)kBigGroupTiles * ng * G ? kReserveBig
+                                                                         : kReserveSmall;
+  const void* kfn = kernel_ptr(fmt, reserve);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -768,6 +813,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = fmt;
+  plan->reserve = reserve;
   plan->persistent = true;
   *out = plan;
   return QD_OK;
@@ -779,7 +825,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt), dim3(plan->args.G),
+  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->reserve), dim3(plan->args.G),
                                                   dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;
