@@ -339,7 +339,10 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       // next barrier only after the stall of `trig`, so this wait holds up
       // no barrier.
       settle_to(trig);
-      for (uint32_t spins = 0; lds_get(stalled) < trig && spins < kSpinLimit; ++spins)
+      // Wait for the stall that ends group `trig` (or, should it have been
+      // missed, for the next activations: then nothing is issued).
+      for (uint32_t spins = 0;
+           lds_get(stalled) < trig && lds_get(staged) <= trig && spins < kSpinLimit; ++spins)
         __builtin_amdgcn_s_sleep(1);
       // Issue at a bounded rate rather than all at once (the control wave's
       // stores and loads on the boundary's critical path queue behind what
@@ -392,16 +395,31 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
         0, kPolicyCoherent);
   wait_stores();                                   // vmcnt(0): the data is in LDS
   if (FMT == QD_FMT_INT4_G64) {
-    for (int i0 = 0; i0 < Kp; i0 += 512) {
-      const int i = i0 + lane * 8;
-      const half8_t h = *reinterpret_cast<const half8_t*>(xs + i);
-      float sum = 0.0f;
+    // One 16-value run per lane, four runs' reads in flight before any sum:
+    // this runs on the group boundary's critical path.
+    const int runs = Kp / 16;
+    const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
+    for (int t0 = 0; t0 < runs; t0 += 256) {
+      half8_t va[4], vb[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += (float)h[e];
-      sum += __shfl_xor(sum, 1);                   // lanes 2q, 2q+1 hold one 16-value run
-      if ((lane & 1) == 0 && i < Kp) {
-        const int t = i >> 4, jj = t >> 4, within = t & 15;
-        xsum[16 * jj + 4 * (within & 3) + (within >> 2)] = sum;
+      for (int u = 0; u < 4; ++u) {
+        const int t = min(t0 + 64 * u + lane, runs - 1);   // clamped read; result kept only if in range
+        va[u] = *reinterpret_cast<const half8_t*>(xs + 16 * t);
+        vb[u] = *reinterpret_cast<const half8_t*>(xs + 16 * t + 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 64 * u + lane;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          sum = __builtin_amdgcn_fdot2((half2_t){va[u][e], va[u][e + 1]}, one2, sum, false);
+          sum = __builtin_amdgcn_fdot2((half2_t){vb[u][e], vb[u][e + 1]}, one2, sum, false);
+        }
+        if (t < runs) {
+          const int jj = t >> 4, within = t & 15;
+          xsum[16 * jj + 4 * (within & 3) + (within >> 2)] = sum;
+        }
       }
     }
   }
@@ -652,8 +670,14 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kReserveBig = 7, kReserveSmall = 4;
 constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
 
+#ifndef QD_PLAN_RESERVE4
+#define QD_PLAN_RESERVE4 0
+#endif
+constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
+
 const void* kernel_ptr(int fmt, int reserve) {
-  if (fmt == QD_FMT_INT4_G64) return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, 0>);
+  if (fmt == QD_FMT_INT4_G64)
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4>);
   return reserve == kReserveBig
              ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveBig>)
              : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveSmall>);
@@ -755,7 +779,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   }
   int64_t total_tiles = 0;
   for (int g = 0; g < ng; ++g) total_tiles += (int64_t)pg[g].R * pg[g].J;
-  const int reserve = fmt == QD_FMT_INT4_G64 ? 0
+  const int reserve = fmt == QD_FMT_INT4_G64 ? kReserveInt4
                       : total_tiles >= (int64_t)kBigGroupTiles * ng * G ? kReserveBig
                                                                          : kReserveSmall;
   const void* kfn = kernel_ptr(fmt, reserve);
