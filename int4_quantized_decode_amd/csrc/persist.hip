@@ -51,12 +51,6 @@ namespace qd {
 namespace {
 
 constexpr int kWaves = 16;
-#ifndef QD_PLAN_RESERVE_SLOTS8
-#define QD_PLAN_RESERVE_SLOTS8 5
-#endif
-#ifndef QD_PLAN_RESERVE_SLOTS4
-#define QD_PLAN_RESERVE_SLOTS4 4
-#endif
 constexpr int kCtl = 15;                // the control wave
 // Compute waves are waves 0 .. 14: the first kCtl - R stream continuously,
 // the last R (a kernel template parameter) load only while the workgroup
@@ -559,9 +553,9 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   }
 }
 
-template <int FMT, int D, int R>
+template <int FMT, int D, int R, int RS>
 __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
-  static_assert(R >= 0 && R < kCtl, "at least one streaming wave");
+  static_assert(R >= 0 && R < kCtl && RS >= 1, "at least one streaming wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = reinterpret_cast<half_t*>(smem);
   float* xsum = reinterpret_cast<float*>(smem + p.x_bytes);
@@ -611,8 +605,7 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
     if (wave < kCtl - R)
       compute_wave<FMT, D, false, R>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
     else
-      compute_wave<FMT, FMT == QD_FMT_INT8_B32 ? QD_PLAN_RESERVE_SLOTS8 : QD_PLAN_RESERVE_SLOTS4, true, R>(
-          p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+      compute_wave<FMT, RS, true, R>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -637,7 +630,7 @@ struct qd_stack_plan {
   int device = 0;
   bool persistent = false;
   int fmt = 0;
-  int reserve = 0;                       // reserve waves of the persistent kernel
+  int reserve = 0;                       // which persistent-kernel instance (wave roles)
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (m > 1, K = 0, mixed formats)
   void* tables = nullptr;
   void* scratch = nullptr;
@@ -661,13 +654,13 @@ struct HostGroup {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Reserve waves per format and step shape (measured on MI355X): int4 tiles
-// carry twice the arithmetic per byte and there every streaming slot is
-// needed; int8 steps whose groups give each workgroup many tiles (8B-shaped:
-// ~50 per group) gain up to 7 reserve waves, while steps with smaller groups
-// (2B/4B-shaped: 15-26) do best with 4, where more reserve tiles run several
-// groups ahead and are then not free for the next stall.
-constexpr int kReserveBig = 7, kReserveSmall = 4;
+// Reserve waves (and tiles each) per format and step shape, as measured on
+// MI355X: int4 tiles carry twice the arithmetic per byte and there every
+// streaming slot is needed; int8 steps whose groups give each workgroup many
+// tiles (8B-shaped: ~50 per group) do best with 7 reserve waves of 3 tiles,
+// steps with smaller groups (2B/4B-shaped: 15-26) with 4 waves of 5 tiles.
+// More reserve tiles than that run several groups ahead and are then not
+// free for the next stall; fewer leave memory idle for part of it.
 constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
 
 #ifndef QD_PLAN_RESERVE4
@@ -675,12 +668,17 @@ constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
 #endif
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 
-const void* kernel_ptr(int fmt, int reserve) {
-  if (fmt == QD_FMT_INT4_G64)
-    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4>);
-  return reserve == kReserveBig
-             ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveBig>)
-             : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserveSmall>);
+enum ReserveShape { kInt4 = 0, kInt8Big = 1, kInt8Small = 2 };
+
+const void* kernel_ptr(int shape) {
+  switch (shape) {
+    case kInt8Big:
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 7, 3>);
+    case kInt8Small:
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 4, 5>);
+    default:
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4>);
+  }
 }
 
 }  // namespace
@@ -779,10 +777,10 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   }
   int64_t total_tiles = 0;
   for (int g = 0; g < ng; ++g) total_tiles += (int64_t)pg[g].R * pg[g].J;
-  const int reserve = fmt == QD_FMT_INT4_G64 ? kReserveInt4
-                      : total_tiles >= (int64_t)kBigGroupTiles * ng * G ? kReserveBig
-                                                                         : kReserveSmall;
-  const void* kfn = kernel_ptr(fmt, reserve);
+  const int reserve = fmt == QD_FMT_INT4_G64 ? kInt4
+                      : total_tiles >= (int64_t)kBigGroupTiles * ng * G ? kInt8Big
+                                                                         : kInt8Small;
+  const void* kfn = kernel_ptr(reserve);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -849,7 +847,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->reserve), dim3(plan->args.G),
+  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->reserve), dim3(plan->args.G),
                                                   dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;
