@@ -39,26 +39,44 @@ __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
   return o;
 }
 
-template <int WAVES>
+// One workgroup: RG consecutive row-groups (16 weight rows each) x all of K.
+// Wave w takes super-blocks j = w, w + WAVES, ...; for each it loads the
+// activation block X[0..15][j*256 .. j*256+255] once (8 A operands) and the
+// RG weight tiles of that super-block, and issues RG x 8 MFMAs, so each
+// activation block read from L2 serves RG tiles.
+template <int WAVES, int RG>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) {
-  __shared__ float4_t red[WAVES][64];
+  __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, rho = lane & 15;
-  const Owner o = find_owner(a, blockIdx.x);
   const uint32_t span = (uint32_t)J * kTileBytes8;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(o.blob + o.local_rg * (int64_t)span, span);
+  Owner o[RG];
+  __amdgpu_buffer_rsrc_t rw[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    // Row-groups past the launch's last read as zero tiles (empty descriptor)
+    // and store nothing.
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
+    o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
+    rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
+  }
   // X rows m >= M fall outside the descriptor and read as zeros.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
   const int64_t K = a.k;
   const int m_row = rho;   // A operand row held by this lane
 
-  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = wave; j < J; j += WAVES) {
     const uint32_t t = (uint32_t)j * kTileBytes8;
-    u32x4 c[4];
+    u32x4 c[RG][4], scw[RG];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) c[s] = bload16(rw, t + 1024 * s + 16 * lane);
-    const u32x4 scw = bload16(rw, t + kMetaOffset8 + 16 * rho);
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+      scw[r] = bload16(rw[r], t + kMetaOffset8 + 16 * rho);
+    }
     half8_t xa[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -66,37 +84,48 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
       const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
       xa[b] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
     }
-    const half8_t scales = __builtin_bit_cast(half8_t, scw);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int r = 0; r < RG; ++r) {
+      const half8_t scales = __builtin_bit_cast(half8_t, scw[r]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const half8_t bq = codes_to_half8(c[s][2 * h], c[s][2 * h + 1]);
-        const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * s + h], bq, zero, 0, 0, 0);
-        const float sc = (float)scales[2 * s + h];
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, p[i], acc[i]);
+        for (int h = 0; h < 2; ++h) {
+          const half8_t bq = codes_to_half8(c[r][s][2 * h], c[r][s][2 * h + 1]);
+          const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * s + h], bq, zero, 0, 0, 0);
+          const float sc = (float)scales[2 * s + h];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf(sc, p[i], acc[r][i]);
+        }
       }
     }
   }
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < RG; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
-  if (wave == 0) {
-    float4_t sum = red[0][lane];
+  // Wave r (< RG) reduces and stores row-group r.
+  if (wave < RG) {
+    const int r = wave;
+    float4_t sum = red[0][r][lane];
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) {
-      const float4_t v = red[w][lane];
+      const float4_t v = red[w][r][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sum[i] += v[i];
     }
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
     // Lane (g, rho) holds output rows m = 4g + i of weight row rho.
-    const int64_t row = o.local_rg * kTileRows + rho;
-    if (row < o.n) {
+    Owner ow = o[0];
+#pragma unroll
+    for (int q = 1; q < RG; ++q)
+      if (q == r) ow = o[q];
+    const int64_t row = ow.local_rg * kTileRows + rho;
+    if (rg < a.total_rg && row < ow.n) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < a.m) o.y[(int64_t)m * o.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
       }
     }
   }
@@ -107,12 +136,20 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
   if (a.total_rg == 0) return hipSuccess;
   if (fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
+  // Enough row-groups to give every CU several: 4 per workgroup, 8 waves
+  // (each activation block then serves 4 tiles).  Otherwise one row-group per
+  // workgroup and up to 16 waves along K.
+  if (a.total_rg >= 4 * 256 && a.J >= 8) {
+    const dim3 grid((uint32_t)ceil_div(a.total_rg, 4));
+    hipLaunchKernelGGL((small_m_int8_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((uint32_t)a.total_rg);
   int w = 16;
   while (w > 4 && (w > a.J || a.total_rg * w > 256 * 32)) w /= 2;
-  if (w == 16) hipLaunchKernelGGL(small_m_int8_kernel<16>, grid, dim3(16 * 64), 0, s, a);
-  else if (w == 8) hipLaunchKernelGGL(small_m_int8_kernel<8>, grid, dim3(8 * 64), 0, s, a);
-  else hipLaunchKernelGGL(small_m_int8_kernel<4>, grid, dim3(4 * 64), 0, s, a);
+  if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
+  else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
+  else hipLaunchKernelGGL((small_m_int8_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -668,12 +668,20 @@ constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
 #endif
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 
+#ifndef QD_PLAN_BIG_R
+#define QD_PLAN_BIG_R 7
+#endif
+#ifndef QD_PLAN_BIG_S
+#define QD_PLAN_BIG_S 3
+#endif
+constexpr int kBigR = QD_PLAN_BIG_R, kBigS = QD_PLAN_BIG_S;
+
 enum ReserveShape { kInt4 = 0, kInt8Big = 1, kInt8Small = 2 };
 
 const void* kernel_ptr(int shape) {
   switch (shape) {
     case kInt8Big:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 7, 3>);
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kBigR, kBigS>);
     case kInt8Small:
       return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 4, 5>);
     default:

@@ -180,6 +180,33 @@ def test_small_m_rows_match_gemv(qd):
         check_vector(Y[i], y1.astype(np.float64), 2 * rmax, X[i], f"row {i}")
 
 
+def test_small_m_many_row_groups(qd):
+    """At least 1024 row-groups: the launch gives each workgroup four
+    row-groups that share one read of each activation block.  Ragged last
+    row-group, a fused pair whose workgroups straddle the member boundary,
+    and m below 16 (rows past m read as zero)."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 2048
+    n1, n2 = 8200, 8200                      # 513 + 513 row-groups, each ragged
+    w1 = si.weights(si.seed_for("sm-many", 1), n1, k)
+    w2 = si.weights(si.seed_for("sm-many", 2), n2, k)
+    for m in (16, 5):
+        X = si.activations(si.seed_for("sm-many-x", m), m, k)
+        xg = _gpu(X)
+        y1 = torch.full((m, n1), float("nan"), dtype=torch.float16, device=DEV)
+        y2 = torch.full((m, n2), float("nan"), dtype=torch.float16, device=DEV)
+        ops = [LinearOp(qd.qpack_int8_b32(_gpu(w1)), xg, y1, 0),
+               LinearOp(qd.qpack_int8_b32(_gpu(w2)), xg, y2, 0)]
+        qd.decode_linear_stack(ops, m)
+        for w, y, name in ((w1, y1, "first"), (w2, y2, "second")):
+            parts = quant.quantize_int8_b32(w)
+            Y_ref = linear.ref_linear("int8_b32", parts, X)
+            rmax = linear.row_max_abs("int8_b32", parts)
+            Yh = _host(y)
+            for i in range(m):
+                check_vector(Yh[i], Y_ref[i], rmax, X[i], f"{name} member m={m} row {i}")
+
+
 # ------------------------------------------------------------------ stack
 
 def _tiny_decoder_ops(qd, fmt, m, layers=2, chained=False):
