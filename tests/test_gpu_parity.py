@@ -424,10 +424,16 @@ def test_plan_replays_launches_when_schedule_exceeds_lds(qd):
     plan.close()
 
 
-@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1"])
+def _sample_picks(decoder):
+    last, mid = decoder.layers - 1, decoder.layers // 2
+    return ["L0.q", "L0.k", f"L{mid}.gate", f"L{mid}.up", f"L{last}.down", f"L{last}.o", "head"]
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1"])
 def test_plan_full_size_sampled(qd, workload):
-    """The full 8B-shaped step in the launch configuration the bench times:
-    every output finite, sampled rows of sampled projections match the oracle."""
+    """The full decoder-shaped step in the launch configuration the bench
+    times: every output finite, sampled rows of sampled projections match
+    the oracle."""
     import bench
     ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
     plan = qd.StackPlan(ops, 1)
@@ -441,7 +447,8 @@ def test_plan_full_size_sampled(qd, workload):
     names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
     for op in ops:
         assert torch.isfinite(op.y).all()
-    picks = ["L0.q", "L0.k", "L17.gate", "L17.up", "L35.down", "L35.o", "head"]
+    assert plan.persistent
+    picks = _sample_picks(wl.decoder)
     rng = np.random.default_rng(11)
     for name in picks:
         i = names.index(name)
@@ -456,3 +463,34 @@ def test_plan_full_size_sampled(qd, workload):
     plan.close()
     del ops
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m16", "qwen3.8-27b-int8-m16"])
+def test_stack_full_size_sampled_m16(qd, workload):
+    """The full 16-token chunked-prefill step as the bench times it (per-group
+    MFMA launches): every output finite, sampled rows of sampled projections
+    match the oracle for all 16 tokens."""
+    import bench
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
+    assert m == 16
+    for op in ops:
+        op.y.fill_(float("nan"))
+    qd.decode_linear_stack(ops, m)
+    torch.cuda.synchronize()
+    wl = si.WORKLOADS[workload]
+    names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
+    for op in ops:
+        assert torch.isfinite(op.y).all()
+    rng = np.random.default_rng(12)
+    for name in _sample_picks(wl.decoder):
+        op = ops[names.index(name)]
+        n, k = op.w.n, op.w.k
+        rows = np.sort(rng.choice(n, 16, replace=False))
+        w_rows = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)[rows].cpu().numpy()
+        X = op.x.cpu().numpy()
+        parts = _oracle_parts(wl.fmt, w_rows)
+        Y_ref = linear.ref_linear(wl.fmt, parts, X)
+        Y = _host(op.y)[:, rows]
+        rmax = linear.row_max_abs(wl.fmt, parts)
+        for t in range(16):
+            check_vector(Y[t], Y_ref[t], rmax, X[t], f"{name} token {t}")
