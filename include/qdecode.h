@@ -130,7 +130,7 @@ qd_status qgemv_int4_g64(const qd_weight* w, const uint16_t* x, uint16_t* y, voi
  * function, zoo Qwen3.8-27B page, vision path section): Y[i, n] =
  * fp16_RNE(sum_k X[i,k] w^[n,k]), X fp16 [m, K] row-major (16-byte aligned),
  * Y fp16 [m, N] row-major.  The contraction runs on the matrix cores.
- * Formats: int8 b32.
+ * Formats: int8 b32 and INT4 g64 (the format is taken from the descriptor).
  */
 qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_t* y, int64_t m, void* stream);
 
@@ -140,7 +140,7 @@ qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_t* y, int6
  * with equal `group` form one group: they must share x, K and format and are
  * fused into one launch.  Group g+1 starts only after group g has written all
  * its outputs, so a later op's x may be an earlier group's y (a dependent
- * chain).  All ops use the same m (1..16; m > 1 needs int8 b32).
+ * chain).  All ops use the same m (1..16, either format).
  */
 typedef struct {
   qd_weight w;

@@ -150,7 +150,6 @@ QD_EXPORT qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_
   qd_status st = check_weight(w, 0);
   if (st != QD_OK) return st;
   if (m < 1 || m > QD_MAX_M) return QD_ESHAPE;
-  if (w->fmt != QD_FMT_INT8_B32) return QD_EFORMAT;
   st = check_io(w, x, y, m);
   if (st != QD_OK) return st;
   return run_linear(w, x, y, m, static_cast<hipStream_t>(stream), true);
@@ -207,7 +206,6 @@ namespace qd {
 qd_status validate_op(const qd_linear_op& op, int64_t m) {
   qd_status st = check_weight(&op.w, 0);
   if (st != QD_OK) return st;
-  if (m > 1 && op.w.fmt != QD_FMT_INT8_B32) return QD_EFORMAT;
   return check_io(&op.w, op.x, op.y, m);
 }
 

@@ -1,5 +1,5 @@
 // Small-M (1 <= m <= 16) quantized GEMM on the matrix cores: a static chunk of
-// up to 16 tokens times an int8 b32 weight matrix.  The zoo's Qwen3.8-27B page
+// up to 16 tokens times an int8 b32 or INT4 g64 weight matrix.  The zoo's Qwen3.8-27B page
 // (vision path section) runs prefill as static S=16 chunks beside the S=1
 // decode function; this is that contraction.
 //
@@ -12,6 +12,15 @@
 // block's fp16 scale in fp32, and the 16 x 16 fp32 results are reduced across
 // waves in LDS.  The path stays bound by the weight stream: at m = 16 each
 // weight byte feeds 32 flops.
+//
+// INT4: a lane holds 16 consecutive codes of its row per 64-wide group (the
+// GEMV layout), i.e. two 8-code halves; each half feeds one 16x16x32 MFMA
+// whose A operand is the matching 8 activations per lane, so the two MFMAs
+// of a group cover its 64 K positions in a permuted order that A and B share.
+// Codes become exact fp16 integers (and-or onto 1024, minus 1024).  With
+// w^ = min + c s per group, y += s * sum(c x) + min * sum(x): the activation
+// sums come from the same two MFMAs run with an all-ones B operand, whose
+// every output column is the sum over the group for that token.
 #include "qd_internal.h"
 #include "tiles.h"
 
@@ -131,25 +140,137 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
   }
 }
 
+// INT4 g64: one workgroup = RG row-groups x all of K, waves along K (as above).
+template <int WAVES, int RG>
+__global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) {
+  __shared__ float4_t red[WAVES][RG][64];
+  const int J = a.J;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, rho = lane & 15;
+  const uint32_t span = (uint32_t)J * kTileBytes4;
+  Owner o[RG];
+  __amdgpu_buffer_rsrc_t rw[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
+    o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
+    rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
+  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
+  const int64_t K = a.k;
+  const int m_row = rho;
+  const half_t one = (half_t)1.0f;
+  const half8_t ones = {one, one, one, one, one, one, one, one};
+  const half2_t minus1024 = {(half_t)-1024.0f, (half_t)-1024.0f};
+
+  float4_t acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = wave; j < J; j += WAVES) {
+    const uint32_t t = (uint32_t)j * kTileBytes4;
+    u32x4 c[RG][2], meta[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+      meta[r] = bload16(rw[r], t + kMetaOffset4 + 16 * rho);
+    }
+    // A operands: group gam, half h -> X[m][j*256 + 64 gam + 16 g + 8 h .. +8].
+    half8_t xa[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t kk = (int64_t)j * kSuperK + 64 * (q >> 1) + 16 * g + 8 * (q & 1);
+      const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
+      xa[q] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
+    }
+    // Per group: sum of x over its 64 positions, for this lane's tokens.
+    float4_t xs[4];
+#pragma unroll
+    for (int gam = 0; gam < 4; ++gam) {
+      const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam], ones, zero, 0, 0, 0);
+      xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam + 1], ones, xs[gam], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const half8_t mt = __builtin_bit_cast(half8_t, meta[r]);
+#pragma unroll
+      for (int gam = 0; gam < 4; ++gam) {
+        const int s = gam >> 1, h = gam & 1;
+        float4_t pc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          // 8 codes (k order) of this lane's row: nibble p holds code (0,2,4,6,1,3,5,7)[p].
+          const uint32_t wd = c[r][s][2 * h + half];
+          const uint32_t mk = 0x000F000Fu, e = 0x64006400u;
+          const half2_t c01 = as_h2((wd & mk) | e) + minus1024;
+          const half2_t c23 = as_h2(((wd >> 4) & mk) | e) + minus1024;
+          const half2_t c45 = as_h2(((wd >> 8) & mk) | e) + minus1024;
+          const half2_t c67 = as_h2(((wd >> 12) & mk) | e) + minus1024;
+          const half8_t bq = {c01[0], c01[1], c23[0], c23[1], c45[0], c45[1], c67[0], c67[1]};
+          pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam + half], bq, pc, 0, 0, 0);
+        }
+        const float sc = (float)mt[gam], mn = (float)mt[4 + gam];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[r][i] = __builtin_fmaf(sc, pc[i], __builtin_fmaf(mn, xs[gam][i], acc[r][i]));
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RG; ++r) red[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave < RG) {
+    const int r = wave;
+    float4_t sum = red[0][r][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const float4_t v = red[w][r][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v[i];
+    }
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
+    Owner ow = o[0];
+#pragma unroll
+    for (int q = 1; q < RG; ++q)
+      if (q == r) ow = o[q];
+    const int64_t row = ow.local_rg * kTileRows + rho;
+    if (rg < a.total_rg && row < ow.n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
   if (a.total_rg == 0) return hipSuccess;
-  if (fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
+  const bool int4 = fmt == QD_FMT_INT4_G64;
+  if (!int4 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
   // Enough row-groups to give every CU several: 4 per workgroup, 8 waves
   // (each activation block then serves 4 tiles).  Otherwise one row-group per
   // workgroup and up to 16 waves along K.
   if (a.total_rg >= 4 * 256 && a.J >= 8) {
     const dim3 grid((uint32_t)ceil_div(a.total_rg, 4));
-    hipLaunchKernelGGL((small_m_int8_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
+    if (int4) hipLaunchKernelGGL((small_m_int4_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int8_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid((uint32_t)a.total_rg);
   int w = 16;
   while (w > 4 && (w > a.J || a.total_rg * w > 256 * 32)) w /= 2;
-  if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
-  else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
-  else hipLaunchKernelGGL((small_m_int8_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+  if (int4) {
+    if (w == 16) hipLaunchKernelGGL((small_m_int4_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_int4_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int4_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+  } else {
+    if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int8_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

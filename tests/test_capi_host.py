@@ -80,7 +80,7 @@ def test_small_m_validation_errors(L):
     x, y = 1 << 20, 1 << 24
     assert lib.qgemm_small_m(ctypes.byref(_w(L)), x, y, 0, None) == 2
     assert lib.qgemm_small_m(ctypes.byref(_w(L)), x, y, 17, None) == 2
-    assert lib.qgemm_small_m(ctypes.byref(_w(L, fmt=2)), x, y, 4, None) == 6
+    assert lib.qgemm_small_m(ctypes.byref(_w(L, fmt=2, k=96)), x, y, 4, None) == 2   # int4: K % 64
 
 
 def test_pack_validation_errors(L):
@@ -105,8 +105,8 @@ def test_stack_validation_errors(L):
     assert lib.decode_linear_stack(ops, 2, 1, None) == 1
     assert lib.decode_linear_stack(ops, 1, 0, None) == 2                      # m out of range
     assert lib.decode_linear_stack(None, 1, 1, None) == 1
-    ops[1] = L.QDLinearOp(_w(L, fmt=2, k=256), 1 << 20, 1 << 25, 1, 0)
-    assert lib.decode_linear_stack(ops, 2, 4, None) == 6                      # int4 at m > 1
+    ops[1] = L.QDLinearOp(_w(L, fmt=2, k=96), 1 << 20, 1 << 25, 1, 0)
+    assert lib.decode_linear_stack(ops, 2, 4, None) == 2                      # int4 needs K % 64
     h = ctypes.c_void_p()
     assert lib.qd_stack_plan_create(ops, 2, 0, ctypes.byref(h)) == 2
     assert lib.qd_stack_plan_create(ops, 2, 1, None) == 1

@@ -151,36 +151,42 @@ def test_gemv_edge_cases(qd, fmt):
 
 # ------------------------------------------------------------------ M <= 16
 
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 @pytest.mark.parametrize("m", [1, 5, 16])
-@pytest.mark.parametrize("n,k", [(16, 256), (200, 1056), (48, 2048), (100, 4096), (64, 12288)])
-def test_small_m_parity(qd, m, n, k):
+@pytest.mark.parametrize("n,k", [(16, 256), (200, 1056), (48, 2048), (100, 4096), (64, 12288),
+                                 (40, 1088)])
+def test_small_m_parity(qd, fmt, m, n, k):
+    _skip_bad_k(fmt, k)
     w = si.weights(si.seed_for("sm", n, k), n, k)
     X = si.activations(si.seed_for("sm-x", m, n, k), m, k)
-    pw = qd.qpack_int8_b32(_gpu(w))
+    pw = _pack(qd, fmt, _gpu(w))
     Y = _host(qd.qgemm_small_m(pw, _gpu(X)))
-    parts = quant.quantize_int8_b32(w)
-    Y_ref = linear.ref_linear("int8_b32", parts, X)
-    rmax = linear.row_max_abs("int8_b32", parts)
+    parts = _oracle_parts(fmt, w)
+    Y_ref = linear.ref_linear(fmt, parts, X)
+    rmax = linear.row_max_abs(fmt, parts)
     for i in range(m):
-        check_vector(Y[i], Y_ref[i], rmax, X[i], f"m={m} row {i}")
+        check_vector(Y[i], Y_ref[i], rmax, X[i], f"{fmt} m={m} row {i}")
 
 
-def test_small_m_rows_match_gemv(qd):
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_small_m_rows_match_gemv(qd, fmt):
     """Each token row of the 16-row chunk agrees with the one-token GEMV on
     that row (the pages' chunked-vs-S=1 consistency idea)."""
     n, k = 512, 4096
     w = si.weights(5, n, k)
     X = si.activations(6, 16, k)
-    pw = qd.qpack_int8_b32(_gpu(w))
+    pw = _pack(qd, fmt, _gpu(w))
     Y = _host(qd.qgemm_small_m(pw, _gpu(X)))
-    parts = quant.quantize_int8_b32(w)
-    rmax = linear.row_max_abs("int8_b32", parts)
+    parts = _oracle_parts(fmt, w)
+    rmax = linear.row_max_abs(fmt, parts)
+    gemv = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
     for i in range(16):
-        y1 = _host(qd.qgemv_int8_b32(pw, _gpu(X[i])))
+        y1 = _host(gemv(pw, _gpu(X[i])))
         check_vector(Y[i], y1.astype(np.float64), 2 * rmax, X[i], f"row {i}")
 
 
-def test_small_m_many_row_groups(qd):
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_small_m_many_row_groups(qd, fmt):
     """At least 1024 row-groups: the launch gives each workgroup four
     row-groups that share one read of each activation block.  Ragged last
     row-group, a fused pair whose workgroups straddle the member boundary,
@@ -195,13 +201,13 @@ def test_small_m_many_row_groups(qd):
         xg = _gpu(X)
         y1 = torch.full((m, n1), float("nan"), dtype=torch.float16, device=DEV)
         y2 = torch.full((m, n2), float("nan"), dtype=torch.float16, device=DEV)
-        ops = [LinearOp(qd.qpack_int8_b32(_gpu(w1)), xg, y1, 0),
-               LinearOp(qd.qpack_int8_b32(_gpu(w2)), xg, y2, 0)]
+        ops = [LinearOp(_pack(qd, fmt, _gpu(w1)), xg, y1, 0),
+               LinearOp(_pack(qd, fmt, _gpu(w2)), xg, y2, 0)]
         qd.decode_linear_stack(ops, m)
         for w, y, name in ((w1, y1, "first"), (w2, y2, "second")):
-            parts = quant.quantize_int8_b32(w)
-            Y_ref = linear.ref_linear("int8_b32", parts, X)
-            rmax = linear.row_max_abs("int8_b32", parts)
+            parts = _oracle_parts(fmt, w)
+            Y_ref = linear.ref_linear(fmt, parts, X)
+            rmax = linear.row_max_abs(fmt, parts)
             Yh = _host(y)
             for i in range(m):
                 check_vector(Yh[i], Y_ref[i], rmax, X[i], f"{name} member m={m} row {i}")
@@ -228,7 +234,7 @@ def _tiny_decoder_ops(qd, fmt, m, layers=2, chained=False):
     return ops, meta
 
 
-@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("int8_b32", 16)])
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("int8_b32", 16), ("int4_g64", 16)])
 def test_stack_parity(qd, fmt, m):
     ops, meta = _tiny_decoder_ops(qd, fmt, m)
     qd.decode_linear_stack(ops, m)
@@ -465,7 +471,7 @@ def test_plan_full_size_sampled(qd, workload):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m16", "qwen3.8-27b-int8-m16"])
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m16", "qwen3-8b-int4-m16", "qwen3.8-27b-int8-m16"])
 def test_stack_full_size_sampled_m16(qd, workload):
     """The full 16-token chunked-prefill step as the bench times it (per-group
     MFMA launches): every output finite, sampled rows of sampled projections
