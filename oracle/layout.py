@@ -30,6 +30,10 @@ int4 g64 tile (T = 2304 = 2*1024 + 256)
   k0 + PERM4[p], PERM4 = (0, 2, 4, 6, 1, 3, 5, 7).
   Bytes 2048..2303: row rho's 16 bytes at 2048 + 16*rho = 4 fp16 scales
   (groups 4j..4j+3) then 4 fp16 mins (same groups).
+
+fp16 tile (T = 8192 = 8*1024)
+  Chunk s (0..7), lane (g, rho): bytes 0..15 = w16[n, 256j + 32s + 8g + i],
+  i = 0..7 (fp16 little endian), so chunk s holds the 32-wide block 8j+s.
 """
 from __future__ import annotations
 
@@ -39,6 +43,8 @@ TILE_ROWS = 16
 SUPER_K = 256
 TILE_BYTES_INT8 = 4352
 TILE_BYTES_INT4 = 2304
+TILE_BYTES_FP16 = 8192
+TILE_BYTES = {"int8_b32": TILE_BYTES_INT8, "int4_g64": TILE_BYTES_INT4, "fp16": TILE_BYTES_FP16}
 PERM4 = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
@@ -50,8 +56,7 @@ def padded(n: int, k: int):
 
 def packed_bytes(fmt: str, n: int, k: int) -> int:
     np_, kp = padded(n, k)
-    t = TILE_BYTES_INT8 if fmt == "int8_b32" else TILE_BYTES_INT4
-    return (np_ // TILE_ROWS) * (kp // SUPER_K) * t
+    return (np_ // TILE_ROWS) * (kp // SUPER_K) * TILE_BYTES[fmt]
 
 
 def _pad(a: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -137,9 +142,29 @@ def untile_int4_g64(blob: np.ndarray, n: int, k: int):
     return q[:n, :k].copy(), sc[:n, : k // 64].copy(), mn[:n, : k // 64].copy()
 
 
+def tile_fp16(w16: np.ndarray) -> np.ndarray:
+    """fp16 [N, K] -> uint8 blob."""
+    n, k = w16.shape
+    np_, kp = padded(n, k)
+    R, J = np_ // 16, kp // 256
+    w = _pad(w16.astype(np.float16), np_, kp)
+    # k = 256 j + 32 s + 8 g + i ;  n = 16 r + rho
+    w = w.reshape(R, 16, J, 8, 4, 8)             # r rho j s g i
+    w = w.transpose(0, 2, 3, 4, 1, 5)            # r j s g rho i
+    return np.ascontiguousarray(w).astype("<f2").view(np.uint8).reshape(-1)
+
+
+def untile_fp16(blob: np.ndarray, n: int, k: int):
+    """Inverse of ``tile_fp16`` (drops the padding); returns (w16,)."""
+    np_, kp = padded(n, k)
+    R, J = np_ // 16, kp // 256
+    w = blob.reshape(R, J, TILE_BYTES_FP16).copy().view("<f2").reshape(R, J, 8, 4, 16, 8)  # r j s g rho i
+    w = w.transpose(0, 4, 1, 2, 3, 5).reshape(np_, kp)                                    # r rho j s g i
+    return (w[:n, :k].astype(np.float16).copy(),)
+
+
 def row_group_slice(fmt: str, n: int, k: int, r: int) -> slice:
     """Byte range of row-group r (rows 16r..16r+15) inside a blob."""
     _, kp = padded(n, k)
-    t = TILE_BYTES_INT8 if fmt == "int8_b32" else TILE_BYTES_INT4
-    span = (kp // SUPER_K) * t
+    span = (kp // SUPER_K) * TILE_BYTES[fmt]
     return slice(r * span, (r + 1) * span)

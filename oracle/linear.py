@@ -24,6 +24,8 @@ def dequantize(fmt: str, parts) -> np.ndarray:
         return quant.dequantize_int8_b32(*parts)
     if fmt == "int4_g64":
         return quant.dequantize_int4_g64(*parts)
+    if fmt == "fp16":
+        return quant.dequantize_fp16(*parts)
     raise ValueError(fmt)
 
 

@@ -34,6 +34,15 @@ int4 g64 (affine min/max, group of 64 along K)
       w^ = m + q * s                        (exact in fp64)
     Canonical packing: uint32 word j of a row holds codes 8j..8j+7, code 8j+i
     in bits [4i, 4i+4) (low nibble = lowest k).
+
+fp16 (unquantized head)
+    Source: zoo Qwen3-VL page, Measured table, "2B int8lin (tied fp16 head)"
+    row (int8 per-block-32 body with the head kept in fp16, against the
+    int8hu row's int8 head).
+      w16 = fp16_RNE(w)                     round to nearest, ties to even
+      w^  = w16                             (exact in fp64)
+    Non-finite input, or a value that rounds beyond the fp16 range, is
+    refused.  K must be a multiple of 32 (the tiled layout's block).
 """
 from __future__ import annotations
 
@@ -41,6 +50,7 @@ import numpy as np
 
 BLOCK8 = 32
 GROUP4 = 64
+BLOCK16 = 32
 QMAX8 = 127
 QMAX4 = 15
 
@@ -117,6 +127,21 @@ def dequantize_int4_g64(codes: np.ndarray, scales: np.ndarray, mins: np.ndarray)
     s = np.repeat(scales.astype(np.float64), GROUP4, axis=1)
     m = np.repeat(mins.astype(np.float64), GROUP4, axis=1)
     return m + codes.astype(np.float64) * s
+
+
+def quantize_fp16(w: np.ndarray):
+    """fp32 [N, K] -> (fp16 [N, K],) rounded to nearest, ties to even."""
+    w = _check_input(w, BLOCK16)
+    with np.errstate(over="ignore"):
+        h = w.astype(np.float16)
+    if np.any(np.isinf(h)):
+        raise ValueError("weight overflows fp16")
+    return (h,)
+
+
+def dequantize_fp16(h: np.ndarray) -> np.ndarray:
+    """fp16 [N, K] -> fp64 [N, K] (exact)."""
+    return h.astype(np.float64)
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:

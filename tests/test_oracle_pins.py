@@ -297,6 +297,96 @@ def test_int8_layout_hand_offsets():
     assert np.count_nonzero(blob) == 1
 
 
+def test_fp16_layout_hand_offsets():
+    n, k = 32, 512
+    h = np.zeros((n, k), np.float16)
+    for off, row, col in _golden_rows("layout_fp16_offsets.txt"):
+        h[:] = 0
+        h[row, col] = np.float16(-2.0)          # bits 0xC000: one nonzero byte
+        blob = layout.tile_fp16(h)
+        hits = np.flatnonzero(blob)
+        assert list(hits) == [off + 1] and blob[off + 1] == 0xC0, (off, row, col, hits)
+
+
+def _fp16_grid():
+    """Every finite fp16 value as (bits, float64), in increasing value order."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    ok = np.isfinite(vals)
+    bits, vals = bits[ok], vals[ok]
+    order = np.argsort(vals, kind="stable")
+    bits, vals = bits[order], vals[order]
+    keep = np.ones(len(vals), bool)             # drop -0 (same value as +0)
+    keep[1:] = vals[1:] != vals[:-1]
+    return bits[keep], vals[keep]
+
+
+def _rne_fp16_brute(x: float, grid_bits, grid_vals):
+    """Round x to the nearest finite fp16 value, ties to the even bit pattern,
+    by searching the whole fp16 grid (None if x rounds beyond the largest)."""
+    i = int(np.searchsorted(grid_vals, x))
+    cand = [j for j in (i - 1, i) if 0 <= j < len(grid_vals)]
+    best = min(cand, key=lambda j: abs(grid_vals[j] - x))
+    ties = [j for j in cand if abs(grid_vals[j] - x) == abs(grid_vals[best] - x)]
+    if len(ties) == 2:
+        best = ties[0] if int(grid_bits[ties[0]]) % 2 == 0 else ties[1]
+    top = grid_vals[-1]                         # 65504
+    if abs(x) >= top + (top - grid_vals[-2]) / 2:
+        return None                             # at or past the midpoint to 65536
+    return best
+
+
+def test_fp16_rounding_brute_force():
+    """The fp16 head's conversion is round-to-nearest-even onto the fp16 grid:
+    random values across the whole exponent range, exact midpoints between
+    neighbours (ties), subnormals and the values around the largest finite."""
+    gb, gv = _fp16_grid()
+    rng = np.random.default_rng(16)
+    xs = list((rng.standard_normal(600) * np.exp2(rng.integers(-26, 16, 600))).astype(np.float32))
+    picks = rng.integers(1, len(gv) - 1, 400)
+    xs += [np.float32((gv[i] + gv[i + 1]) / 2) for i in picks]          # exact midpoints (fit in fp32)
+    xs += [np.float32(v) for v in (0.0, 5.96e-8, 2.98e-8, 2.99e-8, 6.1e-5, 65504.0, 65519.0, -65519.0)]
+    for x in xs:
+        j = _rne_fp16_brute(float(x), gb, gv)
+        assert j is not None
+        (h,) = quant.quantize_fp16(np.full((1, 32), x, np.float32))
+        want = np.uint16(gb[j])
+        got = h.view(np.uint16)[0, 0]
+        # +0 and -0 are the same value; compare values there, bits elsewhere
+        if gv[j] == 0.0:
+            assert h[0, 0] == 0.0
+        else:
+            assert got == want, (x, hex(got), hex(want))
+    for bad in (65520.0, -65520.0, 1e6, np.inf, np.nan):
+        with pytest.raises(ValueError):
+            quant.quantize_fp16(np.full((1, 32), bad, np.float32))
+
+
+def test_fp16_round_trip_bound():
+    """|w - w^| <= half the fp16 spacing at w^ (normal range), and w^ exactly
+    representable values convert to themselves."""
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    (h,) = quant.quantize_fp16(w)
+    wh = quant.dequantize_fp16(h)
+    spacing = np.abs(np.spacing(h.astype(np.float16)).astype(np.float64))
+    assert np.all(np.abs(w.astype(np.float64) - wh) <= spacing / 2)
+    (h2,) = quant.quantize_fp16(h.astype(np.float32))
+    assert np.array_equal(h2.view(np.uint16), h.view(np.uint16))
+
+
+def test_fp16_layout_bijection_and_size():
+    for n, k in ((16, 256), (37, 544), (1, 32), (48, 1024)):
+        rng = np.random.default_rng(n * 1000 + k)
+        (h,) = quant.quantize_fp16(rng.standard_normal((n, k)).astype(np.float32))
+        blob = layout.tile_fp16(h)
+        assert blob.size == layout.packed_bytes("fp16", n, k)
+        (h2,) = layout.untile_fp16(blob, n, k)
+        assert np.array_equal(h2.view(np.uint16), h.view(np.uint16))
+        if n % 16 == 0 and k % 256 == 0:
+            assert blob.size == n * k * 2
+
+
 def test_int4_layout_hand_offsets():
     n, k = 32, 512
     s = np.zeros((n, k // 64), np.float16)
