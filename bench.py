@@ -53,7 +53,7 @@ def build_stack(qd, si, torch, workload, dev):
         groups, model = [("gemv", [("W", n, k)])], "single"
     else:
         groups, model = wl.decoder.groups(), wl.decoder.name
-    pack = qd.qpack_int8_b32 if wl.fmt == "int8_b32" else qd.qpack_int4_g64
+    packers = {"int8_b32": qd.qpack_int8_b32, "int4_g64": qd.qpack_int4_g64, "fp16": qd.qpack_fp16}
     ops, alg_bytes, weight_bytes = [], 0, 0
     for gi, (gname, members) in enumerate(groups):
         k = members[0][2]
@@ -62,7 +62,8 @@ def build_stack(qd, si, torch, workload, dev):
         alg_bytes += m * k * 2
         for pname, n, kk in members:
             w = si.weights_torch(si.matrix_seed(model, pname), n, kk, dev)
-            pw = pack(w)
+            fmt = wl.head_fmt if (pname == "head" and wl.head_fmt) else wl.fmt
+            pw = packers[fmt](w)
             del w
             y = torch.empty((m, n) if m > 1 else (n,), dtype=torch.float16, device=dev)
             ops.append(qd.LinearOp(pw, x_gpu, y, gi))
@@ -276,7 +277,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8" if wl.fmt == "int8_b32" else "int4",
+        "dtype": ("int8" if wl.fmt == "int8_b32" else "int4") + ("+fp16 head" if wl.head_fmt else ""),
         "data": "synthetic (W ~ N(0,0.02) fp32 quantized on the device; x ~ N(0,1) fp16)",
         "config": {"workload": args.workload, "m": m, "path": args.path,
                    "bytes_per_step": alg_bytes, "weight_bytes": weight_bytes,

@@ -56,8 +56,15 @@
  *     4j+2s+1; each little-endian uint32 holds 8 consecutive codes k0..k0+7
  *     with nibble p holding code k0 + (0,2,4,6,1,3,5,7)[p]; then per row rho
  *     at 2048 + 16 rho: 4 fp16 scales, 4 fp16 mins (groups 4j..4j+3).
+ *   fp16, T = 8192: chunk s = 0..7; lane bytes 0..15 = the fp16 weights at
+ *     k = 256j + 32s + 8g + i (i = 0..7).
  *   With N % 16 == 0 and K % 256 == 0 the blob holds exactly N K (1 + 2/32)
- *   (int8) or N K (1/2 + 4/64) (int4) bytes.
+ *   (int8), N K (1/2 + 4/64) (int4) or 2 N K (fp16) bytes.
+ *
+ * Formats
+ *   int8 b32 and INT4 g64 as defined with their packers below.  fp16 is the
+ *   unquantized head of the pages' int8lin variant (zoo Qwen3-VL page,
+ *   Measured table, "2B int8lin (tied fp16 head)" row): w^ = fp16_RNE(w).
  */
 #ifndef QDECODE_H
 #define QDECODE_H
@@ -72,7 +79,7 @@ extern "C" {
 typedef enum {
   QD_OK = 0,
   QD_EINVAL = 1,   /* null pointer, unknown enum, overlapping buffers, bad plan */
-  QD_ESHAPE = 2,   /* K not a multiple of 32 (int8) / 64 (int4), N or K < 0,
+  QD_ESHAPE = 2,   /* K not a multiple of 32 (int8, fp16) / 64 (int4), N or K < 0,
                       K > QD_MAX_K, M outside 1..16, blob smaller than needed */
   QD_EALIGN = 3,   /* blob, x or W not 16-byte aligned */
   QD_ERANGE = 4,   /* (reported through the packer's device flag, see below) */
@@ -81,7 +88,7 @@ typedef enum {
   QD_EDEVICE = 7   /* no usable device, or the plan belongs to another device */
 } qd_status;
 
-typedef enum { QD_FMT_INT8_B32 = 1, QD_FMT_INT4_G64 = 2 } qd_format;
+typedef enum { QD_FMT_INT8_B32 = 1, QD_FMT_INT4_G64 = 2, QD_FMT_FP16 = 3 } qd_format;
 
 enum { QD_MAX_K = 24576, QD_MAX_M = 16 };
 
@@ -110,11 +117,16 @@ const char* qd_status_string(int32_t status);
  * fp16 sets bit 2 (err_flag: device int32, may be NULL; bits are OR-ed in,
  * never cleared); such a block/group is written as zero codes, zero scale.
  * int8: k % 32 == 0.  int4: k % 64 == 0.
+ * qpack_fp16 rounds each weight to fp16 (nearest, ties to even); 8 consecutive
+ * weights holding a non-finite value set bit 1, a value that rounds beyond
+ * the fp16 range sets bit 2, and are written as zeros.  k % 32 == 0.
  */
 qd_status qpack_int8_b32(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
                          int32_t* err_flag, void* stream);
 qd_status qpack_int4_g64(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
                          int32_t* err_flag, void* stream);
+qd_status qpack_fp16(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
+                     int32_t* err_flag, void* stream);
 
 /*
  * One decoded token: y[n] = fp16_RNE(sum_k w^[n,k] x[k]) with fp32
@@ -124,13 +136,14 @@ qd_status qpack_int4_g64(const float* w, int64_t n, int64_t k, void* out, uint64
  */
 qd_status qgemv_int8_b32(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream);
 qd_status qgemv_int4_g64(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream);
+qd_status qgemv_fp16(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream);
 
 /*
  * A static chunk of m tokens (1 <= m <= 16, the pages' S=16 chunked-prefill
  * function, zoo Qwen3.8-27B page, vision path section): Y[i, n] =
  * fp16_RNE(sum_k X[i,k] w^[n,k]), X fp16 [m, K] row-major (16-byte aligned),
  * Y fp16 [m, N] row-major.  The contraction runs on the matrix cores.
- * Formats: int8 b32 and INT4 g64 (the format is taken from the descriptor).
+ * Formats: int8 b32, INT4 g64 and fp16 (the format is taken from the descriptor).
  */
 qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_t* y, int64_t m, void* stream);
 

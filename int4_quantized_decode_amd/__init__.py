@@ -13,16 +13,18 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import (QD_FMT_INT4_G64, QD_FMT_INT8_B32, QD_MAX_K, QD_MAX_M, QDError, QDLinearOp,
+from ._lib import (QD_FMT_FP16, QD_FMT_INT4_G64, QD_FMT_INT8_B32, QD_MAX_K, QD_MAX_M, QDError, QDLinearOp,
                    QDWeight, check, lib)
 
 __all__ = [
     "FORMATS", "PackedWeight", "QDError", "packed_bytes", "qpack_int8_b32", "qpack_int4_g64",
-    "qgemv_int8_b32", "qgemv_int4_g64", "qgemm_small_m", "decode_linear_stack", "StackPlan",
+    "qpack_fp16", "qgemv_int8_b32", "qgemv_int4_g64", "qgemv_fp16", "qgemm_small_m", "decode_linear_stack", "StackPlan",
     "QD_MAX_K", "QD_MAX_M",
 ]
 
-FORMATS = {"int8_b32": QD_FMT_INT8_B32, "int4_g64": QD_FMT_INT4_G64}
+FORMATS = {"int8_b32": QD_FMT_INT8_B32, "int4_g64": QD_FMT_INT4_G64, "fp16": QD_FMT_FP16}
+_PACK = {"int8_b32": "qpack_int8_b32", "int4_g64": "qpack_int4_g64", "fp16": "qpack_fp16"}
+_GEMV = {"int8_b32": "qgemv_int8_b32", "int4_g64": "qgemv_int4_g64", "fp16": "qgemv_fp16"}
 
 
 def _stream() -> int:
@@ -73,12 +75,12 @@ def _pack(fmt: str, w: torch.Tensor, out: torch.Tensor | None, err: torch.Tensor
     own_flag = err is None
     if own_flag:
         err = torch.zeros(1, dtype=torch.int32, device=w.device)
-    fn = lib.qpack_int8_b32 if fmt == "int8_b32" else lib.qpack_int4_g64
-    check(fn(_ptr(w), n, k, _ptr(out), out.numel(), _ptr(err), _stream()), f"qpack_{fmt}")
+    fn = getattr(lib, _PACK[fmt])
+    check(fn(_ptr(w), n, k, _ptr(out), out.numel(), _ptr(err), _stream()), _PACK[fmt])
     if check_errors and own_flag:
         flag = int(err.item())
         if flag:
-            raise QDError(4, f"qpack_{fmt} (device flag {flag})")
+            raise QDError(4, f"{_PACK[fmt]} (device flag {flag})")
     return PackedWeight(fmt, n, k, out)
 
 
@@ -94,6 +96,12 @@ def qpack_int4_g64(w: torch.Tensor, out: torch.Tensor | None = None,
     return _pack("int4_g64", w, out, err, check_errors)
 
 
+def qpack_fp16(w: torch.Tensor, out: torch.Tensor | None = None,
+               err: torch.Tensor | None = None, check_errors: bool = True) -> PackedWeight:
+    """Round fp32 [N, K] (device) to fp16 and pack it in the tiled layout (bit-exact)."""
+    return _pack("fp16", w, out, err, check_errors)
+
+
 def _gemv(fmt: str, w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None) -> torch.Tensor:
     if w.fmt != fmt:
         raise ValueError(f"weight is {w.fmt}, entry point wants {fmt}")
@@ -107,8 +115,8 @@ def _gemv(fmt: str, w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None) ->
         if y.numel() != w.n:
             raise ValueError("y must hold N values")
     d = w.desc()
-    fn = lib.qgemv_int8_b32 if fmt == "int8_b32" else lib.qgemv_int4_g64
-    check(fn(ctypes.byref(d), _ptr(x), _ptr(y), _stream()), f"qgemv_{fmt}")
+    fn = getattr(lib, _GEMV[fmt])
+    check(fn(ctypes.byref(d), _ptr(x), _ptr(y), _stream()), _GEMV[fmt])
     return y
 
 
@@ -120,6 +128,11 @@ def qgemv_int8_b32(w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = No
 def qgemv_int4_g64(w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
     """y = W^ x for one token; x fp16 [K] -> y fp16 [N]."""
     return _gemv("int4_g64", w, x, y)
+
+
+def qgemv_fp16(w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for one token with fp16 weights; x fp16 [K] -> y fp16 [N]."""
+    return _gemv("fp16", w, x, y)
 
 
 def qgemm_small_m(w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libqdecode.so")
 QD_OK = 0
 QD_FMT_INT8_B32 = 1
 QD_FMT_INT4_G64 = 2
+QD_FMT_FP16 = 3
 QD_MAX_K = 24576
 QD_MAX_M = 16
 
@@ -42,9 +43,14 @@ SIGNATURES = {
     "qpack_int4_g64": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "qpack_fp16": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
     "qgemv_int8_b32": (ctypes.c_int32, [ctypes.POINTER(QDWeight), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]),
     "qgemv_int4_g64": (ctypes.c_int32, [ctypes.POINTER(QDWeight), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "qgemv_fp16": (ctypes.c_int32, [ctypes.POINTER(QDWeight), ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]),
     "qgemm_small_m": (ctypes.c_int32, [ctypes.POINTER(QDWeight), ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),

@@ -12,8 +12,8 @@ using namespace qd;
 
 namespace {
 
-bool fmt_ok(int32_t f) { return f == QD_FMT_INT8_B32 || f == QD_FMT_INT4_G64; }
-int64_t k_multiple(int32_t f) { return f == QD_FMT_INT8_B32 ? 32 : 64; }
+bool fmt_ok(int32_t f) { return f == QD_FMT_INT8_B32 || f == QD_FMT_INT4_G64 || f == QD_FMT_FP16; }
+int64_t k_multiple(int32_t f) { return f == QD_FMT_INT4_G64 ? 64 : 32; }
 
 bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
   if (!a || !b || abytes == 0 || bbytes == 0) return false;
@@ -92,9 +92,10 @@ qd_status pack_common(int32_t fmt, const float* w, int64_t n, int64_t k, void* o
     if (overlaps(out, need, w, (uint64_t)n * k * 4)) return QD_EINVAL;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fmt == QD_FMT_INT8_B32
-                     ? launch_pack_int8(w, n, k, static_cast<uint8_t*>(out), err, s)
-                     : launch_pack_int4(w, n, k, static_cast<uint8_t*>(out), err, s);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  hipError_t e = fmt == QD_FMT_INT8_B32   ? launch_pack_int8(w, n, k, o, err, s)
+                 : fmt == QD_FMT_INT4_G64 ? launch_pack_int4(w, n, k, o, err, s)
+                                          : launch_pack_fp16(w, n, k, o, err, s);
   return to_status(e);
 }
 
@@ -129,6 +130,11 @@ QD_EXPORT qd_status qpack_int4_g64(const float* w, int64_t n, int64_t k, void* o
   return pack_common(QD_FMT_INT4_G64, w, n, k, out, out_bytes, err_flag, stream);
 }
 
+QD_EXPORT qd_status qpack_fp16(const float* w, int64_t n, int64_t k, void* out, uint64_t out_bytes,
+                               int32_t* err_flag, void* stream) {
+  return pack_common(QD_FMT_FP16, w, n, k, out, out_bytes, err_flag, stream);
+}
+
 QD_EXPORT qd_status qgemv_int8_b32(const qd_weight* w, const uint16_t* x, uint16_t* y,
                                    void* stream) {
   qd_status st = check_weight(w, QD_FMT_INT8_B32);
@@ -140,6 +146,13 @@ QD_EXPORT qd_status qgemv_int8_b32(const qd_weight* w, const uint16_t* x, uint16
 QD_EXPORT qd_status qgemv_int4_g64(const qd_weight* w, const uint16_t* x, uint16_t* y,
                                    void* stream) {
   qd_status st = check_weight(w, QD_FMT_INT4_G64);
+  if (st == QD_OK) st = check_io(w, x, y, 1);
+  if (st != QD_OK) return st;
+  return run_linear(w, x, y, 1, static_cast<hipStream_t>(stream), false);
+}
+
+QD_EXPORT qd_status qgemv_fp16(const qd_weight* w, const uint16_t* x, uint16_t* y, void* stream) {
+  qd_status st = check_weight(w, QD_FMT_FP16);
   if (st == QD_OK) st = check_io(w, x, y, 1);
   if (st != QD_OK) return st;
   return run_linear(w, x, y, 1, static_cast<hipStream_t>(stream), false);

@@ -140,6 +140,80 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
   }
 }
 
+// fp16 weights (the unquantized head): chunk s of a tile is already the B
+// operand of block s; no dequantization and no scale.
+template <int WAVES, int RG>
+__global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) {
+  __shared__ float4_t red[WAVES][RG][64];
+  const int J = a.J;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, rho = lane & 15;
+  const uint32_t span = (uint32_t)J * kTileBytes16;
+  Owner o[RG];
+  __amdgpu_buffer_rsrc_t rw[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
+    o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
+    rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
+  }
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
+  const int64_t K = a.k;
+  const int m_row = rho;
+
+  float4_t acc[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = wave; j < J; j += WAVES) {
+    const uint32_t t = (uint32_t)j * kTileBytes16;
+    u32x4 c[RG][8];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+    }
+    half8_t xa[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
+      const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
+      xa[b] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[b], __builtin_bit_cast(half8_t, c[r][b]),
+                                                        acc[r], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RG; ++r) red[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave < RG) {
+    const int r = wave;
+    float4_t sum = red[0][r][lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const float4_t v = red[w][r][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[i] += v[i];
+    }
+    const int64_t rg = (int64_t)blockIdx.x * RG + r;
+    Owner ow = o[0];
+#pragma unroll
+    for (int q = 1; q < RG; ++q)
+      if (q == r) ow = o[q];
+    const int64_t row = ow.local_rg * kTileRows + rho;
+    if (rg < a.total_rg && row < ow.n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+      }
+    }
+  }
+}
+
 // INT4 g64: one workgroup = RG row-groups x all of K, waves along K (as above).
 template <int WAVES, int RG>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) {
@@ -248,21 +322,26 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
 
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
   if (a.total_rg == 0) return hipSuccess;
-  const bool int4 = fmt == QD_FMT_INT4_G64;
-  if (!int4 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
+  const bool int4 = fmt == QD_FMT_INT4_G64, fp16 = fmt == QD_FMT_FP16;
+  if (!int4 && !fp16 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
   // Enough row-groups to give every CU several: 4 per workgroup, 8 waves
   // (each activation block then serves 4 tiles).  Otherwise one row-group per
   // workgroup and up to 16 waves along K.
   if (a.total_rg >= 4 * 256 && a.J >= 8) {
     const dim3 grid((uint32_t)ceil_div(a.total_rg, 4));
     if (int4) hipLaunchKernelGGL((small_m_int4_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
+    else if (fp16) hipLaunchKernelGGL((small_m_fp16_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
     else hipLaunchKernelGGL((small_m_int8_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid((uint32_t)a.total_rg);
   int w = 16;
   while (w > 4 && (w > a.J || a.total_rg * w > 256 * 32)) w /= 2;
-  if (int4) {
+  if (fp16) {
+    if (w == 16) hipLaunchKernelGGL((small_m_fp16_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_fp16_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_fp16_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+  } else if (int4) {
     if (w == 16) hipLaunchKernelGGL((small_m_int4_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
     else if (w == 8) hipLaunchKernelGGL((small_m_int4_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
     else hipLaunchKernelGGL((small_m_int4_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);

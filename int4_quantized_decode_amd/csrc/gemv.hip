@@ -148,6 +148,59 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int4_kernel(LinearArgs a) {
   }
 }
 
+// fp16 tiles are twice as large as int8 ones: at most kBatch16 of them are held
+// in registers at once; a wave with more tiles loads the next batch after
+// computing the previous one.
+constexpr int kBatch16 = 3;
+
+template <int WAVES, int TPW>
+__global__ __launch_bounds__(WAVES * 64) void gemv_fp16_kernel(LinearArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int J = a.J;
+  half_t* xs = reinterpret_cast<half_t*>(smem);
+  float* red = reinterpret_cast<float*>(smem + (size_t)J * kSuperK * 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4;
+
+  const Owner o = find_owner(a, blockIdx.x);
+  const uint32_t span = (uint32_t)J * kTileBytes16;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(o.blob + o.local_rg * (int64_t)span, span);
+
+  constexpr int B = TPW < kBatch16 ? TPW : kBatch16;
+  Tile16 T[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) T[t] = load_tile16(rw, wave + t * WAVES, lane);
+  stage_x<WAVES * 64>(a, xs);
+  __syncthreads();
+
+  float acc = 0.0f;
+#pragma unroll
+  for (int t0 = 0; t0 < TPW; t0 += B) {
+    if (t0 > 0) {
+#pragma unroll
+      for (int t = 0; t < B; ++t)
+        if (t0 + t < TPW) T[t] = load_tile16(rw, wave + (t0 + t) * WAVES, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      if (t0 + t < TPW) {
+        const int j = min(wave + (t0 + t) * WAVES, J - 1);
+        acc = tile_dot16(T[t], xs + j * kSuperK, g, acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) red[wave * 16 + lane] = acc;
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w * 16 + lane];
+    const int64_t row = o.local_rg * kTileRows + lane;
+    if (row < o.n) o.y[row] = __builtin_bit_cast(uint16_t, (half_t)sum);
+  }
+}
+
 constexpr int kMaxTPW = 6;
 
 void pick_shape(int64_t total_rg, int J, int* waves, int* tpw) {
@@ -166,7 +219,8 @@ template <int W, int TPW>
 void launch_one(int fmt, const LinearArgs& a, hipStream_t s, size_t lds) {
   const dim3 grid((uint32_t)a.total_rg), block(W * 64);
   if (fmt == QD_FMT_INT8_B32) hipLaunchKernelGGL((gemv_int8_kernel<W, TPW>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((gemv_int4_kernel<W, TPW>), grid, block, lds, s, a);
+  else if (fmt == QD_FMT_INT4_G64) hipLaunchKernelGGL((gemv_int4_kernel<W, TPW>), grid, block, lds, s, a);
+  else hipLaunchKernelGGL((gemv_fp16_kernel<W, TPW>), grid, block, lds, s, a);
 }
 
 template <int W>

@@ -4,7 +4,9 @@
 // int8 b32: symmetric absmax per block of 32 (Qwen3-VL 4B/8B Core AI cards,
 // Files table; zoo Qwen3.8-27B page, Numerics paragraph: absmax head rule, no
 // clipping).  int4 g64: affine min/max per group of 64 (CoreML-LLM handoff
-// page, Architecture paragraph, group_size 64).
+// page, Architecture paragraph, group_size 64).  fp16: the unquantized head of
+// the int8lin variant (zoo Qwen3-VL page, Measured table, "2B int8lin (tied
+// fp16 head)" row), round to nearest even.
 //
 // Bit-exactness rests on IEEE fp32 division rounded to nearest (the library is
 // built with correctly rounded fp32 division, without fast-math), RNE
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256) void pack_int8_kernel(const float* __restrict_
     const half_t s16 = (half_t)s32;
     const float sf = (float)s16;
     if (!finite || __builtin_isinf(sf)) {
-      atomicOr(err, finite ? 2 : 1);
+      if (err) atomicOr(err, finite ? 2 : 1);
     } else {
       sbits = half_bits(s16);
       if (sf != 0.0f) {
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const float* __restrict_
     const half_t m16 = (half_t)mn;
     const float sf = (float)s16, mf = (float)m16;
     if (!finite || __builtin_isinf(sf) || __builtin_isinf(mf)) {
-      atomicOr(err, finite ? 2 : 1);
+      if (err) atomicOr(err, finite ? 2 : 1);
     } else {
       sbits = half_bits(s16);
       mbits = half_bits(m16);
@@ -171,6 +173,45 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const float* __restrict_
   *reinterpret_cast<uint16_t*>(tile + kMetaOffset4 + 16 * rho + 8 + 2 * gamma) = mbits;
 }
 
+// One thread per (row-group r, super-block j, block s in 0..7, lane 16g + rho):
+// 8 consecutive weights of one row, 16 output bytes.
+__global__ __launch_bounds__(256) void pack_fp16_kernel(const float* __restrict__ w, int64_t n,
+                                                        int64_t k, uint8_t* __restrict__ out,
+                                                        int64_t J, int64_t total,
+                                                        int32_t* __restrict__ err) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int lane = (int)(t & 63), rho = lane & 15, g = lane >> 4;
+  const int s = (int)((t >> 6) & 7);
+  const int64_t rj = t >> 9;
+  const int64_t j = rj % J;
+  const int64_t r = rj / J;
+  const int64_t row = r * kTileRows + rho;
+  const int64_t k0 = j * kSuperK + 32 * s + 8 * g;
+  u32x4 packed = {0u, 0u, 0u, 0u};
+  if (row < n && k0 < k) {             // K % 32 == 0: these 8 are wholly in or out
+    const float4_t* src = reinterpret_cast<const float4_t*>(w + row * k + k0);
+    const float4_t f0 = src[0], f1 = src[1];
+    const float v[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+    bool finite = true, fits = true;
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      finite = finite && __builtin_isfinite(v[i]);
+      const half_t hv = (half_t)v[i];
+      fits = fits && !__builtin_isinf((float)hv);
+      h[i] = half_bits(hv);
+    }
+    if (!finite || !fits) {
+      if (err) atomicOr(err, finite ? 2 : 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed[i] = h[2 * i] | (h[2 * i + 1] << 16);
+    }
+  }
+  *reinterpret_cast<u32x4*>(out + rj * kTileBytes16 + 1024 * s + 16 * lane) = packed;
+}
+
 __global__ void fill_zero_kernel(uint16_t* __restrict__ y, int64_t count) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) y[i] = 0;
@@ -196,6 +237,17 @@ hipError_t launch_pack_int4(const float* w, int64_t n, int64_t k, uint8_t* out, 
   if (total == 0) return hipSuccess;
   const int64_t blocks = ceil_div(total, 256);
   hipLaunchKernelGGL(pack_int4_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, w, n, k, out, J,
+                     total, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp16(const float* w, int64_t n, int64_t k, uint8_t* out, int32_t* err,
+                            hipStream_t s) {
+  const int64_t R = ceil_div(n, kTileRows), J = ceil_div(k, kSuperK);
+  const int64_t total = R * J * 512;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = ceil_div(total, 256);
+  hipLaunchKernelGGL(pack_fp16_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, w, n, k, out, J,
                      total, err);
   return hipGetLastError();
 }

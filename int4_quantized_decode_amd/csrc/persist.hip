@@ -716,6 +716,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       if (ops[q].w.k == 0) ok = false;
       if (fmt == 0) fmt = ops[q].w.fmt;
       if (ops[q].w.fmt != fmt) ok = false;
+      if (fmt != QD_FMT_INT8_B32 && fmt != QD_FMT_INT4_G64) ok = false;   // fp16: replay
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
                                hg.R, 0});
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);

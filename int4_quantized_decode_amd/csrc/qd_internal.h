@@ -13,6 +13,7 @@ constexpr int kTileRows = 16;
 constexpr int kSuperK = 256;
 constexpr int kTileBytes8 = 4352;   // 4 x 1024 code bytes + 256 scale bytes
 constexpr int kTileBytes4 = 2304;   // 2 x 1024 code bytes + 256 scale/min bytes
+constexpr int kTileBytes16 = 8192;  // 8 x 1024 bytes of fp16 weights (unquantized head)
 constexpr int kMetaOffset8 = 4096;
 constexpr int kMetaOffset4 = 2048;
 
@@ -26,7 +27,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline int tile_bytes(int fmt) { return fmt == QD_FMT_INT8_B32 ? kTileBytes8 : kTileBytes4; }
+inline int tile_bytes(int fmt) {
+  return fmt == QD_FMT_INT8_B32 ? kTileBytes8 : fmt == QD_FMT_INT4_G64 ? kTileBytes4 : kTileBytes16;
+}
 
 // Up to this many matrices share one activation vector in a fused launch.
 constexpr int kMaxMembers = 4;
@@ -52,6 +55,8 @@ struct LinearArgs {
 hipError_t launch_pack_int8(const float* w, int64_t n, int64_t k, uint8_t* out, int32_t* err,
                             hipStream_t s);
 hipError_t launch_pack_int4(const float* w, int64_t n, int64_t k, uint8_t* out, int32_t* err,
+                            hipStream_t s);
+hipError_t launch_pack_fp16(const float* w, int64_t n, int64_t k, uint8_t* out, int32_t* err,
                             hipStream_t s);
 hipError_t launch_gemv(int fmt, const LinearArgs& a, hipStream_t s);
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s);

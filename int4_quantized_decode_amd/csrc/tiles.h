@@ -142,6 +142,33 @@ __device__ __forceinline__ float tile_dot4(const Tile4& T, const half_t* xs_j, c
   return acc;
 }
 
+// fp16 weights (the unquantized head): chunk s holds the 32-wide block s of
+// the super-block; lane (g, rho) has row rho's 8 values at 8g..8g+7.
+struct Tile16 {
+  u32x4 c[8];
+};
+
+__device__ __forceinline__ Tile16 load_tile16(__amdgpu_buffer_rsrc_t r, int j, int lane) {
+  const uint32_t t = (uint32_t)j * kTileBytes16;
+  Tile16 T;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) T.c[s] = bload16_stream(r, t + 1024 * s + 16 * lane);
+  return T;
+}
+
+// Lane (g, rho)'s share of one fp16 tile: row rho, 8 blocks x 8 values.
+__device__ __forceinline__ float tile_dot16(const Tile16& T, const half_t* xs_j, int g, float acc) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const half8_t w = __builtin_bit_cast(half8_t, T.c[s]);
+    const half8_t x = *reinterpret_cast<const half8_t*>(xs_j + 32 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2((half2_t){w[e], w[e + 1]}, (half2_t){x[e], x[e + 1]}, acc, false);
+  }
+  return acc;
+}
+
 // 8 int8 codes (k order) -> 8 exact fp16 values.
 __device__ __forceinline__ half8_t codes_to_half8(uint32_t d0, uint32_t d1) {
   const uint32_t u0 = d0 ^ 0x80808080u, u1 = d1 ^ 0x80808080u;

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(L):
         assert n in L.SIGNATURES, n
 
 
-@pytest.mark.parametrize("fmt,code", [("int8_b32", 1), ("int4_g64", 2)])
+@pytest.mark.parametrize("fmt,code", [("int8_b32", 1), ("int4_g64", 2), ("fp16", 3)])
 @pytest.mark.parametrize("n,k", [(16, 256), (37, 576), (151936, 4096), (1, 64), (4096, 12288)])
 def test_packed_bytes_matches_layout_spec(L, fmt, code, n, k):
     assert L.lib.qd_packed_bytes(code, n, k) == layout.packed_bytes(fmt, n, k)
@@ -43,7 +43,8 @@ def test_packed_bytes_matches_layout_spec(L, fmt, code, n, k):
 def test_packed_bytes_rejects(L):
     assert L.lib.qd_packed_bytes(1, 16, 48) == 0          # K % 32
     assert L.lib.qd_packed_bytes(2, 16, 96) == 0          # K % 64
-    assert L.lib.qd_packed_bytes(3, 16, 256) == 0         # unknown format
+    assert L.lib.qd_packed_bytes(3, 16, 48) == 0          # fp16: K % 32
+    assert L.lib.qd_packed_bytes(4, 16, 256) == 0         # unknown format
     assert L.lib.qd_packed_bytes(1, -1, 256) == 0
     assert L.lib.qd_packed_bytes(1, 16, L.QD_MAX_K + 256) == 0
 

@@ -33,16 +33,29 @@ def _host(t):
     return t.cpu().numpy()
 
 
+FMTS = ["int8_b32", "int4_g64", "fp16"]
+
+
 def _oracle_parts(fmt, w):
-    return quant.quantize_int8_b32(w) if fmt == "int8_b32" else quant.quantize_int4_g64(w)
+    return {"int8_b32": quant.quantize_int8_b32, "int4_g64": quant.quantize_int4_g64,
+            "fp16": quant.quantize_fp16}[fmt](w)
 
 
 def _oracle_blob(fmt, parts):
-    return layout.tile_int8_b32(*parts) if fmt == "int8_b32" else layout.tile_int4_g64(*parts)
+    return {"int8_b32": layout.tile_int8_b32, "int4_g64": layout.tile_int4_g64,
+            "fp16": layout.tile_fp16}[fmt](*parts)
+
+
+def _pack_fn(qd, fmt):
+    return {"int8_b32": qd.qpack_int8_b32, "int4_g64": qd.qpack_int4_g64, "fp16": qd.qpack_fp16}[fmt]
 
 
 def _pack(qd, fmt, w_gpu):
-    return qd.qpack_int8_b32(w_gpu) if fmt == "int8_b32" else qd.qpack_int4_g64(w_gpu)
+    return _pack_fn(qd, fmt)(w_gpu)
+
+
+def _gemv_fn(qd, fmt):
+    return {"int8_b32": qd.qgemv_int8_b32, "int4_g64": qd.qgemv_int4_g64, "fp16": qd.qgemv_fp16}[fmt]
 
 
 SHAPES = [(16, 256), (200, 1056), (200, 1088), (37, 576), (1, 64), (48, 2048), (2048, 2048),
@@ -52,11 +65,13 @@ SHAPES = [(16, 256), (200, 1056), (200, 1088), (37, 576), (1, 64), (48, 2048), (
 def _skip_bad_k(fmt, k):
     if fmt == "int4_g64" and k % 64:
         pytest.skip("int4 g64 needs K % 64 == 0")
+    if k % 32:
+        pytest.skip("K % 32 == 0 is required")
 
 
 # ------------------------------------------------------------------ packing
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", SHAPES)
 def test_pack_bit_exact(qd, fmt, n, k):
     _skip_bad_k(fmt, k)
@@ -69,7 +84,7 @@ def test_pack_bit_exact(qd, fmt, n, k):
     assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
 
 
-def _adversarial(fmt, n=32, k=512):
+def _adversarial(fmt, n=32, k=512, near_max=True):
     rng = np.random.default_rng(7)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     w[0, :64] = 0.0                                          # zero blocks / groups
@@ -84,10 +99,17 @@ def _adversarial(fmt, n=32, k=512):
     for c in range(16):                                             # near-ties around x.5
         w[7, c] = np.float32((c + 0.5) * 2.0 ** -7 * (1 + (-1) ** c * 2.0 ** -20))
     w[7, 31] = np.float32(127 * 2.0 ** -7)
+    if fmt == "fp16":
+        # exact midpoints between fp16 neighbours (ties), both signs, many exponents
+        base = (rng.standard_normal(k) * np.exp2(rng.integers(-20, 12, k))).astype(np.float16)
+        up = np.nextafter(base, np.float16(np.inf))
+        w[8, :] = ((base.astype(np.float64) + up.astype(np.float64)) / 2).astype(np.float32)
+        if near_max:                   # packing only: products would overflow fp16 outputs
+            w[9, :] = np.float32(65504.0) * np.sign(rng.standard_normal(k)).astype(np.float32)
     return w
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_pack_adversarial_bit_exact(qd, fmt):
     w = _adversarial(fmt)
     pw = _pack(qd, fmt, _gpu(w))
@@ -97,42 +119,68 @@ def test_pack_adversarial_bit_exact(qd, fmt):
     assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_pack_error_flags(qd, fmt):
     w = np.zeros((16, 256), np.float32)
     w[3, 7] = np.nan
     with pytest.raises(qd.QDError):
         _pack(qd, fmt, _gpu(w))
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    pack = qd.qpack_int8_b32 if fmt == "int8_b32" else qd.qpack_int4_g64
+    pack = _pack_fn(qd, fmt)
     pack(_gpu(w), err=err)
     assert int(err.item()) & 1
-    # int8: max|w| / 127 beyond fp16; int4: the group min beyond fp16
-    w[3, 7] = 1e9 if fmt == "int8_b32" else -70000.0
+    # int8: max|w| / 127 beyond fp16; int4: the group min beyond fp16; fp16: the value
+    w[3, 7] = {"int8_b32": 1e9, "int4_g64": -70000.0, "fp16": 65520.0}[fmt]
     err.zero_()
     pack(_gpu(w), err=err)
     assert int(err.item()) & 2
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pack_without_error_flag(qd, fmt):
+    """The error flag may be NULL: bad input is then only written as zeros."""
+    import ctypes
+    from int4_quantized_decode_amd import _lib
+    w = si.weights(si.seed_for("noflag", fmt), 32, 256)
+    w[5, 9] = np.nan
+    wg = _gpu(w)
+    n, k = w.shape
+    out = torch.full((layout.packed_bytes(fmt, n, k),), 0xAB, dtype=torch.uint8, device=DEV)
+    fn = getattr(_lib.lib, {"int8_b32": "qpack_int8_b32", "int4_g64": "qpack_int4_g64",
+                            "fp16": "qpack_fp16"}[fmt])
+    st = fn(wg.data_ptr(), n, k, out.data_ptr(), out.numel(), None,
+            torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    got = _host(out)
+    # the packer writes the block (int8: 32 values), group (int4: 64) or
+    # 8-value run (fp16) holding the NaN as zeros, everything else as usual
+    span = {"int8_b32": 32, "int4_g64": 64, "fp16": 8}[fmt]
+    clean = w.copy()
+    clean[5, 9 // span * span:(9 // span + 1) * span] = 0.0
+    want = _oracle_blob(fmt, _oracle_parts(fmt, clean))
+    diff = np.flatnonzero(got != want)
+    assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:8]}"
+
+
 # ------------------------------------------------------------------ M = 1
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", SHAPES + [(16, 24576)])
 def test_gemv_parity(qd, fmt, n, k):
     _skip_bad_k(fmt, k)
     w = si.weights(si.seed_for("gemv", fmt, n, k), n, k)
     x = si.activations(si.seed_for("gemv-x", fmt, n, k), 1, k)[0]
     pw = _pack(qd, fmt, _gpu(w))
-    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    fn = _gemv_fn(qd, fmt)
     y = _host(fn(pw, _gpu(x)))
     parts = _oracle_parts(fmt, w)
     y_ref = linear.ref_linear(fmt, parts, x)
     check_vector(y, y_ref, linear.row_max_abs(fmt, parts), x, f"{fmt} {n}x{k}")
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_edge_cases(qd, fmt):
-    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    fn = _gemv_fn(qd, fmt)
     # K = 0: y = 0
     pw0 = _pack(qd, fmt, torch.zeros((20, 0), dtype=torch.float32, device=DEV))
     y0 = fn(pw0, torch.zeros(0, dtype=torch.float16, device=DEV),
@@ -142,7 +190,7 @@ def test_gemv_edge_cases(qd, fmt):
     pwn = _pack(qd, fmt, torch.zeros((0, 256), dtype=torch.float32, device=DEV))
     assert fn(pwn, torch.zeros(256, dtype=torch.float16, device=DEV)).numel() == 0
     # all-zero weights give exact zeros; adversarial rows stay in bound
-    w = _adversarial(fmt)
+    w = _adversarial(fmt, near_max=False)
     x = si.activations(99, 1, w.shape[1])[0]
     y = _host(fn(_pack(qd, fmt, _gpu(w)), _gpu(x)))
     parts = _oracle_parts(fmt, w)
@@ -151,7 +199,7 @@ def test_gemv_edge_cases(qd, fmt):
 
 # ------------------------------------------------------------------ M <= 16
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m", [1, 5, 16])
 @pytest.mark.parametrize("n,k", [(16, 256), (200, 1056), (48, 2048), (100, 4096), (64, 12288),
                                  (40, 1088)])
@@ -168,7 +216,7 @@ def test_small_m_parity(qd, fmt, m, n, k):
         check_vector(Y[i], Y_ref[i], rmax, X[i], f"{fmt} m={m} row {i}")
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_small_m_rows_match_gemv(qd, fmt):
     """Each token row of the 16-row chunk agrees with the one-token GEMV on
     that row (the pages' chunked-vs-S=1 consistency idea)."""
@@ -179,13 +227,13 @@ def test_small_m_rows_match_gemv(qd, fmt):
     Y = _host(qd.qgemm_small_m(pw, _gpu(X)))
     parts = _oracle_parts(fmt, w)
     rmax = linear.row_max_abs(fmt, parts)
-    gemv = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    gemv = _gemv_fn(qd, fmt)
     for i in range(16):
         y1 = _host(gemv(pw, _gpu(X[i])))
         check_vector(Y[i], y1.astype(np.float64), 2 * rmax, X[i], f"row {i}")
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_small_m_many_row_groups(qd, fmt):
     """At least 1024 row-groups: the launch gives each workgroup four
     row-groups that share one read of each activation block.  Ragged last
@@ -234,7 +282,8 @@ def _tiny_decoder_ops(qd, fmt, m, layers=2, chained=False):
     return ops, meta
 
 
-@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("int8_b32", 16), ("int4_g64", 16)])
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("fp16", 1), ("int8_b32", 16),
+                                   ("int4_g64", 16), ("fp16", 16)])
 def test_stack_parity(qd, fmt, m):
     ops, meta = _tiny_decoder_ops(qd, fmt, m)
     qd.decode_linear_stack(ops, m)
@@ -248,6 +297,40 @@ def test_stack_parity(qd, fmt, m):
         else:
             for i in range(m):
                 check_vector(y[i], y_ref[i], rmax, x[i], f"{pname} row {i}")
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_stack_mixed_formats_fp16_head(qd, m):
+    """The int8lin variant's step shape: int8 b32 body groups and an fp16 head
+    group in one stack (per-group launches; the plan replays them)."""
+    ops, meta = _tiny_decoder_ops(qd, "int8_b32", m, layers=2)
+    hidden = meta[-1][1].shape[1]
+    w_head = si.weights(si.seed_for("fp16-head"), 1000, hidden)
+    x_head = si.activations(si.seed_for("fp16-head-x", m), m, hidden)
+    y_head = torch.full((m, 1000) if m > 1 else (1000,), float("nan"), dtype=torch.float16, device=DEV)
+    head_op = qd.LinearOp(qd.qpack_fp16(_gpu(w_head)), _gpu(x_head if m > 1 else x_head[0]), y_head,
+                          ops[-1].group + 1)
+    ops = ops[:-1] + [head_op]                       # replace the int8 head
+    meta = meta[:-1] + [("head16", w_head, x_head)]
+    for use_plan in (False, True):
+        for op in ops:
+            op.y.fill_(float("nan"))
+        if use_plan:
+            plan = qd.StackPlan(ops, m)
+            assert not plan.persistent
+            plan.run()
+        else:
+            qd.decode_linear_stack(ops, m)
+        for op, (pname, w, x) in zip(ops, meta):
+            fmt = "fp16" if pname == "head16" else "int8_b32"
+            parts = _oracle_parts(fmt, w)
+            Y = _host(op.y).reshape(m, -1)
+            Y_ref = linear.ref_linear(fmt, parts, x).reshape(m, -1)
+            rmax = linear.row_max_abs(fmt, parts)
+            for t in range(m):
+                check_vector(Y[t], Y_ref[t], rmax, x[t], f"{pname} token {t} plan={use_plan}")
+        if use_plan:
+            plan.close()
 
 
 def test_stack_chain_respects_order(qd):
@@ -285,7 +368,7 @@ def test_stack_chain_respects_order(qd):
 FULL = [("q", 4096, 4096), ("down", 4096, 12288), ("head", 151936, 4096)]
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name,n,k", FULL)
 def test_full_size_sampled(qd, fmt, name, n, k):
     """8B-shaped matrices at full size, in the launch configuration the bench
@@ -294,7 +377,7 @@ def test_full_size_sampled(qd, fmt, name, n, k):
     w_gpu = si.weights_torch(seed, n, k, DEV)
     pw = _pack(qd, fmt, w_gpu)
     x = si.activations(si.seed_for("full-x", name), 1, k)[0]
-    fn = qd.qgemv_int8_b32 if fmt == "int8_b32" else qd.qgemv_int4_g64
+    fn = _gemv_fn(qd, fmt)
     y = _host(fn(pw, _gpu(x)))
     rng = np.random.default_rng(3)
     R = -(-n // 16)
@@ -500,3 +583,34 @@ def test_stack_full_size_sampled_m16(qd, workload):
         rmax = linear.row_max_abs(wl.fmt, parts)
         for t in range(16):
             check_vector(Y[t], Y_ref[t], rmax, X[t], f"{name} token {t}")
+
+
+def test_stack_full_size_sampled_fp16_head(qd):
+    """The full 2B-shaped int8lin step (int8 b32 body, fp16 head 151936 x 2048)
+    as the bench times it: outputs finite, sampled rows match the oracle."""
+    import bench
+    workload = "qwen3-2b-int8-fp16head-m1"
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
+    for op in ops:
+        op.y.fill_(float("nan"))
+    plan = qd.StackPlan(ops, 1)
+    assert not plan.persistent                      # mixed formats replay the launches
+    plan.run()
+    torch.cuda.synchronize()
+    wl = si.WORKLOADS[workload]
+    names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
+    for op in ops:
+        assert torch.isfinite(op.y).all()
+    rng = np.random.default_rng(13)
+    for name in _sample_picks(wl.decoder):
+        op = ops[names.index(name)]
+        fmt = "fp16" if name == "head" else wl.fmt
+        assert op.w.fmt == fmt
+        n, k = op.w.n, op.w.k
+        rows = np.sort(rng.choice(n, 24, replace=False))
+        w_rows = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)[rows].cpu().numpy()
+        x = op.x.cpu().numpy()
+        parts = _oracle_parts(fmt, w_rows)
+        check_vector(_host(op.y)[rows], linear.ref_linear(fmt, parts, x), linear.row_max_abs(fmt, parts),
+                     x, f"{name} ({fmt})")
+    plan.close()
