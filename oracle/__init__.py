@@ -21,6 +21,10 @@ What it computes, and where each step comes from:
 * ``layout`` -- this library's tiled byte layout, rewritten here from its
   prose specification with numpy reshapes (no index arithmetic is shared with
   the HIP packer).
+* ``glue`` -- the element-wise steps either side of the projections: the
+  RMSNorm that feeds q|k|v and gate|up, and the SwiGLU that feeds down (zoo
+  Qwen3-VL page, Architecture paragraph, names a Qwen3 decoder with a SwiGLU
+  MLP; the formulas and the fp16 rounding points are readings).
 * ``linear`` -- the result: dequantize, then multiply, in fp64.  Decode is
   bandwidth-bound because every weight is read once per token (Core AI cards,
   Measured paragraph); the arithmetic is the plain matrix-vector product.
@@ -29,4 +33,4 @@ Readings of points the pages leave open are listed in each function's
 docstring.  Functions whose agreement with the pages rests only on such a
 reading are marked "parity unpinned" (the tiled layout, the INT4 format).
 """
-from . import quant, layout, linear  # noqa: F401
+from . import quant, layout, glue, linear  # noqa: F401

@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import quant
+from . import glue, quant
 
 ROW_CHUNK = 16384   # rows dequantized at a time, to bound memory
 
@@ -72,14 +72,26 @@ def ref_stack(ops):
     ``ops`` is a list of dicts with keys ``fmt``, ``parts`` (canonical
     quantized arrays), ``x`` (fp16 activation, [K] or [M, K]) or ``x_from``
     (index of an earlier op whose output, rounded to fp16, is this op's
-    input).  Returns the list of fp64 outputs.  An op fed by an earlier op
-    sees that op's output rounded to fp16, as a stored fp16 activation is.
+    input; for a SwiGLU prologue a pair [gate op, up op], whose outputs are
+    joined gate first), and optionally ``prologue`` = (kind, gamma, eps), the
+    glue of ``glue.apply_prologue`` that turns the given activation into the
+    multiplied one.  Returns the list of fp64 outputs.  An op fed by an earlier
+    op sees that op's output rounded to fp16, as a stored fp16 activation is.
     """
     outs = []
     for op in ops:
         if "x_from" in op:
-            x = outs[op["x_from"]].astype(np.float16)
+            src = op["x_from"]
+            if isinstance(src, (list, tuple)):
+                x = np.concatenate([outs[i].astype(np.float16).reshape(1, -1) if outs[i].ndim == 1
+                                    else outs[i].astype(np.float16) for i in src], axis=0)
+                if outs[src[0]].ndim == 1:
+                    x = x.reshape(-1)
+            else:
+                x = outs[src].astype(np.float16)
         else:
             x = op["x"]
+        kind, gamma, eps = op.get("prologue", ("none", None, 0.0))
+        x = glue.apply_prologue(kind, x, gamma, eps)
         outs.append(ref_linear(op["fmt"], op["parts"], x))
     return outs

@@ -510,3 +510,123 @@ def _golden_sizes():
             continue
         t = line.split()
         yield t[0], int(t[1]), int(t[2]), int(t[3]), int(t[4]), t[5], float(t[6])
+
+
+# ---------------------------------------------------------------- glue (RMSNorm, SwiGLU)
+
+def _golden_glue():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "glue_hand_values.txt")
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            yield line
+
+
+def test_glue_hand_values():
+    """Hand-derived values, including two double-rounding cases (gamma applied
+    to the stored fp16 normalised value; up applied to the stored fp16 silu)
+    and the tie cases, which a single rounding or another rounding mode fails."""
+    from oracle import glue
+    seen = {"rmsnorm": 0, "swiglu": 0}
+    for line in _golden_glue():
+        kind, rest = line.split(None, 1)
+        seen[kind] += 1
+        if kind == "rmsnorm":
+            head, gam, want = rest.split("|")
+            eps, *xs = head.split()
+            x = np.array([float(v) for v in xs], np.float16)
+            g = np.array([float(v) for v in gam.split()], np.float16)
+            got = glue.rmsnorm_fp16(x, g, float(eps))
+            assert got.dtype == np.float16
+            assert np.array_equal(got.astype(np.float64), [float(v) for v in want.split()]), line
+        else:
+            a, b, want = (float(v) for v in rest.split())
+            got = glue.swiglu_fp16(np.array([a], np.float16), np.array([b], np.float16))
+            assert got.dtype == np.float16 and float(got[0]) == want, (line, float(got[0]))
+            assert math.copysign(1.0, float(got[0])) == math.copysign(1.0, want), line
+    assert seen["rmsnorm"] >= 4 and seen["swiglu"] >= 6
+
+
+def test_rmsnorm_matches_library_rms_norm():
+    """torch's fp64 rms_norm (weight-free) rounded to fp16 is the oracle's
+    normalised value; with gamma the oracle applies it to that fp16 value."""
+    import torch
+    from oracle import glue
+    x = si.activations(71, 4, 1024)
+    g = (RNG.standard_normal(1024) * 0.3 + 1.0).astype(np.float16)
+    for eps in (1e-6, 1e-2):
+        n_lib = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (1024,),
+                                             eps=eps).numpy().astype(np.float16)
+        ones = np.ones(1024, np.float16)
+        n_or = glue.rmsnorm_fp16(x, ones, eps)
+        # the two fp64 statistics may differ in their last bit; that moves an
+        # fp16 rounding at most one step, and only next to a midpoint
+        diff = np.abs(n_or.astype(np.float64) - n_lib.astype(np.float64))
+        ulp = np.spacing(np.abs(n_lib).astype(np.float16)).astype(np.float64)
+        assert np.all(diff <= ulp) and np.mean(diff == 0) > 0.999
+        full = glue.rmsnorm_fp16(x, g, eps)
+        assert np.array_equal(full, (g.astype(np.float64) * n_or.astype(np.float64)).astype(np.float16))
+
+
+def test_rmsnorm_invariants():
+    """Per-token statistic (tokens do not mix), exact power-of-two scale
+    invariance when eps = 0, and the mean over K (not K - 1, not the sum)."""
+    from oracle import glue
+    x = si.activations(72, 3, 256)
+    g = np.full(256, 1.0, np.float16)
+    both = glue.rmsnorm_fp16(x, g, 0.0)
+    for t in range(3):
+        assert np.array_equal(both[t], glue.rmsnorm_fp16(x[t], g, 0.0))
+    x4 = (x.astype(np.float64) * 4).astype(np.float16)
+    assert np.array_equal(glue.rmsnorm_fp16(x4, g, 0.0), both)
+    # a token of K equal values v: mean(x^2) = v^2 exactly, so n = 1
+    for k in (2, 32, 256):
+        v = np.full(k, 0.375, np.float16)
+        assert np.all(glue.rmsnorm_fp16(v, np.ones(k, np.float16), 0.0) == 1.0)
+    assert np.all(np.isfinite(glue.rmsnorm_fp16(np.zeros(64, np.float16), np.ones(64, np.float16), 1e-6)))
+
+
+def test_silu_identities_and_library():
+    """silu(a) - silu(-a) = a, silu(a) = a * expit(a) (scipy's logistic), and
+    fp16(silu) with up = 1 is the SwiGLU output."""
+    from scipy.special import expit
+    from oracle import glue
+    a = np.concatenate([RNG.standard_normal(2000) * 4, np.linspace(-30, 30, 601)])
+    s = glue.silu(a)
+    assert np.allclose(s - glue.silu(-a), a, rtol=0, atol=1e-12 * np.maximum(1, np.abs(a)).max())
+    assert np.allclose(s, a * expit(a), rtol=1e-14, atol=1e-300)
+    a16 = a.astype(np.float16)
+    ones = np.ones_like(a16)
+    assert np.array_equal(glue.swiglu_fp16(a16, ones), glue.silu(a16).astype(np.float16))
+    # up = 2^j scales exactly (no overflow or subnormal results here)
+    big = a16[np.abs(glue.silu(a16)) > 1e-3]
+    for j in (-3, 1, 4):
+        u = np.full(big.shape, 2.0 ** j, np.float16)
+        assert np.array_equal(glue.swiglu_fp16(big, u).astype(np.float64),
+                              glue.swiglu_fp16(big, np.ones_like(big)).astype(np.float64) * 2.0 ** j)
+
+
+def test_prologue_layouts_and_stack():
+    """SwiGLU input layouts (one token: gate then up; M tokens: all gates then
+    all ups), and ref_stack feeding a SwiGLU op from a [gate, up] pair."""
+    from oracle import glue
+    a = si.activations(73, 3, 64)
+    b = si.activations(74, 3, 64)
+    want = glue.swiglu_fp16(a, b)
+    assert np.array_equal(glue.apply_prologue("swiglu", np.concatenate([a, b], 0)), want)
+    assert np.array_equal(glue.apply_prologue("swiglu", np.concatenate([a[1], b[1]])), want[1])
+    w_g, w_u, w_d = si.weights(75, 64, 128), si.weights(76, 64, 128), si.weights(77, 32, 64)
+    pg, pu, pd = (quant.quantize_int8_b32(w) for w in (w_g, w_u, w_d))
+    x = si.activations(78, 1, 128)[0]
+    gam = (RNG.standard_normal(128) * 0.2 + 1).astype(np.float16)
+    outs = linear.ref_stack([
+        {"fmt": "int8_b32", "parts": pg, "x": x, "prologue": ("rmsnorm", gam, 1e-6)},
+        {"fmt": "int8_b32", "parts": pu, "x": x, "prologue": ("rmsnorm", gam, 1e-6)},
+        {"fmt": "int8_b32", "parts": pd, "x_from": [0, 1], "prologue": ("swiglu", None, 0.0)}])
+    xn = glue.rmsnorm_fp16(x, gam, 1e-6)
+    g_ref = linear.ref_linear("int8_b32", pg, xn)
+    u_ref = linear.ref_linear("int8_b32", pu, xn)
+    assert np.array_equal(outs[0], g_ref) and np.array_equal(outs[1], u_ref)
+    h = glue.swiglu_fp16(g_ref.astype(np.float16), u_ref.astype(np.float16))
+    assert np.array_equal(outs[2], linear.ref_linear("int8_b32", pd, h))
