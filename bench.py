@@ -48,12 +48,13 @@ def log(msg):
 def build_stack(qd, si, torch, workload, dev):
     wl = si.WORKLOADS[workload]
     m = wl.m
+    if wl.glue:
+        return build_glue_stack(qd, si, torch, workload, dev)
     if wl.single is not None:
         n, k = wl.single
         groups, model = [("gemv", [("W", n, k)])], "single"
     else:
         groups, model = wl.decoder.groups(), wl.decoder.name
-    packers = {"int8_b32": qd.qpack_int8_b32, "int4_g64": qd.qpack_int4_g64, "fp16": qd.qpack_fp16}
     ops, alg_bytes, weight_bytes = [], 0, 0
     for gi, (gname, members) in enumerate(groups):
         k = members[0][2]
@@ -63,12 +64,84 @@ def build_stack(qd, si, torch, workload, dev):
         for pname, n, kk in members:
             w = si.weights_torch(si.matrix_seed(model, pname), n, kk, dev)
             fmt = wl.head_fmt if (pname == "head" and wl.head_fmt) else wl.fmt
-            pw = packers[fmt](w)
+            pw = PACKERS[fmt](qd)(w)
             del w
             y = torch.empty((m, n) if m > 1 else (n,), dtype=torch.float16, device=dev)
             ops.append(qd.LinearOp(pw, x_gpu, y, gi))
             alg_bytes += pw.blob.numel() + m * n * 2
             weight_bytes += pw.blob.numel()
+    torch.cuda.synchronize()
+    return ops, alg_bytes, weight_bytes, m
+
+
+PACKERS = {"int8_b32": lambda qd: qd.qpack_int8_b32, "int4_g64": lambda qd: qd.qpack_int4_g64,
+           "fp16": lambda qd: qd.qpack_fp16}
+GLUE_EPS = 1e-6
+
+
+def build_glue_stack(qd, si, torch, workload, dev):
+    """The decoder step chained through the fused glue: each layer's q|k|v
+    and gate|up read the RMSNorm of their input (the previous layer's down
+    output, the o output), gate stores silu, down reads the gated product of
+    the gate and up outputs, the head reads the RMSNorm of the last down
+    output.  o reads a synthetic attention output.  Algorithmic bytes add
+    the norm weights and down's second input block."""
+    wl = si.WORKLOADS[workload]
+    m, d = wl.m, wl.decoder
+    H, Q, I = d.hidden, d.q_dim, d.mlp
+    shape = (lambda n: (m, n) if m > 1 else (n,))
+    fmt = wl.fmt
+    ops, alg_bytes, weight_bytes = [], 0, 0
+    gi = 0
+
+    def add(pname, n, k, x, y, **glue):
+        nonlocal alg_bytes, weight_bytes
+        w = si.weights_torch(si.matrix_seed(d.name, pname), n, k, dev)
+        pw = PACKERS[fmt](qd)(w)
+        del w
+        ops.append(qd.LinearOp(pw, x, y, gi, **glue))
+        alg_bytes += pw.blob.numel() + m * n * 2
+        weight_bytes += pw.blob.numel()
+
+    def norm_w(*tag):
+        return torch.from_numpy(si.norm_weight(si.seed_for("gamma", d.name, *tag), H)).to(dev)
+
+    x_in = torch.from_numpy(si.activations(si.activation_seed(workload, "x0"), m, H)
+                            .reshape(shape(H))).to(dev)
+    for layer in range(d.layers):
+        g_attn, g_mlp = norm_w("attn", layer), norm_w("mlp", layer)
+        alg_bytes += m * H * 2 + H * 2
+        for pname, n in ((f"L{layer}.q", Q), (f"L{layer}.k", d.kv_dim), (f"L{layer}.v", d.kv_dim)):
+            add(pname, n, H, x_in, torch.empty(shape(n), dtype=torch.float16, device=dev),
+                prologue="rmsnorm", gamma=g_attn, eps=GLUE_EPS)
+        gi += 1
+        attn = torch.from_numpy(si.activations(si.activation_seed(workload, f"L{layer}.attn"), m, Q)
+                                .reshape(shape(Q))).to(dev)
+        o_y = torch.empty(shape(H), dtype=torch.float16, device=dev)
+        alg_bytes += m * Q * 2
+        add(f"L{layer}.o", H, Q, attn, o_y)
+        gi += 1
+        gu = torch.empty(2 * m * I, dtype=torch.float16, device=dev)
+        alg_bytes += m * H * 2 + H * 2
+        add(f"L{layer}.gate", I, H, o_y, gu[:m * I].view(shape(I)), prologue="rmsnorm", gamma=g_mlp,
+            eps=GLUE_EPS, epilogue="silu")
+        add(f"L{layer}.up", I, H, o_y, gu[m * I:].view(shape(I)), prologue="rmsnorm", gamma=g_mlp,
+            eps=GLUE_EPS)
+        gi += 1
+        x_in = torch.empty(shape(H), dtype=torch.float16, device=dev)
+        alg_bytes += 2 * m * I * 2
+        add(f"L{layer}.down", H, I, gu, x_in, prologue="glu")
+        gi += 1
+    g_fin = norm_w("final")
+    alg_bytes += m * H * 2 + H * 2
+    head_fmt = wl.head_fmt or fmt
+    w = si.weights_torch(si.matrix_seed(d.name, "head"), d.vocab, H, dev)
+    pw = PACKERS[head_fmt](qd)(w)
+    del w
+    ops.append(qd.LinearOp(pw, x_in, torch.empty(shape(d.vocab), dtype=torch.float16, device=dev), gi,
+                           prologue="rmsnorm", gamma=g_fin, eps=GLUE_EPS))
+    alg_bytes += pw.blob.numel() + m * d.vocab * 2
+    weight_bytes += pw.blob.numel()
     torch.cuda.synchronize()
     return ops, alg_bytes, weight_bytes, m
 
@@ -285,7 +358,10 @@ def main():
                    "read_probe_gbs": round(probe, 1), "frac_of_read_probe": round(value / probe, 4),
                    "us_p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
                    "us_p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2),
-                   "tok_per_s_note": "linear stack only; excludes attention, norms and embedding"},
+                   "glue": wl.glue,
+                   "tok_per_s_note": ("linear stack with fused RMSNorm and SwiGLU glue; excludes attention, "
+                                      "residual adds and embedding" if wl.glue else
+                                      "linear stack only; excludes attention, norms and embedding")},
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname,

@@ -148,19 +148,51 @@ qd_status qgemv_fp16(const qd_weight* w, const uint16_t* x, uint16_t* y, void* s
 qd_status qgemm_small_m(const qd_weight* w, const uint16_t* x, uint16_t* y, int64_t m, void* stream);
 
 /*
+ * Glue fused into a stack op (zoo Qwen3-VL page, Architecture paragraph: a
+ * Qwen3 decoder, whose projections are fed by an RMSNorm (q|k|v, gate|up) and
+ * by the SwiGLU of the gate and up outputs (down)).  The pages print neither
+ * formula; the readings are an fp16 model's, with fp32 arithmetic inside:
+ *
+ * Prologue (how the op's x becomes the vector it multiplies), per token:
+ *   QD_PRO_NONE     x itself.
+ *   QD_PRO_RMSNORM  u_k = fp16(gamma_k * fp16(x_k * r)), r = 1 / sqrt(mean_k
+ *                   x_k^2 + eps), the mean over the op's K.  `gamma` is fp16
+ *                   [K] (device, 16-byte aligned), eps finite and > 0.
+ *   QD_PRO_GLU      x holds two fp16 blocks of m x K values, A then B
+ *                   (A = x[0 .. mK), B = x[mK .. 2mK), rows of m tokens), and
+ *                   u = fp16(A * B) element-wise (one correctly rounded
+ *                   product).  With A the gate output under QD_EPI_SILU and B
+ *                   the up output this is the SwiGLU h = fp16(fp16(silu(gate))
+ *                   * up): point the up op's y at the gate op's y + m * K.
+ * Epilogue (what the op stores):
+ *   QD_EPI_NONE     y = fp16(W^ u).
+ *   QD_EPI_SILU     y = fp16(silu(fp16(W^ u))), silu(a) = a / (1 + e^-a).
+ */
+typedef enum { QD_PRO_NONE = 0, QD_PRO_RMSNORM = 1, QD_PRO_GLU = 2 } qd_prologue;
+typedef enum { QD_EPI_NONE = 0, QD_EPI_SILU = 1 } qd_epilogue;
+
+/*
  * One decode step's linear layers, issued back to back on one stream.
- * ops[i] computes ops[i].y = W^_i ops[i].x (m token rows).  Consecutive ops
- * with equal `group` form one group: they must share x, K and format and are
- * fused into one launch.  Group g+1 starts only after group g has written all
- * its outputs, so a later op's x may be an earlier group's y (a dependent
- * chain).  All ops use the same m (1..16, either format).
+ * ops[i] computes ops[i].y = W^_i ops[i].x (m token rows), with the op's
+ * prologue and epilogue.  Consecutive ops with equal `group` form one group:
+ * they must share x, K, format and prologue (with its gamma and eps) and are
+ * fused into one launch; the epilogue is per op.  Group g+1 starts only after
+ * group g has written all its outputs, so a later op's x may be an earlier
+ * group's y (a dependent chain).  All ops use the same m (1..16, any format).
+ * A prologue other than QD_PRO_NONE, or an unknown epilogue, on an op whose
+ * gamma or eps do not match it is QD_EINVAL (gamma must be NULL and eps 0
+ * unless the prologue is QD_PRO_RMSNORM); so is x overlapping any op's y in
+ * its own group.
  */
 typedef struct {
   qd_weight w;
-  const uint16_t* x;
-  uint16_t* y;
+  const uint16_t* x;      /* fp16 [m, K]; [2, m, K] under QD_PRO_GLU */
+  uint16_t* y;            /* fp16 [m, N] */
   int32_t group;
-  int32_t reserved;
+  int32_t prologue;       /* qd_prologue */
+  const uint16_t* gamma;  /* QD_PRO_RMSNORM weight, fp16 [K]; else NULL */
+  float eps;              /* QD_PRO_RMSNORM epsilon; else 0 */
+  int32_t epilogue;       /* qd_epilogue */
 } qd_linear_op;
 
 qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m, void* stream);
@@ -177,9 +209,9 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * valid while the plan lives.  qd_stack_plan_run enqueues one step on
  * `stream` and allocates nothing.  A plan may be run repeatedly but not
  * concurrently.  Steps the persistent kernel does not take (m > 1, mixed
- * formats, a schedule larger than one CU's LDS) are replayed as the same
- * per-group launches decode_linear_stack makes, with the same results;
- * qd_stack_plan_is_persistent tells which.
+ * formats, a schedule larger than one CU's LDS, any op with a prologue or an
+ * epilogue) are replayed as the same per-group launches decode_linear_stack
+ * makes, with the same results; qd_stack_plan_is_persistent tells which.
  */
 typedef struct qd_stack_plan qd_stack_plan;
 

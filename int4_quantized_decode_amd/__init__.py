@@ -13,13 +13,14 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import (QD_FMT_FP16, QD_FMT_INT4_G64, QD_FMT_INT8_B32, QD_MAX_K, QD_MAX_M, QDError, QDLinearOp,
-                   QDWeight, check, lib)
+from ._lib import (QD_EPI_NONE, QD_EPI_SILU, QD_FMT_FP16, QD_FMT_INT4_G64, QD_FMT_INT8_B32, QD_MAX_K,
+                   QD_MAX_M, QD_PRO_GLU, QD_PRO_NONE, QD_PRO_RMSNORM, QDError, QDLinearOp, QDWeight,
+                   check, lib)
 
 __all__ = [
     "FORMATS", "PackedWeight", "QDError", "packed_bytes", "qpack_int8_b32", "qpack_int4_g64",
     "qpack_fp16", "qgemv_int8_b32", "qgemv_int4_g64", "qgemv_fp16", "qgemm_small_m", "decode_linear_stack", "StackPlan",
-    "QD_MAX_K", "QD_MAX_M",
+    "QD_MAX_K", "QD_MAX_M", "LinearOp", "PROLOGUES", "EPILOGUES",
 ]
 
 FORMATS = {"int8_b32": QD_FMT_INT8_B32, "int4_g64": QD_FMT_INT4_G64, "fp16": QD_FMT_FP16}
@@ -152,20 +153,35 @@ def qgemm_small_m(w: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = Non
     return y
 
 
+PROLOGUES = {"none": QD_PRO_NONE, "rmsnorm": QD_PRO_RMSNORM, "glu": QD_PRO_GLU}
+EPILOGUES = {"none": QD_EPI_NONE, "silu": QD_EPI_SILU}
+
+
 @dataclass
 class LinearOp:
     """One projection of a decode step: y = W^ x.  Ops with equal `group`
-    (consecutive) share x and run fused."""
+    (consecutive) share x and run fused.
+
+    prologue "rmsnorm" multiplies fp16(gamma * fp16(x * r)), r = 1 /
+    sqrt(mean(x^2) + eps) per token; "glu" takes x as two blocks of [m, K]
+    (A then B) and multiplies fp16(A * B).  epilogue "silu" stores
+    fp16(silu(fp16(W^ u))).  The formulas are in include/qdecode.h."""
     w: PackedWeight
     x: torch.Tensor
     y: torch.Tensor
     group: int
+    prologue: str = "none"
+    gamma: torch.Tensor | None = None
+    eps: float = 0.0
+    epilogue: str = "none"
 
 
 def _op_array(ops):
     arr = (QDLinearOp * max(1, len(ops)))()
     for i, op in enumerate(ops):
-        arr[i] = QDLinearOp(op.w.desc(), _ptr(op.x), _ptr(op.y), op.group, 0)
+        arr[i] = QDLinearOp(op.w.desc(), _ptr(op.x), _ptr(op.y), op.group, PROLOGUES[op.prologue],
+                            _ptr(op.gamma) if op.gamma is not None else None, op.eps,
+                            EPILOGUES[op.epilogue])
     return arr
 
 

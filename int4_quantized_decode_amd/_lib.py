@@ -28,9 +28,14 @@ class QDWeight(ctypes.Structure):
                 ("data", ctypes.c_void_p), ("bytes", ctypes.c_uint64)]
 
 
+QD_PRO_NONE, QD_PRO_RMSNORM, QD_PRO_GLU = 0, 1, 2
+QD_EPI_NONE, QD_EPI_SILU = 0, 1
+
+
 class QDLinearOp(ctypes.Structure):
     _fields_ = [("w", QDWeight), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("prologue", ctypes.c_int32),
+                ("gamma", ctypes.c_void_p), ("eps", ctypes.c_float), ("epilogue", ctypes.c_int32)]
 
 
 # name -> (restype, argtypes), mirroring include/qdecode.h
@@ -77,7 +82,7 @@ class QDError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "(or python -m int4_quantized_decode_amd.build)")
+                          "(or python int4_quantized_decode_amd/build.py)")
     so = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(so, name)

@@ -1,5 +1,7 @@
 // C ABI of libqdecode: host-side validation, then enqueue on the caller's
 // stream.  Nothing here allocates except qd_stack_plan_create.
+#include <cmath>
+#include <cstddef>
 #include <new>
 #include <vector>
 
@@ -9,6 +11,10 @@
 #define QD_EXPORT extern "C" __attribute__((visibility("default")))
 
 using namespace qd;
+
+static_assert(sizeof(qd_linear_op) == 80 && offsetof(qd_linear_op, gamma) == 64 &&
+                  offsetof(qd_linear_op, eps) == 72 && offsetof(qd_linear_op, epilogue) == 76,
+              "qd_linear_op layout is part of the ABI");
 
 namespace {
 
@@ -42,22 +48,24 @@ qd_status check_weight(const qd_weight* w, int32_t want_fmt) {
   return QD_OK;
 }
 
-// x, y of one product with m token rows.
-qd_status check_io(const qd_weight* w, const uint16_t* x, const uint16_t* y, int64_t m) {
+// x, y of one product with m token rows; x holds x_blocks blocks of m x K
+// values (2 for a gated-product prologue).
+qd_status check_io(const qd_weight* w, const uint16_t* x, const uint16_t* y, int64_t m,
+                   int x_blocks = 1) {
   if (w->n == 0) return QD_OK;
   if (!y) return QD_EINVAL;
   if ((uintptr_t)y % 2) return QD_EALIGN;
   if (w->k == 0) return QD_OK;
   if (!x) return QD_EINVAL;
   if ((uintptr_t)x % 16) return QD_EALIGN;
-  const uint64_t ybytes = (uint64_t)m * w->n * 2, xbytes = (uint64_t)m * w->k * 2;
+  const uint64_t ybytes = (uint64_t)m * w->n * 2, xbytes = (uint64_t)x_blocks * m * w->k * 2;
   if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, w->data, w->bytes)) return QD_EINVAL;
   return QD_OK;
 }
 
 LinearArgs single_args(const qd_weight* w, const uint16_t* x, uint16_t* y, int64_t m) {
   LinearArgs a{};
-  a.mem[0] = Member{static_cast<const uint8_t*>(w->data), y, w->n, 0};
+  a.mem[0] = Member{static_cast<const uint8_t*>(w->data), y, w->n, 0, QD_EPI_NONE};
   a.n_mem = 1;
   a.J = (int)ceil_div(w->k, kSuperK);
   a.k = w->k;
@@ -219,7 +227,20 @@ namespace qd {
 qd_status validate_op(const qd_linear_op& op, int64_t m) {
   qd_status st = check_weight(&op.w, 0);
   if (st != QD_OK) return st;
-  return check_io(&op.w, op.x, op.y, m);
+  if (op.epilogue != QD_EPI_NONE && op.epilogue != QD_EPI_SILU) return QD_EINVAL;
+  if (op.prologue == QD_PRO_RMSNORM) {
+    if (!(std::isfinite(op.eps) && op.eps > 0.0f)) return QD_EINVAL;
+    if (op.w.n > 0 && op.w.k > 0) {
+      if (!op.gamma) return QD_EINVAL;
+      if ((uintptr_t)op.gamma % 16) return QD_EALIGN;
+      if (overlaps(op.y, (uint64_t)m * op.w.n * 2, op.gamma, (uint64_t)op.w.k * 2)) return QD_EINVAL;
+    }
+  } else if (op.prologue == QD_PRO_NONE || op.prologue == QD_PRO_GLU) {
+    if (op.gamma || op.eps != 0.0f) return QD_EINVAL;
+  } else {
+    return QD_EINVAL;
+  }
+  return check_io(&op.w, op.x, op.y, m, op.prologue == QD_PRO_GLU ? 2 : 1);
 }
 
 }  // namespace qd

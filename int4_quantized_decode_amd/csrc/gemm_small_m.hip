@@ -21,6 +21,11 @@
 // w^ = min + c s per group, y += s * sum(c x) + min * sum(x): the activation
 // sums come from the same two MFMAs run with an all-ones B operand, whose
 // every output column is the sum over the group for that token.
+//
+// Glue: the op's prologue is applied to each A operand as it is loaded (the
+// RMSNorm factor of every token is formed once per workgroup first), and its
+// epilogue at the store.
+#include "glue.h"
 #include "qd_internal.h"
 #include "tiles.h"
 
@@ -32,10 +37,11 @@ struct Owner {
   uint16_t* y;
   int64_t n;
   int64_t local_rg;
+  int epi;
 };
 
 __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
-  Owner o{a.mem[0].blob, a.mem[0].y, a.mem[0].n, rg};
+  Owner o{a.mem[0].blob, a.mem[0].y, a.mem[0].n, rg, a.mem[0].epi};
 #pragma unroll
   for (int i = 1; i < kMaxMembers; ++i) {
     if (i < a.n_mem && rg >= a.mem[i].rg_begin) {
@@ -43,9 +49,63 @@ __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
       o.y = a.mem[i].y;
       o.n = a.mem[i].n;
       o.local_rg = rg - a.mem[i].rg_begin;
+      o.epi = a.mem[i].epi;
     }
   }
   return o;
+}
+
+// Where a lane's A operands come from: X rows (token m_row), or the two
+// blocks of a gated product, or X rows with the token's RMSNorm factor r and
+// gamma.  Rows m >= M fall outside the descriptors and read as zeros.
+struct ASrc {
+  __amdgpu_buffer_rsrc_t rx, rb, rg;
+  float r;
+};
+
+// Called by every thread of the workgroup (it may hold a barrier).  Under
+// RMSNorm, wave w forms the factor of tokens w, w + WAVES, ...: each lane
+// sums the squares of its 8-value chunks with eight loads in flight, then the
+// wave adds the lanes' sums in a fixed order.
+template <int WAVES, int PRO>
+__device__ inline ASrc make_asrc(const LinearArgs& a, int m_row, int wave, int lane) {
+  const uint32_t xbytes = (uint32_t)(a.m * a.k * 2);
+  constexpr bool glu = PRO == QD_PRO_GLU, rms = PRO == QD_PRO_RMSNORM;
+  ASrc s;
+  s.rx = make_rsrc(a.x, xbytes);
+  s.rb = make_rsrc(glu ? a.x + (int64_t)a.m * a.k : a.x, glu ? xbytes : 0u);
+  s.rg = make_rsrc(rms ? a.gamma : a.x, rms ? (uint32_t)(a.k * 2) : 0u);
+  s.r = 0.0f;
+  if constexpr (rms) {
+    __shared__ float rinv[QD_MAX_M];
+    const int64_t K = a.k;
+    for (int t = wave; t < a.m; t += WAVES) {
+      float ss = 0.0f;
+      for (int64_t i0 = lane * 8; i0 < K; i0 += 512 * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = bload16(s.rx, (uint32_t)((t * K + i0 + 512 * u) * 2));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + 512 * u < K) ss = sumsq8(v[u], ss);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) rinv[t] = rms_inverse(ss, K, a.eps);
+    }
+    __syncthreads();
+    s.r = m_row < a.m ? rinv[m_row] : 0.0f;
+  }
+  return s;
+}
+
+// The 8 multiplied values X'[m_row][kk .. kk + 8) (zero past K).
+template <int PRO>
+__device__ inline half8_t load_a(const ASrc& s, int64_t K, int m_row, int64_t kk) {
+  const uint32_t off = (uint32_t)((m_row * K + kk) * 2);
+  u32x4 v = bload16(s.rx, off);
+  if constexpr (PRO == QD_PRO_GLU) v = glu8(v, bload16(s.rb, off));
+  if constexpr (PRO == QD_PRO_RMSNORM) v = rms8(v, s.r, bload16(s.rg, (uint32_t)(kk * 2)));
+  return kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
 }
 
 // One workgroup: RG consecutive row-groups (16 weight rows each) x all of K.
@@ -53,7 +113,7 @@ __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
 // activation block X[0..15][j*256 .. j*256+255] once (8 A operands) and the
 // RG weight tiles of that super-block, and issues RG x 8 MFMAs, so each
 // activation block read from L2 serves RG tiles.
-template <int WAVES, int RG>
+template <int WAVES, int RG, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -69,10 +129,9 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
     o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
     rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
   }
-  // X rows m >= M fall outside the descriptor and read as zeros.
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
   const int64_t K = a.k;
   const int m_row = rho;   // A operand row held by this lane
+  const ASrc src = make_asrc<WAVES, PRO>(a, m_row, wave, lane);
 
   float4_t acc[RG];
 #pragma unroll
@@ -90,8 +149,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
-      const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
-      xa[b] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
+      xa[b] = load_a<PRO>(src, K, m_row, kk);
     }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
@@ -134,7 +192,9 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+        if (m < a.m)
+          ow.y[(int64_t)m * ow.n + row] =
+              EPI ? epilogue_bits(sum[i], ow.epi) : __builtin_bit_cast(uint16_t, (half_t)sum[i]);
       }
     }
   }
@@ -142,7 +202,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
 
 // fp16 weights (the unquantized head): chunk s of a tile is already the B
 // operand of block s; no dequantization and no scale.
-template <int WAVES, int RG>
+template <int WAVES, int RG, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -156,9 +216,9 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) 
     o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
     rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
   }
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
   const int64_t K = a.k;
   const int m_row = rho;
+  const ASrc src = make_asrc<WAVES, PRO>(a, m_row, wave, lane);
 
   float4_t acc[RG];
 #pragma unroll
@@ -175,8 +235,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) 
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
-      const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
-      xa[b] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
+      xa[b] = load_a<PRO>(src, K, m_row, kk);
     }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
@@ -208,14 +267,16 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+        if (m < a.m)
+          ow.y[(int64_t)m * ow.n + row] =
+              EPI ? epilogue_bits(sum[i], ow.epi) : __builtin_bit_cast(uint16_t, (half_t)sum[i]);
       }
     }
   }
 }
 
 // INT4 g64: one workgroup = RG row-groups x all of K, waves along K (as above).
-template <int WAVES, int RG>
+template <int WAVES, int RG, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -229,9 +290,9 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
     o[r] = find_owner(a, rg < a.total_rg ? rg : a.total_rg - 1);
     rw[r] = make_rsrc(o[r].blob + o[r].local_rg * (int64_t)span, rg < a.total_rg ? span : 0u);
   }
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.m * a.k * 2));
   const int64_t K = a.k;
   const int m_row = rho;
+  const ASrc src = make_asrc<WAVES, PRO>(a, m_row, wave, lane);
   const half_t one = (half_t)1.0f;
   const half8_t ones = {one, one, one, one, one, one, one, one};
   const half2_t minus1024 = {(half_t)-1024.0f, (half_t)-1024.0f};
@@ -253,8 +314,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int64_t kk = (int64_t)j * kSuperK + 64 * (q >> 1) + 16 * g + 8 * (q & 1);
-      const u32x4 v = bload16(rx, (uint32_t)((m_row * K + kk) * 2));
-      xa[q] = kk < K ? __builtin_bit_cast(half8_t, v) : (half8_t){};
+      xa[q] = load_a<PRO>(src, K, m_row, kk);
     }
     // Per group: sum of x over its 64 positions, for this lane's tokens.
     float4_t xs[4];
@@ -312,16 +372,16 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < a.m) ow.y[(int64_t)m * ow.n + row] = __builtin_bit_cast(uint16_t, (half_t)sum[i]);
+        if (m < a.m)
+          ow.y[(int64_t)m * ow.n + row] =
+              EPI ? epilogue_bits(sum[i], ow.epi) : __builtin_bit_cast(uint16_t, (half_t)sum[i]);
       }
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
-  if (a.total_rg == 0) return hipSuccess;
+template <int PRO, bool EPI>
+hipError_t launch_small_m_pro(int fmt, const LinearArgs& a, hipStream_t s) {
   const bool int4 = fmt == QD_FMT_INT4_G64, fp16 = fmt == QD_FMT_FP16;
   if (!int4 && !fp16 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
   // Enough row-groups to give every CU several: 4 per workgroup, 8 waves
@@ -329,28 +389,44 @@ hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
   // workgroup and up to 16 waves along K.
   if (a.total_rg >= 4 * 256 && a.J >= 8) {
     const dim3 grid((uint32_t)ceil_div(a.total_rg, 4));
-    if (int4) hipLaunchKernelGGL((small_m_int4_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
-    else if (fp16) hipLaunchKernelGGL((small_m_fp16_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int8_kernel<8, 4>), grid, dim3(8 * 64), 0, s, a);
+    if (int4) hipLaunchKernelGGL((small_m_int4_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
+    else if (fp16) hipLaunchKernelGGL((small_m_fp16_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int8_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
     return hipGetLastError();
   }
   const dim3 grid((uint32_t)a.total_rg);
   int w = 16;
   while (w > 4 && (w > a.J || a.total_rg * w > 256 * 32)) w /= 2;
   if (fp16) {
-    if (w == 16) hipLaunchKernelGGL((small_m_fp16_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_fp16_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_fp16_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+    if (w == 16) hipLaunchKernelGGL((small_m_fp16_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_fp16_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_fp16_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
   } else if (int4) {
-    if (w == 16) hipLaunchKernelGGL((small_m_int4_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_int4_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int4_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+    if (w == 16) hipLaunchKernelGGL((small_m_int4_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_int4_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int4_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
   } else {
-    if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int8_kernel<4, 1>), grid, dim3(4 * 64), 0, s, a);
+    if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
+    else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((small_m_int8_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The prologue and the presence of an epilogue are template parameters: the
+// kernels without glue are the plain ones, with nothing of the glue in them.
+hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
+  if (a.total_rg == 0) return hipSuccess;
+  const bool epi = has_glue(a);     // any epilogue (or prologue): the storing kernels
+  switch (a.pro) {
+    case QD_PRO_RMSNORM: return launch_small_m_pro<QD_PRO_RMSNORM, true>(fmt, a, s);
+    case QD_PRO_GLU: return launch_small_m_pro<QD_PRO_GLU, true>(fmt, a, s);
+    default:
+      return epi ? launch_small_m_pro<QD_PRO_NONE, true>(fmt, a, s)
+                 : launch_small_m_pro<QD_PRO_NONE, false>(fmt, a, s);
+  }
 }
 
 }  // namespace qd

@@ -17,7 +17,11 @@
 //     bias folded into the group's min term.  Products run on v_dot2 with
 //     fp32 accumulation; the block scale is applied once per 8 codes;
 //   * per-row partial sums are reduced across the 4 lanes of a row with lane
-//     shuffles, then across waves through LDS, and rounded once to fp16.
+//     shuffles, then across waves through LDS, and rounded once to fp16;
+//   * the op's prologue (RMSNorm, gated product) is applied while x is staged
+//     and its epilogue (silu) at the store, so the glue costs no pass of its
+//     own.
+#include "glue.h"
 #include "qd_internal.h"
 #include "tiles.h"
 
@@ -30,10 +34,11 @@ struct Owner {
   uint16_t* y;
   int64_t n;
   int64_t local_rg;
+  int epi;
 };
 
 __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
-  Owner o{a.mem[0].blob, a.mem[0].y, a.mem[0].n, rg};
+  Owner o{a.mem[0].blob, a.mem[0].y, a.mem[0].n, rg, a.mem[0].epi};
 #pragma unroll
   for (int i = 1; i < kMaxMembers; ++i) {
     if (i < a.n_mem && rg >= a.mem[i].rg_begin) {
@@ -41,25 +46,59 @@ __device__ inline Owner find_owner(const LinearArgs& a, int64_t rg) {
       o.y = a.mem[i].y;
       o.n = a.mem[i].n;
       o.local_rg = rg - a.mem[i].rg_begin;
+      o.epi = a.mem[i].epi;
     }
   }
   return o;
 }
 
-// Stage x (fp16 [k], zero beyond k) into LDS, 16 bytes per thread per step.
-template <int THREADS>
-__device__ inline void stage_x(const LinearArgs& a, half_t* xs) {
+// Stage the multiplied vector (fp16 [k], zero beyond k) into LDS, 16 bytes per
+// thread per step, applying the prologue.  Under RMSNorm the raw x goes to
+// xs and gamma to `aux` (J * 256 halves) in the same pass; after one barrier
+// every thread forms the statistic from the per-wave sums in the same order
+// and normalises its own chunks.  The caller's barrier follows.
+template <int THREADS, bool GLUE>
+__device__ inline void stage_x(const LinearArgs& a, half_t* xs, half_t* aux) {
   const int Kp = a.J * kSuperK;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.k * 2));
+  const uint32_t xbytes = (uint32_t)(a.k * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, xbytes);
+  if (!GLUE || a.pro == QD_PRO_NONE) {
+    for (int i = threadIdx.x * 8; i < Kp; i += THREADS * 8)
+      *reinterpret_cast<u32x4*>(xs + i) = bload16(rx, (uint32_t)i * 2);
+    return;
+  }
+  if (a.pro == QD_PRO_GLU) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.x + a.k, xbytes);   // one token: B follows A
+    for (int i = threadIdx.x * 8; i < Kp; i += THREADS * 8)
+      *reinterpret_cast<u32x4*>(xs + i) = glu8(bload16(rx, (uint32_t)i * 2), bload16(rb, (uint32_t)i * 2));
+    return;
+  }
+  __shared__ float wsum[THREADS / 64];
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gamma, xbytes);
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 8; i < Kp; i += THREADS * 8) {
+    const u32x4 v = bload16(rx, (uint32_t)i * 2);
+    *reinterpret_cast<u32x4*>(aux + i) = bload16(rg, (uint32_t)i * 2);
+    *reinterpret_cast<u32x4*>(xs + i) = v;
+    ss = sumsq8(v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < THREADS / 64; ++w) tot += wsum[w];
+  const float r = rms_inverse(tot, a.k, a.eps);
   for (int i = threadIdx.x * 8; i < Kp; i += THREADS * 8)
-    *reinterpret_cast<u32x4*>(xs + i) = bload16(rx, (uint32_t)i * 2);
+    *reinterpret_cast<u32x4*>(xs + i) =
+        rms8(*reinterpret_cast<const u32x4*>(xs + i), r, *reinterpret_cast<const u32x4*>(aux + i));
 }
 
 // Each wave owns super-blocks j = wave + t * WAVES, t < TPW, of one row-group,
 // and WAVES * TPW >= J.  All of a wave's tile loads are issued in straight-line
 // code before any of them is consumed; a tile past the row-group reads as
 // zeros (no traffic) and contributes nothing, so no branch guards a load.
-template <int WAVES, int TPW>
+template <int WAVES, int TPW, bool GLUE>
 __global__ __launch_bounds__(WAVES * 64) void gemv_int8_kernel(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int J = a.J;
@@ -74,7 +113,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int8_kernel(LinearArgs a) {
   Tile8 T[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) T[t] = load_tile8(rw, wave + t * WAVES, lane);
-  stage_x<WAVES * 64>(a, xs);
+  stage_x<WAVES * 64, GLUE>(a, xs, reinterpret_cast<half_t*>(red + WAVES * 16));
   __syncthreads();
 
   float acc = 0.0f;
@@ -92,11 +131,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int8_kernel(LinearArgs a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[w * 16 + lane];
     const int64_t row = o.local_rg * kTileRows + lane;
-    if (row < o.n) o.y[row] = __builtin_bit_cast(uint16_t, (half_t)sum);
+    if (row < o.n) o.y[row] = GLUE ? epilogue_bits(sum, o.epi) : __builtin_bit_cast(uint16_t, (half_t)sum);
   }
 }
 
-template <int WAVES, int TPW>
+template <int WAVES, int TPW, bool GLUE>
 __global__ __launch_bounds__(WAVES * 64) void gemv_int4_kernel(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int J = a.J;
@@ -112,7 +151,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int4_kernel(LinearArgs a) {
   Tile4 T[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) T[t] = load_tile4(rw, wave + t * WAVES, lane);
-  stage_x<WAVES * 64>(a, xs);
+  stage_x<WAVES * 64, GLUE>(a, xs, reinterpret_cast<half_t*>(red + WAVES * 16));
   __syncthreads();
   // Sum of each 16-value run of x at k = 256j + 64 gamma + 16 g, stored at
   // index 16 j + 4 g + gamma.
@@ -144,7 +183,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int4_kernel(LinearArgs a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[w * 16 + lane];
     const int64_t row = o.local_rg * kTileRows + lane;
-    if (row < o.n) o.y[row] = __builtin_bit_cast(uint16_t, (half_t)sum);
+    if (row < o.n) o.y[row] = GLUE ? epilogue_bits(sum, o.epi) : __builtin_bit_cast(uint16_t, (half_t)sum);
   }
 }
 
@@ -153,7 +192,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_int4_kernel(LinearArgs a) {
 // computing the previous one.
 constexpr int kBatch16 = 3;
 
-template <int WAVES, int TPW>
+template <int WAVES, int TPW, bool GLUE>
 __global__ __launch_bounds__(WAVES * 64) void gemv_fp16_kernel(LinearArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int J = a.J;
@@ -169,7 +208,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp16_kernel(LinearArgs a) {
   Tile16 T[B];
 #pragma unroll
   for (int t = 0; t < B; ++t) T[t] = load_tile16(rw, wave + t * WAVES, lane);
-  stage_x<WAVES * 64>(a, xs);
+  stage_x<WAVES * 64, GLUE>(a, xs, reinterpret_cast<half_t*>(red + WAVES * 16));
   __syncthreads();
 
   float acc = 0.0f;
@@ -197,7 +236,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_fp16_kernel(LinearArgs a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[w * 16 + lane];
     const int64_t row = o.local_rg * kTileRows + lane;
-    if (row < o.n) o.y[row] = __builtin_bit_cast(uint16_t, (half_t)sum);
+    if (row < o.n) o.y[row] = GLUE ? epilogue_bits(sum, o.epi) : __builtin_bit_cast(uint16_t, (half_t)sum);
   }
 }
 
@@ -215,12 +254,20 @@ void pick_shape(int64_t total_rg, int J, int* waves, int* tpw) {
   *tpw = t;
 }
 
+// GLUE selects the kernels that apply a prologue or epilogue; the others are
+// the plain ones, with nothing of the glue in them.
 template <int W, int TPW>
 void launch_one(int fmt, const LinearArgs& a, hipStream_t s, size_t lds) {
   const dim3 grid((uint32_t)a.total_rg), block(W * 64);
-  if (fmt == QD_FMT_INT8_B32) hipLaunchKernelGGL((gemv_int8_kernel<W, TPW>), grid, block, lds, s, a);
-  else if (fmt == QD_FMT_INT4_G64) hipLaunchKernelGGL((gemv_int4_kernel<W, TPW>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((gemv_fp16_kernel<W, TPW>), grid, block, lds, s, a);
+  if (has_glue(a)) {
+    if (fmt == QD_FMT_INT8_B32) hipLaunchKernelGGL((gemv_int8_kernel<W, TPW, true>), grid, block, lds, s, a);
+    else if (fmt == QD_FMT_INT4_G64) hipLaunchKernelGGL((gemv_int4_kernel<W, TPW, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((gemv_fp16_kernel<W, TPW, true>), grid, block, lds, s, a);
+  } else {
+    if (fmt == QD_FMT_INT8_B32) hipLaunchKernelGGL((gemv_int8_kernel<W, TPW, false>), grid, block, lds, s, a);
+    else if (fmt == QD_FMT_INT4_G64) hipLaunchKernelGGL((gemv_int4_kernel<W, TPW, false>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((gemv_fp16_kernel<W, TPW, false>), grid, block, lds, s, a);
+  }
 }
 
 template <int W>
@@ -243,6 +290,7 @@ hipError_t launch_gemv(int fmt, const LinearArgs& a, hipStream_t s) {
   pick_shape(a.total_rg, a.J, &W, &TPW);
   size_t lds = (size_t)a.J * kSuperK * 2 + (size_t)W * 16 * 4;
   if (fmt == QD_FMT_INT4_G64) lds += (size_t)a.J * 16 * 4;
+  if (a.pro == QD_PRO_RMSNORM) lds += (size_t)a.J * kSuperK * 2;   // gamma
   if (W == 16) launch_w<16>(fmt, TPW, a, s, lds);
   else if (W == 8) launch_w<8>(fmt, TPW, a, s, lds);
   else launch_w<4>(fmt, TPW, a, s, lds);

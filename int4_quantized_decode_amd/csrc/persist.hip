@@ -43,6 +43,7 @@
 #include <new>
 #include <vector>
 
+#include "glue.h"
 #include "stack.h"
 #include "tiles.h"
 
@@ -57,13 +58,16 @@ constexpr int kCtl = 15;                // the control wave
 // stalls.  The plan picks R from the step's shape (see plan_create).
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
 
-struct PGroup {         // 32 bytes
+struct PGroup {         // 48 bytes
   const uint16_t* x;
+  const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
   int64_t k;
   int32_t J;            // super-blocks per row
   int32_t R;            // row-groups in the group
   int32_t mem0;         // first member in the member table
   int32_t n_mem;
+  int32_t pro;          // qd_prologue of the group's input
+  float eps;
 };
 
 struct PMember {        // 32 bytes
@@ -71,7 +75,7 @@ struct PMember {        // 32 bytes
   uint16_t* y;
   int64_t n;
   int32_t rg_begin;     // first row-group of this member within its group
-  int32_t pad;
+  int32_t epi;          // qd_epilogue of this member's outputs
 };
 
 struct PSched {         // 16 bytes: one workgroup's part of one group
@@ -81,7 +85,7 @@ struct PSched {         // 16 bytes: one workgroup's part of one group
   int32_t stride;       // distance between this workgroup's successive row-groups
 };
 
-static_assert(sizeof(PGroup) == 32 && sizeof(PMember) == 32 && sizeof(PSched) == 16,
+static_assert(sizeof(PGroup) % 16 == 0 && sizeof(PMember) % 16 == 0 && sizeof(PSched) == 16,
               "schedule records are copied to LDS in 16-byte units");
 
 struct PlanArgs {
@@ -94,7 +98,7 @@ struct PlanArgs {
   int32_t ngroups;
   int32_t nmem;
   int32_t G;
-  int32_t x_bytes;            // LDS layout: x | xsum | red | cnt | groups | members | sched
+  int32_t x_bytes;            // LDS layout: x (+ second operand) | xsum | red | cnt | groups | members | sched
   int32_t xsum_bytes;
   int32_t red_bytes;
   int32_t cnt_bytes;
@@ -152,6 +156,9 @@ struct Sched {
   __device__ int mem0(int gi) const { return uni(g[gi].mem0); }
   __device__ int nmem(int gi) const { return uni(g[gi].n_mem); }
   __device__ const uint16_t* x(int gi) const { return uni_ptr(g[gi].x); }
+  __device__ const uint16_t* gamma(int gi) const { return uni_ptr(g[gi].gamma); }
+  __device__ int pro(int gi) const { return uni(g[gi].pro); }
+  __device__ float eps(int gi) const { return __builtin_bit_cast(float, uni(__builtin_bit_cast(int, g[gi].eps))); }
   __device__ int64_t k(int gi) const { return (int64_t)uni((int)g[gi].k); }
   __device__ int tiles(int gi) const { return uni(s[gi].n); }
   __device__ int off(int gi) const { return uni(s[gi].off); }
@@ -165,6 +172,7 @@ struct Sched {
   __device__ int rg_begin_l(int mi) const { return m[mi].rg_begin; }
   __device__ uint16_t* y_l(int mi) const { return m[mi].y; }
   __device__ int64_t n_l(int mi) const { return m[mi].n; }
+  __device__ int epi_l(int mi) const { return m[mi].epi; }
 };
 
 // Tile hand-out.  A workgroup's tiles of all groups form one sequence
@@ -376,20 +384,53 @@ __device__ __forceinline__ unsigned long long stamp(const PlanArgs& p, int g) {
   return p.epoch * (unsigned long long)p.ngroups + (unsigned long long)(g + 1);
 }
 
-// Stage a group's activation vector (and, for int4, its 16-value run sums) in
-// LDS.  Each load moves 64 lanes x 16 bytes straight from memory into LDS (no
-// registers), all issued before the single wait, so staging costs one memory
-// round trip whatever K is; past K the buffer reads zeros.
-template <int FMT>
+// Move Kp halves from `r` into LDS at xs, 64 lanes x 16 bytes per load,
+// straight from memory (no registers); past the descriptor the loads read
+// zeros.  Each load fills 512 halves, so the LDS written is Kp rounded up to
+// a multiple of 512 halves (x_span).  The caller waits.
+__host__ __device__ constexpr int x_span(int Kp) { return (Kp + 511) / 512 * 512; }
+
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int lane, half_t* xs) {
+  for (int i = 0; i < Kp; i += 512)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(xs + i), 16, (uint32_t)(i * 2 + lane * 16), 0,
+        0, kPolicyCoherent);
+}
+
+// Stage a group's multiplied vector (and, for int4, its 16-value run sums) in
+// LDS.  All loads, and under a prologue the second operand's (gamma, or the
+// gated product's B block) into xs + x_span(Kp), are issued before the single wait,
+// so staging costs one memory round trip whatever K is.  The prologue then
+// runs in place: each lane rewrites the 8-value chunks its own loads brought.
+template <int FMT, bool GLUE>
 __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
                                               float* xsum) {
   const int Kp = S.J(g) * kSuperK;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), (uint32_t)(S.k(g) * 2));
-  for (int i = 0; i < Kp; i += 512)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rx, (__attribute__((address_space(3))) void*)(xs + i), 16, (uint32_t)(i * 2 + lane * 16), 0,
-        0, kPolicyCoherent);
-  wait_stores();                                   // vmcnt(0): the data is in LDS
+  const int64_t k = S.k(g);
+  const uint32_t xbytes = (uint32_t)(k * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), xbytes);
+  dma_to_lds(rx, Kp, lane, xs);
+  if constexpr (GLUE) {
+    const int pro = S.pro(g);
+    half_t* const xs2 = xs + x_span(Kp);            // second operand, after x's whole span
+    if (pro == QD_PRO_GLU) dma_to_lds(make_rsrc(S.x(g) + k, xbytes), Kp, lane, xs2);
+    if (pro == QD_PRO_RMSNORM) dma_to_lds(make_rsrc(S.gamma(g), xbytes), Kp, lane, xs2);
+    wait_stores();                                 // vmcnt(0): the data is in LDS
+    if (pro == QD_PRO_GLU) {
+      for (int i = lane * 8; i < Kp; i += 512)
+        *reinterpret_cast<u32x4*>(xs + i) =
+            glu8(*reinterpret_cast<const u32x4*>(xs + i), *reinterpret_cast<const u32x4*>(xs2 + i));
+    } else if (pro == QD_PRO_RMSNORM) {
+      float ss = 0.0f;
+      for (int i = lane * 8; i < Kp; i += 512) ss = sumsq8(*reinterpret_cast<const u32x4*>(xs + i), ss);
+      const float r = rms_inverse(wave_sum(ss), k, S.eps(g));
+      for (int i = lane * 8; i < Kp; i += 512)
+        *reinterpret_cast<u32x4*>(xs + i) =
+            rms8(*reinterpret_cast<const u32x4*>(xs + i), r, *reinterpret_cast<const u32x4*>(xs2 + i));
+    }
+  } else {
+    wait_stores();                                 // vmcnt(0): the data is in LDS
+  }
   if (FMT == QD_FMT_INT4_G64) {
     // One 16-value run per lane, four runs' reads in flight before any sum:
     // this runs on the group boundary's critical path.
@@ -423,6 +464,7 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
 
 // Row-group rg of group g may belong to a different member in each lane, so
 // the member lookup uses per-lane reads.
+template <bool GLUE>
 __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row, float v) {
   int mi = S.mem0(g);
   const int last = mi + S.nmem(g) - 1;
@@ -432,8 +474,8 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
     // Through a global pointer: a flat store would also count against the LDS
     // counter, making the next LDS wait wait for this store's acknowledgement.
     __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(S.y_l(mi) + n),
-                       __builtin_bit_cast(uint16_t, (half_t)v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+                       GLUE ? epilogue_bits(v, S.epi_l(mi)) : __builtin_bit_cast(uint16_t, (half_t)v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Spin (bounded) until the compute waves have counted `want` tiles against
@@ -456,6 +498,7 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cn
 // row-group's tiles is taken in a fixed order (tiles t = q mod 4 per
 // quarter-wave, then the four quarters), whichever wave computed which tile,
 // so results are deterministic.
+template <bool GLUE>
 __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
                              uint32_t* cnt, int* stalled, bool& dead) {
   const int ntiles = S.tiles(g);
@@ -473,7 +516,7 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
     for (int r = s * J + q; r < (s + 1) * J; r += 4) part += red[r * 16 + row];
     const float sum = quad_reduce(part);
     if (lane == 0) cnt[s] = 0u;                // ready for the next group
-    if (lane < 16) store_row(S, g, rg0 + s * stride, row, sum);
+    if (lane < 16) store_row<GLUE>(S, g, rg0 + s * stride, row, sum);
   }
 }
 
@@ -533,29 +576,29 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   asm volatile("" ::: "memory");
 }
 
-template <int FMT>
+template <int FMT, bool GLUE>
 __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane, half_t* xs,
                              float* xsum, const float* red, uint32_t* cnt, int* stalled,
                              int* staged) {
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  stage_group_x<FMT>(S, 0, lane, xs, xsum);
+  stage_group_x<FMT, GLUE>(S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
-    finish_group(p, S, g, lane, red, cnt, stalled, dead);
+    finish_group<GLUE>(p, S, g, lane, red, cnt, stalled, dead);
     publish(p, g, w, lane);
     if (g + 1 < p.ngroups) {
       wait_group(p, g, lane);
-      stage_group_x<FMT>(S, g + 1, lane, xs, xsum);
+      stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
       if (lane == 0) lds_put(staged, g + 1);
       wg_barrier();               // activations of g + 1 staged
     }
   }
 }
 
-template <int FMT, int D, int R, int RS>
+template <int FMT, int D, int R, int RS, bool GLUE>
 __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   static_assert(R >= 0 && R < kCtl && RS >= 1, "at least one streaming wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -582,7 +625,8 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
     u32x4* dst = reinterpret_cast<u32x4*>(tab);
     const u32x4* gsrc = reinterpret_cast<const u32x4*>(p.groups);
     const u32x4* msrc = reinterpret_cast<const u32x4*>(p.members);
-    const int ng16 = p.ngroups * 2, nm16 = p.nmem * 2;     // 16-byte units
+    const int ng16 = p.ngroups * (int)(sizeof(PGroup) / 16);    // 16-byte units
+    const int nm16 = p.nmem * (int)(sizeof(PMember) / 16);
     for (int i = threadIdx.x; i < ng16 + nm16 + p.ngroups; i += kWaves * 64) {
       u32x4 val;
       if (i < ng16) val = gsrc[i];
@@ -600,7 +644,7 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   __syncthreads();
 
   if (wave == kCtl) {
-    control_wave<FMT>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
+    control_wave<FMT, GLUE>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
   } else {
     const int last = p.ngroups - 1;
     const int total = S.off(last) + S.tiles(last);
@@ -652,6 +696,9 @@ struct HostGroup {
   int J;
   std::vector<PMember> mem;
   int R;
+  const uint16_t* gamma;
+  int pro;
+  float eps;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -683,11 +730,11 @@ enum ReserveShape { kInt4 = 0, kInt8Big = 1, kInt8Small = 2 };
 const void* kernel_ptr(int shape) {
   switch (shape) {
     case kInt8Big:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kBigR, kBigS>);
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kBigR, kBigS, false>);
     case kInt8Small:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 4, 5>);
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 4, 5, false>);
     default:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4>);
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false>);
   }
 }
 
@@ -710,15 +757,20 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   for (int64_t i = 0; ok && i < n_ops;) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
-    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, 0};
+    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, 0,
+                 ops[i].gamma, ops[i].prologue, ops[i].eps};
     for (int64_t q = i; q < e; ++q) {
       if (ops[q].w.n == 0) continue;
       if (ops[q].w.k == 0) ok = false;
       if (fmt == 0) fmt = ops[q].w.fmt;
       if (ops[q].w.fmt != fmt) ok = false;
       if (fmt != QD_FMT_INT8_B32 && fmt != QD_FMT_INT4_G64) ok = false;   // fp16: replay
+      // Glue (a prologue or an epilogue): replay.  The persistent walker's
+      // staging supports it, but that path is switched off until it has
+      // passed its device tests.
+      if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) ok = false;
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
-                               hg.R, 0});
+                               hg.R, ops[q].epilogue});
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);
     }
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
@@ -744,7 +796,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   std::vector<PMember> pm;
   std::vector<PSched> ps((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
-  int maxJ = 1, maxRel = 1, maxSeg = 1;
+  int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1;
   // A step the persistent walker cannot hold (tile counts past int32, LDS
   // beyond one CU's) replays per-group launches instead.
   auto fallback = [&]() {
@@ -756,9 +808,12 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
     if (T > (int64_t)INT32_MAX / 2) return fallback();
-    pg[g] = PGroup{hg.x, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size()};
+    pg[g] = PGroup{hg.x, hg.gamma, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size(),
+                   hg.pro, hg.eps};
     for (const PMember& mm : hg.mem) pm.push_back(mm);
     maxJ = std::max(maxJ, hg.J);
+    // halves of LDS the staging writes: x's span, and the second operand's
+    maxXH = std::max(maxXH, (hg.pro == QD_PRO_NONE ? 1 : 2) * x_span(hg.J * kSuperK));
     // Tile ranges per workgroup: whole row-groups, spread evenly; when the
     // group has fewer row-groups than workgroups some get none (their waves
     // go on prefetching the next groups).  Splitting a row-group across
@@ -777,7 +832,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       maxSeg = std::max<int>(maxSeg, (int)nrg);
     }
   }
-  const size_t x_bytes = align_up((size_t)maxJ * kSuperK * 2, 1024);
+  const size_t x_bytes = (size_t)maxXH * 2;      // a multiple of 1024
   const size_t xsum_bytes = fmt == QD_FMT_INT4_G64 ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
   const size_t red_bytes = align_up((size_t)maxRel * 16 * 4, 16);
   const size_t cnt_bytes = align_up((size_t)maxSeg * 4, 16);

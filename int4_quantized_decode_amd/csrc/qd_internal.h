@@ -39,6 +39,7 @@ struct Member {
   uint16_t* y;           // output, [m, n] fp16 bits
   int64_t n;             // rows of this matrix
   int64_t rg_begin;      // first row-group of this member in the launch's index space
+  int32_t epi;           // qd_epilogue applied to this member's outputs
 };
 
 struct LinearArgs {
@@ -47,9 +48,19 @@ struct LinearArgs {
   int J;                 // super-blocks per row (Kp / 256)
   int64_t k;             // logical K
   int64_t total_rg;      // sum of row-groups over members
-  const uint16_t* x;     // [m, k] fp16 bits
+  const uint16_t* x;     // [m, k] fp16 bits ([2, m, k] under QD_PRO_GLU)
   int m;                 // token rows (1..16)
+  int pro;               // qd_prologue applied to x
+  const uint16_t* gamma; // QD_PRO_RMSNORM weight, fp16 [k]
+  float eps;             // QD_PRO_RMSNORM epsilon
 };
+
+// Whether a launch applies any glue (a prologue, or an epilogue on a member).
+inline bool has_glue(const LinearArgs& a) {
+  bool g = a.pro != QD_PRO_NONE;
+  for (int i = 0; i < a.n_mem; ++i) g = g || a.mem[i].epi != QD_EPI_NONE;
+  return g;
+}
 
 // Launchers (enqueue only; arguments already validated).
 hipError_t launch_pack_int8(const float* w, int64_t n, int64_t k, uint8_t* out, int32_t* err,

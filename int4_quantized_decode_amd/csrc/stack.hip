@@ -4,6 +4,7 @@
 // stream.  The pages run decode as one static S=1 step per token that reads
 // every weight once (zoo Qwen3-VL page, Measured paragraph; Core AI 4B/8B
 // cards, Measured paragraph); this is that step's linear part.
+#include <cstring>
 #include <new>
 
 #include "stack.h"
@@ -34,13 +35,18 @@ qd_status build_groups(const qd_linear_op* ops, int64_t n_ops, int64_t m,
   while (i < n_ops) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
-    // Members of one group share x, K and format; their outputs are disjoint.
+    // Members of one group share x, K, format and prologue; their outputs are
+    // disjoint and none of them overlaps the group's input.
+    const uint64_t xbytes = (uint64_t)(ops[i].prologue == QD_PRO_GLU ? 2 : 1) * m * ops[i].w.k * 2;
     for (int64_t p = i; p < e; ++p) {
-      if (ops[p].w.fmt != ops[i].w.fmt || ops[p].w.k != ops[i].w.k || ops[p].x != ops[i].x)
+      if (ops[p].w.fmt != ops[i].w.fmt || ops[p].w.k != ops[i].w.k || ops[p].x != ops[i].x ||
+          ops[p].prologue != ops[i].prologue || ops[p].gamma != ops[i].gamma ||
+          memcmp(&ops[p].eps, &ops[i].eps, sizeof(float)) != 0)
         return QD_EINVAL;
+      const uint64_t ybytes = (uint64_t)m * ops[p].w.n * 2;
+      if (ops[p].w.k > 0 && same_range_overlap(ops[p].y, ybytes, ops[i].x, xbytes)) return QD_EINVAL;
       for (int64_t q = i; q < p; ++q)
-        if (same_range_overlap(ops[p].y, (uint64_t)m * ops[p].w.n * 2, ops[q].y,
-                               (uint64_t)m * ops[q].w.n * 2))
+        if (same_range_overlap(ops[p].y, ybytes, ops[q].y, (uint64_t)m * ops[q].w.n * 2))
           return QD_EINVAL;
     }
     StackGroup cur{};
@@ -55,13 +61,17 @@ qd_status build_groups(const qd_linear_op* ops, int64_t n_ops, int64_t m,
       LinearArgs& a = cur.args;
       cur.fmt = op.w.fmt;
       cur.zero_fill = op.w.k == 0;
-      a.mem[a.n_mem] = Member{static_cast<const uint8_t*>(op.w.data), op.y, op.w.n, a.total_rg};
+      a.mem[a.n_mem] = Member{static_cast<const uint8_t*>(op.w.data), op.y, op.w.n, a.total_rg,
+                              op.epilogue};
       a.total_rg += ceil_div(op.w.n, kTileRows);
       a.n_mem += 1;
       a.J = (int)ceil_div(op.w.k, kSuperK);
       a.k = op.w.k;
       a.x = op.x;
       a.m = (int)m;
+      a.pro = op.prologue;
+      a.gamma = op.gamma;
+      a.eps = op.eps;
     }
     flush();
     i = e;

@@ -52,11 +52,30 @@ def silu(a: np.ndarray) -> np.ndarray:
         return a64 / (1.0 + np.exp(-a64))
 
 
+def silu_fp16(a: np.ndarray) -> np.ndarray:
+    """The stored activation of fp16 gate outputs: fp16(silu(a))."""
+    return _fp16(silu(a))
+
+
+def glu_fp16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The gating product of two fp16 arrays, stored as fp16: fp16(a * b)
+    (the product of two fp16 values is exact in fp64, so this rounds once)."""
+    return _fp16(np.asarray(a).astype(np.float64) * np.asarray(b).astype(np.float64))
+
+
 def swiglu_fp16(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     """h = fp16(fp16(silu(gate)) * up) element-wise for fp16 gate and up of
     the same shape.  Returns fp16."""
-    s16 = _fp16(silu(gate))
-    return _fp16(s16.astype(np.float64) * np.asarray(up).astype(np.float64))
+    return glu_fp16(silu_fp16(gate), up)
+
+
+def _two_blocks(x: np.ndarray):
+    x = np.asarray(x)
+    if x.ndim == 1:
+        half = x.shape[0] // 2
+        return x[:half], x[half:]
+    x = x.reshape(2, -1, x.shape[-1])
+    return x[0], x[1]
 
 
 def apply_prologue(kind: str, x: np.ndarray, gamma=None, eps: float = 0.0) -> np.ndarray:
@@ -65,16 +84,15 @@ def apply_prologue(kind: str, x: np.ndarray, gamma=None, eps: float = 0.0) -> np
     kind "none": x itself.  "rmsnorm": ``rmsnorm_fp16(x, gamma, eps)``.
     "swiglu": x holds the gate outputs of every token followed by the up
     outputs of every token ([2K] for one token, [2, M, K] or [2M, K] for M
-    tokens); returns ``swiglu_fp16(gate, up)`` of shape [K] or [M, K]."""
+    tokens); returns ``swiglu_fp16(gate, up)`` of shape [K] or [M, K].
+    "glu": the same two blocks, already activated first block:
+    ``glu_fp16(a, b)``."""
     if kind == "none":
         return np.asarray(x)
     if kind == "rmsnorm":
         return rmsnorm_fp16(x, gamma, eps)
     if kind == "swiglu":
-        x = np.asarray(x)
-        if x.ndim == 1:
-            half = x.shape[0] // 2
-            return swiglu_fp16(x[:half], x[half:])
-        x = x.reshape(2, -1, x.shape[-1])
-        return swiglu_fp16(x[0], x[1])
+        return swiglu_fp16(*_two_blocks(x))
+    if kind == "glu":
+        return glu_fp16(*_two_blocks(x))
     raise ValueError(kind)

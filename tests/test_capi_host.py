@@ -126,3 +126,50 @@ def test_read_probe_validation_errors(L):
     assert lib.qd_read_probe(buf, 0, sink, 4, None) == 2                      # ESHAPE
     assert lib.qd_read_probe(buf, 64, sink, 0, None) == 2
     assert lib.qd_read_probe(buf, 64, sink, 65536, None) == 2
+
+
+def test_stack_glue_validation_errors(L):
+    """Prologue and epilogue fields are checked before anything is enqueued."""
+    lib = L.lib
+    x, y, gam = 1 << 20, 1 << 24, 1 << 26
+
+    def one(**kw):
+        f = dict(w=_w(L), x=x, y=y, group=0, prologue=0, gamma=None, eps=0.0, epilogue=0)
+        f.update(kw)
+        arr = (L.QDLinearOp * 1)()
+        arr[0] = L.QDLinearOp(f["w"], f["x"], f["y"], f["group"], f["prologue"], f["gamma"],
+                              f["eps"], f["epilogue"])
+        return lib.decode_linear_stack(arr, 1, 1, None)
+
+    assert one(prologue=3) == 1                                   # unknown prologue
+    assert one(epilogue=2) == 1                                   # unknown epilogue
+    assert one(prologue=1, gamma=None, eps=1e-6) == 1             # RMSNorm without gamma
+    assert one(prologue=1, gamma=gam, eps=0.0) == 1               # eps must be > 0
+    assert one(prologue=1, gamma=gam, eps=float("nan")) == 1
+    assert one(prologue=1, gamma=gam, eps=float("inf")) == 1
+    assert one(prologue=1, gamma=gam + 8, eps=1e-6) == 3          # gamma alignment
+    assert one(prologue=1, gamma=y, eps=1e-6) == 1                # gamma overlaps y
+    assert one(prologue=0, gamma=gam) == 1                        # gamma without RMSNorm
+    assert one(prologue=2, eps=1e-6) == 1                         # eps without RMSNorm
+    # a gated product reads 2 x K halves: y just past K halves overlaps it
+    assert one(prologue=2, y=x + 256 * 2) == 1
+    assert one(prologue=0, w=_w(L, n=0), y=x + 256 * 2) == 0      # N == 0: nothing to run
+
+    arr = (L.QDLinearOp * 2)()
+    arr[0] = L.QDLinearOp(_w(L), x, y, 0, 1, gam, 1e-6, 0)
+    arr[1] = L.QDLinearOp(_w(L), x, y + 4096, 0, 1, gam, 1e-5, 1)  # same group, other eps
+    assert lib.decode_linear_stack(arr, 2, 1, None) == 1
+    arr[1] = L.QDLinearOp(_w(L), x, y + 4096, 0, 0, None, 0.0, 1)  # same group, no prologue
+    assert lib.decode_linear_stack(arr, 2, 1, None) == 1
+    arr[1] = L.QDLinearOp(_w(L), y, x, 0, 1, gam, 1e-6, 0)         # other x; and y over op 0's x
+    assert lib.decode_linear_stack(arr, 2, 1, None) == 1
+    h = ctypes.c_void_p()
+    assert lib.qd_stack_plan_create(arr, 2, 1, ctypes.byref(h)) == 1
+
+
+def test_op_struct_layout(L):
+    """The ctypes mirror of qd_linear_op has the C layout (80 bytes, eps and
+    epilogue after the gamma pointer)."""
+    assert ctypes.sizeof(L.QDLinearOp) == 80
+    assert L.QDLinearOp.gamma.offset == 64 and L.QDLinearOp.eps.offset == 72
+    assert L.QDLinearOp.epilogue.offset == 76

@@ -1,0 +1,267 @@
+"""GPU parity of the fused glue: the RMSNorm and gated-product prologues and
+the silu epilogue of stack ops, against the oracle's glue on the same inputs.
+
+Each op is checked on the activations it actually read (copied back from the
+device after the run), so an error in one op cannot hide behind, or leak
+into, the check of the next.  The glue's own arithmetic is checked directly
+through weights that pass the glued vector through unchanged."""
+import numpy as np
+import pytest
+
+import synthetic_inputs as si
+from oracle import glue, linear, quant
+from tests.numerics import MAX_ERR_COEF, REL_L2, check_vector
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def qd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int4_quantized_decode_amd as qd
+    return qd
+
+
+def _gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _parts(fmt, w):
+    return {"int8_b32": quant.quantize_int8_b32, "int4_g64": quant.quantize_int4_g64,
+            "fp16": quant.quantize_fp16}[fmt](w)
+
+
+def _pack(qd, fmt, w):
+    return {"int8_b32": qd.qpack_int8_b32, "int4_g64": qd.qpack_int4_g64,
+            "fp16": qd.qpack_fp16}[fmt](_gpu(w))
+
+
+def _ulps(a, b):
+    """|a - b| in units of the fp16 spacing at the larger magnitude."""
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    big = np.maximum(np.abs(a64), np.abs(b64)).astype(np.float16)
+    return np.abs(a64 - b64) / np.spacing(big).astype(np.float64)
+
+
+# ------------------------------------------------------- the glue itself, exactly
+
+def _pass_through(fmt, k):
+    """A K x K weight that every format stores exactly as c * I, with c chosen
+    so that c * v is exact in fp32 for fp16 v: fp16 weights hold 1; int8 b32
+    blocks with one nonzero 127/128 get the exact scale 2^-7 and code 127."""
+    c = 1.0 if fmt == "fp16" else 127.0 / 128.0
+    return (np.eye(k, dtype=np.float32) * np.float32(c)), c
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "fp16"])
+@pytest.mark.parametrize("m", [1, 3, 16])
+@pytest.mark.parametrize("path", ["launches", "plan"])
+def test_prologues_and_epilogue_exact(qd, fmt, m, path):
+    """y = fp16(c * glued input).  The gated product is one correctly rounded
+    fp16 multiply, so it must match bit for bit; RMSNorm and silu go through
+    fp32 (statistic, exp, quotient), so an element may sit one fp16 step from
+    the oracle's fp64 rounding, and almost none do."""
+    k = 1056                                     # 4 super-blocks and a ragged tail
+    w, c = _pass_through(fmt, k)
+    pw = _pack(qd, fmt, w)
+    x = si.activations(si.seed_for("glue-x", m), m, k)
+    a = si.activations(si.seed_for("glue-a", m), m, k)
+    b = si.activations(si.seed_for("glue-b", m), m, k)
+    g = a.copy()
+    g[0, :8] = [-65504, -20, -0.0, 20, 65504, 6e-8, -3e-5, 11.5]     # silu edge values
+    gam = si.norm_weight(si.seed_for("glue-gamma"), k)
+    shape = (m, k) if m > 1 else (k,)
+    ab = _gpu(np.concatenate([a, b], 0).reshape(-1))                # [2, m, K]: A block then B
+    xs, gs, as_ = _gpu(x.reshape(shape)), _gpu(gam), _gpu(g.reshape(shape))
+    ys = [torch.full(shape, float("nan"), dtype=torch.float16, device=DEV) for _ in range(3)]
+    ops = [qd.LinearOp(pw, xs, ys[0], 0, prologue="rmsnorm", gamma=gs, eps=EPS),
+           qd.LinearOp(pw, ab, ys[1], 1, prologue="glu"),
+           qd.LinearOp(pw, as_, ys[2], 2, epilogue="silu")]
+    if path == "plan":
+        plan = qd.StackPlan(ops, m)
+        assert not plan.persistent            # steps with glue replay the launches
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        plan.close()
+    else:
+        qd.decode_linear_stack(ops, m)
+    got = [_host(y).reshape(m, k) for y in ys]
+
+    def scaled(v16):   # fp16(c * v), exact product then one rounding
+        return (v16.astype(np.float64) * c).astype(np.float16)
+
+    want_rms = scaled(glue.rmsnorm_fp16(x, gam, EPS))
+    want_glu = scaled(glue.glu_fp16(a, b))
+    want_silu = glue.silu_fp16(scaled(g))
+    bad = np.argwhere(got[1].view(np.uint16) != want_glu.view(np.uint16))
+    assert bad.size == 0, ("gated product", len(bad), [(tuple(i), float(a[tuple(i)]), float(b[tuple(i)]),
+                                                        float(got[1][tuple(i)]), float(want_glu[tuple(i)]))
+                                                       for i in bad[:6]])
+    for name, gv, wv in (("rmsnorm", got[0], want_rms), ("silu", got[2], want_silu)):
+        d = _ulps(gv, wv)
+        assert np.all(np.isfinite(gv.astype(np.float64))), name
+        assert d.max() <= 1.0, (name, d.max(), np.argwhere(d > 1)[:4])
+        assert np.mean(d == 0) >= 0.99, (name, np.mean(d == 0))
+    # signs of zeros and the large-argument limits of silu
+    assert float(got[2][0, 2]) == 0.0 and float(got[2][0, 3]) == float(want_silu[0, 3])
+
+
+# ------------------------------------------------------- decoder-shaped chains
+
+def _check_silu(s_gpu, a_ref, row_max, xin, what):
+    """Stored silu outputs against silu of the oracle's unrounded product:
+    |silu'| <= 1.1, so the product's bound grows by that factor, plus the
+    final fp16 rounding."""
+    s = s_gpu.astype(np.float64)
+    want = glue.silu(a_ref)
+    bound = 1.1 * MAX_ERR_COEF * float(np.linalg.norm(xin.astype(np.float64))) * row_max
+    bound = bound + np.spacing(np.abs(want).astype(np.float16)).astype(np.float64)
+    err = np.abs(s - want)
+    bad = np.flatnonzero(err > bound)
+    assert bad.size == 0, (what, bad[:8], err[bad[:4]], bound[bad[:4]])
+    nrm = float(np.linalg.norm(want))
+    if nrm:
+        assert float(np.linalg.norm(s - want)) / nrm <= 2 * REL_L2, what
+
+
+def _tiny():
+    return si.Decoder("tiny-glue", layers=2, hidden=512, q_heads=4, mlp=1280, vocab=1000,
+                      kv_heads=2, head_dim=64)
+
+
+def _glue_stack(qd, fmt, m, d):
+    """A decode step whose projections feed each other through the glue:
+    RMSNorm before q|k|v, gate|up and the head; silu on gate; the gated
+    product before down; each layer's input is the previous down's output.
+    The attention output feeding o is a synthetic activation (attention is
+    outside the linear path).  Returns the device ops and, per op, what the
+    oracle needs to recompute it."""
+    H, Q, I = d.hidden, d.q_dim, d.mlp
+    shape = (lambda n: (m, n) if m > 1 else (n,))
+    nan = lambda n: torch.full(shape(n), float("nan"), dtype=torch.float16, device=DEV)
+    x_in = _gpu(si.activations(si.seed_for("gs-x0", m), m, H).reshape(shape(H)))
+    ops, meta, gid = [], [], 0
+    keep = []
+    for layer in range(d.layers):
+        g_attn = _gpu(si.norm_weight(si.seed_for("gs-ga", layer), H))
+        g_mlp = _gpu(si.norm_weight(si.seed_for("gs-gm", layer), H))
+        keep += [g_attn, g_mlp]
+        for pname, n in ((f"L{layer}.q", Q), (f"L{layer}.k", d.kv_dim), (f"L{layer}.v", d.kv_dim)):
+            w = si.weights(si.seed_for("gs-w", pname), n, H)
+            op = qd.LinearOp(_pack(qd, fmt, w), x_in, nan(n), gid, prologue="rmsnorm", gamma=g_attn,
+                             eps=EPS)
+            ops.append(op)
+            meta.append((pname, w, "rmsnorm", g_attn, "none"))
+        gid += 1
+        attn = _gpu(si.activations(si.seed_for("gs-attn", layer, m), m, Q).reshape(shape(Q)))
+        keep.append(attn)
+        w = si.weights(si.seed_for("gs-w", f"L{layer}.o"), H, Q)
+        o_y = nan(H)
+        ops.append(qd.LinearOp(_pack(qd, fmt, w), attn, o_y, gid))
+        meta.append((f"L{layer}.o", w, "none", None, "none"))
+        gid += 1
+        gu = torch.full((2 * m * I,), float("nan"), dtype=torch.float16, device=DEV)
+        keep.append(gu)
+        for j, (pname, epi) in enumerate(((f"L{layer}.gate", "silu"), (f"L{layer}.up", "none"))):
+            w = si.weights(si.seed_for("gs-w", pname), I, H)
+            y = gu[j * m * I:(j + 1) * m * I].view(shape(I))
+            ops.append(qd.LinearOp(_pack(qd, fmt, w), o_y, y, gid, prologue="rmsnorm", gamma=g_mlp,
+                                   eps=EPS, epilogue=epi))
+            meta.append((pname, w, "rmsnorm", g_mlp, epi))
+        gid += 1
+        w = si.weights(si.seed_for("gs-w", f"L{layer}.down"), H, I)
+        down_y = nan(H)
+        ops.append(qd.LinearOp(_pack(qd, fmt, w), gu, down_y, gid, prologue="glu"))
+        meta.append((f"L{layer}.down", w, "glu", None, "none"))
+        gid += 1
+        x_in = down_y
+    g_fin = _gpu(si.norm_weight(si.seed_for("gs-gf"), H))
+    keep.append(g_fin)
+    w = si.weights(si.seed_for("gs-w", "head"), d.vocab, H)
+    ops.append(qd.LinearOp(_pack(qd, fmt, w), x_in, nan(d.vocab), gid, prologue="rmsnorm",
+                           gamma=g_fin, eps=EPS))
+    meta.append(("head", w, "rmsnorm", g_fin, "none"))
+    return ops, meta, keep
+
+
+def _check_glue_stack(fmt, m, ops, meta, tag):
+    for op, (pname, w, pro, gam, epi) in zip(ops, meta):
+        x_dev = _host(op.x).astype(np.float16)
+        k = w.shape[1]
+        if pro == "glu":
+            xin = glue.apply_prologue("glu", x_dev.reshape(2, m, k))
+        elif pro == "rmsnorm":
+            xin = glue.rmsnorm_fp16(x_dev.reshape(m, k), _host(gam), EPS)
+        else:
+            xin = x_dev.reshape(m, k)
+        assert np.all(np.isfinite(xin.astype(np.float64))), f"{tag} {pname}: non-finite input"
+        parts = _parts(fmt, w)
+        ref = linear.ref_linear(fmt, parts, xin).reshape(m, -1)
+        rmax = linear.row_max_abs(fmt, parts)
+        y = _host(op.y).reshape(m, -1)
+        for t in range(m):
+            if epi == "silu":
+                _check_silu(y[t], ref[t], rmax, xin[t], f"{tag} {pname} token {t}")
+            else:
+                check_vector(y[t], ref[t], rmax, xin[t], f"{tag} {pname} token {t}")
+
+
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 1), ("int4_g64", 1), ("fp16", 1), ("int8_b32", 16),
+                                   ("int4_g64", 16), ("fp16", 5)])
+def test_glue_stack_launches(qd, fmt, m):
+    ops, meta, keep = _glue_stack(qd, fmt, m, _tiny())
+    qd.decode_linear_stack(ops, m)
+    _check_glue_stack(fmt, m, ops, meta, f"launches {fmt} m={m}")
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_glue_stack_plan_parity_and_determinism(qd, fmt):
+    """A plan of the glued step (it replays the per-group launches): per-op
+    parity and bit-identical repeated runs, outputs poisoned in between."""
+    ops, meta, keep = _glue_stack(qd, fmt, 1, _tiny())
+    plan = qd.StackPlan(ops, 1)
+    assert not plan.persistent
+    first = None
+    for rep in range(3):
+        for op in ops:
+            op.y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        outs = [_host(op.y).copy() for op in ops]
+        if first is None:
+            first = outs
+            _check_glue_stack(fmt, 1, ops, meta, f"plan {fmt}")
+        else:
+            for a, b in zip(first, outs):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    plan.close()
+
+
+@pytest.mark.skip(reason="the persistent kernel's glue staging is switched off (plans with glue "
+                         "replay the launches): its first device run faulted because the second "
+                         "operand overran the LDS x region when K is not a multiple of 512; the "
+                         "layout is fixed and the path stays off until this test has passed")
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_glue_stack_persistent(qd, fmt):
+    """The glued step in the one-launch persistent kernel (staging applies the
+    prologue in LDS): per-op parity.  Needs the persistent glue path on."""
+    ops, meta, keep = _glue_stack(qd, fmt, 1, _tiny())
+    plan = qd.StackPlan(ops, 1)
+    assert plan.persistent
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    _check_glue_stack(fmt, 1, ops, meta, f"persistent {fmt}")
+    plan.close()

@@ -630,3 +630,19 @@ def test_prologue_layouts_and_stack():
     assert np.array_equal(outs[0], g_ref) and np.array_equal(outs[1], u_ref)
     h = glue.swiglu_fp16(g_ref.astype(np.float16), u_ref.astype(np.float16))
     assert np.array_equal(outs[2], linear.ref_linear("int8_b32", pd, h))
+
+
+def test_glu_product_rounds_once_to_even():
+    """fp16(a * b): 3 * (1 + 2^-10) = 1537.5 * 2^-9, a tie, goes to the even
+    1538 * 2^-9; (1 + 2^-10)^2 = 1 + 2^-9 + 2^-20 rounds down to 1 + 2^-9;
+    65504 * 2 overflows to inf (the IEEE result)."""
+    from oracle import glue
+    a = np.array([3.0, 1.0009765625, 65504.0, -0.5], np.float16)
+    b = np.array([1.0009765625, 1.0009765625, 2.0, 0.25], np.float16)
+    with np.errstate(over="ignore"):
+        got = glue.glu_fp16(a, b).astype(np.float64)
+    assert got[0] == 1538 * 2.0 ** -9 and got[1] == 1 + 2.0 ** -9
+    assert np.isinf(got[2]) and got[3] == -0.125
+    x = np.concatenate([a, b])
+    with np.errstate(over="ignore"):
+        assert np.array_equal(glue.apply_prologue("glu", x), glue.glu_fp16(a, b))
