@@ -113,7 +113,7 @@ __device__ inline half8_t load_a(const ASrc& s, int64_t K, int m_row, int64_t kk
 // activation block X[0..15][j*256 .. j*256+255] once (8 A operands) and the
 // RG weight tiles of that super-block, and issues RG x 8 MFMAs, so each
 // activation block read from L2 serves RG tiles.
-template <int WAVES, int RG, int PRO, bool EPI>
+template <int WAVES, int RG, int TPW, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -136,34 +136,47 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
   float4_t acc[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = wave; j < J; j += WAVES) {
-    const uint32_t t = (uint32_t)j * kTileBytes8;
-    u32x4 c[RG][4], scw[RG];
+  for (int j0 = wave; j0 < J; j0 += WAVES * TPW) {
+    // Every load of the batch (TPW super-blocks x RG tiles, and their
+    // activation blocks) is issued before the first product.  A super-block
+    // past K reads zero tiles (no traffic) and zero activations.
+    u32x4 c[TPW][RG][4], scw[TPW][RG];
+    half8_t xa[TPW][8];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
+    for (int u = 0; u < TPW; ++u) {
+      const int j = j0 + u * WAVES;
+      const uint32_t t = (uint32_t)j * kTileBytes8;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
-      scw[r] = bload16(rw[r], t + kMetaOffset8 + 16 * rho);
+      for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) c[u][r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+        scw[u][r] = bload16(rw[r], t + kMetaOffset8 + 16 * rho);
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
+        xa[u][b] = load_a<PRO>(src, K, m_row, kk);
+      }
     }
-    half8_t xa[8];
+    // Keep every load of the batch ahead of the first product: left alone,
+    // the scheduler sinks later tiles' loads to save registers.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
-      xa[b] = load_a<PRO>(src, K, m_row, kk);
-    }
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const half8_t scales = __builtin_bit_cast(half8_t, scw[r]);
+      for (int r = 0; r < RG; ++r) {
+        const half8_t scales = __builtin_bit_cast(half8_t, scw[u][r]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const half8_t bq = codes_to_half8(c[r][s][2 * h], c[r][s][2 * h + 1]);
-          const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * s + h], bq, zero, 0, 0, 0);
-          const float sc = (float)scales[2 * s + h];
+          for (int h = 0; h < 2; ++h) {
+            const half8_t bq = codes_to_half8(c[u][r][s][2 * h], c[u][r][s][2 * h + 1]);
+            const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u][2 * s + h], bq, zero, 0, 0, 0);
+            const float sc = (float)scales[2 * s + h];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf(sc, p[i], acc[r][i]);
+            for (int i = 0; i < 4; ++i) acc[r][i] = __builtin_fmaf(sc, p[i], acc[r][i]);
+          }
         }
       }
     }
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int8_kernel(LinearArgs a) 
 
 // fp16 weights (the unquantized head): chunk s of a tile is already the B
 // operand of block s; no dequantization and no scale.
-template <int WAVES, int RG, int PRO, bool EPI>
+template <int WAVES, int RG, int TPW, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -223,26 +236,36 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) 
   float4_t acc[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = wave; j < J; j += WAVES) {
-    const uint32_t t = (uint32_t)j * kTileBytes16;
-    u32x4 c[RG][8];
+  for (int j0 = wave; j0 < J; j0 += WAVES * TPW) {
+    u32x4 c[TPW][RG][8];
+    half8_t xa[TPW][8];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
+    for (int u = 0; u < TPW; ++u) {
+      const int j = j0 + u * WAVES;
+      const uint32_t t = (uint32_t)j * kTileBytes16;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+      for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) c[u][r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
+        xa[u][b] = load_a<PRO>(src, K, m_row, kk);
+      }
     }
-    half8_t xa[8];
+    // Keep every load of the batch ahead of the first product: left alone,
+    // the scheduler sinks later tiles' loads to save registers.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * g;
-      xa[b] = load_a<PRO>(src, K, m_row, kk);
-    }
+    for (int u = 0; u < TPW; ++u) {
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
+      for (int r = 0; r < RG; ++r) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[b], __builtin_bit_cast(half8_t, c[r][b]),
-                                                        acc[r], 0, 0, 0);
+        for (int b = 0; b < 8; ++b)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u][b], __builtin_bit_cast(half8_t, c[u][r][b]),
+                                                          acc[r], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -276,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_fp16_kernel(LinearArgs a) 
 }
 
 // INT4 g64: one workgroup = RG row-groups x all of K, waves along K (as above).
-template <int WAVES, int RG, int PRO, bool EPI>
+template <int WAVES, int RG, int TPW, int PRO, bool EPI>
 __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) {
   __shared__ float4_t red[WAVES][RG][64];
   const int J = a.J;
@@ -300,53 +323,63 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
   float4_t acc[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r) acc[r] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = wave; j < J; j += WAVES) {
-    const uint32_t t = (uint32_t)j * kTileBytes4;
-    u32x4 c[RG][2], meta[RG];
+  for (int j0 = wave; j0 < J; j0 += WAVES * TPW) {
+    u32x4 c[TPW][RG][2], meta[TPW][RG];
+    half8_t xa[TPW][8];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
+    for (int u = 0; u < TPW; ++u) {
+      const int j = j0 + u * WAVES;
+      const uint32_t t = (uint32_t)j * kTileBytes4;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) c[r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
-      meta[r] = bload16(rw[r], t + kMetaOffset4 + 16 * rho);
+      for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) c[u][r][s] = bload16(rw[r], t + 1024 * s + 16 * lane);
+        meta[u][r] = bload16(rw[r], t + kMetaOffset4 + 16 * rho);
+      }
+      // A operands: group gam, half h -> X[m][j*256 + 64 gam + 16 g + 8 h .. +8].
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t kk = (int64_t)j * kSuperK + 64 * (q >> 1) + 16 * g + 8 * (q & 1);
+        xa[u][q] = load_a<PRO>(src, K, m_row, kk);
+      }
     }
-    // A operands: group gam, half h -> X[m][j*256 + 64 gam + 16 g + 8 h .. +8].
-    half8_t xa[8];
+    // Keep every load of the batch ahead of the first product: left alone,
+    // the scheduler sinks later tiles' loads to save registers.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t kk = (int64_t)j * kSuperK + 64 * (q >> 1) + 16 * g + 8 * (q & 1);
-      xa[q] = load_a<PRO>(src, K, m_row, kk);
-    }
-    // Per group: sum of x over its 64 positions, for this lane's tokens.
-    float4_t xs[4];
-#pragma unroll
-    for (int gam = 0; gam < 4; ++gam) {
-      const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam], ones, zero, 0, 0, 0);
-      xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam + 1], ones, xs[gam], 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const half8_t mt = __builtin_bit_cast(half8_t, meta[r]);
+    for (int u = 0; u < TPW; ++u) {
+      // Per group: sum of x over its 64 positions, for this lane's tokens.
+      float4_t xs[4];
 #pragma unroll
       for (int gam = 0; gam < 4; ++gam) {
-        const int s = gam >> 1, h = gam & 1;
-        float4_t pc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u][2 * gam], ones, zero, 0, 0, 0);
+        xs[gam] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u][2 * gam + 1], ones, xs[gam], 0, 0, 0);
+      }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          // 8 codes (k order) of this lane's row: nibble p holds code (0,2,4,6,1,3,5,7)[p].
-          const uint32_t wd = c[r][s][2 * h + half];
-          const uint32_t mk = 0x000F000Fu, e = 0x64006400u;
-          const half2_t c01 = as_h2((wd & mk) | e) + minus1024;
-          const half2_t c23 = as_h2(((wd >> 4) & mk) | e) + minus1024;
-          const half2_t c45 = as_h2(((wd >> 8) & mk) | e) + minus1024;
-          const half2_t c67 = as_h2(((wd >> 12) & mk) | e) + minus1024;
-          const half8_t bq = {c01[0], c01[1], c23[0], c23[1], c45[0], c45[1], c67[0], c67[1]};
-          pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2 * gam + half], bq, pc, 0, 0, 0);
+      for (int r = 0; r < RG; ++r) {
+        const half8_t mt = __builtin_bit_cast(half8_t, meta[u][r]);
+#pragma unroll
+        for (int gam = 0; gam < 4; ++gam) {
+          const int s = gam >> 1, h = gam & 1;
+          float4_t pc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            // 8 codes (k order) of this lane's row: nibble p holds code (0,2,4,6,1,3,5,7)[p].
+            const uint32_t wd = c[u][r][s][2 * h + half];
+            const uint32_t mk = 0x000F000Fu, e = 0x64006400u;
+            const half2_t c01 = as_h2((wd & mk) | e) + minus1024;
+            const half2_t c23 = as_h2(((wd >> 4) & mk) | e) + minus1024;
+            const half2_t c45 = as_h2(((wd >> 8) & mk) | e) + minus1024;
+            const half2_t c67 = as_h2(((wd >> 12) & mk) | e) + minus1024;
+            const half8_t bq = {c01[0], c01[1], c23[0], c23[1], c45[0], c45[1], c67[0], c67[1]};
+            pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u][2 * gam + half], bq, pc, 0, 0, 0);
+          }
+          const float sc = (float)mt[gam], mn = (float)mt[4 + gam];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[r][i] = __builtin_fmaf(sc, pc[i], __builtin_fmaf(mn, xs[gam][i], acc[r][i]));
         }
-        const float sc = (float)mt[gam], mn = (float)mt[4 + gam];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[r][i] = __builtin_fmaf(sc, pc[i], __builtin_fmaf(mn, xs[gam][i], acc[r][i]));
       }
     }
   }
@@ -380,35 +413,42 @@ __global__ __launch_bounds__(WAVES * 64) void small_m_int4_kernel(LinearArgs a) 
   }
 }
 
+template <int W, int RG, int TPW, int PRO, bool EPI>
+void launch_cfg(int fmt, dim3 grid, const LinearArgs& a, hipStream_t s) {
+  if (fmt == QD_FMT_INT4_G64)
+    hipLaunchKernelGGL((small_m_int4_kernel<W, RG, TPW, PRO, EPI>), grid, dim3(W * 64), 0, s, a);
+  else if (fmt == QD_FMT_FP16)
+    hipLaunchKernelGGL((small_m_fp16_kernel<W, RG, TPW, PRO, EPI>), grid, dim3(W * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((small_m_int8_kernel<W, RG, TPW, PRO, EPI>), grid, dim3(W * 64), 0, s, a);
+}
+
+// Launch shapes, chosen by a sweep over the Qwen3 2B/4B/8B and 27B-shaped
+// projections at m = 16 on MI355X (each shape's launches back to back):
+//  * many row-groups (gate|up, the head): 4-wave workgroups of 2 row-groups
+//    (up to ~4000 row-groups) or 4 row-groups (more), so each activation block
+//    serves 2 or 4 tiles and several workgroups stay resident per CU;
+//  * fewer (q|k|v, o, down: one or two per CU): one row-group per workgroup;
+//    int8 waves issue two super-blocks' loads before their first product
+//    (4 waves), INT4 and fp16 waves one (8 waves).
+enum SmallShape { kRg4W4 = 0, kRg2W4 = 1, kW4T2 = 2, kW8T1 = 3, kW4T1 = 4 };
+
+int pick_small_m(int fmt, int64_t total_rg, int J) {
+  if (total_rg >= 4 * 256 && J >= 8) return total_rg >= 4096 ? kRg4W4 : kRg2W4;
+  if (J < 8) return kW4T1;
+  return fmt == QD_FMT_INT8_B32 ? kW4T2 : kW8T1;
+}
+
 template <int PRO, bool EPI>
-hipError_t launch_small_m_pro(int fmt, const LinearArgs& a, hipStream_t s) {
-  const bool int4 = fmt == QD_FMT_INT4_G64, fp16 = fmt == QD_FMT_FP16;
-  if (!int4 && !fp16 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
-  // Enough row-groups to give every CU several: 4 per workgroup, 8 waves
-  // (each activation block then serves 4 tiles).  Otherwise one row-group per
-  // workgroup and up to 16 waves along K.
-  if (a.total_rg >= 4 * 256 && a.J >= 8) {
-    const dim3 grid((uint32_t)ceil_div(a.total_rg, 4));
-    if (int4) hipLaunchKernelGGL((small_m_int4_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    else if (fp16) hipLaunchKernelGGL((small_m_fp16_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int8_kernel<8, 4, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    return hipGetLastError();
-  }
-  const dim3 grid((uint32_t)a.total_rg);
-  int w = 16;
-  while (w > 4 && (w > a.J || a.total_rg * w > 256 * 32)) w /= 2;
-  if (fp16) {
-    if (w == 16) hipLaunchKernelGGL((small_m_fp16_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_fp16_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_fp16_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
-  } else if (int4) {
-    if (w == 16) hipLaunchKernelGGL((small_m_int4_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_int4_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int4_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
-  } else {
-    if (w == 16) hipLaunchKernelGGL((small_m_int8_kernel<16, 1, PRO, EPI>), grid, dim3(16 * 64), 0, s, a);
-    else if (w == 8) hipLaunchKernelGGL((small_m_int8_kernel<8, 1, PRO, EPI>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((small_m_int8_kernel<4, 1, PRO, EPI>), grid, dim3(4 * 64), 0, s, a);
+hipError_t launch_small_m_pro(int fmt, const LinearArgs& a, hipStream_t s, int shape) {
+  if (fmt != QD_FMT_INT4_G64 && fmt != QD_FMT_FP16 && fmt != QD_FMT_INT8_B32) return hipErrorInvalidValue;
+  const dim3 grid1((uint32_t)a.total_rg);
+  switch (shape) {
+    case kRg4W4: launch_cfg<4, 4, 1, PRO, EPI>(fmt, dim3((uint32_t)ceil_div(a.total_rg, 4)), a, s); break;
+    case kRg2W4: launch_cfg<4, 2, 1, PRO, EPI>(fmt, dim3((uint32_t)ceil_div(a.total_rg, 2)), a, s); break;
+    case kW4T2: launch_cfg<4, 1, 2, PRO, EPI>(fmt, grid1, a, s); break;
+    case kW8T1: launch_cfg<8, 1, 1, PRO, EPI>(fmt, grid1, a, s); break;
+    default: launch_cfg<4, 1, 1, PRO, EPI>(fmt, grid1, a, s); break;
   }
   return hipGetLastError();
 }
@@ -420,12 +460,13 @@ hipError_t launch_small_m_pro(int fmt, const LinearArgs& a, hipStream_t s) {
 hipError_t launch_small_m(int fmt, const LinearArgs& a, hipStream_t s) {
   if (a.total_rg == 0) return hipSuccess;
   const bool epi = has_glue(a);     // any epilogue (or prologue): the storing kernels
+  const int shape = pick_small_m(fmt, a.total_rg, a.J);
   switch (a.pro) {
-    case QD_PRO_RMSNORM: return launch_small_m_pro<QD_PRO_RMSNORM, true>(fmt, a, s);
-    case QD_PRO_GLU: return launch_small_m_pro<QD_PRO_GLU, true>(fmt, a, s);
+    case QD_PRO_RMSNORM: return launch_small_m_pro<QD_PRO_RMSNORM, true>(fmt, a, s, shape);
+    case QD_PRO_GLU: return launch_small_m_pro<QD_PRO_GLU, true>(fmt, a, s, shape);
     default:
-      return epi ? launch_small_m_pro<QD_PRO_NONE, true>(fmt, a, s)
-                 : launch_small_m_pro<QD_PRO_NONE, false>(fmt, a, s);
+      return epi ? launch_small_m_pro<QD_PRO_NONE, true>(fmt, a, s, shape)
+                 : launch_small_m_pro<QD_PRO_NONE, false>(fmt, a, s, shape);
   }
 }
 

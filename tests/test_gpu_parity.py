@@ -234,14 +234,16 @@ def test_small_m_rows_match_gemv(qd, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_small_m_many_row_groups(qd, fmt):
-    """At least 1024 row-groups: the launch gives each workgroup four
-    row-groups that share one read of each activation block.  Ragged last
-    row-group, a fused pair whose workgroups straddle the member boundary,
-    and m below 16 (rows past m read as zero)."""
+@pytest.mark.parametrize("n_each", [8200, 32776])
+def test_small_m_many_row_groups(qd, fmt, n_each):
+    """At least 1024 row-groups: each workgroup takes two (up to ~4096 in the
+    launch) or four row-groups that share one read of each activation block.
+    Ragged last row-group, a fused pair whose workgroups straddle the member
+    boundary (513 + 513 and 2049 + 2049 row-groups), and m below 16 (rows past
+    m read as zero)."""
     from int4_quantized_decode_amd import LinearOp
     k = 2048
-    n1, n2 = 8200, 8200                      # 513 + 513 row-groups, each ragged
+    n1, n2 = n_each, n_each                  # odd row-group counts, each ragged
     w1 = si.weights(si.seed_for("sm-many", 1), n1, k)
     w2 = si.weights(si.seed_for("sm-many", 2), n2, k)
     for m in (16, 5):
