@@ -426,7 +426,7 @@ void launch_cfg(int fmt, dim3 grid, const LinearArgs& a, hipStream_t s) {
 // Launch shapes, chosen by a sweep over the Qwen3 2B/4B/8B and 27B-shaped
 // projections at m = 16 on MI355X (each shape's launches back to back):
 //  * many row-groups (gate|up, the head): 4-wave workgroups of 2 row-groups
-//    (up to ~4000 row-groups) or 4 row-groups (more), so each activation block
+//    (below 2048 row-groups) or 4 row-groups (more), so each activation block
 //    serves 2 or 4 tiles and several workgroups stay resident per CU;
 //  * fewer (q|k|v, o, down: one or two per CU): one row-group per workgroup;
 //    int8 waves issue two super-blocks' loads before their first product
@@ -434,7 +434,7 @@ void launch_cfg(int fmt, dim3 grid, const LinearArgs& a, hipStream_t s) {
 enum SmallShape { kRg4W4 = 0, kRg2W4 = 1, kW4T2 = 2, kW8T1 = 3, kW4T1 = 4 };
 
 int pick_small_m(int fmt, int64_t total_rg, int J) {
-  if (total_rg >= 4 * 256 && J >= 8) return total_rg >= 4096 ? kRg4W4 : kRg2W4;
+  if (total_rg >= 4 * 256 && J >= 8) return total_rg >= 2048 ? kRg4W4 : kRg2W4;
   if (J < 8) return kW4T1;
   return fmt == QD_FMT_INT8_B32 ? kW4T2 : kW8T1;
 }

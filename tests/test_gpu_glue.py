@@ -265,3 +265,48 @@ def test_glue_stack_persistent(qd, fmt):
     assert plan.error() == 0
     _check_glue_stack(fmt, 1, ops, meta, f"persistent {fmt}")
     plan.close()
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-glue-m1", "qwen3-8b-int8-glue-m16"])
+def test_glue_full_size_sampled(qd, workload):
+    """The full 8B-shaped step chained through the glue, as the bench times it
+    (per-group launches): every output finite; sampled rows of sampled
+    projections (RMSNorm-fed q and head, silu-stored gate, up, gated-product-fed
+    down, plain o) match the oracle on the activations each op read."""
+    import bench
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
+    for op in ops:
+        op.y.fill_(float("nan"))
+    qd.decode_linear_stack(ops, m)
+    torch.cuda.synchronize()
+    wl = si.WORKLOADS[workload]
+    d = wl.decoder
+    names = [p for _, ms in d.groups() for p, _, _ in ms]
+    assert len(names) == len(ops)
+    for op in ops:
+        assert torch.isfinite(op.y).all()
+    last, mid = d.layers - 1, d.layers // 2
+    rng = np.random.default_rng(14)
+    for name in ["L0.q", f"L{mid}.gate", f"L{mid}.up", f"L{last}.down", f"L{last}.o", "head"]:
+        op = ops[names.index(name)]
+        n, k = op.w.n, op.w.k
+        x_dev = _host(op.x).astype(np.float16)
+        if op.prologue == "glu":
+            xin = glue.apply_prologue("glu", x_dev.reshape(2, m, k))
+        elif op.prologue == "rmsnorm":
+            xin = glue.rmsnorm_fp16(x_dev.reshape(m, k), _host(op.gamma), op.eps)
+        else:
+            xin = x_dev.reshape(m, k)
+        rows = np.sort(rng.choice(n, 16, replace=False))
+        w_rows = si.weights_torch(si.matrix_seed(d.name, name), n, k, DEV)[rows].cpu().numpy()
+        parts = _parts(wl.fmt, w_rows)
+        ref = linear.ref_linear(wl.fmt, parts, xin).reshape(m, -1)
+        rmax = linear.row_max_abs(wl.fmt, parts)
+        y = _host(op.y).reshape(m, -1)[:, rows]
+        for t in range(m):
+            if op.epilogue == "silu":
+                _check_silu(y[t], ref[t], rmax, xin[t], f"{name} token {t}")
+            else:
+                check_vector(y[t], ref[t], rmax, xin[t], f"{name} token {t}")
+    del ops
+    torch.cuda.empty_cache()

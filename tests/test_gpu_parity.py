@@ -236,7 +236,7 @@ def test_small_m_rows_match_gemv(qd, fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n_each", [8200, 32776])
 def test_small_m_many_row_groups(qd, fmt, n_each):
-    """At least 1024 row-groups: each workgroup takes two (up to ~4096 in the
+    """At least 1024 row-groups: each workgroup takes two (below 2048 in the
     launch) or four row-groups that share one read of each activation block.
     Ragged last row-group, a fused pair whose workgroups straddle the member
     boundary (513 + 513 and 2049 + 2049 row-groups), and m below 16 (rows past
