@@ -225,6 +225,17 @@ def test_glue_stack_launches(qd, fmt, m):
     _check_glue_stack(fmt, m, ops, meta, f"launches {fmt} m={m}")
 
 
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 16), ("int4_g64", 16), ("fp16", 5)])
+def test_glue_stack_plan_multi_token(qd, fmt, m):
+    """A plan of the glued step at m > 1 (it replays the glued launches)."""
+    ops, meta, keep = _glue_stack(qd, fmt, m, _tiny())
+    plan = qd.StackPlan(ops, m)
+    plan.run()
+    torch.cuda.synchronize()
+    _check_glue_stack(fmt, m, ops, meta, f"plan {fmt} m={m}")
+    plan.close()
+
+
 @pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 def test_glue_stack_plan_parity_and_determinism(qd, fmt):
     """A plan of the glued step (it replays the per-group launches): per-op

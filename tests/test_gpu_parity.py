@@ -616,3 +616,52 @@ def test_stack_full_size_sampled_fp16_head(qd):
         check_vector(_host(op.y)[rows], linear.ref_linear(fmt, parts, x), linear.row_max_abs(fmt, parts),
                      x, f"{name} ({fmt})")
     plan.close()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_plan_multi_token_groups(qd, fmt):
+    """A plan at m > 1 (it replays the per-group launches): groups of many
+    shapes (K = 1088, a ragged super-block tail; 4096 x 4096; K = 12288; a
+    fused pair; a group large enough for multi-row-group workgroups) and m
+    below 16.  Runs repeat with outputs poisoned in between and are
+    bit-identical; the plan's outputs equal decode_linear_stack's."""
+    from int4_quantized_decode_amd import LinearOp
+    shapes = [("a", [(200, 1088), (72, 1088)]), ("b", [(4096, 4096)]), ("c", [(512, 12288)]),
+              ("d", [(16400, 2048)])]
+    for m in (16, 5):
+        ops, meta = [], []
+        for gid, (gname, mems) in enumerate(shapes):
+            k = mems[0][1]
+            X = si.activations(si.seed_for("splitk-x", gname, m), m, k)
+            xg = _gpu(X)
+            for i, (n, kk) in enumerate(mems):
+                w = si.weights(si.seed_for("splitk-w", gname, i), n, kk)
+                y = torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+                ops.append(LinearOp(_pack(qd, fmt, _gpu(w)), xg, y, gid))
+                meta.append((f"{gname}{i}", w, X))
+        plan = qd.StackPlan(ops, m)
+        assert not plan.persistent
+        first = None
+        for rep in range(3):
+            for op in ops:
+                op.y.fill_(float("nan"))
+            plan.run()
+            outs = [_host(op.y).copy() for op in ops]
+            if first is None:
+                first = outs
+                for Y, (name, w, X) in zip(outs, meta):
+                    parts = _oracle_parts(fmt, w)
+                    Y_ref = linear.ref_linear(fmt, parts, X)
+                    rmax = linear.row_max_abs(fmt, parts)
+                    for t in range(m):
+                        check_vector(Y[t], Y_ref[t], rmax, X[t], f"{fmt} {name} m={m} token {t}")
+            else:
+                for a_, b_ in zip(first, outs):
+                    assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
+        # the same launches as decode_linear_stack: the same bytes
+        for op in ops:
+            op.y.fill_(float("nan"))
+        qd.decode_linear_stack(ops, m)
+        for op, Yp in zip(ops, first):
+            assert np.array_equal(_host(op.y).view(np.uint16), Yp.view(np.uint16))
+        plan.close()
