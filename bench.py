@@ -336,7 +336,8 @@ def main():
     kname = ("stack_kernel (persistent, one launch per step)" if persistent else
              f"{family} family, {ngroups} fused launch{'es' if ngroups > 1 else ''} per step "
              f"(kernels plus launch gaps)")
-    traffic = recorded_traffic("stack_kernel" if persistent else "gemv_launches", args.workload)
+    traffic = recorded_traffic("stack_kernel" if persistent else
+                               ("small_m_launches" if m > 1 else "gemv_launches"), args.workload)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
