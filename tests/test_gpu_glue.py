@@ -117,6 +117,44 @@ def test_prologues_and_epilogue_exact(qd, fmt, m, path):
     assert float(got[2][0, 2]) == 0.0 and float(got[2][0, 3]) == float(want_silu[0, 3])
 
 
+@pytest.mark.parametrize("m", [1, 16])
+def test_glue_largest_k_sampled(qd, m):
+    """The glue at the largest K (24576; the gated product reads 2 x 24576
+    values per token): a weight whose row n picks one input position k_n,
+    spread over all of K including its last element, so y[n] is the glued
+    value at k_n scaled by 127/128 (exact, as in the pass-through test)."""
+    k, n = 24576, 96
+    c = 127.0 / 128.0
+    ks = np.unique(np.concatenate([np.linspace(0, k - 1, n - 3).astype(int), [1, k - 2, k - 1]]))[:n]
+    n = len(ks)
+    w = np.zeros((n, k), np.float32)
+    w[np.arange(n), ks] = np.float32(c)
+    pw = _pack(qd, "int8_b32", w)
+    x = si.activations(si.seed_for("glue-maxk-x", m), m, k)
+    a = si.activations(si.seed_for("glue-maxk-a", m), m, k)
+    b = si.activations(si.seed_for("glue-maxk-b", m), m, k)
+    gam = si.norm_weight(si.seed_for("glue-maxk-g"), k)
+    shape = (m, n) if m > 1 else (n,)
+    ys = [torch.full(shape, float("nan"), dtype=torch.float16, device=DEV) for _ in range(3)]
+    xs = _gpu(x if m > 1 else x[0])
+    ab = _gpu(np.concatenate([a, b], 0).reshape(-1))
+    as_ = _gpu(a if m > 1 else a[0])
+    ops = [qd.LinearOp(pw, xs, ys[0], 0, prologue="rmsnorm", gamma=_gpu(gam), eps=EPS),
+           qd.LinearOp(pw, ab, ys[1], 1, prologue="glu"),
+           qd.LinearOp(pw, as_, ys[2], 2, epilogue="silu")]
+    qd.decode_linear_stack(ops, m)
+    got = [_host(y).reshape(m, n) for y in ys]
+
+    def scaled(v16):
+        return (v16.astype(np.float64) * c).astype(np.float16)
+
+    want = [scaled(glue.rmsnorm_fp16(x, gam, EPS)[:, ks]), scaled(glue.glu_fp16(a, b)[:, ks]),
+            glue.silu_fp16(scaled(a[:, ks]))]
+    assert np.array_equal(got[1].view(np.uint16), want[1].view(np.uint16)), "gated product"
+    for name, gv, wv in (("rmsnorm", got[0], want[0]), ("silu", got[2], want[2])):
+        assert _ulps(gv, wv).max() <= 1.0, name
+
+
 # ------------------------------------------------------- decoder-shaped chains
 
 def _check_silu(s_gpu, a_ref, row_max, xin, what):

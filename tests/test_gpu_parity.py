@@ -202,7 +202,7 @@ def test_gemv_edge_cases(qd, fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m", [1, 5, 16])
 @pytest.mark.parametrize("n,k", [(16, 256), (200, 1056), (48, 2048), (100, 4096), (64, 12288),
-                                 (40, 1088)])
+                                 (40, 1088), (24, 24576)])
 def test_small_m_parity(qd, fmt, m, n, k):
     _skip_bad_k(fmt, k)
     w = si.weights(si.seed_for("sm", n, k), n, k)
@@ -459,13 +459,13 @@ def test_plan_chain_respects_order(qd):
 
 def test_plan_ragged_and_uneven_groups(qd):
     """Groups with fewer row-groups than workgroups (most workgroups get none),
-    long K (activations staged in many 1 KiB blocks), K that is not a multiple
+    long K up to the largest accepted (activations staged in many 1 KiB blocks), K that is not a multiple
     of 256 or gives an odd number of 256-wide blocks, ragged row tails, and
     groups with more row-groups than workgroups whose ranges straddle member
     boundaries."""
     from int4_quantized_decode_amd import LinearOp
     shapes = [[(24, 12288)], [(37, 2048), (5, 2048), (100, 2048)], [(4000, 512)], [(16, 256)],
-              [(9, 4096)], [(40, 768)], [(33, 1056)],
+              [(9, 4096)], [(40, 768)], [(33, 1056)], [(20, 24576)],      # the largest K
               # at least one row-group per workgroup: whole-row-group ranges, several of
               # which straddle a boundary between members
               [(4096, 256), (1024, 256), (1024, 256)], [(2000, 512), (1000, 512), (1200, 512)]]
