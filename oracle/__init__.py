@@ -31,6 +31,7 @@ What it computes, and where each step comes from:
 
 Readings of points the pages leave open are listed in each function's
 docstring.  Functions whose agreement with the pages rests only on such a
-reading are marked "parity unpinned" (the tiled layout, the INT4 format).
+reading are marked "parity unpinned" (the tiled layout, the INT4 format, the
+glue formulas and their fp16 rounding points).
 """
 from . import quant, layout, glue, linear  # noqa: F401

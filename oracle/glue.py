@@ -18,6 +18,11 @@ here are the plainest ones for a Qwen3 decoder run in fp16:
 
 Every value here is computed in fp64 and rounded to fp16 (nearest, ties to
 even) exactly where the readings above store an fp16 value.
+
+Parity unpinned by the pages: they fix neither formula, the epsilon, nor the
+rounding points.  The pins tie this module to the mathematics (hand-derived
+values, torch's rms_norm, scipy's logistic, exact invariants), not to the
+pages.
 """
 from __future__ import annotations
 
