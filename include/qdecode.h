@@ -200,9 +200,14 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
 /*
  * The same step as a persistent plan: one kernel launch per step that walks
  * every group in order, keeping the weight stream going across group
- * boundaries (weights of later groups are fetched while a group completes; a
- * group's activations are read only after every op of the group before it
- * has finished, so an op may consume an earlier op's output).
+ * boundaries (weights of later groups are fetched while a group completes).
+ * Every group's products start only after every workgroup has finished the
+ * group before it.  The plan orders each boundary from the step's buffers:
+ * a group's activations are read ahead of that barrier only when no earlier
+ * group writes any byte of them, and a group's outputs are made visible
+ * before its completion is signalled only when a later group reads or
+ * rewrites them.  Results equal those of decode_linear_stack's sequential
+ * launches, so an op may consume (or overwrite) an earlier op's buffers.
  * qd_stack_plan_create validates `ops` exactly as decode_linear_stack does,
  * copies the descriptors to the device and allocates the plan's scratch
  * (completion stamps, an error word) once; the pointers in `ops` must stay

@@ -58,7 +58,14 @@ constexpr int kCtl = 15;                // the control wave
 // stalls.  The plan picks R from the step's shape (see plan_create).
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
 
-struct PGroup {         // 48 bytes
+// Ordering a group needs around its boundary, from the plan's overlap
+// analysis of the step's buffers.
+enum : int32_t {
+  kStageEarly = 1,      // no earlier group writes any byte of x: it may be staged before the barrier
+  kAckOutputs = 2,      // a later group reads or rewrites an output: stores complete before the stamp
+};
+
+struct PGroup {         // 64 bytes
   const uint16_t* x;
   const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
   int64_t k;
@@ -68,6 +75,8 @@ struct PGroup {         // 48 bytes
   int32_t n_mem;
   int32_t pro;          // qd_prologue of the group's input
   float eps;
+  int32_t order;        // kStageEarly | kAckOutputs
+  int32_t pad[3];
 };
 
 struct PMember {        // 32 bytes
@@ -158,6 +167,7 @@ struct Sched {
   __device__ const uint16_t* x(int gi) const { return uni_ptr(g[gi].x); }
   __device__ const uint16_t* gamma(int gi) const { return uni_ptr(g[gi].gamma); }
   __device__ int pro(int gi) const { return uni(g[gi].pro); }
+  __device__ int order(int gi) const { return uni(g[gi].order); }
   __device__ float eps(int gi) const { return __builtin_bit_cast(float, uni(__builtin_bit_cast(int, g[gi].eps))); }
   __device__ int64_t k(int gi) const { return (int64_t)uni((int)g[gi].k); }
   __device__ int tiles(int gi) const { return uni(s[gi].n); }
@@ -521,8 +531,11 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
 }
 
 // Publish that this workgroup has finished every row it owes group g.
-__device__ __forceinline__ void publish(const PlanArgs& p, int g, int w, int lane) {
-  wait_stores();                                            // outputs before the stamp
+// When no later group of the step reads or rewrites the outputs, they need
+// only be visible when the kernel ends, and the stamp goes out without
+// waiting for the stores to complete.
+__device__ __forceinline__ void publish(const PlanArgs& p, const Sched& S, int g, int w, int lane) {
+  if (S.order(g) & kAckOutputs) wait_stores();              // outputs before the stamp
   if (lane == 0)
     __hip_atomic_store(&p.flags[w], stamp(p, g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -588,10 +601,15 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
     finish_group<GLUE>(p, S, g, lane, red, cnt, stalled, dead);
-    publish(p, g, w, lane);
+    publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
+      // Activations no earlier group writes are staged while the stamps are
+      // awaited; the others only once every workgroup has finished g.  The
+      // compute waves start g + 1 after the barrier either way.
+      const bool early = (S.order(g + 1) & kStageEarly) != 0;
+      if (early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
       wait_group(p, g, lane);
-      stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+      if (!early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
       if (lane == 0) lds_put(staged, g + 1);
       wg_barrier();               // activations of g + 1 staged
     }
@@ -699,7 +717,38 @@ struct HostGroup {
   const uint16_t* gamma;
   int pro;
   float eps;
+  int32_t order = 0;
 };
+
+bool ranges_overlap(const void* a, uint64_t an, const void* b, uint64_t bn) {
+  if (!a || !b || !an || !bn) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Boundary ordering from the buffers (one token row): a group's x may be
+// staged early unless an earlier group's output overlaps it; a group's
+// stores must complete before its stamp if a later group's x or output
+// overlaps one of its outputs.
+void order_groups(std::vector<HostGroup>& gs) {
+  const size_t n = gs.size();
+  for (size_t i = 0; i < n; ++i) {
+    const uint64_t xb = (uint64_t)gs[i].k * 2 * (gs[i].pro == QD_PRO_GLU ? 2 : 1);
+    bool early = true;
+    for (size_t j = 0; j < i; ++j) {
+      for (const PMember& pj : gs[j].mem) {
+        const uint64_t yj = (uint64_t)pj.n * 2;
+        bool reads = ranges_overlap(gs[i].x, xb, pj.y, yj) ||
+                     (gs[i].pro == QD_PRO_RMSNORM && ranges_overlap(gs[i].gamma, (uint64_t)gs[i].k * 2, pj.y, yj));
+        bool rewrites = false;
+        for (const PMember& pi : gs[i].mem) rewrites = rewrites || ranges_overlap(pi.y, (uint64_t)pi.n * 2, pj.y, yj);
+        if (reads) early = false;
+        if (reads || rewrites) gs[j].order |= kAckOutputs;
+      }
+    }
+    if (early) gs[i].order |= kStageEarly;
+  }
+}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -790,6 +839,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return QD_OK;
   }
 
+  order_groups(groups);
   const int G = cus;
   const int ng = (int)groups.size();
   std::vector<PGroup> pg(ng);
@@ -809,7 +859,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     const int64_t J = hg.J, R = hg.R, T = R * J;
     if (T > (int64_t)INT32_MAX / 2) return fallback();
     pg[g] = PGroup{hg.x, hg.gamma, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size(),
-                   hg.pro, hg.eps};
+                   hg.pro, hg.eps, hg.order, {0, 0, 0}};
     for (const PMember& mm : hg.mem) pm.push_back(mm);
     maxJ = std::max(maxJ, hg.J);
     // halves of LDS the staging writes: x's span, and the second operand's

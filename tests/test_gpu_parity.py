@@ -665,3 +665,63 @@ def test_plan_multi_token_groups(qd, fmt):
         for op, Yp in zip(ops, first):
             assert np.array_equal(_host(op.y).view(np.uint16), Yp.view(np.uint16))
         plan.close()
+
+
+def test_plan_buffer_orderings(qd):
+    """The persistent step orders each boundary from the step's buffers: an
+    input no earlier output overlaps is staged early, one that an earlier
+    output overlaps (not only the previous group's) only after the barrier;
+    outputs a later group reads or rewrites are stored before the stamp.
+    Checked against a sequential model of the buffers: a group reading the
+    output of two groups back, a group rewriting an earlier group's output
+    (the later value must win), a group overwriting an earlier group's input
+    that a later group then reads, and independent groups between them."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 1024
+    nbuf = 6
+    bufs = [torch.empty(k, dtype=torch.float16, device=DEV) for _ in range(nbuf)]
+    init = [si.activations(si.seed_for("order-buf", i), 1, k)[0] for i in range(nbuf)]
+    # (x buffer, y buffer) per group, in step order; all matrices are k x k
+    prog = [(0, 1),   # g0: independent input
+            (2, 3),   # g1: independent (early staging)
+            (1, 4),   # g2: reads g0's output, two groups back
+            (5, 3),   # g3: rewrites g1's output
+            (4, 0),   # g4: reads g2's output, overwrites g0's input
+            (0, 2),   # g5: reads g4's output from g0's old input buffer
+            (3, 5)]   # g6: reads g3's rewrite of buffer 3
+    ws = [si.weights(si.seed_for("order-w", g), k, k) for g in range(len(prog))]
+    pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
+    ops = [LinearOp(pws[g], bufs[xb], bufs[yb], g) for g, (xb, yb) in enumerate(prog)]
+    plan = qd.StackPlan(ops, 1)
+    assert plan.persistent
+    # the sequential model, with each stored output rounded to fp16
+    state = [v.astype(np.float16) for v in init]
+    want, xin = [None] * len(prog), [None] * len(prog)
+    for g, (xb, yb) in enumerate(prog):
+        parts = quant.quantize_int8_b32(ws[g])
+        xin[g] = state[xb].copy()
+        want[g] = linear.ref_linear("int8_b32", parts, xin[g])
+        state[yb] = want[g].astype(np.float16)
+    final_writer = {}
+    for g, (xb, yb) in enumerate(prog):
+        final_writer[yb] = g
+    first = None
+    for rep in range(3):
+        for i, b in enumerate(bufs):
+            b.copy_(_gpu(init[i]))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        outs = [_host(b).copy() for b in bufs]
+        if first is None:
+            first = outs
+            for yb, g in final_writer.items():
+                parts = quant.quantize_int8_b32(ws[g])
+                # the input the kernel saw was the device's own earlier output: bound the
+                # chain by the rows' magnitudes along the path (at most 3 products deep)
+                check_vector(outs[yb], want[g], 4 * linear.row_max_abs("int8_b32", parts),
+                             xin[g].astype(np.float64), f"buffer {yb} (group {g})")
+        else:
+            for a_, b_ in zip(first, outs):
+                assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
+    plan.close()
