@@ -50,6 +50,8 @@ def build_stack(qd, si, torch, workload, dev):
     m = wl.m
     if wl.glue:
         return build_glue_stack(qd, si, torch, workload, dev)
+    if wl.chain:
+        return build_chain_stack(qd, si, torch, workload, dev)
     if wl.single is not None:
         n, k = wl.single
         groups, model = [("gemv", [("W", n, k)])], "single"
@@ -77,6 +79,56 @@ def build_stack(qd, si, torch, workload, dev):
 PACKERS = {"int8_b32": lambda qd: qd.qpack_int8_b32, "int4_g64": lambda qd: qd.qpack_int4_g64,
            "fp16": lambda qd: qd.qpack_fp16}
 GLUE_EPS = 1e-6
+
+
+def build_chain_stack(qd, si, torch, workload, dev):
+    """The decoder step with a true dependency at every boundary (each group
+    reads an earlier group's output; see synthetic_inputs).  Weights are
+    drawn as for the other workloads and scaled to standard deviation
+    1/sqrt(K), so that activations keep their size along the 145-group
+    chain instead of overflowing fp16; quantized bytes and timing do not
+    depend on that scale."""
+    wl = si.WORKLOADS[workload]
+    m, d = wl.m, wl.decoder
+    H, Q, I = d.hidden, d.q_dim, d.mlp
+    shape = (lambda n: (m, n) if m > 1 else (n,))
+    ops, alg_bytes, weight_bytes = [], 0, 0
+    gi = 0
+
+    def add(pname, n, k, x, fmt=wl.fmt):
+        nonlocal alg_bytes, weight_bytes
+        w = si.weights_torch(si.matrix_seed(d.name, pname), n, k, dev)
+        w.mul_(1.0 / (si.W_STD * k ** 0.5))
+        pw = PACKERS[fmt](qd)(w)
+        del w
+        y = torch.empty(shape(n), dtype=torch.float16, device=dev)
+        ops.append(qd.LinearOp(pw, x, y, gi))
+        alg_bytes += pw.blob.numel() + m * n * 2
+        weight_bytes += pw.blob.numel()
+        return y
+
+    x_in = torch.from_numpy(si.activations(si.activation_seed(workload, "x0"), m, H)
+                            .reshape(shape(H))).to(dev)
+    for layer in range(d.layers):
+        alg_bytes += m * H * 2
+        q_y = add(f"L{layer}.q", Q, H, x_in)
+        add(f"L{layer}.k", d.kv_dim, H, x_in)
+        add(f"L{layer}.v", d.kv_dim, H, x_in)
+        gi += 1
+        alg_bytes += m * Q * 2
+        o_y = add(f"L{layer}.o", H, Q, q_y)
+        gi += 1
+        alg_bytes += m * H * 2
+        gate_y = add(f"L{layer}.gate", I, H, o_y)
+        add(f"L{layer}.up", I, H, o_y)
+        gi += 1
+        alg_bytes += m * I * 2
+        x_in = add(f"L{layer}.down", H, I, gate_y)
+        gi += 1
+    alg_bytes += m * H * 2
+    add("head", d.vocab, H, x_in, fmt=wl.head_fmt or wl.fmt)
+    torch.cuda.synchronize()
+    return ops, alg_bytes, weight_bytes, m
 
 
 def build_glue_stack(qd, si, torch, workload, dev):
@@ -359,7 +411,7 @@ def main():
                    "read_probe_gbs": round(probe, 1), "frac_of_read_probe": round(value / probe, 4),
                    "us_p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
                    "us_p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2),
-                   "glue": wl.glue,
+                   "glue": wl.glue, "chained": wl.chain or wl.glue,
                    "tok_per_s_note": ("linear stack with fused RMSNorm and SwiGLU glue; excludes attention, "
                                       "residual adds and embedding" if wl.glue else
                                       "linear stack only; excludes attention, norms and embedding")},

@@ -755,10 +755,11 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Reserve waves (and tiles each) per format and step shape, as measured on
 // MI355X: int4 tiles carry twice the arithmetic per byte and there every
 // streaming slot is needed; int8 steps whose groups give each workgroup many
-// tiles (8B-shaped: ~50 per group) do best with 7 reserve waves of 3 tiles,
-// steps with smaller groups (2B/4B-shaped: 15-26) with 4 waves of 5 tiles.
-// More reserve tiles than that run several groups ahead and are then not
-// free for the next stall; fewer leave memory idle for part of it.
+// tiles (8B-shaped: ~50 per group) do best with 7 reserve waves of 2 tiles
+// (the 8 streaming waves then sit two to a SIMD), steps with smaller groups
+// (2B/4B-shaped: 15-26) with 4 waves of 5 tiles.  More reserve tiles than
+// that run several groups ahead and are then not free for the next stall;
+// fewer leave memory idle for part of it.
 constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
 
 #ifndef QD_PLAN_RESERVE4
@@ -770,7 +771,7 @@ constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 #define QD_PLAN_BIG_R 7
 #endif
 #ifndef QD_PLAN_BIG_S
-#define QD_PLAN_BIG_S 3
+#define QD_PLAN_BIG_S 2
 #endif
 constexpr int kBigR = QD_PLAN_BIG_R, kBigS = QD_PLAN_BIG_S;
 

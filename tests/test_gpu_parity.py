@@ -520,7 +520,8 @@ def _sample_picks(decoder):
     return ["L0.q", "L0.k", f"L{mid}.gate", f"L{mid}.up", f"L{last}.down", f"L{last}.o", "head"]
 
 
-@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1"])
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1",
+                                      "qwen3-8b-int8-chain-m1"])
 def test_plan_full_size_sampled(qd, workload):
     """The full decoder-shaped step in the launch configuration the bench
     times: every output finite, sampled rows of sampled projections match
@@ -546,8 +547,12 @@ def test_plan_full_size_sampled(qd, workload):
         op = ops[i]
         n, k = op.w.n, op.w.k
         rows = np.sort(rng.choice(n, 24, replace=False))
-        w_rows = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)[rows].cpu().numpy()
-        x = op.x.cpu().numpy()
+        w_full = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)
+        if wl.chain:                                   # the chained step's weight scale
+            w_full.mul_(1.0 / (si.W_STD * k ** 0.5))
+        w_rows = w_full[rows].cpu().numpy()
+        del w_full
+        x = op.x.cpu().numpy()                         # the activation the op read
         parts = _oracle_parts(wl.fmt, w_rows)
         y_ref = linear.ref_linear(wl.fmt, parts, x)
         check_vector(_host(op.y)[rows], y_ref, linear.row_max_abs(wl.fmt, parts), x, name)
