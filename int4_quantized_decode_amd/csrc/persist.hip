@@ -774,6 +774,13 @@ constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 #define QD_PLAN_BIG_S 2
 #endif
 constexpr int kBigR = QD_PLAN_BIG_R, kBigS = QD_PLAN_BIG_S;
+#ifndef QD_PLAN_SMALL_R
+#define QD_PLAN_SMALL_R 4
+#endif
+#ifndef QD_PLAN_SMALL_S
+#define QD_PLAN_SMALL_S 5
+#endif
+constexpr int kSmallR = QD_PLAN_SMALL_R, kSmallS = QD_PLAN_SMALL_S;
 
 enum ReserveShape { kInt4 = 0, kInt8Big = 1, kInt8Small = 2 };
 
@@ -782,7 +789,7 @@ const void* kernel_ptr(int shape) {
     case kInt8Big:
       return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kBigR, kBigS, false>);
     case kInt8Small:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, 4, 5, false>);
+      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kSmallR, kSmallS, false>);
     default:
       return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false>);
   }
