@@ -694,7 +694,6 @@ struct qd_stack_plan {
   int device = 0;
   bool persistent = false;
   int fmt = 0;
-  int reserve = 0;                       // which persistent-kernel instance (wave roles)
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (m > 1, K = 0, mixed formats)
   void* tables = nullptr;
   void* scratch = nullptr;
@@ -752,47 +751,30 @@ void order_groups(std::vector<HostGroup>& gs) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Reserve waves (and tiles each) per format and step shape, as measured on
-// MI355X: int4 tiles carry twice the arithmetic per byte and there every
-// streaming slot is needed; int8 steps whose groups give each workgroup many
-// tiles (8B-shaped: ~50 per group) do best with 7 reserve waves of 2 tiles
-// (the 8 streaming waves then sit two to a SIMD), steps with smaller groups
-// (2B/4B-shaped: 15-26) with 4 waves of 5 tiles.  More reserve tiles than
-// that run several groups ahead and are then not free for the next stall;
-// fewer leave memory idle for part of it.
-constexpr int kBigGroupTiles = 40;     // mean tiles per workgroup per group
-
+// Reserve waves (and tiles each) per format, as measured on MI355X.  int8:
+// 7 reserve waves of 2 tiles, the 8 streaming waves then sitting two to a
+// SIMD; this was best for the 2B-, 4B- and 8B-shaped steps alike (15 to 50
+// tiles per workgroup per group).  More reserve tiles run several groups
+// ahead and are then not free for the next stall; fewer leave memory idle
+// for part of it.  INT4 tiles carry twice the arithmetic per byte and there
+// every streaming slot is needed: no reserve waves.
 #ifndef QD_PLAN_RESERVE4
 #define QD_PLAN_RESERVE4 0
 #endif
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 
-#ifndef QD_PLAN_BIG_R
-#define QD_PLAN_BIG_R 7
+#ifndef QD_PLAN_RESERVE8_R
+#define QD_PLAN_RESERVE8_R 7
 #endif
-#ifndef QD_PLAN_BIG_S
-#define QD_PLAN_BIG_S 2
+#ifndef QD_PLAN_RESERVE8_S
+#define QD_PLAN_RESERVE8_S 2
 #endif
-constexpr int kBigR = QD_PLAN_BIG_R, kBigS = QD_PLAN_BIG_S;
-#ifndef QD_PLAN_SMALL_R
-#define QD_PLAN_SMALL_R 4
-#endif
-#ifndef QD_PLAN_SMALL_S
-#define QD_PLAN_SMALL_S 5
-#endif
-constexpr int kSmallR = QD_PLAN_SMALL_R, kSmallS = QD_PLAN_SMALL_S;
+constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 
-enum ReserveShape { kInt4 = 0, kInt8Big = 1, kInt8Small = 2 };
-
-const void* kernel_ptr(int shape) {
-  switch (shape) {
-    case kInt8Big:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kBigR, kBigS, false>);
-    case kInt8Small:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kSmallR, kSmallS, false>);
-    default:
-      return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false>);
-  }
+const void* kernel_ptr(int fmt) {
+  if (fmt == QD_FMT_INT8_B32)
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false>);
+  return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false>);
 }
 
 }  // namespace
@@ -902,12 +884,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     delete plan;
     return QD_EDEVICE;
   }
-  int64_t total_tiles = 0;
-  for (int g = 0; g < ng; ++g) total_tiles += (int64_t)pg[g].R * pg[g].J;
-  const int reserve = fmt == QD_FMT_INT4_G64 ? kInt4
-                      : total_tiles >= (int64_t)kBigGroupTiles * ng * G ? kInt8Big
-                                                                         : kInt8Small;
-  const void* kfn = kernel_ptr(reserve);
+  const void* kfn = kernel_ptr(fmt);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -962,7 +939,6 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = fmt;
-  plan->reserve = reserve;
   plan->persistent = true;
   *out = plan;
   return QD_OK;
@@ -974,7 +950,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->reserve), dim3(plan->args.G),
+  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt), dim3(plan->args.G),
                                                   dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;
