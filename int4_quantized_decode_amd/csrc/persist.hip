@@ -545,6 +545,10 @@ __device__ __forceinline__ void publish(const PlanArgs& p, const Sched& S, int g
 // polls are kept two deep, so a stamp that lands while one poll is in flight
 // is seen by the next one, already on its way.
 constexpr int kMaxWorkgroups = 512;
+#ifndef QD_POLL_DEPTH
+#define QD_POLL_DEPTH 2
+#endif
+constexpr int kPollDepth = QD_POLL_DEPTH;
 
 __device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4]) {
   // The clobbers keep the compiler from merging two polls of the same
@@ -573,14 +577,19 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(p.flags, (uint32_t)p.G * 8);
-  u32x4 a[4], b[4];
-  poll_stamps(rf, lane, a);
-  for (uint32_t spins = 0;; spins += 2) {
-    poll_stamps(rf, lane, b);
-    if (stamps_reached(a, p.G, lane, target)) break;
-    poll_stamps(rf, lane, a);
-    if (stamps_reached(b, p.G, lane, target)) break;
-    if (spins > kSpinLimit) {
+  // kPollDepth polls in flight: each check consumes the oldest and issues a
+  // new one, so a stamp is seen about one poll interval after it lands.
+  u32x4 v[kPollDepth][4];
+#pragma unroll
+  for (int i = 0; i < kPollDepth - 1; ++i) poll_stamps(rf, lane, v[i]);
+  bool done = false;
+  for (uint32_t spins = 0; !done; spins += kPollDepth) {
+#pragma unroll
+    for (int i = 0; i < kPollDepth; ++i) {
+      poll_stamps(rf, lane, v[(i + kPollDepth - 1) % kPollDepth]);
+      if (!done && stamps_reached(v[i], p.G, lane, target)) done = true;
+    }
+    if (!done && spins > kSpinLimit) {
       if (lane == 0) atomicOr(p.err, 1u);
       break;
     }
