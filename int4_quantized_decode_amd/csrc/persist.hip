@@ -65,6 +65,12 @@ enum : int32_t {
   kAckOutputs = 2,      // a later group reads or rewrites an output: stores complete before the stamp
 };
 
+#ifndef QD_EARLY_CACHED
+#define QD_EARLY_CACHED 0
+#endif
+// Cache policy of early staging (activations nothing in the step writes).
+constexpr int kEarlyPolicy = QD_EARLY_CACHED ? kPolicyDefault : kPolicyCoherent;
+
 struct PGroup {         // 64 bytes
   const uint16_t* x;
   const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
@@ -400,11 +406,12 @@ __device__ __forceinline__ unsigned long long stamp(const PlanArgs& p, int g) {
 // a multiple of 512 halves (x_span).  The caller waits.
 __host__ __device__ constexpr int x_span(int Kp) { return (Kp + 511) / 512 * 512; }
 
+template <int POLICY>
 __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int lane, half_t* xs) {
   for (int i = 0; i < Kp; i += 512)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(xs + i), 16, (uint32_t)(i * 2 + lane * 16), 0,
-        0, kPolicyCoherent);
+        0, POLICY);
 }
 
 // Stage a group's multiplied vector (and, for int4, its 16-value run sums) in
@@ -412,19 +419,22 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
 // gated product's B block) into xs + x_span(Kp), are issued before the single wait,
 // so staging costs one memory round trip whatever K is.  The prologue then
 // runs in place: each lane rewrites the 8-value chunks its own loads brought.
-template <int FMT, bool GLUE>
+template <int FMT, bool GLUE, int POLICY = kPolicyCoherent>
 __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
                                               float* xsum) {
+  // POLICY: device-coherent for activations an earlier group of the step may
+  // have written; cached for the others, which nothing in the step writes
+  // (the workgroups of an XCD then share one L2 copy).
   const int Kp = S.J(g) * kSuperK;
   const int64_t k = S.k(g);
   const uint32_t xbytes = (uint32_t)(k * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), xbytes);
-  dma_to_lds(rx, Kp, lane, xs);
+  dma_to_lds<POLICY>(rx, Kp, lane, xs);
   if constexpr (GLUE) {
     const int pro = S.pro(g);
     half_t* const xs2 = xs + x_span(Kp);            // second operand, after x's whole span
-    if (pro == QD_PRO_GLU) dma_to_lds(make_rsrc(S.x(g) + k, xbytes), Kp, lane, xs2);
-    if (pro == QD_PRO_RMSNORM) dma_to_lds(make_rsrc(S.gamma(g), xbytes), Kp, lane, xs2);
+    if (pro == QD_PRO_GLU) dma_to_lds<POLICY>(make_rsrc(S.x(g) + k, xbytes), Kp, lane, xs2);
+    if (pro == QD_PRO_RMSNORM) dma_to_lds<POLICY>(make_rsrc(S.gamma(g), xbytes), Kp, lane, xs2);
     wait_stores();                                 // vmcnt(0): the data is in LDS
     if (pro == QD_PRO_GLU) {
       for (int i = lane * 8; i < Kp; i += 512)
@@ -551,18 +561,27 @@ constexpr int kMaxWorkgroups = 512;
 #define QD_POLL_DEPTH 1
 #endif
 constexpr int kPollDepth = QD_POLL_DEPTH;
+#ifndef QD_POLL_SKIP
+#define QD_POLL_SKIP 0
+#endif
+constexpr bool kPollSkip = QD_POLL_SKIP != 0;
 
-__device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4]) {
+// skip: this lane has already seen all its stamps reach the target; its
+// reads then fall outside the buffer (zeros, no memory access).
+__device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4],
+                                            bool skip = false) {
   // The clobbers keep the compiler from merging two polls of the same
   // addresses into one load or hoisting a poll out of the loop.
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int b = 0; b < 4; ++b) v[b] = bload16_coherent(rf, (uint32_t)(128 * b + 2 * lane) * 8);
+  for (int b = 0; b < 4; ++b)
+    v[b] = bload16_coherent(rf, skip ? 0xFFFFFFF0u : (uint32_t)(128 * b + 2 * lane) * 8);
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int lane,
-                                               unsigned long long target) {
+// This lane's stamps all at the target (lanes past G hold none).
+__device__ __forceinline__ bool lane_reached(const u32x4 (&v)[4], int G, int lane,
+                                             unsigned long long target) {
   bool ok = true;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -571,7 +590,12 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
     const unsigned long long s1 = ((unsigned long long)v[b][3] << 32) | v[b][2];
     ok = ok && (i >= G || s0 >= target) && (i + 1 >= G || s1 >= target);
   }
-  return __ballot(!ok) == 0ull;
+  return ok;
+}
+
+__device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int lane,
+                                               unsigned long long target) {
+  return __ballot(!lane_reached(v, G, lane, target)) == 0ull;
 }
 
 __device__ void wait_group(const PlanArgs& p, int g, int lane) {
@@ -579,6 +603,24 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(p.flags, (uint32_t)p.G * 8);
+  if (kPollSkip) {
+    // One poll in flight; a lane whose stamps have all been seen stops
+    // reading them, so later polls carry only the stamps still awaited.
+    bool mine = false;
+    for (uint32_t spins = 0;; ++spins) {
+      u32x4 v1[4];
+      poll_stamps(rf, lane, v1, mine);
+      mine = mine || lane_reached(v1, p.G, lane, target);
+      if (__ballot(!mine) == 0ull) break;
+      if (spins > kSpinLimit) {
+        if (lane == 0) atomicOr(p.err, 1u);
+        break;
+      }
+    }
+    wait_stores();
+    asm volatile("" ::: "memory");
+    return;
+  }
   // kPollDepth polls in flight: each check consumes the oldest and issues a
   // new one, so a stamp is seen about one poll interval after it lands.
   u32x4 v[kPollDepth][4];
@@ -607,7 +649,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  stage_group_x<FMT, GLUE>(S, 0, lane, xs, xsum);
+  stage_group_x<FMT, GLUE, kEarlyPolicy>(S, 0, lane, xs, xsum);   // nothing written yet
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
@@ -618,7 +660,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // awaited; the others only once every workgroup has finished g.  The
       // compute waves start g + 1 after the barrier either way.
       const bool early = (S.order(g + 1) & kStageEarly) != 0;
-      if (early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+      if (early) stage_group_x<FMT, GLUE, kEarlyPolicy>(S, g + 1, lane, xs, xsum);
       wait_group(p, g, lane);
       if (!early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
       if (lane == 0) lds_put(staged, g + 1);
