@@ -565,6 +565,10 @@ constexpr int kPollDepth = QD_POLL_DEPTH;
 #define QD_POLL_SKIP 0
 #endif
 constexpr bool kPollSkip = QD_POLL_SKIP != 0;
+#ifndef QD_ERR_LAZY
+#define QD_ERR_LAZY 0
+#endif
+constexpr bool kErrLazy = QD_ERR_LAZY != 0;
 
 // skip: this lane has already seen all its stamps reach the target; its
 // reads then fall outside the buffer (zeros, no memory access).
@@ -599,7 +603,10 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
 }
 
 __device__ void wait_group(const PlanArgs& p, int g, int lane) {
-  if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+  // After an earlier wait timed out (any workgroup's), waits are skipped so
+  // the kernel still finishes.  kErrLazy: the error word is read together
+  // with each poll instead of before the first, off the critical path.
+  if (!kErrLazy && __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(p.flags, (uint32_t)p.G * 8);
@@ -609,9 +616,11 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
     bool mine = false;
     for (uint32_t spins = 0;; ++spins) {
       u32x4 v1[4];
+      uint32_t e = 0;
+      if (kErrLazy) e = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       poll_stamps(rf, lane, v1, mine);
       mine = mine || lane_reached(v1, p.G, lane, target);
-      if (__ballot(!mine) == 0ull) break;
+      if (__ballot(!mine) == 0ull || e != 0u) break;
       if (spins > kSpinLimit) {
         if (lane == 0) atomicOr(p.err, 1u);
         break;
@@ -630,8 +639,10 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   for (uint32_t spins = 0; !done; spins += kPollDepth) {
 #pragma unroll
     for (int i = 0; i < kPollDepth; ++i) {
+      uint32_t e = 0;
+      if (kErrLazy) e = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       poll_stamps(rf, lane, v[(i + kPollDepth - 1) % kPollDepth]);
-      if (!done && stamps_reached(v[i], p.G, lane, target)) done = true;
+      if (!done && (stamps_reached(v[i], p.G, lane, target) || e != 0u)) done = true;
     }
     if (!done && spins > kSpinLimit) {
       if (lane == 0) atomicOr(p.err, 1u);
