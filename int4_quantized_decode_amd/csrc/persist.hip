@@ -65,12 +65,6 @@ enum : int32_t {
   kAckOutputs = 2,      // a later group reads or rewrites an output: stores complete before the stamp
 };
 
-#ifndef QD_EARLY_CACHED
-#define QD_EARLY_CACHED 0
-#endif
-// Cache policy of early staging (activations nothing in the step writes).
-constexpr int kEarlyPolicy = QD_EARLY_CACHED ? kPolicyDefault : kPolicyCoherent;
-
 struct PGroup {         // 64 bytes
   const uint16_t* x;
   const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
@@ -419,12 +413,13 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
 // gated product's B block) into xs + x_span(Kp), are issued before the single wait,
 // so staging costs one memory round trip whatever K is.  The prologue then
 // runs in place: each lane rewrites the 8-value chunks its own loads brought.
+// POLICY: device-coherent for activations an earlier group of the step may
+// have written; cached for the others, which nothing in the step writes, so
+// the workgroups of an XCD share one L2 copy (8B step 1367-1372 vs 1375-1378
+// us coherent).
 template <int FMT, bool GLUE, int POLICY = kPolicyCoherent>
 __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
                                               float* xsum) {
-  // POLICY: device-coherent for activations an earlier group of the step may
-  // have written; cached for the others, which nothing in the step writes
-  // (the workgroups of an XCD then share one L2 copy).
   const int Kp = S.J(g) * kSuperK;
   const int64_t k = S.k(g);
   const uint32_t xbytes = (uint32_t)(k * 2);
@@ -561,31 +556,18 @@ constexpr int kMaxWorkgroups = 512;
 #define QD_POLL_DEPTH 1
 #endif
 constexpr int kPollDepth = QD_POLL_DEPTH;
-#ifndef QD_POLL_SKIP
-#define QD_POLL_SKIP 0
-#endif
-constexpr bool kPollSkip = QD_POLL_SKIP != 0;
-#ifndef QD_ERR_LAZY
-#define QD_ERR_LAZY 0
-#endif
-constexpr bool kErrLazy = QD_ERR_LAZY != 0;
 
-// skip: this lane has already seen all its stamps reach the target; its
-// reads then fall outside the buffer (zeros, no memory access).
-__device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4],
-                                            bool skip = false) {
+__device__ __forceinline__ void poll_stamps(__amdgpu_buffer_rsrc_t rf, int lane, u32x4 (&v)[4]) {
   // The clobbers keep the compiler from merging two polls of the same
   // addresses into one load or hoisting a poll out of the loop.
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-    v[b] = bload16_coherent(rf, skip ? 0xFFFFFFF0u : (uint32_t)(128 * b + 2 * lane) * 8);
+  for (int b = 0; b < 4; ++b) v[b] = bload16_coherent(rf, (uint32_t)(128 * b + 2 * lane) * 8);
   asm volatile("" ::: "memory");
 }
 
-// This lane's stamps all at the target (lanes past G hold none).
-__device__ __forceinline__ bool lane_reached(const u32x4 (&v)[4], int G, int lane,
-                                             unsigned long long target) {
+__device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int lane,
+                                               unsigned long long target) {
   bool ok = true;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -594,42 +576,14 @@ __device__ __forceinline__ bool lane_reached(const u32x4 (&v)[4], int G, int lan
     const unsigned long long s1 = ((unsigned long long)v[b][3] << 32) | v[b][2];
     ok = ok && (i >= G || s0 >= target) && (i + 1 >= G || s1 >= target);
   }
-  return ok;
-}
-
-__device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int lane,
-                                               unsigned long long target) {
-  return __ballot(!lane_reached(v, G, lane, target)) == 0ull;
+  return __ballot(!ok) == 0ull;
 }
 
 __device__ void wait_group(const PlanArgs& p, int g, int lane) {
-  // After an earlier wait timed out (any workgroup's), waits are skipped so
-  // the kernel still finishes.  kErrLazy: the error word is read together
-  // with each poll instead of before the first, off the critical path.
-  if (!kErrLazy && __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
+  if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
   const __amdgpu_buffer_rsrc_t rf = make_rsrc(p.flags, (uint32_t)p.G * 8);
-  if (kPollSkip) {
-    // One poll in flight; a lane whose stamps have all been seen stops
-    // reading them, so later polls carry only the stamps still awaited.
-    bool mine = false;
-    for (uint32_t spins = 0;; ++spins) {
-      u32x4 v1[4];
-      uint32_t e = 0;
-      if (kErrLazy) e = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      poll_stamps(rf, lane, v1, mine);
-      mine = mine || lane_reached(v1, p.G, lane, target);
-      if (__ballot(!mine) == 0ull || e != 0u) break;
-      if (spins > kSpinLimit) {
-        if (lane == 0) atomicOr(p.err, 1u);
-        break;
-      }
-    }
-    wait_stores();
-    asm volatile("" ::: "memory");
-    return;
-  }
   // kPollDepth polls in flight: each check consumes the oldest and issues a
   // new one, so a stamp is seen about one poll interval after it lands.
   u32x4 v[kPollDepth][4];
@@ -639,10 +593,8 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   for (uint32_t spins = 0; !done; spins += kPollDepth) {
 #pragma unroll
     for (int i = 0; i < kPollDepth; ++i) {
-      uint32_t e = 0;
-      if (kErrLazy) e = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       poll_stamps(rf, lane, v[(i + kPollDepth - 1) % kPollDepth]);
-      if (!done && (stamps_reached(v[i], p.G, lane, target) || e != 0u)) done = true;
+      if (!done && stamps_reached(v[i], p.G, lane, target)) done = true;
     }
     if (!done && spins > kSpinLimit) {
       if (lane == 0) atomicOr(p.err, 1u);
@@ -660,7 +612,9 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  stage_group_x<FMT, GLUE, kEarlyPolicy>(S, 0, lane, xs, xsum);   // nothing written yet
+  // Group 0's activations: nothing of this launch has written anything yet
+  // (earlier launches' writes are visible at kernel start).
+  stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
@@ -671,7 +625,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // awaited; the others only once every workgroup has finished g.  The
       // compute waves start g + 1 after the barrier either way.
       const bool early = (S.order(g + 1) & kStageEarly) != 0;
-      if (early) stage_group_x<FMT, GLUE, kEarlyPolicy>(S, g + 1, lane, xs, xsum);
+      if (early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
       wait_group(p, g, lane);
       if (!early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
       if (lane == 0) lds_put(staged, g + 1);
