@@ -37,7 +37,9 @@
  *     work is enqueued on `stream` and runs asynchronously.  On any error
  *     nothing is enqueued.  Errors raised while a kernel runs surface at the
  *     next synchronizing HIP call.
- *   - Outputs must not overlap inputs.
+ *   - An op's output must not overlap its own inputs (x, gamma, weights).  In
+ *     a stack, the outputs of one group must not overlap each other; a later
+ *     group may read or overwrite an earlier group's buffers.
  *   - The functions hold no global mutable state and are thread-safe, except
  *     that one qd_stack_plan must not run on two streams at once.
  *
@@ -81,7 +83,7 @@ typedef enum {
   QD_EINVAL = 1,   /* null pointer, unknown enum, overlapping buffers, bad plan */
   QD_ESHAPE = 2,   /* K not a multiple of 32 (int8, fp16) / 64 (int4), N or K < 0,
                       K > QD_MAX_K, M outside 1..16, blob smaller than needed */
-  QD_EALIGN = 3,   /* blob, x or W not 16-byte aligned */
+  QD_EALIGN = 3,   /* blob, x, gamma or W not 16-byte aligned */
   QD_ERANGE = 4,   /* (reported through the packer's device flag, see below) */
   QD_ELAUNCH = 5,  /* a HIP launch or runtime call failed */
   QD_EFORMAT = 6,  /* weight format not supported by this entry point */
@@ -206,8 +208,11 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * a group's activations are read ahead of that barrier only when no earlier
  * group writes any byte of them, and a group's outputs are made visible
  * before its completion is signalled only when a later group reads or
- * rewrites them.  Results equal those of decode_linear_stack's sequential
- * launches, so an op may consume (or overwrite) an earlier op's buffers.
+ * rewrites them.  A step computes what decode_linear_stack's sequential
+ * launches compute, so an op may consume (or overwrite) an earlier op's
+ * buffers; the persistent kernel sums each row's tiles in its own fixed order,
+ * so its outputs may differ from the launches' in the last bit (and are the
+ * same from run to run).
  * qd_stack_plan_create validates `ops` exactly as decode_linear_stack does,
  * copies the descriptors to the device and allocates the plan's scratch
  * (completion stamps, an error word) once; the pointers in `ops` must stay
