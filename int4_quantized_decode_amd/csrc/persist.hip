@@ -63,6 +63,9 @@ constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent rou
 enum : int32_t {
   kStageEarly = 1,      // no earlier group writes any byte of x: it may be staged before the barrier
   kAckOutputs = 2,      // a later group reads or rewrites an output: stores complete before the stamp
+  kNoWait = 4,          // a further row range of the op(s) before: no device-wide wait at the boundary
+  kCleanLines = 8,      // x is written earlier in the step, but no cache can hold a stale copy of its
+                        // lines: after the barrier it is read through the caches
 };
 
 struct PGroup {         // 64 bytes
@@ -75,23 +78,25 @@ struct PGroup {         // 64 bytes
   int32_t n_mem;
   int32_t pro;          // qd_prologue of the group's input
   float eps;
-  int32_t order;        // kStageEarly | kAckOutputs
+  int32_t order;        // kStageEarly | kAckOutputs | kNoWait | kCleanLines
   int32_t pad[3];
 };
 
-struct PMember {        // 32 bytes
+struct PMember {        // 48 bytes
   const uint8_t* blob;
   uint16_t* y;
   int64_t n;
   int32_t rg_begin;     // first row-group of this member within its group
   int32_t epi;          // qd_epilogue of this member's outputs
+  int64_t ld;           // elements between token rows of y (m > 1)
+  int64_t pad;
 };
 
 struct PSched {         // 16 bytes: one workgroup's part of one group
   int32_t n;            // tiles (whole row-groups: a multiple of the group's J)
   int32_t off;          // tiles of this workgroup in the groups before this one
   int32_t rg0;          // first row-group
-  int32_t stride;       // distance between this workgroup's successive row-groups
+  int32_t nseg;         // row-groups (rg0, rg0 + 1, ...)
 };
 
 static_assert(sizeof(PGroup) % 16 == 0 && sizeof(PMember) % 16 == 0 && sizeof(PSched) == 16,
@@ -112,6 +117,7 @@ struct PlanArgs {
   int32_t red_bytes;
   int32_t cnt_bytes;
   int32_t tab_bytes;
+  int32_t m;                  // token rows (1 .. 16)
 };
 
 template <int FMT> struct Fmt;
@@ -173,7 +179,7 @@ struct Sched {
   __device__ int tiles(int gi) const { return uni(s[gi].n); }
   __device__ int off(int gi) const { return uni(s[gi].off); }
   __device__ int rg0(int gi) const { return uni(s[gi].rg0); }
-  __device__ int stride(int gi) const { return uni(s[gi].stride); }
+  __device__ int nseg(int gi) const { return uni(s[gi].nseg); }
   __device__ int rg_begin(int mi) const { return uni(m[mi].rg_begin); }
   __device__ const uint8_t* blob(int mi) const { return uni_ptr(m[mi].blob); }
   __device__ uint16_t* y(int mi) const { return uni_ptr(m[mi].y); }
@@ -183,6 +189,7 @@ struct Sched {
   __device__ uint16_t* y_l(int mi) const { return m[mi].y; }
   __device__ int64_t n_l(int mi) const { return m[mi].n; }
   __device__ int epi_l(int mi) const { return m[mi].epi; }
+  __device__ int64_t ld(int mi) const { return (int64_t)uni((int)m[mi].ld); }
 };
 
 // Tile hand-out.  A workgroup's tiles of all groups form one sequence
@@ -195,13 +202,14 @@ struct TileRef {
   int j;      // super-block within the row
   int rel;    // tile index relative to the first row-group of the range (t - rg0 J)
   int seg;    // row-group relative to the first row-group of the range
+  int nv;     // (units) row-groups the unit holds
 };
 
 struct IssueCursor {
   int g;                // current group (-1 before the first)
   int off_next;         // sequence index where the next group starts
   int u, seg, j;        // last issued tile: index within the workgroup's part, (segment, super-block)
-  int J, rg0, stride;
+  int J, rg0, nseg;
   int mem, mem_last;
 };
 
@@ -223,7 +231,7 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
       ++c.g;
       c.J = S.J(c.g);
       c.rg0 = S.rg0(c.g);
-      c.stride = S.stride(c.g);
+      c.nseg = S.nseg(c.g);
       c.off_next = c.g + 1 < ngroups ? S.off(c.g + 1) : total;
       c.u = 0;
       c.seg = 0;
@@ -238,7 +246,7 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
       c.j -= c.J;
       ++c.seg;
     }
-    const int rg = c.rg0 + c.seg * c.stride;
+    const int rg = c.rg0 + c.seg;
     while (c.mem < c.mem_last && rg >= S.rg_begin(c.mem + 1)) ++c.mem;
     base = S.blob(c.mem) + ((int64_t)(rg - S.rg_begin(c.mem)) * c.J + c.j) * T;
     nbytes = T;
@@ -248,6 +256,73 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
     ref.seg = c.seg;
   }
   return Fmt<FMT>::load(make_rsrc(base, nbytes), lane);
+}
+
+// Up to 16 token rows: the sequence is made of units, U row-groups at one
+// super-block (unit-row major: units (q, 0), (q, 1), ... (q, J - 1), then
+// q + 1), so that one activation block serves U tiles.  The last unit of a
+// range may hold fewer row-groups; its missing tiles read as zeros.
+template <int U>
+struct Unit8 {
+  Tile8 w[U];
+};
+
+template <int U>
+__device__ __forceinline__ Unit8<U> issue_unit(const Sched& S, int ngroups, int total, uint32_t* next,
+                                               IssueCursor& c, TileRef& ref, int lane, bool take = true) {
+  uint32_t got = (uint32_t)total;
+  if (take && lane == 0) got = atomicAdd(next, 1u);
+  const int idx = uni((int)got);
+  const uint8_t* base[U];
+  uint32_t nbytes[U];
+#pragma unroll
+  for (int q = 0; q < U; ++q) {
+    base[q] = nullptr;
+    nbytes[q] = 0;
+  }
+  ref.g = ngroups;
+  ref.nv = 0;
+  if (idx < total) {
+    while (idx >= c.off_next) {                       // enter the group holding idx
+      ++c.g;
+      c.J = S.J(c.g);
+      c.rg0 = S.rg0(c.g);
+      c.nseg = S.nseg(c.g);
+      c.off_next = c.g + 1 < ngroups ? S.off(c.g + 1) : total;
+      c.u = 0;
+      c.seg = 0;
+      c.j = 0;
+      c.mem = S.mem0(c.g);
+      c.mem_last = c.mem + S.nmem(c.g) - 1;
+    }
+    const int u = idx - S.off(c.g);
+    c.j += u - c.u;
+    c.u = u;
+    while (c.j >= c.J) {                              // c.seg counts units here
+      c.j -= c.J;
+      ++c.seg;
+    }
+    const int seg0 = c.seg * U;
+    const int nv = min(U, c.nseg - seg0);
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (q < nv) {
+        const int rg = c.rg0 + seg0 + q;
+        while (c.mem < c.mem_last && rg >= S.rg_begin(c.mem + 1)) ++c.mem;
+        base[q] = S.blob(c.mem) + ((int64_t)(rg - S.rg_begin(c.mem)) * c.J + c.j) * kTileBytes8;
+        nbytes[q] = kTileBytes8;
+      }
+    }
+    ref.g = c.g;
+    ref.j = c.j;
+    ref.rel = seg0 * c.J + c.j;                       // partial slot of the unit's first tile
+    ref.seg = seg0;
+    ref.nv = nv;
+  }
+  Unit8<U> t;
+#pragma unroll
+  for (int q = 0; q < U; ++q) t.w[q] = load_tile8(make_rsrc(base[q], nbytes[q]), 0, lane);
+  return t;
 }
 
 // Reserve-wave pacing, in ticks of the 100 MHz real-time counter per tile:
@@ -273,6 +348,48 @@ template <>
 __device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs,
                                                            const float* xsum, int j, int g, float acc) {
   return tile_dot4(T, xs + j * kSuperK, xsum + 16 * j, g, acc);
+}
+
+// Up to 16 token rows (MT = 16, int8 only).  The activation block
+// X[0..15][256 j .. 256 j + 255] in the matrix-core A layout: lane (gq, rho)
+// holds token rho's 8 values at K positions 32 b + 8 gq of every 32-block b.
+// The blocks are read from memory, not staged (16 x K does not fit in LDS for
+// the longest K).  Token rows past m and K positions past K read as zeros
+// (out-of-range offsets: no memory traffic).  Activations nothing in the step
+// writes go through the caches; the others are read device-coherently.
+__device__ __forceinline__ void load_xblock(const Sched& S, int g, int j, int m, int lane,
+                                            bool coherent, u32x4 (&xa)[8]) {
+  const int gq = lane >> 4, rho = lane & 15;
+  const int64_t K = S.k(g);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), (uint32_t)(m * K * 2));
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int64_t kk = (int64_t)j * kSuperK + 32 * b + 8 * gq;
+    const uint32_t off = kk < K ? (uint32_t)((rho * K + kk) * 2) : 0x80000000u;
+    xa[b] = coherent ? bload16_coherent(rx, off) : bload16(rx, off);
+  }
+}
+
+// The tile's 16 x 16 product with the activation block on the matrix cores
+// (B operand = the lane's 8 codes of one 32-block, as in the small-M
+// kernels).  Lane (gq, rho) gets tokens 4 gq + i of weight row rho.
+__device__ __forceinline__ float4_t tile_mfma8(const Tile8& T, const u32x4 (&xa)[8]) {
+  const half8_t scales = __builtin_bit_cast(half8_t, T.sc);
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8_t bq = codes_to_half8(T.c[s][2 * h], T.c[s][2 * h + 1]);
+      const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float4_t pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(half8_t, xa[2 * s + h]), bq, zero, 0, 0, 0);
+      const float sc = (float)scales[2 * s + h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, pr[i], acc[i]);
+    }
+  }
+  return acc;
 }
 
 // Keep a load where it is written: the scheduler may not move code across
@@ -304,16 +421,28 @@ __device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const
 // group).  After each tile a wave writes the tile's 16 row partials to their
 // own LDS slot and counts the tile against its row-group, so the control wave
 // can finish a row-group as soon as its last tile is in.
-template <int FMT, int D, bool RESERVE, int R>
+template <int FMT, int MT, int U> struct RingOf { using type = typename Fmt<FMT>::Tile; };
+template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit8<U>; };
+
+template <int FMT, int D, bool RESERVE, int R, int MT, int U>
 __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint32_t* next,
                              int lane, const half_t* xs, const float* xsum, float* red,
                              uint32_t* cnt, const int* stalled, const int* staged) {
-  using Tile = typename Fmt<FMT>::Tile;
+  using Tile = typename RingOf<FMT, MT, U>::type;
   const int ng = p.ngroups;
   const int g4 = lane >> 4;
   IssueCursor ic{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0};
   Tile ring[D];
   TileRef ref[D];
+  auto next_tile = [&](TileRef& r, int ln, bool take = true) {
+    if constexpr (MT == 1) return issue<FMT>(S, ng, total, next, ic, r, ln, take);
+    else return issue_unit<U>(S, ng, total, next, ic, r, ln, take);
+  };
+  // MT > 1: each slot's activation block, loaded with the tile when the
+  // block is already readable (nothing in the step writes it, or its group's
+  // boundary has passed), else when the tile is computed.
+  u32x4 xr[MT > 1 ? D : 1][8];
+  bool xl[MT > 1 ? D : 1];
   int cg = -1;                      // last group whose activations this wave has waited for
   auto settle_to = [&](int g) {
     while (cg < g) {
@@ -321,17 +450,52 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       if (cg < ng) wg_barrier();
     }
   };
-  auto compute = [&](const Tile& t, const TileRef& r) {
+  auto early_x = [&](int s) {
+    if constexpr (MT > 1) {
+      xl[s] = false;
+      if (ref[s].g < ng) {
+        const int ord = S.order(ref[s].g);
+        const bool early = (ord & kStageEarly) != 0;
+        if (early || uni(lds_get(staged)) >= ref[s].g) {
+          load_xblock(S, ref[s].g, ref[s].j, p.m, lane, !(ord & (kStageEarly | kCleanLines)), xr[s]);
+          xl[s] = true;
+        }
+      }
+    }
+  };
+  auto compute = [&](int s) {
+    const Tile& t = ring[s];
+    const TileRef& r = ref[s];
     settle_to(r.g);
-    const float part = quad_reduce(tile_dot<FMT>(t, xs, xsum, r.j, g4, 0.0f));
-    if (lane < 16) red[r.rel * 16 + lane] = part;
+    if constexpr (MT == 1) {
+      const float part = quad_reduce(tile_dot<FMT>(t, xs, xsum, r.j, g4, 0.0f));
+      if (lane < 16) red[r.rel * 16 + lane] = part;
+    } else {
+      if (!xl[s]) load_xblock(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr[s]);
+      // Each tile's 16 x 16 partial, one float4 per lane, in the tile's own
+      // slot (row-group seg + q: J slots further on).
+      const int J = S.J(r.g);
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        if (q < r.nv) reinterpret_cast<float4_t*>(red)[(r.rel + q * J) * 64 + lane] = tile_mfma8(t.w[q], xr[s]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (lane == 0) __hip_atomic_fetch_add(cnt + r.seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) {
+      if constexpr (MT == 1) {
+        __hip_atomic_fetch_add(cnt + r.seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+          if (q < r.nv)
+            __hip_atomic_fetch_add(cnt + r.seg + q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
   };
   if (!RESERVE) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane);
+      ring[s] = next_tile(ref[s], lane);
+      early_x(s);
       QD_PIN_ISSUE();
     }
     // The ring is consumed and refilled in slot order with a single loop
@@ -339,8 +503,9 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
     for (;;) {
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        if (ref[s].g < ng) compute(ring[s], ref[s]);
-        ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane);
+        if (ref[s].g < ng) compute(s);
+        ring[s] = next_tile(ref[s], lane);
+        early_x(s);
         QD_PIN_ISSUE();
       }
       if (ref[0].g >= ng) break;   // slot 0 was refilled first: nothing left for later slots
@@ -366,19 +531,20 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       bool stop = false, exhausted = false;
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        const uint32_t due = t0 + pace_ticks<FMT>(s * R + r);
+        const uint32_t due = t0 + pace_ticks<FMT>((s * R + r) * (MT == 1 ? 1 : U));
         while (!stop && (int32_t)((uint32_t)__builtin_amdgcn_s_memrealtime() - due) < 0) {
           stop = lds_get(staged) > trig;
           if (!stop) __builtin_amdgcn_s_sleep(2);
         }
         stop = stop || lds_get(staged) > trig;
-        ring[s] = issue<FMT>(S, ng, total, next, ic, ref[s], lane, !stop);
+        ring[s] = next_tile(ref[s], lane, !stop);
+        early_x(s);
         exhausted = exhausted || (!stop && ref[s].g >= ng);
         QD_PIN_ISSUE();
       }
 #pragma unroll
       for (int s = 0; s < D; ++s)
-        if (ref[s].g < ng) compute(ring[s], ref[s]);
+        if (ref[s].g < ng) compute(s);
       if (exhausted) break;         // the sequence is used up
       trig = cg > trig ? cg : trig + 1;
     }
@@ -493,6 +659,28 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Up to 16 token rows of row-group rg: lane (gq, rho) holds tokens 4 gq + i
+// of weight row rho (the MFMA output layout).
+__device__ __forceinline__ void store_rows16(const PlanArgs& p, const Sched& S, int g, int rg,
+                                             int lane, float4_t v) {
+  int mi = S.mem0(g);
+  const int last = mi + S.nmem(g) - 1;
+  while (mi < last && rg >= S.rg_begin(mi + 1)) ++mi;
+  const int gq = lane >> 4, rho = lane & 15;
+  const int64_t n = (int64_t)(rg - S.rg_begin(mi)) * kTileRows + rho;
+  if (n >= S.n(mi)) return;
+  uint16_t* const y = S.y(mi);
+  const int64_t ld = S.ld(mi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 4 * gq + i;
+    if (tok < p.m)
+      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(y + tok * ld + n),
+                         __builtin_bit_cast(uint16_t, (half_t)v[i]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Spin (bounded) until the compute waves have counted `want` tiles against
 // row-group slot `seg`.  After one timed-out wait (an error) later waits are
 // skipped.
@@ -513,7 +701,7 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cn
 // row-group's tiles is taken in a fixed order (tiles t = q mod 4 per
 // quarter-wave, then the four quarters), whichever wave computed which tile,
 // so results are deterministic.
-template <bool GLUE>
+template <bool GLUE, int MT>
 __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
                              uint32_t* cnt, int* stalled, bool& dead) {
   const int ntiles = S.tiles(g);
@@ -522,16 +710,29 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
     return;
   }
   const int J = S.J(g);
-  const int rg0 = S.rg0(g), stride = S.stride(g), nseg = ntiles / J;
+  const int rg0 = S.rg0(g), nseg = S.nseg(g);
   const int row = lane & 15, q = lane >> 4;
   for (int s = 0; s < nseg; ++s) {
     wait_count(p, cnt, s, (uint32_t)J, dead);
     if (s == nseg - 1 && lane == 0) lds_put(stalled, g);   // every tile of g is in
+    if constexpr (MT != 1) {
+      // Each lane sums its float4 over the row-group's tiles in tile order.
+      const float4_t* r4 = reinterpret_cast<const float4_t*>(red);
+      float4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int r = s * J; r < (s + 1) * J; ++r) {
+        const float4_t v = r4[r * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += v[i];
+      }
+      if (lane == 0) cnt[s] = 0u;
+      store_rows16(p, S, g, rg0 + s, lane, sum);
+      continue;
+    }
     float part = 0.0f;
     for (int r = s * J + q; r < (s + 1) * J; r += 4) part += red[r * 16 + row];
     const float sum = quad_reduce(part);
     if (lane == 0) cnt[s] = 0u;                // ready for the next group
-    if (lane < 16) store_row<GLUE>(S, g, rg0 + s * stride, row, sum);
+    if (lane < 16) store_row<GLUE>(S, g, rg0 + s, row, sum);
   }
 }
 
@@ -605,7 +806,7 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   asm volatile("" ::: "memory");
 }
 
-template <int FMT, bool GLUE>
+template <int FMT, bool GLUE, int MT>
 __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane, half_t* xs,
                              float* xsum, const float* red, uint32_t* cnt, int* stalled,
                              int* staged) {
@@ -614,27 +815,33 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   __builtin_amdgcn_s_setprio(3);
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
-  stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
+  if constexpr (MT == 1) stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
-    finish_group<GLUE>(p, S, g, lane, red, cnt, stalled, dead);
+    finish_group<GLUE, MT>(p, S, g, lane, red, cnt, stalled, dead);
     publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
       // Activations no earlier group writes are staged while the stamps are
       // awaited; the others only once every workgroup has finished g.  The
       // compute waves start g + 1 after the barrier either way.
+      // (MT > 1: the compute waves read the activations themselves.)
       const bool early = (S.order(g + 1) & kStageEarly) != 0;
-      if (early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
-      wait_group(p, g, lane);
-      if (!early) stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+      if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+      // A further row range of the same op(s) reads nothing group g writes,
+      // and needs what g needed, which g's own boundary already waited for.
+      if (!(S.order(g + 1) & kNoWait)) wait_group(p, g, lane);
+      if (MT == 1 && !early) {
+        if (S.order(g + 1) & kCleanLines) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+        else stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+      }
       if (lane == 0) lds_put(staged, g + 1);
       wg_barrier();               // activations of g + 1 staged
     }
   }
 }
 
-template <int FMT, int D, int R, int RS, bool GLUE>
+template <int FMT, int D, int R, int RS, bool GLUE, int MT, int U>
 __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   static_assert(R >= 0 && R < kCtl && RS >= 1, "at least one streaming wave");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -680,14 +887,14 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   __syncthreads();
 
   if (wave == kCtl) {
-    control_wave<FMT, GLUE>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
+    control_wave<FMT, GLUE, MT>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
   } else {
     const int last = p.ngroups - 1;
     const int total = S.off(last) + S.tiles(last);
     if (wave < kCtl - R)
-      compute_wave<FMT, D, false, R>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+      compute_wave<FMT, D, false, R, MT, U>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
     else
-      compute_wave<FMT, RS, true, R>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+      compute_wave<FMT, RS, true, R, MT, U>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -712,7 +919,8 @@ struct qd_stack_plan {
   int device = 0;
   bool persistent = false;
   int fmt = 0;
-  std::vector<qd::StackGroup> replay;    // launch-per-group fallback (m > 1, K = 0, mixed formats)
+  bool multi = false;                    // m > 1 (int8 only)
+  std::vector<qd::StackGroup> replay;    // launch-per-group fallback (K = 0, mixed formats, glue, ...)
   void* tables = nullptr;
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
@@ -730,6 +938,7 @@ struct HostGroup {
   int64_t k;
   int J;
   std::vector<PMember> mem;
+  std::vector<int64_t> src;    // the step group each member comes from (outputs of one never overlap)
   int R;
   const uint16_t* gamma;
   int pro;
@@ -743,28 +952,129 @@ bool ranges_overlap(const void* a, uint64_t an, const void* b, uint64_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Boundary ordering from the buffers (one token row): a group's x may be
-// staged early unless an earlier group's output overlaps it; a group's
-// stores must complete before its stamp if a later group's x or output
-// overlaps one of its outputs.
-void order_groups(std::vector<HostGroup>& gs) {
+// Bytes a member's outputs span: m rows of n, ld apart.
+uint64_t y_span(const PMember& pm, int64_t m) { return ((uint64_t)(m - 1) * pm.ld + pm.n) * 2; }
+
+// Whole cache lines (128 bytes) holding [p, p + n), as [a, b).
+struct Lines {
+  uintptr_t a = 0, b = 0;
+  bool hits(const Lines& o) const { return a < o.b && o.a < b; }
+};
+Lines lines_of(const void* p, uint64_t n) {
+  if (!p || !n) return {};
+  const uintptr_t a = (uintptr_t)p;
+  return {a & ~(uintptr_t)127, (a + n + 127) & ~(uintptr_t)127};
+}
+
+// Boundary ordering from the buffers: a group's x may be read early unless
+// an earlier group's output overlaps it; a group's stores must complete
+// before its stamp if a later group's x or output overlaps one of its
+// outputs.  Outputs within one group of the step are disjoint, also once the
+// group is split into row ranges (whose byte spans interleave when m > 1).
+void order_groups(std::vector<HostGroup>& gs, int64_t m, int64_t tbytes) {
   const size_t n = gs.size();
   for (size_t i = 0; i < n; ++i) {
-    const uint64_t xb = (uint64_t)gs[i].k * 2 * (gs[i].pro == QD_PRO_GLU ? 2 : 1);
+    const uint64_t xb = (uint64_t)m * gs[i].k * 2 * (gs[i].pro == QD_PRO_GLU ? 2 : 1);
     bool early = true;
     for (size_t j = 0; j < i; ++j) {
-      for (const PMember& pj : gs[j].mem) {
-        const uint64_t yj = (uint64_t)pj.n * 2;
+      for (size_t b = 0; b < gs[j].mem.size(); ++b) {
+        const PMember& pj = gs[j].mem[b];
+        const uint64_t yj = y_span(pj, m);
         bool reads = ranges_overlap(gs[i].x, xb, pj.y, yj) ||
                      (gs[i].pro == QD_PRO_RMSNORM && ranges_overlap(gs[i].gamma, (uint64_t)gs[i].k * 2, pj.y, yj));
         bool rewrites = false;
-        for (const PMember& pi : gs[i].mem) rewrites = rewrites || ranges_overlap(pi.y, (uint64_t)pi.n * 2, pj.y, yj);
+        for (size_t a = 0; a < gs[i].mem.size(); ++a)
+          rewrites = rewrites || (gs[i].src[a] != gs[j].src[b] &&
+                                  ranges_overlap(gs[i].mem[a].y, y_span(gs[i].mem[a], m), pj.y, yj));
         if (reads) early = false;
         if (reads || rewrites) gs[j].order |= kAckOutputs;
       }
     }
     if (early) gs[i].order |= kStageEarly;
   }
+  // A group whose x an earlier group writes may still read it through the
+  // caches when no cache can hold a stale copy of its lines.  The caches
+  // start each launch clean; the lines are then fetched fresh unless, before
+  // the last group writing them, some access brought them in: an earlier
+  // write, an activation read by an earlier group (after its own barrier), or
+  // a weight read or early activation read (these happen at any point of the
+  // step).  So one group of the step (all its row ranges) may write the
+  // lines; its stores are disjoint byte ranges.  Checked per 128-byte line.
+  auto acts = [&](const HostGroup& g, Lines out[2]) {
+    out[0] = lines_of(g.x, (uint64_t)m * g.k * 2 * (g.pro == QD_PRO_GLU ? 2 : 1));
+    out[1] = g.pro == QD_PRO_RMSNORM ? lines_of(g.gamma, (uint64_t)g.k * 2) : Lines{};
+  };
+  for (size_t i = 0; i < n; ++i) {
+    if (gs[i].order & kStageEarly) continue;
+    Lines ai[2];
+    acts(gs[i], ai);
+    auto touches = [&](const Lines& l) { return l.hits(ai[0]) || l.hits(ai[1]); };
+    size_t last_write = 0;
+    int64_t writer = -1;            // the step group writing the lines
+    bool clean = true;
+    for (size_t j = 0; j < i; ++j) {
+      for (size_t b = 0; b < gs[j].mem.size(); ++b) {
+        if (!touches(lines_of(gs[j].mem[b].y, y_span(gs[j].mem[b], m)))) continue;
+        if (writer >= 0 && writer != gs[j].src[b]) clean = false;
+        writer = gs[j].src[b];
+        last_write = j;
+      }
+    }
+    for (size_t j = 0; clean && j < n; ++j) {
+      for (const PMember& pj : gs[j].mem)
+        if (touches(lines_of(pj.blob, (uint64_t)ceil_div(pj.n, kTileRows) * gs[j].J * tbytes)))
+          clean = false;
+      if (j == i) continue;
+      if ((gs[j].order & kStageEarly) || j <= last_write) {
+        Lines aj[2];
+        acts(gs[j], aj);
+        if (touches(aj[0]) || touches(aj[1])) clean = false;
+      }
+    }
+    if (clean) gs[i].order |= kCleanLines;
+  }
+}
+
+// Split groups into row ranges of at most `tiles` tiles per workgroup (G
+// workgroups), so that one range's 16 x 16 tile partials fit in LDS.  Each
+// range is a group of its own whose members are the slices of the original
+// members it covers; ranges after the first carry kNoWait.  False if a
+// single row-group has more tiles than that.
+bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G) {
+  std::vector<HostGroup> out;
+  for (HostGroup& hg : gs) {
+    const int64_t per_wg = tiles / hg.J;
+    if (per_wg < 1) return false;
+    const int64_t piece = per_wg * G;
+    if (hg.R <= piece) {
+      out.push_back(std::move(hg));
+      continue;
+    }
+    for (int64_t a = 0; a < hg.R; a += piece) {
+      const int64_t b = std::min<int64_t>(hg.R, a + piece);
+      HostGroup pg{hg.x, hg.k, hg.J, {}, {}, 0, hg.gamma, hg.pro, hg.eps};
+      pg.order = hg.order;
+      for (size_t q = 0; q < hg.mem.size(); ++q) {
+        const PMember& mm = hg.mem[q];
+        const int64_t r0 = mm.rg_begin, r1 = r0 + ceil_div(mm.n, kTileRows);
+        const int64_t lo = std::max(a, r0), hi = std::min(b, r1);
+        if (lo >= hi) continue;
+        const int64_t skip = lo - r0;   // row-groups of the member before this range
+        PMember slice = mm;
+        slice.blob = mm.blob + skip * hg.J * (int64_t)kTileBytes8;
+        slice.y = mm.y + skip * kTileRows;
+        slice.n = std::min<int64_t>(mm.n - skip * kTileRows, (hi - lo) * kTileRows);
+        slice.rg_begin = pg.R;
+        pg.mem.push_back(slice);
+        pg.src.push_back(hg.src[q]);
+        pg.R += (int)(hi - lo);
+      }
+      if (a > 0) pg.order |= kNoWait;
+      out.push_back(std::move(pg));
+    }
+  }
+  gs = std::move(out);
+  return true;
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -789,10 +1099,33 @@ constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
 #endif
 constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 
-const void* kernel_ptr(int fmt) {
+// Up to 16 token rows (int8): each ring slot also holds an activation block,
+// so rings are shorter.
+#ifndef QD_PLAN_RING16
+#define QD_PLAN_RING16 1
+#endif
+#ifndef QD_PLAN_RESERVE16_R
+#define QD_PLAN_RESERVE16_R 7
+#endif
+#ifndef QD_PLAN_UNIT16
+#define QD_PLAN_UNIT16 2
+#endif
+#ifndef QD_PLAN_RESERVE16_S
+#define QD_PLAN_RESERVE16_S 1
+#endif
+// Tiles per workgroup per group at up to 16 token rows: their 1 KB partials
+// are held in LDS until the row-group is reduced.
+#ifndef QD_PLAN_TILES16
+#define QD_PLAN_TILES16 96
+#endif
+
+const void* kernel_ptr(int fmt, bool multi) {
+  if (multi)
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
+                                                        QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>);
   if (fmt == QD_FMT_INT8_B32)
-    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false>);
-  return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false>);
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
+  return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false, 1, 1>);
 }
 
 }  // namespace
@@ -807,14 +1140,16 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   if (!plan) return QD_ELAUNCH;
   plan->device = dev;
 
-  // Persistent walker: one token row, one format, no empty-K groups.
+  // Persistent walker: one format, no empty-K groups, no glue; one token row,
+  // or up to 16 with int8 weights.
   std::vector<HostGroup> groups;
-  bool ok = (m == 1);
+  const bool multi = m > 1;
+  bool ok = (m >= 1 && m <= 16);
   int fmt = 0;
   for (int64_t i = 0; ok && i < n_ops;) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
-    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, 0,
+    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, 0,
                  ops[i].gamma, ops[i].prologue, ops[i].eps};
     for (int64_t q = i; q < e; ++q) {
       if (ops[q].w.n == 0) continue;
@@ -822,12 +1157,14 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       if (fmt == 0) fmt = ops[q].w.fmt;
       if (ops[q].w.fmt != fmt) ok = false;
       if (fmt != QD_FMT_INT8_B32 && fmt != QD_FMT_INT4_G64) ok = false;   // fp16: replay
+      if (multi && fmt != QD_FMT_INT8_B32) ok = false;                    // INT4 at m > 1: replay
       // Glue (a prologue or an epilogue): replay.  The persistent walker's
       // staging supports it, but that path is switched off until it has
       // passed its device tests.
       if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) ok = false;
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
-                               hg.R, ops[q].epilogue});
+                               hg.R, ops[q].epilogue, ops[q].w.n, 0});
+      hg.src.push_back(i);
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);
     }
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
@@ -847,8 +1184,13 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return QD_OK;
   }
 
-  order_groups(groups);
   const int G = cus;
+  if (multi && !split_rows(groups, QD_PLAN_TILES16, G)) {
+    plan->replay = std::move(replay);
+    *out = plan;
+    return QD_OK;
+  }
+  order_groups(groups, m, tile_bytes(fmt));
   const int ng = (int)groups.size();
   std::vector<PGroup> pg(ng);
   std::vector<PMember> pm;
@@ -882,17 +1224,20 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       // Contiguous row-groups: each workgroup streams one contiguous range.
       // (Interleaving them, row-group w + i G to workgroup w, measured 2-11%
       // slower: the contiguous streams keep DRAM pages open.)
-      const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0, stride = 1;
-      ps[(size_t)g * G + w] = PSched{(int32_t)(nrg * J), off[w], (int32_t)r0, (int32_t)stride};
+      // Several token rows: the sequence holds units of QD_PLAN_UNIT16 row-groups.
+      const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
+      const int64_t n = (multi ? ceil_div(nrg, (int64_t)QD_PLAN_UNIT16) : nrg) * J;
+      ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
       if (nrg == 0) continue;
-      off[w] += (int32_t)(nrg * J);
+      off[w] += (int32_t)n;
       maxRel = std::max<int>(maxRel, (int)(nrg * J));
       maxSeg = std::max<int>(maxSeg, (int)nrg);
     }
   }
-  const size_t x_bytes = (size_t)maxXH * 2;      // a multiple of 1024
+  // Several token rows: no staged activations, and 16 x 16 partials per tile.
+  const size_t x_bytes = multi ? 0 : (size_t)maxXH * 2;      // a multiple of 1024
   const size_t xsum_bytes = fmt == QD_FMT_INT4_G64 ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
-  const size_t red_bytes = align_up((size_t)maxRel * 16 * 4, 16);
+  const size_t red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   const size_t cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   const size_t tab_bytes = (size_t)ng * sizeof(PGroup) + pm.size() * sizeof(PMember) +
                            (size_t)ng * sizeof(PSched);
@@ -902,7 +1247,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     delete plan;
     return QD_EDEVICE;
   }
-  const void* kfn = kernel_ptr(fmt);
+  const void* kfn = kernel_ptr(fmt, multi);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -954,9 +1299,11 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.red_bytes = (int32_t)red_bytes;
   a.cnt_bytes = (int32_t)cnt_bytes;
   a.tab_bytes = (int32_t)tab_bytes;
+  a.m = (int32_t)m;
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = fmt;
+  plan->multi = multi;
   plan->persistent = true;
   *out = plan;
   return QD_OK;
@@ -968,7 +1315,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt), dim3(plan->args.G),
+  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->multi), dim3(plan->args.G),
                                                   dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;

@@ -521,14 +521,16 @@ def _sample_picks(decoder):
 
 
 @pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1",
-                                      "qwen3-8b-int8-chain-m1"])
+                                      "qwen3-8b-int8-chain-m1", "qwen3-8b-int8-m16",
+                                      "qwen3-8b-int8-chain-m16",
+                                      "qwen3.8-27b-int8-m16"])
 def test_plan_full_size_sampled(qd, workload):
     """The full decoder-shaped step in the launch configuration the bench
     times: every output finite, sampled rows of sampled projections match
-    the oracle."""
+    the oracle (every token row at m = 16)."""
     import bench
     ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
-    plan = qd.StackPlan(ops, 1)
+    plan = qd.StackPlan(ops, m)
     for op in ops:
         op.y.fill_(float("nan"))
     plan.run()
@@ -552,10 +554,12 @@ def test_plan_full_size_sampled(qd, workload):
             w_full.mul_(1.0 / (si.W_STD * k ** 0.5))
         w_rows = w_full[rows].cpu().numpy()
         del w_full
-        x = op.x.cpu().numpy()                         # the activation the op read
+        x = op.x.cpu().numpy().reshape(m, k)           # the activations the op read
         parts = _oracle_parts(wl.fmt, w_rows)
-        y_ref = linear.ref_linear(wl.fmt, parts, x)
-        check_vector(_host(op.y)[rows], y_ref, linear.row_max_abs(wl.fmt, parts), x, name)
+        y_ref = linear.ref_linear(wl.fmt, parts, x).reshape(m, -1)
+        y_got = _host(op.y).reshape(m, n)[:, rows]
+        for t in range(m):
+            check_vector(y_got[t], y_ref[t], linear.row_max_abs(wl.fmt, parts), x[t], f"{name} token {t}")
     plan.close()
     del ops
     torch.cuda.empty_cache()
@@ -625,11 +629,12 @@ def test_stack_full_size_sampled_fp16_head(qd):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_plan_multi_token_groups(qd, fmt):
-    """A plan at m > 1 (it replays the per-group launches): groups of many
-    shapes (K = 1088, a ragged super-block tail; 4096 x 4096; K = 12288; a
-    fused pair; a group large enough for multi-row-group workgroups) and m
-    below 16.  Runs repeat with outputs poisoned in between and are
-    bit-identical; the plan's outputs equal decode_linear_stack's."""
+    """A plan at m > 1 (int8: the persistent kernel; INT4: it replays the
+    per-group launches): groups of many shapes (K = 1088, a ragged
+    super-block tail; 4096 x 4096; K = 12288; a fused pair; a group large
+    enough for multi-row-group workgroups) and m below 16.  Runs repeat with
+    outputs poisoned in between and are bit-identical; a replaying plan's
+    outputs equal decode_linear_stack's."""
     from int4_quantized_decode_amd import LinearOp
     shapes = [("a", [(200, 1088), (72, 1088)]), ("b", [(4096, 4096)]), ("c", [(512, 12288)]),
               ("d", [(16400, 2048)])]
@@ -645,7 +650,7 @@ def test_plan_multi_token_groups(qd, fmt):
                 ops.append(LinearOp(_pack(qd, fmt, _gpu(w)), xg, y, gid))
                 meta.append((f"{gname}{i}", w, X))
         plan = qd.StackPlan(ops, m)
-        assert not plan.persistent
+        assert plan.persistent == (fmt == "int8_b32")
         first = None
         for rep in range(3):
             for op in ops:
@@ -663,29 +668,91 @@ def test_plan_multi_token_groups(qd, fmt):
             else:
                 for a_, b_ in zip(first, outs):
                     assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
-        # the same launches as decode_linear_stack: the same bytes
-        for op in ops:
-            op.y.fill_(float("nan"))
-        qd.decode_linear_stack(ops, m)
-        for op, Yp in zip(ops, first):
-            assert np.array_equal(_host(op.y).view(np.uint16), Yp.view(np.uint16))
+        if not plan.persistent:
+            # the same launches as decode_linear_stack: the same bytes
+            for op in ops:
+                op.y.fill_(float("nan"))
+            qd.decode_linear_stack(ops, m)
+            for op, Yp in zip(ops, first):
+                assert np.array_equal(_host(op.y).view(np.uint16), Yp.view(np.uint16))
+        assert plan.error() == 0
         plan.close()
 
 
-def test_plan_buffer_orderings(qd):
+def test_plan_multi_token_split_and_chain(qd):
+    """The persistent kernel at m > 1: a group too large for one range of
+    tile partials per workgroup is split into row ranges (a member crossing
+    the split, a ragged last row-group), a group reads an earlier group's
+    output (activation blocks read only after the boundary), and a later
+    group reads a member of the split group.  Oracle parity per token row,
+    with each dependent input taken from the plan's own fp16 output, and
+    bit-identical repeats, at m = 16 and m = 3."""
+    from int4_quantized_decode_amd import LinearOp
+    shapes = {"a": (4096, 1024), "b": (1000, 4096), "c0": (5024, 12288), "c1": (4010, 12288),
+              "d": (600, 5024)}
+    ws = {name: si.weights(si.seed_for("split-w", name), n, k) for name, (n, k) in shapes.items()}
+    parts = {name: quant.quantize_int8_b32(w) for name, w in ws.items()}
+    pws = {name: qd.qpack_int8_b32(_gpu(w)) for name, w in ws.items()}
+    for m in (16, 3):
+        xa = si.activations(si.seed_for("split-xa", m), m, 1024)
+        xc = si.activations(si.seed_for("split-xc", m), m, 12288)
+        y = {name: torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+             for name, (n, _) in shapes.items()}
+        xa_g, xc_g = _gpu(xa), _gpu(xc)
+        ops = [LinearOp(pws["a"], xa_g, y["a"], 0),
+               LinearOp(pws["b"], y["a"], y["b"], 1),          # reads group 0's output
+               LinearOp(pws["c0"], xc_g, y["c0"], 2),          # split into row ranges
+               LinearOp(pws["c1"], xc_g, y["c1"], 2),
+               LinearOp(pws["d"], y["c0"], y["d"], 3)]          # reads a member of the split group
+        plan = qd.StackPlan(ops, m)
+        assert plan.persistent
+        first = None
+        for rep in range(3):
+            for t in y.values():
+                t.fill_(float("nan"))
+            plan.run()
+            torch.cuda.synchronize()
+            assert plan.error() == 0
+            outs = {name: _host(t).copy() for name, t in y.items()}
+            if first is None:
+                first = outs
+            else:
+                for name in outs:
+                    assert np.array_equal(first[name].view(np.uint16), outs[name].view(np.uint16)), name
+        inputs = {"a": xa, "b": first["a"].astype(np.float64), "c0": xc, "c1": xc,
+                  "d": first["c0"].astype(np.float64)}
+        for name in shapes:
+            Y_ref = linear.ref_linear("int8_b32", parts[name], inputs[name])
+            rmax = linear.row_max_abs("int8_b32", parts[name])
+            for t in range(m):
+                check_vector(first[name][t], Y_ref[t], rmax, inputs[name][t], f"{name} m={m} token {t}")
+        plan.close()
+
+
+@pytest.mark.parametrize("m,packed", [(1, False), (1, True), (16, False), (16, True)])
+def test_plan_buffer_orderings(qd, m, packed):
     """The persistent step orders each boundary from the step's buffers: an
     input no earlier output overlaps is staged early, one that an earlier
-    output overlaps (not only the previous group's) only after the barrier;
-    outputs a later group reads or rewrites are stored before the stamp.
-    Checked against a sequential model of the buffers: a group reading the
-    output of two groups back, a group rewriting an earlier group's output
-    (the later value must win), a group overwriting an earlier group's input
-    that a later group then reads, and independent groups between them."""
+    output overlaps (not only the previous group's) only after the barrier,
+    through the caches only when no earlier access can have left a stale
+    copy of its cache lines; outputs a later group reads or rewrites are
+    stored before the stamp.  Checked against a sequential model of the
+    buffers: a group reading the output of two groups back, a group
+    rewriting an earlier group's output (the later value must win), a group
+    overwriting an earlier group's input that a later group then reads, and
+    independent groups between them.  Separate buffers, and buffers packed
+    16 bytes apart in one allocation (neighbours share cache lines); one and
+    16 token rows."""
     from int4_quantized_decode_amd import LinearOp
     k = 1024
     nbuf = 6
-    bufs = [torch.empty(k, dtype=torch.float16, device=DEV) for _ in range(nbuf)]
-    init = [si.activations(si.seed_for("order-buf", i), 1, k)[0] for i in range(nbuf)]
+    shape = (m, k) if m > 1 else (k,)
+    if packed:
+        big = torch.empty(nbuf * (m * k + 8), dtype=torch.float16, device=DEV)
+        bufs = [big[i * (m * k + 8):i * (m * k + 8) + m * k].view(shape) for i in range(nbuf)]
+    else:
+        bufs = [torch.empty(shape, dtype=torch.float16, device=DEV) for _ in range(nbuf)]
+    init = [si.activations(si.seed_for("order-buf", i, m), m, k).reshape(shape) for i in range(nbuf)]
     # (x buffer, y buffer) per group, in step order; all matrices are k x k
     prog = [(0, 1),   # g0: independent input
             (2, 3),   # g1: independent (early staging)
@@ -697,7 +764,7 @@ def test_plan_buffer_orderings(qd):
     ws = [si.weights(si.seed_for("order-w", g), k, k) for g in range(len(prog))]
     pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
     ops = [LinearOp(pws[g], bufs[xb], bufs[yb], g) for g, (xb, yb) in enumerate(prog)]
-    plan = qd.StackPlan(ops, 1)
+    plan = qd.StackPlan(ops, m)
     assert plan.persistent
     # the sequential model, with each stored output rounded to fp16
     state = [v.astype(np.float16) for v in init]
@@ -724,8 +791,11 @@ def test_plan_buffer_orderings(qd):
                 parts = quant.quantize_int8_b32(ws[g])
                 # the input the kernel saw was the device's own earlier output: bound the
                 # chain by the rows' magnitudes along the path (at most 3 products deep)
-                check_vector(outs[yb], want[g], 4 * linear.row_max_abs("int8_b32", parts),
-                             xin[g].astype(np.float64), f"buffer {yb} (group {g})")
+                got, ref, xs = (outs[yb].reshape(m, k), want[g].reshape(m, k),
+                                xin[g].astype(np.float64).reshape(m, k))
+                for t in range(m):
+                    check_vector(got[t], ref[t], 4 * linear.row_max_abs("int8_b32", parts),
+                                 xs[t], f"buffer {yb} (group {g}) token {t}")
         else:
             for a_, b_ in zip(first, outs):
                 assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
