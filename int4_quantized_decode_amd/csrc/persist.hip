@@ -40,6 +40,7 @@
 // and every later wait is skipped, so the kernel always finishes.
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -71,6 +72,7 @@ enum : int32_t {
 struct PGroup {         // 64 bytes
   const uint16_t* x;
   const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
+  const uint16_t* xt;     // m > 1: x in matrix-core order (plan scratch), or null
   int64_t k;
   int32_t J;            // super-blocks per row
   int32_t R;            // row-groups in the group
@@ -79,7 +81,7 @@ struct PGroup {         // 64 bytes
   int32_t pro;          // qd_prologue of the group's input
   float eps;
   int32_t order;        // kStageEarly | kAckOutputs | kNoWait | kCleanLines
-  int32_t pad[3];
+  int32_t pad;
 };
 
 struct PMember {        // 48 bytes
@@ -89,7 +91,7 @@ struct PMember {        // 48 bytes
   int32_t rg_begin;     // first row-group of this member within its group
   int32_t epi;          // qd_epilogue of this member's outputs
   int64_t ld;           // elements between token rows of y (m > 1)
-  int64_t pad;
+  uint16_t* yt;         // m > 1: where the outputs also go in matrix-core order, or null
 };
 
 struct PSched {         // 16 bytes: one workgroup's part of one group
@@ -172,6 +174,7 @@ struct Sched {
   __device__ int nmem(int gi) const { return uni(g[gi].n_mem); }
   __device__ const uint16_t* x(int gi) const { return uni_ptr(g[gi].x); }
   __device__ const uint16_t* gamma(int gi) const { return uni_ptr(g[gi].gamma); }
+  __device__ const uint16_t* xt(int gi) const { return uni_ptr(g[gi].xt); }
   __device__ int pro(int gi) const { return uni(g[gi].pro); }
   __device__ int order(int gi) const { return uni(g[gi].order); }
   __device__ float eps(int gi) const { return __builtin_bit_cast(float, uni(__builtin_bit_cast(int, g[gi].eps))); }
@@ -190,6 +193,7 @@ struct Sched {
   __device__ int64_t n_l(int mi) const { return m[mi].n; }
   __device__ int epi_l(int mi) const { return m[mi].epi; }
   __device__ int64_t ld(int mi) const { return (int64_t)uni((int)m[mi].ld); }
+  __device__ uint16_t* yt(int mi) const { return uni_ptr(m[mi].yt); }
 };
 
 // Tile hand-out.  A workgroup's tiles of all groups form one sequence
@@ -354,11 +358,27 @@ __device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const
 // X[0..15][256 j .. 256 j + 255] in the matrix-core A layout: lane (gq, rho)
 // holds token rho's 8 values at K positions 32 b + 8 gq of every 32-block b.
 // The blocks are read from memory, not staged (16 x K does not fit in LDS for
-// the longest K).  Token rows past m and K positions past K read as zeros
-// (out-of-range offsets: no memory traffic).  Activations nothing in the step
-// writes go through the caches; the others are read device-coherently.
+// the longest K).
+//
+// Matrix-core order: where the plan keeps a copy of x in it (xt), 16-byte
+// chunk c = 16 (k / 8) + t holds x[t][8 (k / 8) .. 8 (k / 8) + 7] for token
+// rows t < 16 (zeros past m and past K), so each load of the block is one
+// contiguous KiB.  Copies are written only where nothing can leave a stale
+// line of them in a cache, and are read through the caches.
+//
+// Otherwise x is read in place: token rows past m and K positions past K read
+// as zeros (out-of-range offsets: no memory traffic).  Activations nothing in
+// the step writes go through the caches; the others are read
+// device-coherently unless their lines are known clean.
 __device__ __forceinline__ void load_xblock(const Sched& S, int g, int j, int m, int lane,
                                             bool coherent, u32x4 (&xa)[8]) {
+  const uint16_t* xt = S.xt(g);
+  if (xt) {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(xt, (uint32_t)S.J(g) * 8192u);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) xa[b] = bload16(rt, (uint32_t)((j * 8 + b) * 1024 + lane * 16));
+    return;
+  }
   const int gq = lane >> 4, rho = lane & 15;
   const int64_t K = S.k(g);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(S.x(g), (uint32_t)(m * K * 2));
@@ -670,14 +690,21 @@ __device__ __forceinline__ void store_rows16(const PlanArgs& p, const Sched& S, 
   const int64_t n = (int64_t)(rg - S.rg_begin(mi)) * kTileRows + rho;
   if (n >= S.n(mi)) return;
   uint16_t* const y = S.y(mi);
+  uint16_t* const yt = S.yt(mi);
   const int64_t ld = S.ld(mi);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = 4 * gq + i;
-    if (tok < p.m)
-      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(y + tok * ld + n),
-                         __builtin_bit_cast(uint16_t, (half_t)v[i]), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    if (tok < p.m) {
+      const uint16_t h = __builtin_bit_cast(uint16_t, (half_t)v[i]);
+      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(y + tok * ld + n), h,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The later group reading these outputs as its x finds them here in
+      // matrix-core order too.
+      if (yt)
+        __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(yt + ((n >> 3) * 16 + tok) * 8 + (n & 7)),
+                           h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -899,6 +926,33 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Before a step with up to 16 token rows: copy the activations no group of
+// the step writes into matrix-core order (see load_xblock), 256 chunks of 16
+// bytes per workgroup, chunk-contiguous stores.  Chunks of token rows past m
+// or past K are left as they are (zero since the plan was made).
+struct XtJob {
+  const uint16_t* x;    // [m, k]
+  uint16_t* t;          // the copy
+  int64_t k;
+  int64_t first_block;  // first workgroup of this job
+};
+
+__global__ __launch_bounds__(256) void xt_copy_kernel(const XtJob* jobs, int njobs, int m) {
+  int lo = 0, hi = njobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (jobs[mid].first_block <= (int64_t)blockIdx.x) lo = mid;
+    else hi = mid - 1;
+  }
+  const XtJob jb = jobs[lo];
+  const int64_t c = ((int64_t)blockIdx.x - jb.first_block) * 256 + threadIdx.x;
+  const int64_t k8 = c >> 4;
+  const int tok = (int)(c & 15);
+  if (tok >= m || k8 * 8 >= jb.k) return;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k8 * 8);
+  *reinterpret_cast<u32x4*>(jb.t + c * 8) = v;
+}
+
 #ifndef QD_PLAN_RING8
 #define QD_PLAN_RING8 3
 #endif
@@ -924,6 +978,10 @@ struct qd_stack_plan {
   void* tables = nullptr;
   void* scratch = nullptr;
   size_t scratch_bytes = 0;
+  void* xt = nullptr;                    // m > 1: activation copies in matrix-core order
+  void* xt_jobs = nullptr;               // copies made before each step
+  int xt_njobs = 0;
+  int64_t xt_blocks = 0;
   qd::PlanArgs args{};
   size_t lds = 0;
   unsigned long long epoch = 0;
@@ -939,11 +997,13 @@ struct HostGroup {
   int J;
   std::vector<PMember> mem;
   std::vector<int64_t> src;    // the step group each member comes from (outputs of one never overlap)
+  std::vector<int64_t> yt_off; // m > 1: byte offset of each member's matrix-core copy in the plan's copies, or -1
   int R;
   const uint16_t* gamma;
   int pro;
   float eps;
   int32_t order = 0;
+  int64_t xt_off = -1;         // m > 1: byte offset of the group's x copy, or -1
 };
 
 bool ranges_overlap(const void* a, uint64_t an, const void* b, uint64_t bn) {
@@ -1052,8 +1112,9 @@ bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G) {
     }
     for (int64_t a = 0; a < hg.R; a += piece) {
       const int64_t b = std::min<int64_t>(hg.R, a + piece);
-      HostGroup pg{hg.x, hg.k, hg.J, {}, {}, 0, hg.gamma, hg.pro, hg.eps};
+      HostGroup pg{hg.x, hg.k, hg.J, {}, {}, {}, 0, hg.gamma, hg.pro, hg.eps};
       pg.order = hg.order;
+      pg.xt_off = hg.xt_off;
       for (size_t q = 0; q < hg.mem.size(); ++q) {
         const PMember& mm = hg.mem[q];
         const int64_t r0 = mm.rg_begin, r1 = r0 + ceil_div(mm.n, kTileRows);
@@ -1067,6 +1128,7 @@ bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G) {
         slice.rg_begin = pg.R;
         pg.mem.push_back(slice);
         pg.src.push_back(hg.src[q]);
+        pg.yt_off.push_back(hg.yt_off[q] < 0 ? -1 : hg.yt_off[q] + skip * kTileRows * 16 * 2);
         pg.R += (int)(hi - lo);
       }
       if (a > 0) pg.order |= kNoWait;
@@ -1149,7 +1211,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   for (int64_t i = 0; ok && i < n_ops;) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
-    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, 0,
+    HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, {}, 0,
                  ops[i].gamma, ops[i].prologue, ops[i].eps};
     for (int64_t q = i; q < e; ++q) {
       if (ops[q].w.n == 0) continue;
@@ -1163,8 +1225,9 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       // passed its device tests.
       if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) ok = false;
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
-                               hg.R, ops[q].epilogue, ops[q].w.n, 0});
+                               hg.R, ops[q].epilogue, ops[q].w.n, nullptr});
       hg.src.push_back(i);
+      hg.yt_off.push_back(-1);
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);
     }
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
@@ -1185,18 +1248,62 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   }
 
   const int G = cus;
+  order_groups(groups, m, tile_bytes(fmt));
+  // Several token rows: copies of the activations in matrix-core order.  An
+  // activation no group writes is copied before the step; one that is
+  // exactly an earlier op's whole output (the last write to any of its
+  // bytes) is written in that order by the op itself.  Other activations are
+  // read in place.
+  std::vector<XtJob> jobs;
+  int64_t xt_total = 0;
+  if (multi) {
+    std::map<std::pair<const void*, int64_t>, int64_t> early_slots;
+    std::map<std::pair<size_t, size_t>, int64_t> out_slots;
+    auto new_slot = [&](int J) {
+      const int64_t off = xt_total;
+      xt_total += (int64_t)align_up((size_t)J * 8192, 256);
+      return off;
+    };
+    for (size_t g = 0; g < groups.size(); ++g) {
+      HostGroup& hg = groups[g];
+      if (hg.order & kStageEarly) {
+        const auto key = std::make_pair((const void*)hg.x, hg.k);
+        auto it = early_slots.find(key);
+        if (it == early_slots.end()) {
+          it = early_slots.emplace(key, new_slot(hg.J)).first;
+          jobs.push_back(XtJob{hg.x, reinterpret_cast<uint16_t*>((uintptr_t)it->second), hg.k, 0});
+        }
+        hg.xt_off = it->second;
+        continue;
+      }
+      size_t p = SIZE_MAX, q = 0;
+      for (size_t j = 0; j < g; ++j)
+        for (size_t b = 0; b < groups[j].mem.size(); ++b)
+          if (ranges_overlap(hg.x, (uint64_t)m * hg.k * 2, groups[j].mem[b].y, y_span(groups[j].mem[b], m))) {
+            p = j;
+            q = b;
+          }
+      if (p == SIZE_MAX) continue;
+      const PMember& pq = groups[p].mem[q];
+      if ((const void*)pq.y != (const void*)hg.x || pq.n != hg.k || pq.ld != hg.k) continue;
+      auto it = out_slots.find(std::make_pair(p, q));
+      if (it == out_slots.end()) it = out_slots.emplace(std::make_pair(p, q), new_slot(hg.J)).first;
+      groups[p].yt_off[q] = it->second;
+      hg.xt_off = it->second;
+    }
+  }
   if (multi && !split_rows(groups, QD_PLAN_TILES16, G)) {
     plan->replay = std::move(replay);
     *out = plan;
     return QD_OK;
   }
-  order_groups(groups, m, tile_bytes(fmt));
   const int ng = (int)groups.size();
   std::vector<PGroup> pg(ng);
   std::vector<PMember> pm;
   std::vector<PSched> ps((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1;
+  std::vector<int64_t> xt_fix, yt_fix;   // copy offsets, made pointers once the copies exist
   // A step the persistent walker cannot hold (tile counts past int32, LDS
   // beyond one CU's) replays per-group launches instead.
   auto fallback = [&]() {
@@ -1208,9 +1315,13 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
     if (T > (int64_t)INT32_MAX / 2) return fallback();
-    pg[g] = PGroup{hg.x, hg.gamma, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size(),
-                   hg.pro, hg.eps, hg.order, {0, 0, 0}};
-    for (const PMember& mm : hg.mem) pm.push_back(mm);
+    pg[g] = PGroup{hg.x, hg.gamma, nullptr, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size(),
+                   hg.pro, hg.eps, hg.order, 0};
+    xt_fix.push_back(hg.xt_off);
+    for (size_t b = 0; b < hg.mem.size(); ++b) {
+      pm.push_back(hg.mem[b]);
+      yt_fix.push_back(hg.yt_off[b]);
+    }
     maxJ = std::max(maxJ, hg.J);
     // halves of LDS the staging writes: x's span, and the second operand's
     maxXH = std::max(maxXH, (hg.pro == QD_PRO_NONE ? 1 : 2) * x_span(hg.J * kSuperK));
@@ -1262,6 +1373,40 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return fallback();
   }
 
+  // The activation copies (zeroed once: token rows past m and K positions
+  // past K stay zero) and the table of copies made before each step.
+  if (xt_total > 0) {
+    int64_t blocks = 0;
+    for (XtJob& jb : jobs) {
+      jb.first_block = blocks;
+      blocks += ceil_div(ceil_div(jb.k, 8) * 16, 256);
+    }
+    void* dj = nullptr;
+    if (hipMalloc(&plan->xt, (size_t)xt_total) != hipSuccess ||
+        hipMemset(plan->xt, 0, (size_t)xt_total) != hipSuccess ||
+        (!jobs.empty() && hipMalloc(&dj, sizeof(XtJob) * jobs.size()) != hipSuccess)) {
+      if (plan->xt) (void)hipFree(plan->xt);
+      delete plan;
+      return QD_ELAUNCH;
+    }
+    uint8_t* const xb = static_cast<uint8_t*>(plan->xt);
+    for (XtJob& jb : jobs) jb.t = reinterpret_cast<uint16_t*>(xb + reinterpret_cast<uintptr_t>(jb.t));
+    if (!jobs.empty() &&
+        hipMemcpy(dj, jobs.data(), sizeof(XtJob) * jobs.size(), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(plan->xt);
+      (void)hipFree(dj);
+      delete plan;
+      return QD_ELAUNCH;
+    }
+    plan->xt_jobs = dj;
+    plan->xt_njobs = (int)jobs.size();
+    plan->xt_blocks = blocks;
+    for (int g = 0; g < ng; ++g)
+      if (xt_fix[g] >= 0) pg[g].xt = reinterpret_cast<const uint16_t*>(xb + xt_fix[g]);
+    for (size_t i = 0; i < pm.size(); ++i)
+      if (yt_fix[i] >= 0) pm[i].yt = reinterpret_cast<uint16_t*>(xb + yt_fix[i]);
+  }
+
   // Device tables, then scratch.
   const size_t o_groups = 0;
   const size_t o_mem = align_up(o_groups + sizeof(PGroup) * ng, 256);
@@ -1280,6 +1425,8 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       hipMemset(plan->scratch, 0, s_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     if (plan->tables) (void)hipFree(plan->tables);
     if (plan->scratch) (void)hipFree(plan->scratch);
+    if (plan->xt) (void)hipFree(plan->xt);
+    if (plan->xt_jobs) (void)hipFree(plan->xt_jobs);
     delete plan;
     return QD_ELAUNCH;
   }
@@ -1313,6 +1460,11 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return QD_EDEVICE;
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
+  if (plan->xt_njobs > 0) {
+    hipLaunchKernelGGL(xt_copy_kernel, dim3((unsigned)plan->xt_blocks), dim3(256), 0, s,
+                       static_cast<const XtJob*>(plan->xt_jobs), plan->xt_njobs, (int)plan->args.m);
+    if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
+  }
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
   const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->multi), dim3(plan->args.G),
@@ -1347,6 +1499,8 @@ void plan_destroy(qd_stack_plan* plan) {
   if (!plan) return;
   if (plan->tables) (void)hipFree(plan->tables);
   if (plan->scratch) (void)hipFree(plan->scratch);
+  if (plan->xt) (void)hipFree(plan->xt);
+  if (plan->xt_jobs) (void)hipFree(plan->xt_jobs);
   delete plan;
 }
 
