@@ -974,6 +974,7 @@ struct qd_stack_plan {
   bool persistent = false;
   int fmt = 0;
   bool multi = false;                    // m > 1 (int8 only)
+  bool glue = false;                     // one token row with a prologue or an epilogue
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (K = 0, mixed formats, glue, ...)
   void* tables = nullptr;
   void* scratch = nullptr;
@@ -1181,13 +1182,18 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #define QD_PLAN_TILES16 96
 #endif
 
-const void* kernel_ptr(int fmt, bool multi) {
+// One token row with glue: the staging applies the prologue in LDS and the
+// row stores apply the epilogue (a separate instance, so steps without glue
+// run the plain kernel).
+const void* kernel_ptr(int fmt, bool multi, bool glue) {
   if (multi)
     return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
                                                         QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>);
   if (fmt == QD_FMT_INT8_B32)
-    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
-  return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false, 1, 1>);
+    return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
+                : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
+  return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, true, 1, 1>)
+              : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false, 1, 1>);
 }
 
 }  // namespace
@@ -1206,6 +1212,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   // or up to 16 with int8 weights.
   std::vector<HostGroup> groups;
   const bool multi = m > 1;
+  bool glue = false;
   bool ok = (m >= 1 && m <= 16);
   int fmt = 0;
   for (int64_t i = 0; ok && i < n_ops;) {
@@ -1220,10 +1227,11 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       if (ops[q].w.fmt != fmt) ok = false;
       if (fmt != QD_FMT_INT8_B32 && fmt != QD_FMT_INT4_G64) ok = false;   // fp16: replay
       if (multi && fmt != QD_FMT_INT8_B32) ok = false;                    // INT4 at m > 1: replay
-      // Glue (a prologue or an epilogue): replay.  The persistent walker's
-      // staging supports it, but that path is switched off until it has
-      // passed its device tests.
-      if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) ok = false;
+      // Glue (a prologue or an epilogue): at one token row only.
+      if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) {
+        glue = true;
+        if (multi) ok = false;
+      }
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
                                hg.R, ops[q].epilogue, ops[q].w.n, nullptr});
       hg.src.push_back(i);
@@ -1358,7 +1366,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     delete plan;
     return QD_EDEVICE;
   }
-  const void* kfn = kernel_ptr(fmt, multi);
+  const void* kfn = kernel_ptr(fmt, multi, glue);
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -1451,6 +1459,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   plan->lds = lds;
   plan->fmt = fmt;
   plan->multi = multi;
+  plan->glue = glue;
   plan->persistent = true;
   *out = plan;
   return QD_OK;
@@ -1467,7 +1476,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   }
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->multi), dim3(plan->args.G),
+  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->multi, plan->glue), dim3(plan->args.G),
                                                   dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;

@@ -89,7 +89,8 @@ def test_prologues_and_epilogue_exact(qd, fmt, m, path):
            qd.LinearOp(pw, as_, ys[2], 2, epilogue="silu")]
     if path == "plan":
         plan = qd.StackPlan(ops, m)
-        assert not plan.persistent            # steps with glue replay the launches
+        # the persistent kernel takes glue at one token row (int8; fp16 steps replay)
+        assert plan.persistent == (m == 1 and fmt != "fp16")
         plan.run()
         torch.cuda.synchronize()
         assert plan.error() == 0
@@ -276,11 +277,11 @@ def test_glue_stack_plan_multi_token(qd, fmt, m):
 
 @pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 def test_glue_stack_plan_parity_and_determinism(qd, fmt):
-    """A plan of the glued step (it replays the per-group launches): per-op
+    """A plan of the glued step (the persistent kernel at one token row): per-op
     parity and bit-identical repeated runs, outputs poisoned in between."""
     ops, meta, keep = _glue_stack(qd, fmt, 1, _tiny())
     plan = qd.StackPlan(ops, 1)
-    assert not plan.persistent
+    assert plan.persistent
     first = None
     for rep in range(3):
         for op in ops:
@@ -298,14 +299,11 @@ def test_glue_stack_plan_parity_and_determinism(qd, fmt):
     plan.close()
 
 
-@pytest.mark.skip(reason="the persistent kernel's glue staging is switched off (plans with glue "
-                         "replay the launches): its first device run faulted because the second "
-                         "operand overran the LDS x region when K is not a multiple of 512; the "
-                         "layout is fixed and the path stays off until this test has passed")
 @pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 def test_glue_stack_persistent(qd, fmt):
     """The glued step in the one-launch persistent kernel (staging applies the
-    prologue in LDS): per-op parity.  Needs the persistent glue path on."""
+    prologue in LDS, after x's whole LDS span, so K not a multiple of 512
+    stays inside the region): per-op parity."""
     ops, meta, keep = _glue_stack(qd, fmt, 1, _tiny())
     plan = qd.StackPlan(ops, 1)
     assert plan.persistent
@@ -316,17 +314,28 @@ def test_glue_stack_persistent(qd, fmt):
     plan.close()
 
 
-@pytest.mark.parametrize("workload", ["qwen3-8b-int8-glue-m1", "qwen3-8b-int8-glue-m16"])
-def test_glue_full_size_sampled(qd, workload):
+@pytest.mark.parametrize("workload,path", [("qwen3-8b-int8-glue-m1", "launches"),
+                                           ("qwen3-8b-int8-glue-m1", "plan"),
+                                           ("qwen3-8b-int8-glue-m16", "launches")])
+def test_glue_full_size_sampled(qd, workload, path):
     """The full 8B-shaped step chained through the glue, as the bench times it
-    (per-group launches): every output finite; sampled rows of sampled
-    projections (RMSNorm-fed q and head, silu-stored gate, up, gated-product-fed
-    down, plain o) match the oracle on the activations each op read."""
+    (the persistent plan at one token row, per-group launches): every output
+    finite; sampled rows of sampled projections (RMSNorm-fed q and head,
+    silu-stored gate, up, gated-product-fed down, plain o) match the oracle on
+    the activations each op read."""
     import bench
     ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
     for op in ops:
         op.y.fill_(float("nan"))
-    qd.decode_linear_stack(ops, m)
+    if path == "plan":
+        plan = qd.StackPlan(ops, m)
+        assert plan.persistent
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        plan.close()
+    else:
+        qd.decode_linear_stack(ops, m)
     torch.cuda.synchronize()
     wl = si.WORKLOADS[workload]
     d = wl.decoder
