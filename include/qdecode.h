@@ -219,11 +219,11 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * valid while the plan lives.  qd_stack_plan_run enqueues one step on
  * `stream` and allocates nothing.  A plan may be run repeatedly but not
  * concurrently.  The persistent kernel takes steps of one format, int8 b32
- * or INT4 g64 at m = 1 and int8 b32 at m = 2..16.  Steps it does not take
- * (fp16 weights, INT4 at m > 1, mixed formats, a schedule larger than one
- * CU's LDS, a single row-group too long for it at m > 1, any op with a
- * prologue or an epilogue) are replayed as the same per-group launches
- * decode_linear_stack makes, with the same results;
+ * or INT4 g64 at m = 1 (with or without glue) and int8 b32 at m = 2..16
+ * (without glue).  Steps it does not take (fp16 weights, INT4 at m > 1,
+ * mixed formats, a schedule larger than one CU's LDS, a single row-group too
+ * long for it at m > 1, glue at m > 1) are replayed as the same per-group
+ * launches decode_linear_stack makes, with the same results;
  * qd_stack_plan_is_persistent tells which.
  */
 typedef struct qd_stack_plan qd_stack_plan;

@@ -36,6 +36,11 @@ def _host(t):
 FMTS = ["int8_b32", "int4_g64", "fp16"]
 
 
+INT4_M16_OFF = pytest.mark.skip(reason="the persistent kernel's INT4 instance at m > 1 is switched off "
+                                       "(plans replay the launches): it passed these tests, but a longer "
+                                       "device run of it ended in a memory fault whose cause is not found")
+
+
 def _oracle_parts(fmt, w):
     return {"int8_b32": quant.quantize_int8_b32, "int4_g64": quant.quantize_int4_g64,
             "fp16": quant.quantize_fp16}[fmt](w)
@@ -523,6 +528,7 @@ def _sample_picks(decoder):
 @pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1",
                                       "qwen3-8b-int8-chain-m1", "qwen3-8b-int8-m16",
                                       "qwen3-8b-int8-chain-m16",
+                                      pytest.param("qwen3-8b-int4-m16", marks=INT4_M16_OFF),
                                       "qwen3.8-27b-int8-m16"])
 def test_plan_full_size_sampled(qd, workload):
     """The full decoder-shaped step in the launch configuration the bench
@@ -629,8 +635,8 @@ def test_stack_full_size_sampled_fp16_head(qd):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_plan_multi_token_groups(qd, fmt):
-    """A plan at m > 1 (int8: the persistent kernel; INT4: it replays the
-    per-group launches): groups of many shapes (K = 1088, a ragged
+    """A plan at m > 1 (int8: the persistent kernel; INT4 and fp16: it replays
+    the per-group launches): groups of many shapes (K = 1088, a ragged
     super-block tail; 4096 x 4096; K = 12288; a fused pair; a group large
     enough for multi-row-group workgroups) and m below 16.  Runs repeat with
     outputs poisoned in between and are bit-identical; a replaying plan's
@@ -679,7 +685,8 @@ def test_plan_multi_token_groups(qd, fmt):
         plan.close()
 
 
-def test_plan_multi_token_split_and_chain(qd):
+@pytest.mark.parametrize("fmt", ["int8_b32", pytest.param("int4_g64", marks=INT4_M16_OFF)])
+def test_plan_multi_token_split_and_chain(qd, fmt):
     """The persistent kernel at m > 1: a group too large for one range of
     tile partials per workgroup is split into row ranges (a member crossing
     the split, a ragged last row-group), a group reads an earlier group's
@@ -688,11 +695,11 @@ def test_plan_multi_token_split_and_chain(qd):
     with each dependent input taken from the plan's own fp16 output, and
     bit-identical repeats, at m = 16 and m = 3."""
     from int4_quantized_decode_amd import LinearOp
-    shapes = {"a": (4096, 1024), "b": (1000, 4096), "c0": (5024, 12288), "c1": (4010, 12288),
-              "d": (600, 5024)}
+    shapes = {"a": (4096, 1024), "b": (1000, 4096), "c0": (5056, 12288), "c1": (4010, 12288),
+              "d": (600, 5056)}
     ws = {name: si.weights(si.seed_for("split-w", name), n, k) for name, (n, k) in shapes.items()}
-    parts = {name: quant.quantize_int8_b32(w) for name, w in ws.items()}
-    pws = {name: qd.qpack_int8_b32(_gpu(w)) for name, w in ws.items()}
+    parts = {name: _oracle_parts(fmt, w) for name, w in ws.items()}
+    pws = {name: _pack(qd, fmt, _gpu(w)) for name, w in ws.items()}
     for m in (16, 3):
         xa = si.activations(si.seed_for("split-xa", m), m, 1024)
         xc = si.activations(si.seed_for("split-xc", m), m, 12288)
@@ -722,8 +729,8 @@ def test_plan_multi_token_split_and_chain(qd):
         inputs = {"a": xa, "b": first["a"].astype(np.float64), "c0": xc, "c1": xc,
                   "d": first["c0"].astype(np.float64)}
         for name in shapes:
-            Y_ref = linear.ref_linear("int8_b32", parts[name], inputs[name])
-            rmax = linear.row_max_abs("int8_b32", parts[name])
+            Y_ref = linear.ref_linear(fmt, parts[name], inputs[name])
+            rmax = linear.row_max_abs(fmt, parts[name])
             for t in range(m):
                 check_vector(first[name][t], Y_ref[t], rmax, inputs[name][t], f"{name} m={m} token {t}")
         plan.close()
