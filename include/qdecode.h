@@ -215,9 +215,12 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * same from run to run).
  * qd_stack_plan_create validates `ops` exactly as decode_linear_stack does,
  * copies the descriptors to the device and allocates the plan's scratch
- * (completion stamps, an error word) once; the pointers in `ops` must stay
- * valid while the plan lives.  qd_stack_plan_run enqueues one step on
- * `stream` and allocates nothing.  A plan may be run repeatedly but not
+ * (completion stamps, an error word and, at m > 1, copies of the step's
+ * activations in the order the matrix cores read them: 8 KiB per 256 input
+ * features per group, about 28 MB for an 8B-shaped step) once; the pointers
+ * in `ops` must stay valid while the plan lives.  qd_stack_plan_run enqueues
+ * one step on `stream` (at m > 1 a small copy kernel for the activations no
+ * op of the step writes, then the persistent kernel) and allocates nothing.  A plan may be run repeatedly but not
  * concurrently.  The persistent kernel takes steps of one format, int8 b32
  * or INT4 g64 at m = 1 (with or without glue) and int8 b32 at m = 2..16
  * (without glue).  Steps it does not take (fp16 weights, INT4 at m > 1,
