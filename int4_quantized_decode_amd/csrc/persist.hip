@@ -1021,11 +1021,12 @@ __global__ __launch_bounds__(256) void xt_copy_kernel(const XtJob* jobs, int njo
   *reinterpret_cast<u32x4*>(jb.t + c * 8) = v;
 }
 
+// Streaming ring depth per format (tiles per streaming wave), measured.
 #ifndef QD_PLAN_RING8
 #define QD_PLAN_RING8 3
 #endif
 #ifndef QD_PLAN_RING4
-#define QD_PLAN_RING4 4
+#define QD_PLAN_RING4 2
 #endif
 constexpr int kRing8 = QD_PLAN_RING8;
 constexpr int kRing4 = QD_PLAN_RING4;
@@ -1215,12 +1216,17 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // SIMD; this was best for the 2B-, 4B- and 8B-shaped steps alike (15 to 50
 // tiles per workgroup per group).  More reserve tiles run several groups
 // ahead and are then not free for the next stall; fewer leave memory idle
-// for part of it.  INT4 tiles carry twice the arithmetic per byte and there
-// every streaming slot is needed: no reserve waves.
+// for part of it.  INT4: no reserve waves, and rings of 2 tiles per
+// streaming wave (8B INT4 step 993-996 us; rings of 1, 3, 4 and 6 took 1098,
+// 1043-1050, 1089-1104 and 1111 us; 2 x 4, 4 x 2 and 7 x 2 reserve tiles with
+// rings of 2 took 1051-1059, 1021-1025 and 1095-1109 us).
 #ifndef QD_PLAN_RESERVE4
 #define QD_PLAN_RESERVE4 0
 #endif
-constexpr int kReserveInt4 = QD_PLAN_RESERVE4;
+#ifndef QD_PLAN_RESERVE4_S
+#define QD_PLAN_RESERVE4_S 4
+#endif
+constexpr int kReserveInt4 = QD_PLAN_RESERVE4, kReserveInt4S = QD_PLAN_RESERVE4_S;
 
 #ifndef QD_PLAN_RESERVE8_R
 #define QD_PLAN_RESERVE8_R 7
@@ -1260,8 +1266,8 @@ const void* kernel_ptr(int fmt, bool multi, bool glue) {
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
-  return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, true, 1, 1>)
-              : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, 4, false, 1, 1>);
+  return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, kReserveInt4S, true, 1, 1>)
+              : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, kReserveInt4S, false, 1, 1>);
 }
 
 }  // namespace
