@@ -10,31 +10,41 @@
 //     streaming compute waves, reserve compute waves and 1 control wave.  The
 //     workgroup's share of every group's schedule lives in LDS, so no wave
 //     waits on a memory round trip to find its next tiles;
-//   * a group's tiles (row-group major) are split into one range per
-//     workgroup, on row-group boundaries whenever the group has at least one
-//     row-group per workgroup; compute waves take tiles of the workgroup's
-//     sequence from an LDS counter, in order, across group boundaries;
+//   * a group's row-groups are split into one contiguous range per
+//     workgroup; compute waves take tiles (at up to 16 token rows: units of
+//     two row-groups at one super-block) of the workgroup's sequence from an
+//     LDS counter, in order, across group boundaries;
 //   * a streaming wave keeps a ring of tiles in registers and refills a slot
 //     as soon as it is consumed.  Its loads are accepted only as fast as
 //     memory delivers, so at a group boundary its ring holds landed data and
 //     it has nothing more to issue; reserve waves hold no tiles until the
 //     workgroup has computed every tile of a group and then issue the next
 //     tiles while the device synchronises, so memory keeps streaming;
-//   * compute waves write each tile's row partials to their own LDS slot and
+//   * compute waves write each tile's partials to their own LDS slot and
 //     count the tile against its row-group; the control wave reduces and
 //     stores each row-group as soon as it is complete (fixed-order sums:
 //     deterministic), publishes that the workgroup has finished the group
 //     (one completion stamp per workgroup), waits until every workgroup has
-//     published it, then stages the next activation vector straight into LDS
-//     and releases the compute waves (one barrier per group), so an op may
-//     consume an earlier op's output;
+//     published it, and releases the compute waves (one barrier per group),
+//     so an op may consume an earlier op's output;
+//   * one token row: the control wave stages each group's activation vector
+//     (and, with glue, gamma or the gated product's second block) straight
+//     into LDS and applies the prologue there;
+//   * up to 16 token rows (int8): compute waves read the activation blocks
+//     themselves, from copies in matrix-core order where the plan keeps them
+//     (made before the step, or written by the op producing them), and the
+//     partials are 16 x 16 per tile; groups too large for the partials in
+//     LDS are split into row ranges that need no device-wide wait between
+//     them;
 //   * compute waves issue no global stores or atomics.
 //
-// Data another workgroup reads (outputs, split-row-group partials, stamps) is
-// written with device-coherent stores and read with device-coherent loads,
-// which are served at the level all of the device's L2s share; a writer waits
-// for its data stores to complete before it publishes a stamp.  No L2-wide
-// write-back or invalidate is issued.
+// Ordering around each boundary is decided from the step's buffers when the
+// plan is made: activations no earlier group writes are read ahead of the
+// barrier with ordinary loads; outputs a later group reads or rewrites are
+// acknowledged before the stamp; activations an earlier group wrote are read
+// after it, device-coherently unless no cache can hold a stale copy of their
+// lines.  Outputs and stamps are written with device-coherent stores.  No
+// L2-wide write-back or invalidate is issued.
 //
 // Waits are bounded: a wait that exceeds its spin limit sets an error word
 // and every later wait is skipped, so the kernel always finishes.
@@ -55,8 +65,8 @@ namespace {
 constexpr int kWaves = 16;
 constexpr int kCtl = 15;                // the control wave
 // Compute waves are waves 0 .. 14: the first kCtl - R stream continuously,
-// the last R (a kernel template parameter) load only while the workgroup
-// stalls.  The plan picks R from the step's shape (see plan_create).
+// the last R (a kernel template parameter, chosen per format and row count
+// from measurements; see kernel_ptr) load only while the workgroup stalls.
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
 
 // Ordering a group needs around its boundary, from the plan's overlap
@@ -204,15 +214,17 @@ struct Sched {
 struct TileRef {
   int g;      // group (ngroups: no tile)
   int j;      // super-block within the row
-  int rel;    // tile index relative to the first row-group of the range (t - rg0 J)
-  int seg;    // row-group relative to the first row-group of the range
-  int nv;     // (units) row-groups the unit holds
+  int rel;    // partial slot: the tile's index in the workgroup's range of the group
+              // (row-group major; a unit's: its first tile's)
+  int seg;    // row-group within the range (a unit's: its first)
+  int nv;     // units: row-groups the unit holds
 };
 
 struct IssueCursor {
   int g;                // current group (-1 before the first)
   int off_next;         // sequence index where the next group starts
-  int u, seg, j;        // last issued tile: index within the workgroup's part, (segment, super-block)
+  int u, seg, j;        // last issued tile (or unit): index within the workgroup's part,
+                        // (segment, super-block); for units seg counts units
   int J, rg0, nseg;
   int mem, mem_last;
 };
@@ -501,9 +513,10 @@ __device__ __forceinline__ float4_t tile_mfma(const Tile4& T, const u32x4 (&xa)[
 // group's activations are staged, then waits for the next stall.
 //
 // Both wait for "activations of group g staged" (one workgroup barrier per
-// group).  After each tile a wave writes the tile's 16 row partials to their
-// own LDS slot and counts the tile against its row-group, so the control wave
-// can finish a row-group as soon as its last tile is in.
+// group).  After each tile a wave writes the tile's partials (16 row sums;
+// 16 x 16 at up to 16 token rows) to their own LDS slot and counts the tile
+// against its row-group, so the control wave can finish a row-group as soon
+// as its last tile is in.
 template <int FMT, int MT, int U> struct RingOf { using type = typename Fmt<FMT>::Tile; };
 template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>; };
 
@@ -665,9 +678,9 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
 // so staging costs one memory round trip whatever K is.  The prologue then
 // runs in place: each lane rewrites the 8-value chunks its own loads brought.
 // POLICY: device-coherent for activations an earlier group of the step may
-// have written; cached for the others, which nothing in the step writes, so
-// the workgroups of an XCD share one L2 copy (8B step 1367-1372 vs 1375-1378
-// us coherent).
+// have written (unless no cache can hold a stale copy of their lines); cached
+// for the others, so the workgroups of an XCD share one L2 copy (8B step
+// 1367-1372 vs 1375-1378 us coherent).
 template <int FMT, bool GLUE, int POLICY = kPolicyCoherent>
 __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
                                               float* xsum) {
@@ -791,9 +804,10 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cn
 
 // Reduce the compute waves' partials of group g row-group by row-group, as
 // each row-group's last tile is counted, and write its rows.  The sum over a
-// row-group's tiles is taken in a fixed order (tiles t = q mod 4 per
-// quarter-wave, then the four quarters), whichever wave computed which tile,
-// so results are deterministic.
+// row-group's tiles is taken in a fixed order whichever wave computed which
+// tile (one row: tiles t = q mod 4 per quarter-wave, then the four quarters;
+// up to 16 rows: each lane its float4 over the tiles in order), so results
+// are deterministic.
 template <int FMT, bool GLUE, int MT>
 __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
                              uint32_t* cnt, int* stalled, bool& dead) {
