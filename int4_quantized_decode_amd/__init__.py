@@ -213,8 +213,9 @@ class StackPlan:
 
     @property
     def persistent(self) -> bool:
-        """True if runs use the one-launch persistent kernel, False if they
-        replay per-group launches."""
+        """True if runs use the persistent kernel (one launch per step; at
+        m > 1 a small activation-copy launch first), False if they replay the
+        per-group launches."""
         v = ctypes.c_int32(0)
         check(lib.qd_stack_plan_is_persistent(self._h, ctypes.byref(v)), "qd_stack_plan_is_persistent")
         return bool(v.value)
