@@ -64,9 +64,11 @@ struct ASrc {
 };
 
 // Called by every thread of the workgroup (it may hold a barrier).  Under
-// RMSNorm, wave w forms the factor of tokens w, w + WAVES, ...: each lane
-// sums the squares of its 8-value chunks with eight loads in flight, then the
-// wave adds the lanes' sums in a fixed order.
+// RMSNorm, wave w forms the factors of tokens w, w + WAVES, ..., two tokens
+// per pass: each lane sums the squares of its 8-value chunks with sixteen
+// loads in flight (one memory round trip per two tokens: this runs before the
+// workgroup's first product), then the wave adds the lanes' sums in a fixed
+// order.
 template <int WAVES, int PRO>
 __device__ inline ASrc make_asrc(const LinearArgs& a, int m_row, int wave, int lane) {
   const uint32_t xbytes = (uint32_t)(a.m * a.k * 2);
@@ -79,18 +81,31 @@ __device__ inline ASrc make_asrc(const LinearArgs& a, int m_row, int wave, int l
   if constexpr (rms) {
     __shared__ float rinv[QD_MAX_M];
     const int64_t K = a.k;
-    for (int t = wave; t < a.m; t += WAVES) {
-      float ss = 0.0f;
+    for (int t0 = wave; t0 < a.m; t0 += 2 * WAVES) {
+      // The second token may be past m: its loads fall outside the buffer
+      // (zeros, no traffic) and its factor is not stored.
+      const int t1 = t0 + WAVES;
+      float ss0 = 0.0f, ss1 = 0.0f;
       for (int64_t i0 = lane * 8; i0 < K; i0 += 512 * 8) {
-        u32x4 v[8];
+        u32x4 v0[8], v1[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = bload16(s.rx, (uint32_t)((t * K + i0 + 512 * u) * 2));
+        for (int u = 0; u < 8; ++u) {
+          v0[u] = bload16(s.rx, (uint32_t)((t0 * K + i0 + 512 * u) * 2));
+          v1[u] = bload16(s.rx, (uint32_t)((t1 * K + i0 + 512 * u) * 2));
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (i0 + 512 * u < K) ss = sumsq8(v[u], ss);
+          if (i0 + 512 * u < K) {
+            ss0 = sumsq8(v0[u], ss0);
+            ss1 = sumsq8(v1[u], ss1);
+          }
       }
-      ss = wave_sum(ss);
-      if (lane == 0) rinv[t] = rms_inverse(ss, K, a.eps);
+      ss0 = wave_sum(ss0);
+      ss1 = wave_sum(ss1);
+      if (lane == 0) {
+        rinv[t0] = rms_inverse(ss0, K, a.eps);
+        if (t1 < a.m) rinv[t1] = rms_inverse(ss1, K, a.eps);
+      }
     }
     __syncthreads();
     s.r = m_row < a.m ? rinv[m_row] : 0.0f;
