@@ -221,13 +221,16 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * in `ops` must stay valid while the plan lives.  qd_stack_plan_run enqueues
  * one step on `stream` (at m > 1 a small copy kernel for the activations no
  * op of the step writes, then the persistent kernel) and allocates nothing.  A plan may be run repeatedly but not
- * concurrently.  The persistent kernel takes steps of one format, int8 b32
- * or INT4 g64 at m = 1 (with or without glue) and int8 b32 at m = 2..16
- * (without glue).  Steps it does not take (fp16 weights, INT4 at m > 1,
- * mixed formats, a schedule larger than one CU's LDS, a single row-group too
- * long for it at m > 1, glue at m > 1) are replayed as the same per-group
- * launches decode_linear_stack makes, with the same results;
- * qd_stack_plan_is_persistent tells which.
+ * concurrently.  The persistent kernel takes groups of one format, int8
+ * b32 or INT4 g64 at m = 1 (with or without glue) and int8 b32 at m = 2..16
+ * (without glue).  It runs the step's leading groups that qualify; from the
+ * first group that does not (say an fp16 head), the rest of the step is
+ * replayed after it as the same per-group launches decode_linear_stack
+ * makes.  A step whose first group does not qualify (fp16 weights, INT4 at
+ * m > 1, glue at m > 1), or whose schedule is larger than one CU's LDS or has
+ * a row-group too long for it at m > 1, is replayed whole, with the same
+ * results as decode_linear_stack; qd_stack_plan_is_persistent tells whether
+ * the persistent kernel runs.
  */
 typedef struct qd_stack_plan qd_stack_plan;
 

@@ -1058,6 +1058,7 @@ struct qd_stack_plan {
   int fmt = 0;
   bool multi = false;                    // m > 1
   bool glue = false;                     // one token row with a prologue or an epilogue
+  std::vector<qd::StackGroup> tail;      // groups replayed after the persistent kernel
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (K = 0, mixed formats, glue, ...)
   void* tables = nullptr;
   void* scratch = nullptr;
@@ -1296,32 +1297,38 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   if (!plan) return QD_ELAUNCH;
   plan->device = dev;
 
-  // Persistent walker: one format, no empty-K groups, no glue; one token row,
-  // or up to 16 with int8 weights.
+  // Persistent walker: one format, no empty-K groups; one token row (with or
+  // without glue), or up to 16 with int8 weights and no glue.  The leading
+  // groups that qualify run in the persistent kernel; from the first group
+  // that does not (another format, say an fp16 head), the rest of the step
+  // is replayed as per-group launches after it on the same stream.
   std::vector<HostGroup> groups;
   const bool multi = m > 1;
   bool glue = false;
   bool ok = (m >= 1 && m <= 16);
   int fmt = 0;
+  int64_t split = n_ops;                 // first op replayed after the persistent kernel
   for (int64_t i = 0; ok && i < n_ops;) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
     HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, {}, 0,
                  ops[i].gamma, ops[i].prologue, ops[i].eps};
+    bool gok = true, gglue = false;
+    int gfmt = fmt;
     for (int64_t q = i; q < e; ++q) {
       if (ops[q].w.n == 0) continue;
-      if (ops[q].w.k == 0) ok = false;
-      if (fmt == 0) fmt = ops[q].w.fmt;
-      if (ops[q].w.fmt != fmt) ok = false;
-      if (fmt != QD_FMT_INT8_B32 && fmt != QD_FMT_INT4_G64) ok = false;   // fp16: replay
+      if (ops[q].w.k == 0) gok = false;
+      if (gfmt == 0) gfmt = ops[q].w.fmt;
+      if (ops[q].w.fmt != gfmt) gok = false;
+      if (gfmt != QD_FMT_INT8_B32 && gfmt != QD_FMT_INT4_G64) gok = false;   // fp16: replay
       // INT4 at several token rows: replay.  Its persistent instance passed
       // every parity test but one longer device run of it ended in a memory
       // fault whose cause is not found; it stays off until one is.
-      if (multi && fmt != QD_FMT_INT8_B32) ok = false;
+      if (multi && gfmt != QD_FMT_INT8_B32) gok = false;
       // Glue (a prologue or an epilogue): at one token row only.
       if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) {
-        glue = true;
-        if (multi) ok = false;
+        gglue = true;
+        if (multi) gok = false;
       }
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
                                hg.R, ops[q].epilogue, ops[q].w.n, nullptr});
@@ -1329,9 +1336,17 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       hg.yt_off.push_back(-1);
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);
     }
+    if (!gok) {
+      split = i;
+      break;
+    }
+    fmt = gfmt;
+    glue = glue || gglue;
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
     i = e;
   }
+  std::vector<StackGroup> tail;
+  if (ok && split < n_ops && build_groups(ops + split, n_ops - split, m, &tail) != QD_OK) ok = false;
   int cus = 0;
   if (ok && !groups.empty()) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -1551,6 +1566,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   plan->fmt = fmt;
   plan->multi = multi;
   plan->glue = glue;
+  plan->tail = std::move(tail);
   plan->persistent = true;
   *out = plan;
   return QD_OK;
@@ -1573,6 +1589,8 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
     --plan->epoch;
     return QD_ELAUNCH;
   }
+  // The groups after the persistent part, in stream order behind it.
+  if (!plan->tail.empty() && launch_groups(plan->tail, s) != hipSuccess) return QD_ELAUNCH;
   return QD_OK;
 }
 

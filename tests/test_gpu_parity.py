@@ -309,7 +309,8 @@ def test_stack_parity(qd, fmt, m):
 @pytest.mark.parametrize("m", [1, 16])
 def test_stack_mixed_formats_fp16_head(qd, m):
     """The int8lin variant's step shape: int8 b32 body groups and an fp16 head
-    group in one stack (per-group launches; the plan replays them)."""
+    group in one stack (per-group launches; the plan runs the body in the
+    persistent kernel and replays the head's launch after it)."""
     ops, meta = _tiny_decoder_ops(qd, "int8_b32", m, layers=2)
     hidden = meta[-1][1].shape[1]
     w_head = si.weights(si.seed_for("fp16-head"), 1000, hidden)
@@ -324,7 +325,7 @@ def test_stack_mixed_formats_fp16_head(qd, m):
             op.y.fill_(float("nan"))
         if use_plan:
             plan = qd.StackPlan(ops, m)
-            assert not plan.persistent
+            assert plan.persistent
             plan.run()
         else:
             qd.decode_linear_stack(ops, m)
@@ -611,9 +612,10 @@ def test_stack_full_size_sampled_fp16_head(qd):
     for op in ops:
         op.y.fill_(float("nan"))
     plan = qd.StackPlan(ops, 1)
-    assert not plan.persistent                      # mixed formats replay the launches
+    assert plan.persistent                          # int8 body persistent, fp16 head replayed after it
     plan.run()
     torch.cuda.synchronize()
+    assert plan.error() == 0
     wl = si.WORKLOADS[workload]
     names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
     for op in ops:
@@ -630,6 +632,48 @@ def test_stack_full_size_sampled_fp16_head(qd):
         parts = _oracle_parts(fmt, w_rows)
         check_vector(_host(op.y)[rows], linear.ref_linear(fmt, parts, x), linear.row_max_abs(fmt, parts),
                      x, f"{name} ({fmt})")
+    plan.close()
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_plan_persistent_prefix_and_replayed_tail(qd, m):
+    """A step whose first group qualifies for the persistent kernel and whose
+    later groups do not all qualify: int8 -> fp16 -> int8, each group reading
+    the one before it.  The plan runs the first group persistently and
+    replays the other two after it; each output matches the oracle on the
+    fp16 input the device produced, and repeated runs are bit-identical."""
+    from int4_quantized_decode_amd import LinearOp
+    k0, n0, n1, n2 = 1024, 2048, 1536, 640
+    w0 = si.weights(si.seed_for("tail-w0"), n0, k0)
+    w1 = si.weights(si.seed_for("tail-w1"), n1, n0)
+    w2 = si.weights(si.seed_for("tail-w2"), n2, n1)
+    x0 = si.activations(si.seed_for("tail-x0", m), m, k0)
+    shape = (lambda n: (m, n) if m > 1 else (n,))
+    ys = [torch.full(shape(n), float("nan"), dtype=torch.float16, device=DEV) for n in (n0, n1, n2)]
+    ops = [LinearOp(qd.qpack_int8_b32(_gpu(w0)), _gpu(x0.reshape(shape(k0))), ys[0], 0),
+           LinearOp(qd.qpack_fp16(_gpu(w1)), ys[0], ys[1], 1),
+           LinearOp(qd.qpack_int8_b32(_gpu(w2)), ys[1], ys[2], 2)]
+    plan = qd.StackPlan(ops, m)
+    assert plan.persistent
+    first = None
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        outs = [_host(y).reshape(m, -1).copy() for y in ys]
+        if first is None:
+            first = outs
+        else:
+            for a_, b_ in zip(first, outs):
+                assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
+    xs = [x0, first[0].astype(np.float64), first[1].astype(np.float64)]
+    for i, (fmt, w) in enumerate((("int8_b32", w0), ("fp16", w1), ("int8_b32", w2))):
+        parts = _oracle_parts(fmt, w)
+        Y_ref = linear.ref_linear(fmt, parts, xs[i]).reshape(m, -1)
+        for t in range(m):
+            check_vector(first[i][t], Y_ref[t], linear.row_max_abs(fmt, parts), xs[i][t], f"group {i} token {t}")
     plan.close()
 
 
