@@ -635,6 +635,35 @@ def test_stack_full_size_sampled_fp16_head(qd):
     plan.close()
 
 
+def test_plan_multi_token_longest_k(qd):
+    """The 16-token persistent step at the longest K the packers accept
+    (K = 24576, 96 super-blocks: exactly the per-workgroup tile budget, one
+    row-group per workgroup, so 263 row-groups split into two row ranges),
+    against the oracle on every token row, and repeated runs bit-identical.
+    Every valid K therefore fits that budget."""
+    from int4_quantized_decode_amd import LinearOp
+    m, n, k = 16, 4200, 24576
+    w = si.weights(si.seed_for("longk-w", k), n, k)
+    X = si.activations(si.seed_for("longk-x", k), m, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+    plan = qd.StackPlan([LinearOp(qd.qpack_int8_b32(_gpu(w)), _gpu(X), y, 0)], m)
+    assert plan.persistent
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    Y = _host(y).copy()
+    y.fill_(float("nan"))
+    plan.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(y).view(np.uint16), Y.view(np.uint16))
+    parts = quant.quantize_int8_b32(w)
+    Y_ref = linear.ref_linear("int8_b32", parts, X)
+    rmax = linear.row_max_abs("int8_b32", parts)
+    for t in range(m):
+        check_vector(Y[t], Y_ref[t], rmax, X[t], f"K={k} token {t}")
+    plan.close()
+
+
 @pytest.mark.parametrize("m", [1, 4])
 def test_plan_persistent_prefix_and_replayed_tail(qd, m):
     """A step whose first group qualifies for the persistent kernel and whose
