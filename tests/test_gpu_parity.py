@@ -526,7 +526,26 @@ def _sample_picks(decoder):
     return ["L0.q", "L0.k", f"L{mid}.gate", f"L{mid}.up", f"L{last}.down", f"L{last}.o", "head"]
 
 
+def test_single_gemv_config_bench_path(qd):
+    """The single 2048 x 2048 int8 GEMV configuration through the bench's own
+    builder and launch path (qgemv via decode_linear_stack), every output
+    against the oracle."""
+    import bench
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, "gemv-2048x2048-int8", DEV)
+    assert len(ops) == 1 and m == 1
+    op = ops[0]
+    op.y.fill_(float("nan"))
+    qd.decode_linear_stack(ops, 1)
+    torch.cuda.synchronize()
+    w = si.weights_torch(si.matrix_seed("single", "W"), 2048, 2048, DEV).cpu().numpy()
+    parts = quant.quantize_int8_b32(w)
+    x = op.x.cpu().numpy()
+    check_vector(_host(op.y), linear.ref_linear("int8_b32", parts, x), linear.row_max_abs("int8_b32", parts),
+                 x, "C1 2048x2048")
+
+
 @pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int4-m1", "qwen3.8-27b-int8-m1",
+                                      "qwen3-2b-int8-m1", "qwen3-4b-int8-m1",
                                       "qwen3-8b-int8-chain-m1", "qwen3-8b-int8-m16",
                                       "qwen3-8b-int8-chain-m16",
                                       pytest.param("qwen3-8b-int4-m16", marks=INT4_M16_OFF),
