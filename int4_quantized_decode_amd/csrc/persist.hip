@@ -826,7 +826,19 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
       // Each lane sums its float4 over the row-group's tiles in tile order.
       const float4_t* r4 = reinterpret_cast<const float4_t*>(red);
       float4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int r = s * J; r < (s + 1) * J; ++r) {
+      int r = s * J;
+      const int rend = (s + 1) * J;
+      // Four partials' reads ahead of their adds (same order of addition).
+      for (; r + 4 <= rend; r += 4) {
+        float4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = r4[(r + u) * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[i] += v[u][i];
+      }
+      for (; r < rend; ++r) {
         const float4_t v = r4[r * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sum[i] += v[i];
@@ -835,8 +847,19 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
       store_rows16<FMT>(p, S, g, rg0 + s, lane, sum);
       continue;
     }
+    // This runs on the group's critical path for its last row-group: four
+    // partials' reads ahead of their adds (same order of addition).
     float part = 0.0f;
-    for (int r = s * J + q; r < (s + 1) * J; r += 4) part += red[r * 16 + row];
+    int r = s * J + q;
+    const int rend = (s + 1) * J;
+    for (; r + 12 < rend; r += 16) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = red[(r + 4 * u) * 16 + row];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) part += v[u];
+    }
+    for (; r < rend; r += 4) part += red[r * 16 + row];
     const float sum = quad_reduce(part);
     if (lane == 0) cnt[s] = 0u;                // ready for the next group
     if (lane < 16) store_row<GLUE>(S, g, rg0 + s, row, sum);
