@@ -910,7 +910,18 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
   return __ballot(!ok) == 0ull;
 }
 
-__device__ void wait_group(const PlanArgs& p, int g, int lane) {
+// Sleeps of 512 cycles before the first poll (see wait_group), per path,
+// measured: one token row, before a dependent group (8B chained step 1505
+// with 2, 1543 with none; 1 and 4 took 1513 and 1516 us), and up to 16 token
+// rows (8B step 2025 with 6, 2118 with none; 2, 4 and 8 took 2063, 2037 and
+// 2023, the chained step 2065 with 6 and 2085 with 8).
+#ifndef QD_POLL_DELAY
+#define QD_POLL_DELAY 2
+#endif
+#ifndef QD_POLL_DELAY16
+#define QD_POLL_DELAY16 6
+#endif
+__device__ void wait_group(const PlanArgs& p, int g, int lane, int delay) {
   if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
@@ -918,6 +929,12 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane) {
   // kPollDepth polls in flight: each check consumes the oldest and issues a
   // new one, so a stamp is seen about one poll interval after it lands.
   u32x4 v[kPollDepth][4];
+  // Called straight after the workgroup's own stamp, a first poll would find
+  // most stamps missing, and every poll is a device-coherent read queued with
+  // the weight stream: wait a fraction of a microsecond first.  (When the
+  // next activations are staged before the wait, that round trip already
+  // spaces the poll out: no delay.)
+  for (int d = 0; d < delay; ++d) __builtin_amdgcn_s_sleep(8);
 #pragma unroll
   for (int i = 0; i < kPollDepth - 1; ++i) poll_stamps(rf, lane, v[i]);
   bool done = false;
@@ -960,7 +977,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
       // and needs what g needed, which g's own boundary already waited for.
-      if (!(S.order(g + 1) & kNoWait)) wait_group(p, g, lane);
+      if (!(S.order(g + 1) & kNoWait))
+        wait_group(p, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
         else stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
