@@ -242,6 +242,12 @@ qd_status qd_stack_plan_run(qd_stack_plan* plan, void* stream);
 qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error);
 /* *out = 1 if runs use the persistent kernel, 0 if they replay launches. */
 qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out);
+/* Diagnostics (not part of the method): bound every wait of the persistent
+ * kernel by `polls` polls (default 2^20, about a second) for the following
+ * runs.  A small bound makes waits time out, which exercises the error word:
+ * such a run's outputs are incomplete and qd_stack_plan_error reports it.
+ * No effect on plans that replay launches.  QD_EINVAL for a null plan. */
+qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
 void qd_stack_plan_destroy(qd_stack_plan* plan);
 
 /*

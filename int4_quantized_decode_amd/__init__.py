@@ -220,6 +220,11 @@ class StackPlan:
         check(lib.qd_stack_plan_is_persistent(self._h, ctypes.byref(v)), "qd_stack_plan_is_persistent")
         return bool(v.value)
 
+    def set_spin_limit(self, polls: int) -> None:
+        """Diagnostics: bound every wait of the persistent kernel by `polls`
+        polls for the following runs (default 2**20, about a second)."""
+        check(lib.qd_stack_plan_set_spin_limit(self._h, polls), "qd_stack_plan_set_spin_limit")
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             lib.qd_stack_plan_destroy(self._h)

@@ -218,6 +218,12 @@ QD_EXPORT qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32
   return QD_OK;
 }
 
+QD_EXPORT qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls) {
+  if (!plan) return QD_EINVAL;
+  plan_set_spin_limit(plan, polls);
+  return QD_OK;
+}
+
 QD_EXPORT void qd_stack_plan_destroy(qd_stack_plan* plan) { plan_destroy(plan); }
 
 // ---- validation helpers shared with stack.hip --------------------------------

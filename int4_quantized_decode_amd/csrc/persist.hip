@@ -67,7 +67,8 @@ constexpr int kCtl = 15;                // the control wave
 // Compute waves are waves 0 .. 14: the first kCtl - R stream continuously,
 // the last R (a kernel template parameter, chosen per format and row count
 // from measurements; see kernel_ptr) load only while the workgroup stalls.
-constexpr uint32_t kSpinLimit = 1u << 20;   // polls (each a device-coherent round trip): ~1 s
+constexpr uint32_t kSpinLimit = 1u << 20;   // default wait bound, polls (each a device-coherent
+                                            // round trip): ~1 s; a plan may set another
 
 // Ordering a group needs around its boundary, from the plan's overlap
 // analysis of the step's buffers.
@@ -130,6 +131,7 @@ struct PlanArgs {
   int32_t cnt_bytes;
   int32_t tab_bytes;
   int32_t m;                  // token rows (1 .. 16)
+  uint32_t spin_limit;        // bound of every wait, in polls
 };
 
 template <int FMT> struct Fmt;
@@ -619,7 +621,7 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       // Wait for the stall that ends group `trig` (or, should it have been
       // missed, for the next activations: then nothing is issued).
       for (uint32_t spins = 0;
-           lds_get(stalled) < trig && lds_get(staged) <= trig && spins < kSpinLimit; ++spins)
+           lds_get(stalled) < trig && lds_get(staged) <= trig && spins < p.spin_limit; ++spins)
         __builtin_amdgcn_s_sleep(1);
       // Issue at a bounded rate rather than all at once (the control wave's
       // stores and loads on the boundary's critical path queue behind what
@@ -793,7 +795,7 @@ __device__ __forceinline__ void store_rows16(const PlanArgs& p, const Sched& S, 
 __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cnt, int seg,
                                            uint32_t want, bool& dead) {
   for (uint32_t spins = 0; !dead && lds_get(cnt + seg) < want; ++spins) {
-    if (spins > kSpinLimit) {
+    if (spins > p.spin_limit) {
       atomicOr(p.err, 2u);
       dead = true;
     }
@@ -944,7 +946,7 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane, int delay) {
       poll_stamps(rf, lane, v[(i + kPollDepth - 1) % kPollDepth]);
       if (!done && stamps_reached(v[i], p.G, lane, target)) done = true;
     }
-    if (!done && spins > kSpinLimit) {
+    if (!done && spins > p.spin_limit) {
       if (lane == 0) atomicOr(p.err, 1u);
       break;
     }
@@ -1602,6 +1604,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.cnt_bytes = (int32_t)cnt_bytes;
   a.tab_bytes = (int32_t)tab_bytes;
   a.m = (int32_t)m;
+  a.spin_limit = kSpinLimit;
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = fmt;
@@ -1653,6 +1656,8 @@ qd_status plan_error(qd_stack_plan* plan, int32_t* out_error) {
 }
 
 bool plan_is_persistent(const qd_stack_plan* plan) { return plan->persistent; }
+
+void plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls) { plan->args.spin_limit = polls; }
 
 void plan_destroy(qd_stack_plan* plan) {
   if (!plan) return;

@@ -23,6 +23,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
 qd_status plan_run(qd_stack_plan* plan, hipStream_t s);
 qd_status plan_error(qd_stack_plan* plan, int32_t* out_error);
 bool plan_is_persistent(const qd_stack_plan* plan);
+void plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
 void plan_destroy(qd_stack_plan* plan);
 
 }  // namespace qd

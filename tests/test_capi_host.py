@@ -114,6 +114,7 @@ def test_stack_validation_errors(L):
     assert lib.qd_stack_plan_run(None, None) == 1
     v = ctypes.c_int32(5)
     assert lib.qd_stack_plan_is_persistent(None, ctypes.byref(v)) == 1
+    assert lib.qd_stack_plan_set_spin_limit(None, 0) == 1
 
 
 def test_read_probe_validation_errors(L):

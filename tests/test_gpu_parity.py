@@ -654,6 +654,43 @@ def test_stack_full_size_sampled_fp16_head(qd):
     plan.close()
 
 
+@pytest.mark.parametrize("m", [1, 16])
+def test_plan_wait_timeout_reported_and_recovers(qd, m):
+    """The persistent kernel's waits are bounded.  With the bound set to no
+    polls from the host, waits time out: the run still ends, the error word
+    reports it, and the plan resets its scratch; with the default bound
+    restored the next run is correct (oracle parity on a chained step)."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 1024
+    ws = [si.weights(si.seed_for("timeout-w", g), k, k) for g in range(3)]
+    x0 = si.activations(si.seed_for("timeout-x", m), m, k)
+    shape = (m, k) if m > 1 else (k,)
+    ys = [torch.empty(shape, dtype=torch.float16, device=DEV) for _ in range(3)]
+    xs = [_gpu(x0.reshape(shape)), ys[0], ys[1]]
+    ops = [LinearOp(qd.qpack_int8_b32(_gpu(w)), xs[g], ys[g], g) for g, w in enumerate(ws)]
+    plan = qd.StackPlan(ops, m)
+    assert plan.persistent
+    plan.set_spin_limit(0)
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() != 0
+    plan.set_spin_limit(1 << 20)
+    for y in ys:
+        y.fill_(float("nan"))
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    x = x0.astype(np.float64)
+    for g, w in enumerate(ws):
+        parts = quant.quantize_int8_b32(w)
+        Y = _host(ys[g]).reshape(m, k)
+        Y_ref = linear.ref_linear("int8_b32", parts, x).reshape(m, k)
+        for t in range(m):
+            check_vector(Y[t], Y_ref[t], linear.row_max_abs("int8_b32", parts), x[t], f"group {g} token {t}")
+        x = Y.astype(np.float64)
+    plan.close()
+
+
 def test_plan_multi_token_longest_k(qd):
     """The 16-token persistent step at the longest K the packers accept
     (K = 24576, 96 super-blocks: exactly the per-workgroup tile budget, one
