@@ -248,6 +248,37 @@ qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out);
  * such a run's outputs are incomplete and qd_stack_plan_error reports it.
  * No effect on plans that replay launches.  QD_EINVAL for a null plan. */
 qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
+/* Diagnostics (not part of the method): the schedule qd_stack_plan_create
+ * would build for `ops` on a device of `workgroups` compute units, computed
+ * on the host alone (no device call; the pointers in `ops` are only compared
+ * and offset, never dereferenced, so any values that pass the validation of
+ * decode_linear_stack will do).  Writes int64 words to `out` (host memory,
+ * caller-owned) and their count to *out_len:
+ *   header, 16 words: version (1), persistent (0/1), format, m, glue (0/1),
+ *     prefix ops (ops [0, prefix) run in the persistent kernel, the rest are
+ *     replayed after it), groups G_n, members M_n, workgroups W, bytes of the
+ *     activation copies, copy jobs J_n, dynamic LDS bytes, then LDS bytes of
+ *     the staged activations, the tile partials, the row-group counters and
+ *     the schedule tables;
+ *   G_n groups of 10 words, in the order the kernel runs them: x, gamma, K,
+ *     super-blocks J, row-groups R, first member, members, prologue, order
+ *     flags (1 = may stage early, 2 = acknowledges its stores before its
+ *     stamp, 4 = waits for nothing (a later row range of a split group),
+ *     8 = reads its activations through the caches), offset of its activation
+ *     copy in the plan's copies or -1;
+ *   M_n members of 7 words: weight blob, y, rows N, first row-group within
+ *     the group, epilogue, elements between token rows of y, offset of the
+ *     copy of its outputs or -1;
+ *   G_n x W schedule entries of 4 words, group-major: tiles, tiles of this
+ *     workgroup in earlier groups, first row-group, row-groups;
+ *   J_n copy jobs of 4 words: x, offset of its copy, K, first block.
+ * A step that replays whole gives the header alone.  With cap below the
+ * count, *out_len is still set and nothing is written: QD_OK when out is
+ * NULL (a size query), else QD_ESHAPE.  QD_EINVAL for a null out_len, a
+ * negative cap or workgroups outside 1..512; otherwise the status
+ * decode_linear_stack's validation gives. */
+qd_status qd_stack_plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,
+                                 int64_t* out, int64_t cap, int64_t* out_len);
 void qd_stack_plan_destroy(qd_stack_plan* plan);
 
 /*

@@ -191,6 +191,23 @@ def decode_linear_stack(ops, m: int = 1) -> None:
     check(lib.decode_linear_stack(arr, len(ops), m, _stream()), "decode_linear_stack")
 
 
+def describe_stack_plan(ops, m: int = 1, workgroups: int | None = None) -> list:
+    """Diagnostics: the int64 words of qd_stack_plan_describe for `ops`, the
+    schedule a plan gets on a device of `workgroups` compute units (default:
+    the current device's).  Host-only; the word layout is in
+    include/qdecode.h."""
+    if workgroups is None:
+        workgroups = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    arr = _op_array(ops)
+    n = ctypes.c_int64(0)
+    check(lib.qd_stack_plan_describe(arr, len(ops), m, workgroups, None, 0, ctypes.byref(n)),
+          "qd_stack_plan_describe")
+    buf = (ctypes.c_int64 * n.value)()
+    check(lib.qd_stack_plan_describe(arr, len(ops), m, workgroups, buf, n.value, ctypes.byref(n)),
+          "qd_stack_plan_describe")
+    return list(buf)
+
+
 class StackPlan:
     """A validated decode step kept on the device; run() enqueues one step.
 

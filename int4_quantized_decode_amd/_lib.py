@@ -67,6 +67,9 @@ SIGNATURES = {
     "qd_stack_plan_error": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "qd_stack_plan_is_persistent": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "qd_stack_plan_set_spin_limit": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint32]),
+    "qd_stack_plan_describe": (ctypes.c_int32, [ctypes.POINTER(QDLinearOp), ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                                ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "qd_read_probe": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p]),
     "qd_stack_plan_destroy": (None, [ctypes.c_void_p]),

@@ -226,6 +226,12 @@ QD_EXPORT qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t p
 
 QD_EXPORT void qd_stack_plan_destroy(qd_stack_plan* plan) { plan_destroy(plan); }
 
+QD_EXPORT qd_status qd_stack_plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,
+                                           int64_t* out, int64_t cap, int64_t* out_len) {
+  if (!out_len || cap < 0) return QD_EINVAL;
+  return plan_describe(ops, n_ops, m, workgroups, out, cap, out_len);
+}
+
 // ---- validation helpers shared with stack.hip --------------------------------
 
 namespace qd {

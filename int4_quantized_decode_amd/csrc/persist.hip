@@ -323,12 +323,19 @@ __device__ __forceinline__ Unit<FMT, U> issue_unit(const Sched& S, int ngroups, 
     }
     const int seg0 = c.seg * U;
     const int nv = min(U, c.nseg - seg0);
+    // The cursor follows the member of the unit's first row-group, which
+    // only moves forward along the sequence.  A unit's later row-groups may
+    // lie in the next members: each finds its own from there, without
+    // moving the cursor, since the unit's next super-block starts again
+    // from its first row-group.
+    while (c.mem < c.mem_last && c.rg0 + seg0 >= S.rg_begin(c.mem + 1)) ++c.mem;
 #pragma unroll
     for (int q = 0; q < U; ++q) {
       if (q < nv) {
         const int rg = c.rg0 + seg0 + q;
-        while (c.mem < c.mem_last && rg >= S.rg_begin(c.mem + 1)) ++c.mem;
-        base[q] = S.blob(c.mem) + ((int64_t)(rg - S.rg_begin(c.mem)) * c.J + c.j) * T;
+        int mi = c.mem;
+        while (mi < c.mem_last && rg >= S.rg_begin(mi + 1)) ++mi;
+        base[q] = S.blob(mi) + ((int64_t)(rg - S.rg_begin(mi)) * c.J + c.j) * T;
         nbytes[q] = T;
       }
     }
@@ -1328,18 +1335,29 @@ const void* kernel_ptr(int fmt, bool multi, bool glue) {
               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, kReserveInt4S, false, 1, 1>);
 }
 
-}  // namespace
+// The persistent step's tables, built on the host alone: the groups in step
+// order with their boundary ordering, their row-range split at several token
+// rows, the activation-copy slots, the per-workgroup schedules and the LDS
+// the kernel needs, for G workgroups.  Copy addresses are byte offsets into
+// the plan's copies until those exist.
+struct PlanLayout {
+  bool persistent = false;     // false: the whole step replays per-group launches
+  int fmt = 0;
+  bool multi = false, glue = false;
+  int64_t split = 0;           // ops [0, split) run in the persistent kernel; the rest replay after it
+  int G = 0;
+  std::vector<PGroup> pg;
+  std::vector<PMember> pm;
+  std::vector<PSched> ps;      // [group][workgroup]
+  std::vector<int64_t> xt_fix, yt_fix;   // per group / member: offset of its copy, or -1
+  std::vector<XtJob> jobs;     // copies made before each step (t holds the offset)
+  int64_t xt_total = 0, xt_blocks = 0;
+  size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
+};
 
-qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out) {
-  std::vector<StackGroup> replay;
-  qd_status st = build_groups(ops, n_ops, m, &replay);
-  if (st != QD_OK) return st;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return QD_EDEVICE;
-  qd_stack_plan* plan = new (std::nothrow) qd_stack_plan;
-  if (!plan) return QD_ELAUNCH;
-  plan->device = dev;
-
+void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanLayout* L) {
+  *L = PlanLayout{};
+  L->G = G;
   // Persistent walker: one format, no empty-K groups; one token row (with or
   // without glue), or up to 16 with int8 weights and no glue.  The leading
   // groups that qualify run in the persistent kernel; from the first group
@@ -1348,10 +1366,10 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   std::vector<HostGroup> groups;
   const bool multi = m > 1;
   bool glue = false;
-  bool ok = (m >= 1 && m <= 16);
+  if (m < 1 || m > 16 || G < 1 || G > kMaxWorkgroups) return;
   int fmt = 0;
-  int64_t split = n_ops;                 // first op replayed after the persistent kernel
-  for (int64_t i = 0; ok && i < n_ops;) {
+  int64_t split = n_ops;
+  for (int64_t i = 0; i < n_ops;) {
     int64_t e = i + 1;
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
     HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, {}, 0,
@@ -1388,24 +1406,9 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
     i = e;
   }
-  std::vector<StackGroup> tail;
-  if (ok && split < n_ops && build_groups(ops + split, n_ops - split, m, &tail) != QD_OK) ok = false;
-  int cus = 0;
-  if (ok && !groups.empty()) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0 || cus > kMaxWorkgroups)
-      ok = false;
-  } else {
-    ok = false;
-  }
-  if (!ok) {
-    plan->replay = std::move(replay);
-    *out = plan;
-    return QD_OK;
-  }
-
-  const int G = cus;
+  if (groups.empty()) return;
   order_groups(groups, m, tile_bytes(fmt));
+
   // Several token rows: copies of the activations in matrix-core order.  An
   // activation no group writes is copied before the step; one that is
   // exactly an earlier op's whole output (the last write to any of its
@@ -1443,41 +1446,40 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       if (p == SIZE_MAX) continue;
       const PMember& pq = groups[p].mem[q];
       if ((const void*)pq.y != (const void*)hg.x || pq.n != hg.k || pq.ld != hg.k) continue;
+      // The copy's order repeats every 256 rows, and a row range cut out of
+      // the member (split_rows, below) addresses its part of the copy by a
+      // plain offset: so every cut must fall a whole number of 256-row
+      // blocks into the member, else the member writes no copy.
+      const int64_t piece = (int64_t)(QD_PLAN_TILES16 / groups[p].J) * G;
+      const int64_t r0 = pq.rg_begin, r1 = r0 + ceil_div(pq.n, kTileRows);
+      bool cuts_aligned = true;
+      for (int64_t a = piece; piece > 0 && a < groups[p].R; a += piece)
+        if (a > r0 && a < r1 && (a - r0) % (256 / kTileRows) != 0) cuts_aligned = false;
+      if (!cuts_aligned) continue;
       auto it = out_slots.find(std::make_pair(p, q));
       if (it == out_slots.end()) it = out_slots.emplace(std::make_pair(p, q), new_slot(hg.J)).first;
       groups[p].yt_off[q] = it->second;
       hg.xt_off = it->second;
     }
   }
-  if (multi && !split_rows(groups, QD_PLAN_TILES16, G, tile_bytes(fmt))) {
-    plan->replay = std::move(replay);
-    *out = plan;
-    return QD_OK;
-  }
+  if (multi && !split_rows(groups, QD_PLAN_TILES16, G, tile_bytes(fmt))) return;
   const int ng = (int)groups.size();
-  std::vector<PGroup> pg(ng);
-  std::vector<PMember> pm;
-  std::vector<PSched> ps((size_t)ng * G);
+  L->pg.resize(ng);
+  L->ps.resize((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1;
-  std::vector<int64_t> xt_fix, yt_fix;   // copy offsets, made pointers once the copies exist
-  // A step the persistent walker cannot hold (tile counts past int32, LDS
-  // beyond one CU's) replays per-group launches instead.
-  auto fallback = [&]() {
-    plan->replay = std::move(replay);
-    *out = plan;
-    return QD_OK;
-  };
   for (int g = 0; g < ng; ++g) {
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
-    if (T > (int64_t)INT32_MAX / 2) return fallback();
-    pg[g] = PGroup{hg.x, hg.gamma, nullptr, hg.k, hg.J, hg.R, (int32_t)pm.size(), (int32_t)hg.mem.size(),
-                   hg.pro, hg.eps, hg.order, 0};
-    xt_fix.push_back(hg.xt_off);
+    // A step the persistent walker cannot hold (tile counts past int32)
+    // replays per-group launches instead.
+    if (T > (int64_t)INT32_MAX / 2) return;
+    L->pg[g] = PGroup{hg.x, hg.gamma, nullptr, hg.k, hg.J, hg.R, (int32_t)L->pm.size(), (int32_t)hg.mem.size(),
+                      hg.pro, hg.eps, hg.order, 0};
+    L->xt_fix.push_back(hg.xt_off);
     for (size_t b = 0; b < hg.mem.size(); ++b) {
-      pm.push_back(hg.mem[b]);
-      yt_fix.push_back(hg.yt_off[b]);
+      L->pm.push_back(hg.mem[b]);
+      L->yt_fix.push_back(hg.yt_off[b]);
     }
     maxJ = std::max(maxJ, hg.J);
     // halves of LDS the staging writes: x's span, and the second operand's
@@ -1495,7 +1497,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
       // Several token rows: the sequence holds units of QD_PLAN_UNIT16 row-groups.
       const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
       const int64_t n = (multi ? ceil_div(nrg, (int64_t)QD_PLAN_UNIT16) : nrg) * J;
-      ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
+      L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
       if (nrg == 0) continue;
       off[w] += (int32_t)n;
       maxRel = std::max<int>(maxRel, (int)(nrg * J));
@@ -1503,19 +1505,65 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     }
   }
   // Several token rows: no staged activations, and 16 x 16 partials per tile.
-  const size_t x_bytes = multi ? 0 : (size_t)maxXH * 2;      // a multiple of 1024
-  const size_t xsum_bytes = fmt == QD_FMT_INT4_G64 && !multi ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
-  const size_t red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
-  const size_t cnt_bytes = align_up((size_t)maxSeg * 4, 16);
-  const size_t tab_bytes = (size_t)ng * sizeof(PGroup) + pm.size() * sizeof(PMember) +
-                           (size_t)ng * sizeof(PSched);
-  const size_t lds = x_bytes + xsum_bytes + red_bytes + cnt_bytes + tab_bytes + 16;   // + counter, stall flag
+  L->x_bytes = multi ? 0 : (size_t)maxXH * 2;      // a multiple of 1024
+  L->xsum_bytes = fmt == QD_FMT_INT4_G64 && !multi ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
+  L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
+  L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
+  L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
+  L->lds = L->x_bytes + L->xsum_bytes + L->red_bytes + L->cnt_bytes + L->tab_bytes + 16;   // + counter, stall flag
+  int64_t blocks = 0;
+  for (XtJob& jb : jobs) {
+    jb.first_block = blocks;
+    blocks += 2 * ceil_div(jb.k, kSuperK);         // 512 chunks per super-block
+  }
+  L->jobs = std::move(jobs);
+  L->xt_total = xt_total;
+  L->xt_blocks = blocks;
+  L->fmt = fmt;
+  L->multi = multi;
+  L->glue = glue;
+  L->split = split;
+  L->persistent = true;
+}
+
+}  // namespace
+
+qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out) {
+  std::vector<StackGroup> replay;
+  qd_status st = build_groups(ops, n_ops, m, &replay);
+  if (st != QD_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QD_EDEVICE;
+  qd_stack_plan* plan = new (std::nothrow) qd_stack_plan;
+  if (!plan) return QD_ELAUNCH;
+  plan->device = dev;
+  // Whatever the persistent kernel cannot take replays per-group launches.
+  auto fallback = [&]() {
+    plan->replay = std::move(replay);
+    *out = plan;
+    return QD_OK;
+  };
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fallback();
+  }
+  PlanLayout L;
+  layout_plan(ops, n_ops, m, cus, &L);
+  if (!L.persistent) return fallback();
+  std::vector<StackGroup> tail;
+  if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) return fallback();
+  const int G = L.G, ng = (int)L.pg.size();
+  std::vector<PGroup>& pg = L.pg;
+  std::vector<PMember>& pm = L.pm;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
     delete plan;
     return QD_EDEVICE;
   }
-  const void* kfn = kernel_ptr(fmt, multi, glue);
+  // LDS beyond one CU's: replay.
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue);
+  const size_t lds = L.lds;
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
   if (lds > 65536 &&
@@ -1532,50 +1580,45 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
 
   // The activation copies (zeroed once: token rows past m and K positions
   // past K stay zero) and the table of copies made before each step.
-  if (xt_total > 0) {
-    int64_t blocks = 0;
-    for (XtJob& jb : jobs) {
-      jb.first_block = blocks;
-      blocks += 2 * ceil_div(jb.k, kSuperK);         // 512 chunks per super-block
-    }
+  if (L.xt_total > 0) {
     void* dj = nullptr;
-    if (hipMalloc(&plan->xt, (size_t)xt_total) != hipSuccess ||
-        hipMemset(plan->xt, 0, (size_t)xt_total) != hipSuccess ||
-        (!jobs.empty() && hipMalloc(&dj, sizeof(XtJob) * jobs.size()) != hipSuccess)) {
+    if (hipMalloc(&plan->xt, (size_t)L.xt_total) != hipSuccess ||
+        hipMemset(plan->xt, 0, (size_t)L.xt_total) != hipSuccess ||
+        (!L.jobs.empty() && hipMalloc(&dj, sizeof(XtJob) * L.jobs.size()) != hipSuccess)) {
       if (plan->xt) (void)hipFree(plan->xt);
       delete plan;
       return QD_ELAUNCH;
     }
     uint8_t* const xb = static_cast<uint8_t*>(plan->xt);
-    for (XtJob& jb : jobs) jb.t = reinterpret_cast<uint16_t*>(xb + reinterpret_cast<uintptr_t>(jb.t));
-    if (!jobs.empty() &&
-        hipMemcpy(dj, jobs.data(), sizeof(XtJob) * jobs.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    for (XtJob& jb : L.jobs) jb.t = reinterpret_cast<uint16_t*>(xb + reinterpret_cast<uintptr_t>(jb.t));
+    if (!L.jobs.empty() &&
+        hipMemcpy(dj, L.jobs.data(), sizeof(XtJob) * L.jobs.size(), hipMemcpyHostToDevice) != hipSuccess) {
       (void)hipFree(plan->xt);
       (void)hipFree(dj);
       delete plan;
       return QD_ELAUNCH;
     }
     plan->xt_jobs = dj;
-    plan->xt_njobs = (int)jobs.size();
-    plan->xt_blocks = blocks;
+    plan->xt_njobs = (int)L.jobs.size();
+    plan->xt_blocks = L.xt_blocks;
     for (int g = 0; g < ng; ++g)
-      if (xt_fix[g] >= 0) pg[g].xt = reinterpret_cast<const uint16_t*>(xb + xt_fix[g]);
+      if (L.xt_fix[g] >= 0) pg[g].xt = reinterpret_cast<const uint16_t*>(xb + L.xt_fix[g]);
     for (size_t i = 0; i < pm.size(); ++i)
-      if (yt_fix[i] >= 0) pm[i].yt = reinterpret_cast<uint16_t*>(xb + yt_fix[i]);
+      if (L.yt_fix[i] >= 0) pm[i].yt = reinterpret_cast<uint16_t*>(xb + L.yt_fix[i]);
   }
 
   // Device tables, then scratch.
   const size_t o_groups = 0;
   const size_t o_mem = align_up(o_groups + sizeof(PGroup) * ng, 256);
   const size_t o_sched = align_up(o_mem + sizeof(PMember) * pm.size(), 256);
-  const size_t t_bytes = align_up(o_sched + sizeof(PSched) * ps.size(), 256);
+  const size_t t_bytes = align_up(o_sched + sizeof(PSched) * L.ps.size(), 256);
   const size_t s_flags = 0;
   const size_t s_err = align_up(sizeof(unsigned long long) * G, 256);
   const size_t s_bytes = s_err + 256;
   std::vector<uint8_t> host(t_bytes, 0);
   memcpy(host.data() + o_groups, pg.data(), sizeof(PGroup) * ng);
   memcpy(host.data() + o_mem, pm.data(), sizeof(PMember) * pm.size());
-  memcpy(host.data() + o_sched, ps.data(), sizeof(PSched) * ps.size());
+  memcpy(host.data() + o_sched, L.ps.data(), sizeof(PSched) * L.ps.size());
   if (hipMalloc(&plan->tables, t_bytes) != hipSuccess ||
       hipMalloc(&plan->scratch, s_bytes) != hipSuccess ||
       hipMemcpy(plan->tables, host.data(), t_bytes, hipMemcpyHostToDevice) != hipSuccess ||
@@ -1598,21 +1641,55 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.ngroups = ng;
   a.nmem = (int32_t)pm.size();
   a.G = G;
-  a.x_bytes = (int32_t)x_bytes;
-  a.xsum_bytes = (int32_t)xsum_bytes;
-  a.red_bytes = (int32_t)red_bytes;
-  a.cnt_bytes = (int32_t)cnt_bytes;
-  a.tab_bytes = (int32_t)tab_bytes;
+  a.x_bytes = (int32_t)L.x_bytes;
+  a.xsum_bytes = (int32_t)L.xsum_bytes;
+  a.red_bytes = (int32_t)L.red_bytes;
+  a.cnt_bytes = (int32_t)L.cnt_bytes;
+  a.tab_bytes = (int32_t)L.tab_bytes;
   a.m = (int32_t)m;
   a.spin_limit = kSpinLimit;
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
-  plan->fmt = fmt;
-  plan->multi = multi;
-  plan->glue = glue;
+  plan->fmt = L.fmt;
+  plan->multi = L.multi;
+  plan->glue = L.glue;
   plan->tail = std::move(tail);
   plan->persistent = true;
   *out = plan;
+  return QD_OK;
+}
+
+qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,
+                        int64_t* out, int64_t cap, int64_t* out_len) {
+  if (workgroups < 1 || workgroups > kMaxWorkgroups) return QD_EINVAL;
+  std::vector<StackGroup> replay;
+  qd_status st = build_groups(ops, n_ops, m, &replay);
+  if (st != QD_OK) return st;
+  PlanLayout L;
+  layout_plan(ops, n_ops, m, workgroups, &L);
+  if (L.persistent) {
+    std::vector<StackGroup> tail;
+    if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) L = PlanLayout{};
+  }
+  std::vector<int64_t> v = {1, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
+                            (int64_t)L.pg.size(), (int64_t)L.pm.size(), L.G, L.xt_total,
+                            (int64_t)L.jobs.size(), (int64_t)L.lds, (int64_t)L.x_bytes,
+                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes};
+  auto addr = [](const void* p) { return (int64_t)(uintptr_t)p; };
+  for (size_t g = 0; g < L.pg.size(); ++g) {
+    const PGroup& p = L.pg[g];
+    v.insert(v.end(), {addr(p.x), addr(p.gamma), p.k, p.J, p.R, p.mem0, p.n_mem, p.pro, p.order, L.xt_fix[g]});
+  }
+  for (size_t i = 0; i < L.pm.size(); ++i) {
+    const PMember& p = L.pm[i];
+    v.insert(v.end(), {addr(p.blob), addr(p.y), p.n, p.rg_begin, p.epi, p.ld, L.yt_fix[i]});
+  }
+  for (const PSched& s : L.ps) v.insert(v.end(), {s.n, s.off, s.rg0, s.nseg});
+  for (const XtJob& j : L.jobs)
+    v.insert(v.end(), {addr(j.x), (int64_t)reinterpret_cast<uintptr_t>(j.t), j.k, j.first_block});
+  *out_len = (int64_t)v.size();
+  if (cap < (int64_t)v.size()) return out ? QD_ESHAPE : QD_OK;
+  std::copy(v.begin(), v.end(), out);
   return QD_OK;
 }
 

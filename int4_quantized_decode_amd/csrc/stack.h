@@ -25,5 +25,7 @@ qd_status plan_error(qd_stack_plan* plan, int32_t* out_error);
 bool plan_is_persistent(const qd_stack_plan* plan);
 void plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
 void plan_destroy(qd_stack_plan* plan);
+qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,
+                        int64_t* out, int64_t cap, int64_t* out_len);
 
 }  // namespace qd

@@ -865,6 +865,118 @@ def test_plan_multi_token_split_and_chain(qd, fmt):
         plan.close()
 
 
+@pytest.mark.parametrize("fmt", ["int8_b32", pytest.param("int4_g64", marks=INT4_M16_OFF)])
+def test_plan_multi_token_unit_across_members(qd, fmt):
+    """At m > 1 each workgroup takes its row-groups two at a time (a unit at
+    one super-block), and a unit may hold the last row-group of one member
+    and the first of the next.  Each of its tiles must come from its own
+    member's weights, also when the members' blobs are not adjacent in
+    memory (a spacer buffer between them here).  Members with odd row-group
+    counts and ragged last row-groups, K spanning several super-blocks with
+    a ragged tail; oracle parity per token at m = 16 and 3."""
+    from int4_quantized_decode_amd import LinearOp
+    K = 1088
+    shapes = [(4075, K), (1000, K), (1613, K)]          # 255 + 63 + 101 row-groups
+    ws = [si.weights(si.seed_for("unit-w", fmt, i), n, k) for i, (n, k) in enumerate(shapes)]
+    pws, spacers = [], []
+    for w in ws:
+        pws.append(_pack(qd, fmt, _gpu(w)))
+        spacers.append(torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
+    for m in (16, 3):
+        x = si.activations(si.seed_for("unit-x", fmt, m), m, K)
+        x_g = _gpu(x)
+        ys = [torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV) for n, _ in shapes]
+        ops = [LinearOp(pw, x_g, y, 0) for pw, y in zip(pws, ys)]
+        v = qd.describe_stack_plan(ops, m)
+        G, ng, nm = v[8], v[6], v[7]
+        assert v[1] == 1 and ng == 1 and nm == 3
+        starts = {v[16 + 10 * ng + 7 * i + 3] for i in range(1, nm)}     # members' first row-groups
+        sched = [v[16 + 10 * ng + 7 * nm + 4 * w:16 + 10 * ng + 7 * nm + 4 * w + 4] for w in range(G)]
+        crossing = sum(1 for _, _, rg0, nseg in sched for u in range(0, nseg - 1, 2) if rg0 + u + 1 in starts)
+        assert crossing >= 1, "no unit holds row-groups of two members"
+        plan = qd.StackPlan(ops, m)
+        assert plan.persistent
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        for i, (w, y) in enumerate(zip(ws, ys)):
+            parts = _oracle_parts(fmt, w)
+            Y_ref = linear.ref_linear(fmt, parts, x)
+            rmax = linear.row_max_abs(fmt, parts)
+            got = _host(y)
+            for t in range(m):
+                check_vector(got[t], Y_ref[t], rmax, x[t], f"{fmt} member {i} m={m} token {t}")
+        plan.close()
+    del spacers
+
+
+def test_plan_multi_token_copy_of_a_split_member(qd):
+    """At m > 1 an op whose whole output is a later group's activation also
+    writes it in matrix-core order, and a group split into row ranges
+    addresses its part of that copy by an offset.  Group 0's second member
+    starts 4 row-groups in, so the split (every 1024 row-groups at K = 5120
+    on 256 workgroups) cuts it inside a 256-row block: it writes no copy and
+    group 1 reads its activation in place.  Group 2's first member is cut at
+    a whole block and keeps its copy, both slices writing it, and group 3
+    reads it.  The schedule is checked on the host, then the step's outputs:
+    the consumers in full, the producers on sampled rows around and away
+    from the cut, against the oracle."""
+    from int4_quantized_decode_amd import LinearOp
+    m, fmt = 16, "int8_b32"
+    shapes = {"a": (64, 5120), "b": (24576, 5120), "c": (512, 24576),
+              "d": (24576, 5120), "e": (64, 5120), "f": (512, 24576)}
+    ws = {name: si.weights(si.seed_for("cut-w", name), n, k) for name, (n, k) in shapes.items()}
+    pws = {name: _pack(qd, fmt, _gpu(w)) for name, w in ws.items()}
+    x = si.activations(si.seed_for("cut-x", m), m, 5120)
+    x_g = _gpu(x)
+    y = {name: torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
+         for name, (n, _) in shapes.items()}
+    ops = [LinearOp(pws["a"], x_g, y["a"], 0), LinearOp(pws["b"], x_g, y["b"], 0),
+           LinearOp(pws["c"], y["b"], y["c"], 1),
+           LinearOp(pws["d"], x_g, y["d"], 2), LinearOp(pws["e"], x_g, y["e"], 2),
+           LinearOp(pws["f"], y["d"], y["f"], 3)]
+    # The schedule this device gets: b's slices carry no copy, d's do.
+    v = qd.describe_stack_plan(ops, m)
+    ng, nm = v[6], v[7]
+    groups = [v[16 + 10 * i:26 + 10 * i] for i in range(ng)]
+    members = [v[16 + 10 * ng + 7 * i:23 + 10 * ng + 7 * i] for i in range(nm)]
+    yptr = {name: t.data_ptr() for name, t in y.items()}
+    if v[8] != 256:
+        pytest.skip("the cuts are laid out for 256 compute units")
+    assert v[1] == 1 and ng == 6                                  # persistent, groups 0 and 2 split
+    in_y = lambda p, name: yptr[name] <= p < yptr[name] + shapes[name][0] * 2
+    assert [mb[6] for mb in members if in_y(mb[1], "b")] == [-1, -1]
+    d_copies = [mb[6] for mb in members if in_y(mb[1], "d")]
+    assert len(d_copies) == 2 and min(d_copies) >= 0 and d_copies[1] - d_copies[0] == 1024 * 512
+    assert groups[[g[0] for g in groups].index(yptr["b"])][9] == -1      # c reads in place
+    assert groups[[g[0] for g in groups].index(yptr["d"])][9] >= 0       # f reads d's copy
+
+    plan = qd.StackPlan(ops, m)
+    assert plan.persistent
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    out = {name: _host(t).copy() for name, t in y.items()}
+    for name, src in (("c", "b"), ("f", "d")):
+        parts = _oracle_parts(fmt, ws[name])
+        xin = out[src].astype(np.float64)
+        Y_ref = linear.ref_linear(fmt, parts, xin)
+        rmax = linear.row_max_abs(fmt, parts)
+        for t in range(m):
+            check_vector(out[name][t], Y_ref[t], rmax, xin[t], f"{name} token {t}")
+    rng = np.random.default_rng(si.seed_for("cut-rows"))
+    for name in ("a", "b", "d", "e"):
+        N = shapes[name][0]
+        rows = np.unique(np.concatenate([np.arange(min(N, 48)), np.arange(max(0, N - 48), N),
+                                         np.arange(16256, 16448) % N, rng.integers(0, N, 200)]))
+        parts = _oracle_parts(fmt, ws[name][rows])
+        Y_ref = linear.ref_linear(fmt, parts, x)
+        rmax = linear.row_max_abs(fmt, parts)
+        for t in range(m):
+            check_vector(out[name][t][rows], Y_ref[t], rmax, x[t], f"{name} token {t}")
+    plan.close()
+
+
 @pytest.mark.parametrize("m,packed", [(1, False), (1, True), (16, False), (16, True)])
 def test_plan_buffer_orderings(qd, m, packed):
     """The persistent step orders each boundary from the step's buffers: an

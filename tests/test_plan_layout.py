@@ -1,0 +1,460 @@
+"""Host-side checks of the persistent step's schedule (no GPU needed).
+
+qd_stack_plan_describe returns the tables qd_stack_plan_create builds, from
+the host alone.  These tests build decode-step op lists with synthetic
+addresses (the pointers are only compared and offset) and check the tables
+against properties stated here independently of the library:
+
+* every output row of every op in the persistent prefix is computed exactly
+  once, by one member slice, and the replayed tail starts where it should;
+* each group's members tile its row-groups in order, and each group's
+  row-groups are split over the workgroups as one contiguous range each,
+  disjoint and covering, with tile offsets that are running sums;
+* boundary ordering: a group may stage early exactly when no earlier group
+  writes its activation (or RMSNorm weight); a group acknowledges its stores
+  exactly when a later group reads them or overwrites them; later row ranges
+  of a split group wait for nothing; reading through the caches only where
+  one step group writes the lines and nothing brought them in before;
+* at several token rows, the activation copies: slots disjoint and sized for
+  the matrix-core order, one copy job per activation no group writes, and an
+  op's outputs copied only when they are exactly a later group's activation,
+  at offsets that stay valid under the row-range split;
+* the LDS the kernel asks for fits one CU (160 KiB).
+"""
+import ctypes
+from dataclasses import dataclass
+
+import pytest
+
+from synthetic_inputs import QWEN3_2B, QWEN3_8B, QWEN38_27B, Decoder
+
+FMT = {"int8_b32": 1, "int4_g64": 2, "fp16": 3}
+PRO_NONE, PRO_RMSNORM, PRO_GLU = 0, 1, 2
+EPI_NONE, EPI_SILU = 0, 1
+EARLY, ACK, NOWAIT, CLEAN = 1, 2, 4, 8
+TILE_BYTES = {1: 4352, 2: 2304}
+LDS_MAX = 160 * 1024
+
+
+@pytest.fixture(scope="module")
+def L():
+    from int4_quantized_decode_amd import _lib
+    return _lib
+
+
+class Heap:
+    """Bump allocator of synthetic device addresses."""
+
+    def __init__(self):
+        self.top = 1 << 36
+
+    def take(self, nbytes, align=4096):
+        self.top = (self.top + align - 1) // align * align
+        p = self.top
+        self.top += max(nbytes, 1)
+        return p
+
+
+@dataclass
+class Op:
+    fmt: int
+    n: int
+    k: int
+    data: int
+    nbytes: int
+    x: int
+    y: int
+    group: int
+    pro: int = PRO_NONE
+    gamma: int = 0
+    eps: float = 0.0
+    epi: int = EPI_NONE
+
+
+class StepBuilder:
+    def __init__(self, L, m):
+        self.L, self.m, self.heap, self.ops, self.gid = L, m, Heap(), [], 0
+
+    def act(self, k):
+        return self.heap.take(self.m * k * 2)
+
+    def group(self, members, x, fmt, pro=PRO_NONE, gamma=0, epis=None, ys=None):
+        """members: [(n, k)]; returns the output addresses."""
+        out = []
+        for i, (n, k) in enumerate(members):
+            nb = self.L.lib.qd_packed_bytes(fmt, n, k)
+            y = ys[i] if ys else self.heap.take(self.m * n * 2)
+            self.ops.append(Op(fmt, n, k, self.heap.take(nb), nb, x, y, self.gid, pro, gamma,
+                               1e-6 if pro == PRO_RMSNORM else 0.0,
+                               epis[i] if epis else EPI_NONE))
+            out.append(y)
+        self.gid += 1
+        return out
+
+    def array(self):
+        arr = (self.L.QDLinearOp * len(self.ops))()
+        for i, o in enumerate(self.ops):
+            w = self.L.QDWeight(o.fmt, 0, o.n, o.k, o.data, o.nbytes)
+            arr[i] = self.L.QDLinearOp(w, o.x, o.y, o.group, o.pro, o.gamma or None, o.eps, o.epi)
+        return arr
+
+
+def step_ops(L, dec: Decoder, m, fmt, layers=None, chain=False, glue=False, head_fmt=None):
+    """One decode step's op list: q|k|v -> o -> gate|up -> down per layer,
+    then the head.  Plain: every group reads an activation of its own.
+    Chained: each group reads an earlier group's output.  Glued (one token
+    row): RMSNorm before q|k|v, gate|up and the head, silu on gate, the
+    gated product before down."""
+    b = StepBuilder(L, m)
+    H, Q, KV, I = dec.hidden, dec.q_dim, dec.kv_dim, dec.mlp
+    f = FMT[fmt]
+    h = b.act(H)
+    for _ in range(dec.layers if layers is None else layers):
+        if glue:
+            g1, g2, g3 = (b.heap.take(H * 2) for _ in range(3))
+            q, _, _ = b.group([(Q, H), (KV, H), (KV, H)], h, f, PRO_RMSNORM, g1)
+            o, = b.group([(H, Q)], q, f)
+            gu = b.heap.take(m * 2 * I * 2)
+            b.group([(I, H), (I, H)], o, f, PRO_RMSNORM, g2, epis=[EPI_SILU, EPI_NONE],
+                    ys=[gu, gu + m * I * 2])
+            h, = b.group([(H, I)], gu, f, PRO_GLU)
+            hg = g3
+        elif chain:
+            q, _, _ = b.group([(Q, H), (KV, H), (KV, H)], h, f)
+            o, = b.group([(H, Q)], q, f)
+            g, _ = b.group([(I, H), (I, H)], o, f)
+            h, = b.group([(H, I)], g, f)
+        else:
+            b.group([(Q, H), (KV, H), (KV, H)], b.act(H), f)
+            b.group([(H, Q)], b.act(Q), f)
+            b.group([(I, H), (I, H)], b.act(H), f)
+            b.group([(H, I)], b.act(I), f)
+            h = b.act(H)
+    hf = FMT[head_fmt or fmt]
+    if glue:
+        b.group([(dec.vocab, H)], h, hf, PRO_RMSNORM, hg)
+    else:
+        b.group([(dec.vocab, H)], h, hf)
+    return b
+
+
+def describe(L, b, workgroups=256):
+    arr = b.array()
+    n = ctypes.c_int64(0)
+    st = L.lib.qd_stack_plan_describe(arr, len(b.ops), b.m, workgroups, None, 0, ctypes.byref(n))
+    assert st == 0, L.lib.qd_status_string(st)
+    buf = (ctypes.c_int64 * n.value)()
+    assert L.lib.qd_stack_plan_describe(arr, len(b.ops), b.m, workgroups, buf, n.value,
+                                        ctypes.byref(n)) == 0
+    v = list(buf)
+    keys = ["version", "persistent", "fmt", "m", "glue", "prefix", "ngroups", "nmem", "G",
+            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes"]
+    d = dict(zip(keys, v[:16]))
+    pos = 16
+
+    def take(count, width, names):
+        nonlocal pos
+        out = []
+        for _ in range(count):
+            out.append(dict(zip(names, v[pos:pos + width])))
+            pos += width
+        return out
+
+    d["groups"] = take(d["ngroups"], 10, ["x", "gamma", "k", "J", "R", "mem0", "nmem", "pro", "order",
+                                          "xt"])
+    d["members"] = take(d["nmem"], 7, ["blob", "y", "n", "rg_begin", "epi", "ld", "yt"])
+    d["sched"] = take(d["ngroups"] * d["G"], 4, ["n", "off", "rg0", "nseg"])
+    d["jobs"] = take(d["njobs"], 4, ["x", "t", "k", "first_block"])
+    assert pos == len(v)
+    return d
+
+
+def overlap(a, an, b, bn):
+    return an > 0 and bn > 0 and a < b + bn and b < a + an
+
+
+def x_bytes(g, m):
+    return m * g["k"] * 2 * (2 if g["pro"] == PRO_GLU else 1)
+
+
+def attach_sources(b, d):
+    """Map each member slice to its op: (op index, first row)."""
+    by_blob = sorted((o.data, i) for i, o in enumerate(b.ops))
+    src = []
+    for mb in d["members"]:
+        lo, hi = 0, len(by_blob) - 1
+        while lo < hi:
+            mid = (lo + hi + 1) // 2
+            if by_blob[mid][0] <= mb["blob"]:
+                lo = mid
+            else:
+                hi = mid - 1
+        op_i = by_blob[lo][1]
+        o = b.ops[op_i]
+        J = -(-o.k // 256)
+        skip, rem = divmod(mb["blob"] - o.data, J * TILE_BYTES[o.fmt])
+        assert rem == 0 and 0 <= skip * 16 < o.n, "slice blob is not a row-group start of its op"
+        assert mb["y"] == o.y + skip * 16 * 2, "slice y does not match its blob"
+        assert mb["ld"] == o.n and mb["epi"] == o.epi
+        src.append((op_i, skip * 16))
+    return src
+
+
+def check_layout(b, d, lds_fits=True):
+    m, ops = b.m, b.ops
+    G, gs, ms = d["G"], d["groups"], d["members"]
+    assert d["version"] == 1 and d["persistent"] == 1 and d["m"] == m
+    src = attach_sources(b, d)
+
+    # Rows: every op of the prefix is covered exactly once by its slices.
+    rows = {i: [] for i in range(d["prefix"]) if ops[i].n > 0}
+    for j, (op_i, r0) in enumerate(src):
+        assert op_i < d["prefix"], "a replayed op appears in the persistent tables"
+        rows[op_i].append((r0, r0 + ms[j]["n"]))
+    for op_i, rs in rows.items():
+        rs.sort()
+        assert rs and rs[0][0] == 0 and rs[-1][1] == ops[op_i].n, f"op {op_i} not covered"
+        assert all(rs[t][1] == rs[t + 1][0] for t in range(len(rs) - 1)), f"op {op_i} rows overlap/gap"
+
+    for gi, g in enumerate(gs):
+        mem = list(range(g["mem0"], g["mem0"] + g["nmem"]))
+        assert mem and (gi == 0 or gs[gi - 1]["mem0"] + gs[gi - 1]["nmem"] == g["mem0"])
+        rg = 0
+        for j in mem:
+            o = ops[src[j][0]]
+            assert ms[j]["rg_begin"] == rg and o.x == g["x"] and o.k == g["k"] and o.pro == g["pro"]
+            assert g["J"] == -(-o.k // 256) and g["gamma"] == o.gamma
+            rg += -(-ms[j]["n"] // 16)
+        assert rg == g["R"]
+        # Each workgroup one contiguous range; ranges cover [0, R) in order,
+        # balanced within one row-group.
+        sch = d["sched"][gi * G:(gi + 1) * G]
+        assert sch[0]["rg0"] == 0
+        assert all(sch[w]["rg0"] + sch[w]["nseg"] == sch[w + 1]["rg0"] for w in range(G - 1))
+        assert sch[-1]["rg0"] + sch[-1]["nseg"] == g["R"]
+        assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 1
+        unit = 2 if m > 1 else 1
+        assert all(s["n"] == -(-s["nseg"] // unit) * g["J"] for s in sch)
+    # Tile offsets: running sums over the groups a workgroup has work in.
+    for w in range(G):
+        acc = 0
+        for gi in range(len(gs)):
+            s = d["sched"][gi * G + w]
+            if s["nseg"]:
+                assert s["off"] == acc
+                acc += s["n"]
+
+    # Boundary ordering.  The flags belong to the step's groups (one op
+    # group, all its row ranges); the ranges of a split group each carry
+    # them, and the ranges after the first also wait for nothing.
+    def out_span(j):
+        return ms[j]["y"], ((m - 1) * ms[j]["ld"] + ms[j]["n"]) * 2
+
+    step_group = [ops[s[0]].group for s in src]
+    sg = []                                   # [(group indices, member indices)]
+    for gi, g in enumerate(gs):
+        later_range = gi > 0 and step_group[gs[gi - 1]["mem0"]] == step_group[g["mem0"]]
+        assert bool(g["order"] & NOWAIT) == later_range, f"group {gi} no-wait flag"
+        if not later_range:
+            sg.append(([], []))
+        sg[-1][0].append(gi)
+        sg[-1][1].extend(range(g["mem0"], g["mem0"] + g["nmem"]))
+
+    def reads(g, j):
+        return (overlap(g["x"], x_bytes(g, m), *out_span(j)) or
+                (g["pro"] == PRO_RMSNORM and overlap(g["gamma"], g["k"] * 2, *out_span(j))))
+
+    def lines(p, n):
+        return (p & ~127, (p + n + 127) & ~127) if p and n else (0, 0)
+
+    def hits(a, b):
+        return a[0] < b[1] and b[0] < a[1]
+
+    def acts(g):
+        return [lines(g["x"], x_bytes(g, m)),
+                lines(g["gamma"], g["k"] * 2) if g["pro"] == PRO_RMSNORM else (0, 0)]
+
+    early = [not any(reads(gs[gl[0]], j) for _, mj in sg[:i] for j in mj) for i, (gl, _) in enumerate(sg)]
+    for i, (gi_list, mem) in enumerate(sg):
+        g = gs[gi_list[0]]
+        e = early[i]
+        ack = any(reads(gs[sg[t][0][0]], j) or
+                  any(step_group[u] != step_group[j] and overlap(*out_span(u), *out_span(j)) for u in sg[t][1])
+                  for t in range(i + 1, len(sg)) for j in mem)
+        # Cache-read flag: one step group writes the activation's lines, and
+        # no weight, no early read and no read up to that writer touches them.
+        clean = False
+        if not e:
+            mine = acts(g)
+            touch = lambda l: any(hits(l, a) for a in mine)
+            writers, last = set(), -1
+            for t in range(i):
+                if any(touch(lines(*out_span(j))) for j in sg[t][1]):
+                    writers.add(t)
+                    last = t
+            clean = len(writers) <= 1
+            for t, (gl, mj) in enumerate(sg):
+                h = gs[gl[0]]
+                if any(touch(lines(ms[j]["blob"], -(-ms[j]["n"] // 16) * h["J"] * TILE_BYTES[d["fmt"]]))
+                       for j in mj):
+                    clean = False
+                if t != i and (early[t] or t <= last) and any(touch(a) for a in acts(h)):
+                    clean = False
+        for gi in gi_list:
+            o = gs[gi]["order"]
+            assert bool(o & EARLY) == e, f"group {gi} early flag"
+            assert bool(o & ACK) == ack, f"group {gi} acknowledge flag"
+            assert bool(o & CLEAN) == clean, f"group {gi} cache-read flag"
+
+    # Activation copies (several token rows).
+    if m == 1:
+        assert d["xt_total"] == 0 and d["njobs"] == 0
+        assert all(g["xt"] == -1 for g in gs) and all(mb["yt"] == -1 for mb in ms)
+    else:
+        slots = {}
+        for g in gs:
+            if g["xt"] >= 0:
+                size = -(-g["J"] * 8192 // 256) * 256
+                assert slots.setdefault(g["xt"], size) == size
+        spans = sorted(slots.items())
+        assert all(a + s <= b2 for (a, s), (b2, _) in zip(spans, spans[1:]))
+        assert not spans or spans[-1][0] + spans[-1][1] <= d["xt_total"]
+        job_keys = {(jb["x"], jb["k"]): jb["t"] for jb in d["jobs"]}
+        assert len(job_keys) == d["njobs"]
+        blocks = 0
+        for jb in d["jobs"]:
+            assert jb["first_block"] == blocks
+            blocks += 2 * -(-jb["k"] // 256)
+        for gi, g in enumerate(gs):
+            if g["order"] & EARLY:
+                assert g["xt"] == job_keys[(g["x"], g["k"])]
+        # Output copies: member slices of one op share the op's copy, at
+        # 512 bytes per row-group of skip, with skip whole 256-row blocks.
+        base = {}
+        for j, mb in enumerate(ms):
+            if mb["yt"] < 0:
+                continue
+            op_i, r0 = src[j]
+            assert r0 % 256 == 0, "copy offset cut inside a 256-row block"
+            b0 = base.setdefault(op_i, mb["yt"] - r0 * 32)
+            assert mb["yt"] == b0 + r0 * 32
+        for op_i, b0 in base.items():
+            o = ops[op_i]
+            consumers = [g for g in gs if g["xt"] == b0]
+            assert consumers and all(g["x"] == o.y and g["k"] == o.n and g["pro"] == PRO_NONE
+                                     for g in consumers)
+            assert all(not (g["order"] & EARLY) for g in consumers)
+        for g in gs:
+            if g["xt"] >= 0 and not g["order"] & EARLY:
+                assert g["xt"] in base.values()
+    # (With few workgroups a group's partials outgrow one CU's LDS; the plan
+    # then replays launches, which the device check in plan creation decides.)
+    assert d["lds"] <= LDS_MAX or not lds_fits
+    assert d["lds"] >= d["x_bytes"] + d["red_bytes"] + d["cnt_bytes"] + d["tab_bytes"]
+
+
+CASES = [
+    ("qwen3-8b int8 m1", QWEN3_8B, 1, "int8_b32", {}),
+    ("qwen3-8b int4 m1", QWEN3_8B, 1, "int4_g64", {}),
+    ("qwen3-2b int8 m1", QWEN3_2B, 1, "int8_b32", {}),
+    ("qwen3-8b int8 m16", QWEN3_8B, 16, "int8_b32", {}),
+    ("qwen3-8b int8 chain m1", QWEN3_8B, 1, "int8_b32", {"chain": True}),
+    ("qwen3-8b int8 chain m16", QWEN3_8B, 16, "int8_b32", {"chain": True}),
+    ("qwen3-8b int8 glue m1", QWEN3_8B, 1, "int8_b32", {"glue": True}),
+    ("qwen3.8-27b int8 m16 (4 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 4}),
+    ("qwen3.8-27b int8 chain m16 (3 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 3, "chain": True}),
+    ("qwen3-8b int8 chain m5", QWEN3_8B, 5, "int8_b32", {"chain": True, "layers": 4}),
+]
+
+
+@pytest.mark.parametrize("name,dec,m,fmt,kw", CASES, ids=[c[0] for c in CASES])
+def test_plan_layout_invariants(L, name, dec, m, fmt, kw):
+    b = step_ops(L, dec, m, fmt, **kw)
+    d = describe(L, b)
+    assert d["prefix"] == len(b.ops) and d["glue"] == int(bool(kw.get("glue")))
+    check_layout(b, d)
+
+
+@pytest.mark.parametrize("workgroups", [1, 7, 80, 255, 304, 512])
+def test_plan_layout_other_workgroup_counts(L, workgroups):
+    for m, kw in ((1, {"chain": True}), (16, {"chain": True}), (16, {})):
+        b = step_ops(L, QWEN3_8B, m, "int8_b32", layers=2, **kw)
+        d = describe(L, b, workgroups)
+        assert d["G"] == workgroups
+        check_layout(b, d, lds_fits=workgroups >= 80)
+
+
+def test_plan_layout_fp16_head_is_replayed_tail(L):
+    b = step_ops(L, QWEN3_2B, 1, "int8_b32", layers=3, head_fmt="fp16")
+    d = describe(L, b)
+    assert d["persistent"] == 1 and d["prefix"] == len(b.ops) - 1
+    check_layout(b, d)
+
+
+@pytest.mark.parametrize("m,fmt,kw", [(16, "int4_g64", {}), (16, "int8_b32", {"glue": True}),
+                                      (1, "fp16", {})])
+def test_plan_layout_replays_whole(L, m, fmt, kw):
+    b = step_ops(L, QWEN3_8B, m, fmt, layers=1, **kw)
+    d = describe(L, b)
+    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 16 + 4
+
+
+def test_plan_layout_copy_not_cut_inside_a_block(L):
+    """A producing member starting 4 row-groups into a group long enough to
+    be split: with 8 workgroups the cuts come every 48 row-groups, 44 into
+    the member first, so it writes no copy and its consumer reads its
+    activation in place.  With the producer first the cuts fall at whole
+    256-row blocks of it and the copy is kept."""
+    b = StepBuilder(L, 16)
+    x = b.act(4096)
+    _, q = b.group([(64, 4096), (4096, 4096)], x, 1)
+    b.group([(512, 4096)], q, 1)
+    d = describe(L, b, 8)
+    check_layout(b, d)
+    assert d["groups"][0]["R"] < 260 and len(d["groups"]) > 2      # split into row ranges
+    assert all(mb["yt"] == -1 for mb in d["members"])
+    assert d["groups"][-1]["xt"] == -1
+    b = StepBuilder(L, 16)
+    x = b.act(4096)
+    q, _ = b.group([(4096, 4096), (64, 4096)], x, 1)
+    b.group([(512, 4096)], q, 1)
+    d = describe(L, b, 8)
+    check_layout(b, d)
+    assert any(mb["yt"] >= 0 for mb in d["members"]) and d["groups"][-1]["xt"] >= 0
+
+
+def test_plan_describe_errors(L):
+    b = step_ops(L, QWEN3_2B, 1, "int8_b32", layers=1)
+    arr, n = b.array(), ctypes.c_int64(0)
+    lib = L.lib
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, None, 0, None) == 1
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 0, None, 0, ctypes.byref(n)) == 1
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 513, None, 0, ctypes.byref(n)) == 1
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, None, -1, ctypes.byref(n)) == 1
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 17, 256, None, 0, ctypes.byref(n)) == 2
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, None, 0, ctypes.byref(n)) == 0
+    need = n.value
+    small = (ctypes.c_int64 * 4)()
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, small, 4, ctypes.byref(n)) == 2
+    assert n.value == need and list(small) == [0, 0, 0, 0]
+
+
+def test_plan_layout_copy_cuts_on_256_workgroups(L):
+    """The layout the GPU test of the same name runs: at K = 5120 the split
+    comes every 1024 row-groups; b (starting 4 row-groups in) is cut 1020
+    row-groups in and writes no copy, d is cut at a whole block and both its
+    slices write its copy, 1024 x 512 bytes apart."""
+    b = StepBuilder(L, 16)
+    x = b.act(5120)
+    _, yb = b.group([(64, 5120), (24576, 5120)], x, 1)
+    b.group([(512, 24576)], yb, 1)
+    yd, _ = b.group([(24576, 5120), (64, 5120)], x, 1)
+    b.group([(512, 24576)], yd, 1)
+    d = describe(L, b, 256)
+    check_layout(b, d)
+    gs, ms = d["groups"], d["members"]
+    assert [g["R"] for g in gs] == [1024, 516, 32, 1024, 516, 32]
+    assert gs[2]["xt"] == -1 and gs[5]["xt"] >= 0
+    d_slices = [mb["yt"] for mb in ms if yd <= mb["y"] < yd + 24576 * 2]
+    assert len(d_slices) == 2 and d_slices[0] == gs[5]["xt"] and d_slices[1] - d_slices[0] == 1024 * 512
+    assert all(mb["yt"] == -1 for mb in ms if yb <= mb["y"] < yb + 24576 * 2)
