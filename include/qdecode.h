@@ -222,12 +222,12 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * one step on `stream` (at m > 1 a small copy kernel for the activations no
  * op of the step writes, then the persistent kernel) and allocates nothing.  A plan may be run repeatedly but not
  * concurrently.  The persistent kernel takes groups of one format, int8
- * b32 or INT4 g64 at m = 1 (with or without glue) and int8 b32 at m = 2..16
- * (without glue).  It runs the step's leading groups that qualify; from the
- * first group that does not (say an fp16 head), the rest of the step is
- * replayed after it as the same per-group launches decode_linear_stack
- * makes.  A step whose first group does not qualify (fp16 weights, INT4 at
- * m > 1, glue at m > 1), or whose schedule is larger than one CU's LDS or has
+ * b32 or INT4 g64, at m = 1 with or without glue and at m = 2..16 without
+ * glue.  It runs the step's leading groups that qualify; from the first
+ * group that does not (say an fp16 head), the rest of the step is replayed
+ * after it as the same per-group launches decode_linear_stack makes.  A
+ * step whose first group does not qualify (fp16 weights, glue at m > 1), or
+ * whose schedule is larger than one CU's LDS or has
  * a row-group too long for it at m > 1, is replayed whole, with the same
  * results as decode_linear_stack; qd_stack_plan_is_persistent tells whether
  * the persistent kernel runs.

@@ -30,7 +30,7 @@
 //   * one token row: the control wave stages each group's activation vector
 //     (and, with glue, gamma or the gated product's second block) straight
 //     into LDS and applies the prologue there;
-//   * up to 16 token rows (int8): compute waves read the activation blocks
+//   * up to 16 token rows: compute waves read the activation blocks
 //     themselves, from copies in matrix-core order where the plan keeps them
 //     (made before the step, or written by the op producing them), and the
 //     partials are 16 x 16 per tile; groups too large for the partials in
@@ -1326,8 +1326,11 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 // run the plain kernel).
 const void* kernel_ptr(int fmt, bool multi, bool glue) {
   if (multi)
-    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
-                                                        QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>);
+    return fmt == QD_FMT_INT8_B32
+               ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
+                                                             QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>)
+               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
+                                                             QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>);
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
@@ -1359,7 +1362,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   *L = PlanLayout{};
   L->G = G;
   // Persistent walker: one format, no empty-K groups; one token row (with or
-  // without glue), or up to 16 with int8 weights and no glue.  The leading
+  // without glue), or up to 16 without glue.  The leading
   // groups that qualify run in the persistent kernel; from the first group
   // that does not (another format, say an fp16 head), the rest of the step
   // is replayed as per-group launches after it on the same stream.
@@ -1382,10 +1385,6 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       if (gfmt == 0) gfmt = ops[q].w.fmt;
       if (ops[q].w.fmt != gfmt) gok = false;
       if (gfmt != QD_FMT_INT8_B32 && gfmt != QD_FMT_INT4_G64) gok = false;   // fp16: replay
-      // INT4 at several token rows: replay.  Its persistent instance passed
-      // every parity test but one longer device run of it ended in a memory
-      // fault whose cause is not found; it stays off until one is.
-      if (multi && gfmt != QD_FMT_INT8_B32) gok = false;
       // Glue (a prologue or an epilogue): at one token row only.
       if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) {
         gglue = true;
@@ -1698,8 +1697,12 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess || dev != plan->device) return QD_EDEVICE;
   if (!plan->persistent) return launch_groups(plan->replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH;
   if (plan->xt_njobs > 0) {
-    hipLaunchKernelGGL(xt_copy_kernel<QD_FMT_INT8_B32>, dim3((unsigned)plan->xt_blocks), dim3(256), 0, s,
-                       static_cast<const XtJob*>(plan->xt_jobs), plan->xt_njobs, (int)plan->args.m);
+    if (plan->fmt == QD_FMT_INT8_B32)
+      hipLaunchKernelGGL(xt_copy_kernel<QD_FMT_INT8_B32>, dim3((unsigned)plan->xt_blocks), dim3(256), 0, s,
+                         static_cast<const XtJob*>(plan->xt_jobs), plan->xt_njobs, (int)plan->args.m);
+    else
+      hipLaunchKernelGGL(xt_copy_kernel<QD_FMT_INT4_G64>, dim3((unsigned)plan->xt_blocks), dim3(256), 0, s,
+                         static_cast<const XtJob*>(plan->xt_jobs), plan->xt_njobs, (int)plan->args.m);
     if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
   }
   plan->args.epoch = ++plan->epoch;

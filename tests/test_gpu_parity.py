@@ -36,11 +36,6 @@ def _host(t):
 FMTS = ["int8_b32", "int4_g64", "fp16"]
 
 
-INT4_M16_OFF = pytest.mark.skip(reason="the persistent kernel's INT4 instance at m > 1 is switched off "
-                                       "(plans replay the launches): it passed these tests, but a longer "
-                                       "device run of it ended in a memory fault whose cause is not found")
-
-
 def _oracle_parts(fmt, w):
     return {"int8_b32": quant.quantize_int8_b32, "int4_g64": quant.quantize_int4_g64,
             "fp16": quant.quantize_fp16}[fmt](w)
@@ -548,7 +543,7 @@ def test_single_gemv_config_bench_path(qd):
                                       "qwen3-2b-int8-m1", "qwen3-4b-int8-m1",
                                       "qwen3-8b-int8-chain-m1", "qwen3-8b-int8-m16",
                                       "qwen3-8b-int8-chain-m16",
-                                      pytest.param("qwen3-8b-int4-m16", marks=INT4_M16_OFF),
+                                      "qwen3-8b-int4-m16",
                                       "qwen3.8-27b-int8-m16"])
 def test_plan_full_size_sampled(qd, workload):
     """The full decoder-shaped step in the launch configuration the bench
@@ -764,7 +759,7 @@ def test_plan_persistent_prefix_and_replayed_tail(qd, m):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_plan_multi_token_groups(qd, fmt):
-    """A plan at m > 1 (int8: the persistent kernel; INT4 and fp16: it replays
+    """A plan at m > 1 (int8 and INT4: the persistent kernel; fp16: it replays
     the per-group launches): groups of many shapes (K = 1088, a ragged
     super-block tail; 4096 x 4096; K = 12288; a fused pair; a group large
     enough for multi-row-group workgroups) and m below 16.  Runs repeat with
@@ -785,7 +780,7 @@ def test_plan_multi_token_groups(qd, fmt):
                 ops.append(LinearOp(_pack(qd, fmt, _gpu(w)), xg, y, gid))
                 meta.append((f"{gname}{i}", w, X))
         plan = qd.StackPlan(ops, m)
-        assert plan.persistent == (fmt == "int8_b32")
+        assert plan.persistent == (fmt != "fp16")
         first = None
         for rep in range(3):
             for op in ops:
@@ -814,7 +809,7 @@ def test_plan_multi_token_groups(qd, fmt):
         plan.close()
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", pytest.param("int4_g64", marks=INT4_M16_OFF)])
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 def test_plan_multi_token_split_and_chain(qd, fmt):
     """The persistent kernel at m > 1: a group too large for one range of
     tile partials per workgroup is split into row ranges (a member crossing
@@ -865,7 +860,7 @@ def test_plan_multi_token_split_and_chain(qd, fmt):
         plan.close()
 
 
-@pytest.mark.parametrize("fmt", ["int8_b32", pytest.param("int4_g64", marks=INT4_M16_OFF)])
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
 def test_plan_multi_token_unit_across_members(qd, fmt):
     """At m > 1 each workgroup takes its row-groups two at a time (a unit at
     one super-block), and a unit may hold the last row-group of one member

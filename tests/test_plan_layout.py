@@ -358,6 +358,8 @@ CASES = [
     ("qwen3-8b int4 m1", QWEN3_8B, 1, "int4_g64", {}),
     ("qwen3-2b int8 m1", QWEN3_2B, 1, "int8_b32", {}),
     ("qwen3-8b int8 m16", QWEN3_8B, 16, "int8_b32", {}),
+    ("qwen3-8b int4 m16", QWEN3_8B, 16, "int4_g64", {}),
+    ("qwen3-8b int4 chain m3", QWEN3_8B, 3, "int4_g64", {"chain": True, "layers": 4}),
     ("qwen3-8b int8 chain m1", QWEN3_8B, 1, "int8_b32", {"chain": True}),
     ("qwen3-8b int8 chain m16", QWEN3_8B, 16, "int8_b32", {"chain": True}),
     ("qwen3-8b int8 glue m1", QWEN3_8B, 1, "int8_b32", {"glue": True}),
@@ -391,8 +393,7 @@ def test_plan_layout_fp16_head_is_replayed_tail(L):
     check_layout(b, d)
 
 
-@pytest.mark.parametrize("m,fmt,kw", [(16, "int4_g64", {}), (16, "int8_b32", {"glue": True}),
-                                      (1, "fp16", {})])
+@pytest.mark.parametrize("m,fmt,kw", [(16, "int8_b32", {"glue": True}), (1, "fp16", {}), (16, "fp16", {})])
 def test_plan_layout_replays_whole(L, m, fmt, kw):
     b = step_ops(L, QWEN3_8B, m, fmt, layers=1, **kw)
     d = describe(L, b)
