@@ -1315,6 +1315,26 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #ifndef QD_PLAN_RESERVE16_S
 #define QD_PLAN_RESERVE16_S 1
 #endif
+// INT4 at up to 16 token rows: its own shape (tiles of 2304 rather than 4352
+// bytes), measured on the 8B INT4 step (us): reserve waves of one unit
+// 0 / 2 / 3 / 4 / 5 / 6 / 7 / 10 gave 1671 / 1608 / 1607 / 1621-1634 / 1630 /
+// 1650 / 1709 / 2038 (from two boxes); units of 3 row-groups 1636 with 4
+// reserve waves.  A ring of 2 units, two units per reserve wave and units of
+// 4 spill registers.
+#ifndef QD_PLAN_RING16_INT4
+#define QD_PLAN_RING16_INT4 QD_PLAN_RING16
+#endif
+#ifndef QD_PLAN_RESERVE16_INT4_R
+#define QD_PLAN_RESERVE16_INT4_R 3
+#endif
+#ifndef QD_PLAN_RESERVE16_INT4_S
+#define QD_PLAN_RESERVE16_INT4_S QD_PLAN_RESERVE16_S
+#endif
+#ifndef QD_PLAN_UNIT16_INT4
+#define QD_PLAN_UNIT16_INT4 QD_PLAN_UNIT16
+#endif
+// Row-groups per unit at up to 16 token rows.
+constexpr int unit16(int fmt) { return fmt == QD_FMT_INT8_B32 ? QD_PLAN_UNIT16 : QD_PLAN_UNIT16_INT4; }
 // Tiles per workgroup per group at up to 16 token rows: their 1 KB partials
 // are held in LDS until the row-group is reduced.
 #ifndef QD_PLAN_TILES16
@@ -1329,8 +1349,9 @@ const void* kernel_ptr(int fmt, bool multi, bool glue) {
     return fmt == QD_FMT_INT8_B32
                ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
                                                              QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>)
-               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
-                                                             QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>);
+               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16_INT4,
+                                                             QD_PLAN_RESERVE16_INT4_R, QD_PLAN_RESERVE16_INT4_S,
+                                                             false, 16, QD_PLAN_UNIT16_INT4>);
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
@@ -1493,9 +1514,9 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       // Contiguous row-groups: each workgroup streams one contiguous range.
       // (Interleaving them, row-group w + i G to workgroup w, measured 2-11%
       // slower: the contiguous streams keep DRAM pages open.)
-      // Several token rows: the sequence holds units of QD_PLAN_UNIT16 row-groups.
+      // Several token rows: the sequence holds units of unit16(fmt) row-groups.
       const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
-      const int64_t n = (multi ? ceil_div(nrg, (int64_t)QD_PLAN_UNIT16) : nrg) * J;
+      const int64_t n = (multi ? ceil_div(nrg, (int64_t)unit16(fmt)) : nrg) * J;
       L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
       if (nrg == 0) continue;
       off[w] += (int32_t)n;
