@@ -272,9 +272,9 @@ qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
  *   G_n x W schedule entries of 4 words, group-major: tiles, tiles of this
  *     workgroup in earlier groups, first row-group, row-groups;
  *   J_n copy jobs of 4 words: x, offset of its copy, K, first block.
- * A step that replays whole gives the header alone.  With cap below the
- * count, *out_len is still set and nothing is written: QD_OK when out is
- * NULL (a size query), else QD_ESHAPE.  QD_EINVAL for a null out_len, a
+ * A step that replays whole gives the header alone.  With out NULL only
+ * *out_len is set (a size query, QD_OK); with cap below the count *out_len is
+ * set, nothing is written and the result is QD_ESHAPE.  QD_EINVAL for a null out_len, a
  * negative cap or workgroups outside 1..512; otherwise the status
  * decode_linear_stack's validation gives. */
 qd_status qd_stack_plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,

@@ -1708,7 +1708,8 @@ qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32
   for (const XtJob& j : L.jobs)
     v.insert(v.end(), {addr(j.x), (int64_t)reinterpret_cast<uintptr_t>(j.t), j.k, j.first_block});
   *out_len = (int64_t)v.size();
-  if (cap < (int64_t)v.size()) return out ? QD_ESHAPE : QD_OK;
+  if (!out) return QD_OK;                           // a size query
+  if (cap < (int64_t)v.size()) return QD_ESHAPE;
   std::copy(v.begin(), v.end(), out);
   return QD_OK;
 }

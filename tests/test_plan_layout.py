@@ -435,6 +435,8 @@ def test_plan_describe_errors(L):
     assert lib.qd_stack_plan_describe(arr, len(b.ops), 17, 256, None, 0, ctypes.byref(n)) == 2
     assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, None, 0, ctypes.byref(n)) == 0
     need = n.value
+    assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, None, need + 100, ctypes.byref(n)) == 0
+    assert n.value == need
     small = (ctypes.c_int64 * 4)()
     assert lib.qd_stack_plan_describe(arr, len(b.ops), 1, 256, small, 4, ctypes.byref(n)) == 2
     assert n.value == need and list(small) == [0, 0, 0, 0]
