@@ -649,8 +649,8 @@ def test_stack_full_size_sampled_fp16_head(qd):
     plan.close()
 
 
-@pytest.mark.parametrize("m", [1, 16])
-def test_plan_wait_timeout_reported_and_recovers(qd, m):
+@pytest.mark.parametrize("m,fmt", [(1, "int8_b32"), (16, "int8_b32"), (16, "int4_g64")])
+def test_plan_wait_timeout_reported_and_recovers(qd, m, fmt):
     """The persistent kernel's waits are bounded.  With the bound set to no
     polls from the host, waits time out: the run still ends, the error word
     reports it, and the plan resets its scratch; with the default bound
@@ -662,7 +662,7 @@ def test_plan_wait_timeout_reported_and_recovers(qd, m):
     shape = (m, k) if m > 1 else (k,)
     ys = [torch.empty(shape, dtype=torch.float16, device=DEV) for _ in range(3)]
     xs = [_gpu(x0.reshape(shape)), ys[0], ys[1]]
-    ops = [LinearOp(qd.qpack_int8_b32(_gpu(w)), xs[g], ys[g], g) for g, w in enumerate(ws)]
+    ops = [LinearOp(_pack(qd, fmt, _gpu(w)), xs[g], ys[g], g) for g, w in enumerate(ws)]
     plan = qd.StackPlan(ops, m)
     assert plan.persistent
     plan.set_spin_limit(0)
@@ -677,16 +677,17 @@ def test_plan_wait_timeout_reported_and_recovers(qd, m):
     assert plan.error() == 0
     x = x0.astype(np.float64)
     for g, w in enumerate(ws):
-        parts = quant.quantize_int8_b32(w)
+        parts = _oracle_parts(fmt, w)
         Y = _host(ys[g]).reshape(m, k)
-        Y_ref = linear.ref_linear("int8_b32", parts, x).reshape(m, k)
+        Y_ref = linear.ref_linear(fmt, parts, x).reshape(m, k)
         for t in range(m):
-            check_vector(Y[t], Y_ref[t], linear.row_max_abs("int8_b32", parts), x[t], f"group {g} token {t}")
+            check_vector(Y[t], Y_ref[t], linear.row_max_abs(fmt, parts), x[t], f"group {g} token {t}")
         x = Y.astype(np.float64)
     plan.close()
 
 
-def test_plan_multi_token_longest_k(qd):
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+def test_plan_multi_token_longest_k(qd, fmt):
     """The 16-token persistent step at the longest K the packers accept
     (K = 24576, 96 super-blocks: exactly the per-workgroup tile budget, one
     row-group per workgroup, so 263 row-groups split into two row ranges),
@@ -697,7 +698,7 @@ def test_plan_multi_token_longest_k(qd):
     w = si.weights(si.seed_for("longk-w", k), n, k)
     X = si.activations(si.seed_for("longk-x", k), m, k)
     y = torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)
-    plan = qd.StackPlan([LinearOp(qd.qpack_int8_b32(_gpu(w)), _gpu(X), y, 0)], m)
+    plan = qd.StackPlan([LinearOp(_pack(qd, fmt, _gpu(w)), _gpu(X), y, 0)], m)
     assert plan.persistent
     plan.run()
     torch.cuda.synchronize()
@@ -707,9 +708,9 @@ def test_plan_multi_token_longest_k(qd):
     plan.run()
     torch.cuda.synchronize()
     assert np.array_equal(_host(y).view(np.uint16), Y.view(np.uint16))
-    parts = quant.quantize_int8_b32(w)
-    Y_ref = linear.ref_linear("int8_b32", parts, X)
-    rmax = linear.row_max_abs("int8_b32", parts)
+    parts = _oracle_parts(fmt, w)
+    Y_ref = linear.ref_linear(fmt, parts, X)
+    rmax = linear.row_max_abs(fmt, parts)
     for t in range(m):
         check_vector(Y[t], Y_ref[t], rmax, X[t], f"K={k} token {t}")
     plan.close()
@@ -972,8 +973,9 @@ def test_plan_multi_token_copy_of_a_split_member(qd):
     plan.close()
 
 
-@pytest.mark.parametrize("m,packed", [(1, False), (1, True), (16, False), (16, True)])
-def test_plan_buffer_orderings(qd, m, packed):
+@pytest.mark.parametrize("m,packed,fmt", [(1, False, "int8_b32"), (1, True, "int8_b32"), (16, False, "int8_b32"),
+                                          (16, True, "int8_b32"), (16, False, "int4_g64"), (16, True, "int4_g64")])
+def test_plan_buffer_orderings(qd, m, packed, fmt):
     """The persistent step orders each boundary from the step's buffers: an
     input no earlier output overlaps is staged early, one that an earlier
     output overlaps (not only the previous group's) only after the barrier,
@@ -1005,7 +1007,7 @@ def test_plan_buffer_orderings(qd, m, packed):
             (0, 2),   # g5: reads g4's output from g0's old input buffer
             (3, 5)]   # g6: reads g3's rewrite of buffer 3
     ws = [si.weights(si.seed_for("order-w", g), k, k) for g in range(len(prog))]
-    pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
+    pws = [_pack(qd, fmt, _gpu(w)) for w in ws]
     ops = [LinearOp(pws[g], bufs[xb], bufs[yb], g) for g, (xb, yb) in enumerate(prog)]
     plan = qd.StackPlan(ops, m)
     assert plan.persistent
@@ -1013,9 +1015,9 @@ def test_plan_buffer_orderings(qd, m, packed):
     state = [v.astype(np.float16) for v in init]
     want, xin = [None] * len(prog), [None] * len(prog)
     for g, (xb, yb) in enumerate(prog):
-        parts = quant.quantize_int8_b32(ws[g])
+        parts = _oracle_parts(fmt, ws[g])
         xin[g] = state[xb].copy()
-        want[g] = linear.ref_linear("int8_b32", parts, xin[g])
+        want[g] = linear.ref_linear(fmt, parts, xin[g])
         state[yb] = want[g].astype(np.float16)
     final_writer = {}
     for g, (xb, yb) in enumerate(prog):
@@ -1031,13 +1033,13 @@ def test_plan_buffer_orderings(qd, m, packed):
         if first is None:
             first = outs
             for yb, g in final_writer.items():
-                parts = quant.quantize_int8_b32(ws[g])
+                parts = _oracle_parts(fmt, ws[g])
                 # the input the kernel saw was the device's own earlier output: bound the
                 # chain by the rows' magnitudes along the path (at most 3 products deep)
                 got, ref, xs = (outs[yb].reshape(m, k), want[g].reshape(m, k),
                                 xin[g].astype(np.float64).reshape(m, k))
                 for t in range(m):
-                    check_vector(got[t], ref[t], 4 * linear.row_max_abs("int8_b32", parts),
+                    check_vector(got[t], ref[t], 4 * linear.row_max_abs(fmt, parts),
                                  xs[t], f"buffer {yb} (group {g}) token {t}")
         else:
             for a_, b_ in zip(first, outs):
