@@ -461,3 +461,60 @@ def test_plan_layout_copy_cuts_on_256_workgroups(L):
     d_slices = [mb["yt"] for mb in ms if yd <= mb["y"] < yd + 24576 * 2]
     assert len(d_slices) == 2 and d_slices[0] == gs[5]["xt"] and d_slices[1] - d_slices[0] == 1024 * 512
     assert all(mb["yt"] == -1 for mb in ms if yb <= mb["y"] < yb + 24576 * 2)
+
+
+def _random_step(L, rng):
+    """A random valid step: groups of 1-3 members with random N and K; each
+    group's activation is fresh, an earlier op's whole output (when its N
+    matches K) or a slice of one; outputs are fresh or overwrite an earlier
+    op's output of the same size."""
+    fmt = int(rng.choice([1, 2]))
+    m = int(rng.choice([1, 2, 5, 16]))
+    b = StepBuilder(L, m)
+    outs = []                               # (address, n) of earlier outputs
+    for _ in range(int(rng.integers(1, 9))):
+        k = int(rng.choice([256, 512, 1024, 1088, 2048, 4096]))
+        if fmt == 2 and k % 64:
+            k = 1024
+        cands = [(y, n) for y, n in outs if n >= k]
+        r = rng.random()
+        if cands and r < 0.4:
+            y, n = cands[int(rng.integers(len(cands)))]
+            x = y if n == k or m > 1 else y + 2 * int(rng.integers(0, (n - k) // 8 + 1)) * 8
+        else:
+            x = b.act(k)
+        members = [(int(rng.choice([16, 48, 100, 256, 1000, 4096, 6000])), k)
+                   for _ in range(int(rng.integers(1, 4)))]
+        ys = []
+        for n, _ in members:
+            same = [y for y, nn in outs if nn == n and not overlap(y, m * n * 2, x, m * k * 2)]
+            if same and rng.random() < 0.2 and all(y not in ys for y in same[:1]):
+                ys.append(same[0])
+            else:
+                ys.append(b.heap.take(m * n * 2))
+        if len(set(ys)) != len(ys):
+            ys = [b.heap.take(m * n * 2) for n, _ in members]
+        got = b.group(members, x, fmt, ys=ys)
+        outs.extend(zip(got, [n for n, _ in members]))
+    return b
+
+
+def test_plan_layout_random_steps(L):
+    """200 random steps through the same invariants, at random workgroup
+    counts.  Steps the validation rejects (an output overlapping its own
+    group's input, say) are skipped."""
+    import numpy as np
+    rng = np.random.default_rng(20261203)
+    checked = 0
+    for _ in range(200):
+        b = _random_step(L, rng)
+        G = int(rng.choice([3, 8, 64, 80, 256, 304]))
+        arr, n = b.array(), ctypes.c_int64(0)
+        if L.lib.qd_stack_plan_describe(arr, len(b.ops), b.m, G, None, 0, ctypes.byref(n)) != 0:
+            continue
+        d = describe(L, b, G)
+        if not d["persistent"]:
+            continue
+        check_layout(b, d, lds_fits=G >= 80)
+        checked += 1
+    assert checked >= 100
