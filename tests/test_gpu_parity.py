@@ -1045,3 +1045,74 @@ def test_plan_buffer_orderings(qd, m, packed, fmt):
             for a_, b_ in zip(first, outs):
                 assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
     plan.close()
+
+
+def test_plan_random_steps_against_sequential_model(qd):
+    """Random steps run as persistent plans against a sequential model of the
+    buffers built from the oracle: groups of 1-3 members in one fp16 arena;
+    each group reads a fresh region, an earlier op's whole output or (one
+    token row) a slice of one; outputs go to fresh regions or overwrite an
+    earlier op's output.  Every region's final value is checked (bound 8x
+    the acceptance bound: inputs chain through up to six groups, and a
+    wrongly ordered read would be off by the whole value)."""
+    from int4_quantized_decode_amd import LinearOp
+    rng = np.random.default_rng(si.seed_for("random-steps"))
+    arena_n = 1 << 21
+    for case in range(24):
+        fmt = ["int8_b32", "int4_g64"][case % 2]
+        m = [1, 5, 16][(case // 2) % 3]
+        init = si.activations(si.seed_for("random-arena", case), 1, arena_n)[0]
+        arena = _gpu(init)
+        model = init.astype(np.float64).copy()
+        top = 0
+
+        def take(n):
+            nonlocal top
+            off = top
+            top += (n + 63) // 64 * 64
+            assert top <= arena_n
+            return off
+
+        ops, prog, outs = [], [], []
+        for g in range(int(rng.integers(2, 7))):
+            k = int(rng.choice([256, 512, 1024, 1088]))
+            cands = [(o, n) for o, n in outs if (n == k or (m == 1 and n >= k))]
+            if cands and rng.random() < 0.6:
+                o, n = cands[int(rng.integers(len(cands)))]
+                xo = o + (8 * int(rng.integers(0, (n - k) // 8 + 1)) if m == 1 else 0)
+            else:
+                xo = take(m * k)
+            members = []
+            for _ in range(int(rng.integers(1, 4))):
+                n = int(rng.choice([16, 48, 100, 256, 1000, 1088]))
+                same = [o for o, nn in outs if nn == n and not (o < xo + m * k and xo < o + m * n)
+                        and all(o != mo for mo, _, _ in members)]
+                yo = same[0] if same and rng.random() < 0.25 else take(m * n)
+                w = si.weights(si.seed_for("random-w", case, g, len(members)), n, k)
+                members.append((yo, n, w))
+            for yo, n, w in members:
+                ops.append(LinearOp(_pack(qd, fmt, _gpu(w)), arena[xo:xo + m * k].view(m, k) if m > 1
+                                    else arena[xo:xo + k], arena[yo:yo + m * n].view(m, n) if m > 1
+                                    else arena[yo:yo + n], g))
+            prog.append((xo, k, members))
+            outs.extend((yo, n) for yo, n, _ in members)
+        plan = qd.StackPlan(ops, m)
+        assert plan.persistent, f"case {case}"
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        got = _host(arena).astype(np.float64)
+        # sequential model: each group reads its input, then writes its outputs
+        final = {}
+        for xo, k, members in prog:
+            X = model[xo:xo + m * k].reshape(m, k).copy()
+            for yo, n, w in members:
+                parts = _oracle_parts(fmt, w)
+                Y = linear.ref_linear(fmt, parts, X)
+                model[yo:yo + m * n] = Y.astype(np.float16).astype(np.float64).reshape(-1)
+                final[yo] = (n, Y, X, linear.row_max_abs(fmt, parts))
+        for yo, (n, Y, X, rmax) in final.items():
+            G_ = got[yo:yo + m * n].reshape(m, n)
+            for t in range(m):
+                check_vector(G_[t], Y[t], 8 * rmax, X[t], f"case {case} ({fmt}, m={m}) output at {yo} token {t}")
+        plan.close()
