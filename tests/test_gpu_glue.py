@@ -368,3 +368,79 @@ def test_glue_full_size_sampled(qd, workload, path):
                 check_vector(y[t], ref[t], rmax, xin[t], f"{name} token {t}")
     del ops
     torch.cuda.empty_cache()
+
+
+def test_plan_random_glued_steps_against_sequential_model(qd):
+    """Random one-token steps with glue, run by the persistent kernel's glued
+    instance, against a sequential model of the buffers built from the
+    oracle: each group takes no prologue, RMSNorm (its own gamma) or the
+    gated product of two blocks, and each member stores with or without
+    silu.  Inputs are fresh, an earlier op's output or a slice of one;
+    outputs are fresh or overwrite an earlier output.  Every region's final
+    value is checked (bound 8x the acceptance bound, for chained inputs)."""
+    from int4_quantized_decode_amd import LinearOp
+    rng = np.random.default_rng(si.seed_for("random-glued-steps"))
+    arena_n = 1 << 20
+    for case in range(16):
+        fmt = ["int8_b32", "int4_g64"][case % 2]
+        init = si.activations(si.seed_for("random-glued-arena", case), 1, arena_n)[0]
+        arena = _gpu(init)
+        model = init.astype(np.float64).copy()
+        top = 0
+
+        def take(n):
+            nonlocal top
+            off = top
+            top += (n + 63) // 64 * 64
+            assert top <= arena_n
+            return off
+
+        ops, prog, outs = [], [], []
+        for g in range(int(rng.integers(2, 7))):
+            k = int(rng.choice([256, 512, 1024, 1088]))
+            pro = ["none", "rmsnorm", "glu"][int(rng.integers(3))]
+            span = 2 * k if pro == "glu" else k
+            cands = [(o, n) for o, n in outs if n >= span]
+            if cands and rng.random() < 0.6:
+                o, n = cands[int(rng.integers(len(cands)))]
+                xo = o + 8 * int(rng.integers(0, (n - span) // 8 + 1))
+            else:
+                xo = take(span)
+            gamma = None
+            if pro == "rmsnorm":
+                gamma = _gpu((1.0 + 0.25 * rng.standard_normal(k)).astype(np.float16))
+            members = []
+            for _ in range(int(rng.integers(1, 4))):
+                n = int(rng.choice([16, 48, 100, 256, 1000, 2176]))
+                same = [o for o, nn in outs if nn == n and not (o < xo + span and xo < o + n)
+                        and all(o != mo for mo, _, _, _ in members)]
+                yo = same[0] if same and rng.random() < 0.25 else take(n)
+                epi = "silu" if rng.random() < 0.4 else "none"
+                w = si.weights(si.seed_for("random-glued-w", case, g, len(members)), n, k)
+                members.append((yo, n, w, epi))
+            for yo, n, w, epi in members:
+                ops.append(LinearOp(_pack(qd, fmt, w), arena[xo:xo + span], arena[yo:yo + n], g,
+                                    prologue=pro, gamma=gamma, eps=EPS if pro == "rmsnorm" else 0.0,
+                                    epilogue=epi))
+            prog.append((xo, k, span, pro, None if gamma is None else _host(gamma), members))
+            outs.extend((yo, n) for yo, n, _, _ in members)
+        plan = qd.StackPlan(ops, 1)
+        assert plan.persistent, f"case {case}"
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        got = _host(arena).astype(np.float64)
+        final = {}
+        for xo, k, span, pro, gam, members in prog:
+            raw = model[xo:xo + span].astype(np.float16)
+            X = glue.apply_prologue(pro, raw, gam, EPS).astype(np.float64)
+            for yo, n, w, epi in members:
+                parts = _parts(fmt, w)
+                Y = linear.ref_linear(fmt, parts, X)
+                if epi == "silu":
+                    Y = glue.silu_fp16(Y.astype(np.float16)).astype(np.float64)
+                model[yo:yo + n] = Y.astype(np.float16).astype(np.float64)
+                final[yo] = (n, Y, X, linear.row_max_abs(fmt, parts))
+        for yo, (n, Y, X, rmax) in final.items():
+            check_vector(got[yo:yo + n], Y, 8 * rmax, X, f"case {case} ({fmt}) output at {yo}")
+        plan.close()
