@@ -18,7 +18,11 @@ int8 b32 (symmetric absmax, block of 32 along K)
     Readings (the pages give only the names): divisor 127, code -128 unused;
     the quotient uses the STORED fp16 scale so codes and dequantization agree;
     rounding is half-to-even; an all-zero block has scale 0 and codes 0;
-    non-finite input or a scale beyond fp16 range is refused.
+    non-finite input or a scale beyond fp16 range is refused.  The clamp to
+    +-127 acts only when the stored scale rounded below a/127 by more than
+    the half step it leaves, which happens for fp16-subnormal scales
+    (a < 127 * 2^-14): e.g. a = 127 * 1.4 * 2^-24 stores s = 2^-24 and
+    |w| / s reaches 177.8.
 
 int4 g64 (affine min/max, group of 64 along K)
     Source: CoreML-LLM handoff page, Architecture paragraph ("INT4
@@ -27,13 +31,21 @@ int4 g64 (affine min/max, group of 64 along K)
     unpinned by the pages).
 
     Per group of 64 weights w (fp32):
-      mn, mx = min w, max w                 exact
+      mn, mx = min w, max w                 exact; IEEE 754-2019 minimum and
+                                            maximum, which order -0 below +0
       s = fp16_RNE(fl32(fl32(mx - mn) / 15)),  m = fp16_RNE(mn)
       q = 0                                 if s == 0
         = clamp(rint(fl32(fl32(w - m) / s)), 0, 15)
       w^ = m + q * s                        (exact in fp64)
     Canonical packing: uint32 word j of a row holds codes 8j..8j+7, code 8j+i
     in bits [4i, 4i+4) (low nibble = lowest k).
+
+    Readings: a group whose least value is zero stores the min -0 (bits
+    0x8000) when any of its zeros is -0, else +0; the sign of a zero max never
+    reaches a stored bit (mx - mn is +0 or exactly |mn|).  The clamp to 0..15
+    acts when fp16 rounding of the min or the scale moves a code past the
+    ends, e.g. a group 0.3 + 1e-5 u, whose range gives s ~ 3e-6 while
+    |mn - m| reaches 1.2e-4.
 
 fp16 (unquantized head)
     Source: zoo Qwen3-VL page, Measured table, "2B int8lin (tied fp16 head)"
@@ -53,6 +65,24 @@ GROUP4 = 64
 BLOCK16 = 32
 QMAX8 = 127
 QMAX4 = 15
+
+
+def _clamp_codes(qf: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """Clamp rounded quotients to the code range [lo, hi]."""
+    return np.clip(qf, lo, hi)
+
+
+def _group_min_max(groups: np.ndarray):
+    """Per group (last axis): IEEE 754-2019 minimum and maximum, which order
+    -0 below +0 whatever order the zeros come in."""
+    mn = np.min(groups, axis=-1)
+    mx = np.max(groups, axis=-1)
+    zero = groups == 0
+    neg_zero = np.any(zero & np.signbit(groups), axis=-1)
+    pos_zero = np.any(zero & ~np.signbit(groups), axis=-1)
+    mn = np.where(mn == 0, np.where(neg_zero, np.float32(-0.0), np.float32(0.0)), mn)
+    mx = np.where(mx == 0, np.where(pos_zero, np.float32(0.0), np.float32(-0.0)), mx)
+    return mn.astype(np.float32), mx.astype(np.float32)
 
 
 def _check_input(w: np.ndarray, mult: int) -> np.ndarray:
@@ -84,7 +114,7 @@ def quantize_int8_b32(w: np.ndarray):
         quot = (blocks / sf).astype(np.float32)
     qf = np.rint(quot)
     qf = np.where(sf == 0, np.float32(0), qf)
-    q = np.clip(qf, -QMAX8, QMAX8).astype(np.int8)
+    q = _clamp_codes(qf, -QMAX8, QMAX8).astype(np.int8)
     return q.reshape(n, k), s16
 
 
@@ -100,8 +130,7 @@ def quantize_int4_g64(w: np.ndarray):
     n, k = w.shape
     groups = w.reshape(n, k // GROUP4, GROUP4)
     if k:
-        mn = np.min(groups, axis=2)
-        mx = np.max(groups, axis=2)
+        mn, mx = _group_min_max(groups)
     else:
         mn = mx = np.zeros((n, 0), np.float32)
     rng = (mx - mn).astype(np.float32)
@@ -118,7 +147,7 @@ def quantize_int4_g64(w: np.ndarray):
         quot = (shifted / sf).astype(np.float32)
     qf = np.rint(quot)
     qf = np.where(sf == 0, np.float32(0), qf)
-    q = np.clip(qf, 0, QMAX4).astype(np.uint8)
+    q = _clamp_codes(qf, 0, QMAX4).astype(np.uint8)
     return q.reshape(n, k), s16, m16
 
 

@@ -12,6 +12,7 @@ import pytest
 import synthetic_inputs as si
 from oracle import layout, linear, quant
 from tests import exact_fp as X
+from tests import hard_weights
 
 RNG = np.random.default_rng(12345)
 
@@ -179,27 +180,170 @@ def test_int8_refuses_bad_input():
         quant.quantize_int8_b32(np.zeros((2, 48), np.float32))
 
 
+def _int8_mismatches(w, q, s):
+    bad = []
+    for n in range(w.shape[0]):
+        for b in range(w.shape[1] // 32):
+            codes, s_ref, amb = _brute_int8(w[n, 32 * b:32 * b + 32])
+            if float(s[n, b]) != s_ref:
+                bad.append((n, b, "scale"))
+            for i in range(32):
+                got = int(q[n, 32 * b + i])
+                if (abs(got - codes[i]) > 1) if amb[i] else (got != codes[i]):
+                    bad.append((n, b, i))
+    return bad
+
+
+def _int8_clamp_events(w):
+    """(high, low) counts of weights whose exact quotient by the stored scale
+    lies beyond +-127.5: those the clamp decides."""
+    hi = lo = 0
+    for n in range(w.shape[0]):
+        for b in range(w.shape[1] // 32):
+            blk = w[n, 32 * b:32 * b + 32]
+            s = Fraction(X.fp16(X.fp32(max(abs(Fraction(float(v))) for v in blk) / 127)))
+            if s == 0:
+                continue
+            for v in blk:
+                t = Fraction(float(v)) / s
+                hi += t > Fraction(255, 2)
+                lo += t < -Fraction(255, 2)
+    return hi, lo
+
+
+def test_int8_clamp_subnormal_scales_brute_force():
+    """Blocks with fp16-subnormal scales that round well below a/127 reach
+    the +-127 clamp on both signs; codes must still be the nearest of the
+    255 levels (the clamp picks the end level)."""
+    w = hard_weights.int8_clamp_rows(256)
+    hi, lo = _int8_clamp_events(w)
+    assert hi > 0 and lo > 0, (hi, lo)
+    q, s = quant.quantize_int8_b32(w)
+    assert _int8_mismatches(w, q, s) == []
+    assert int(q.min()) == -127 and int(q.max()) == 127
+
+
 # ---------------------------------------------------------------- int4 g64
+
+def _brute_int4(blk):
+    """Reference for one group: scale and min from the definition's
+    roundings, codes by exhaustive search of the nearest of 16 levels."""
+    mn, mx = Fraction(float(blk.min())), Fraction(float(blk.max()))
+    s_ref = X.fp16(X.fp32(Fraction(X.fp32(mx - mn)) / 15))
+    m_ref = X.fp16(mn)
+    S, M = Fraction(s_ref), Fraction(m_ref)
+    codes, ambiguous = [], []
+    for v in blk:
+        W = Fraction(float(v))
+        if S == 0:
+            codes.append(0)
+            ambiguous.append(False)
+            continue
+        codes.append(min(range(16), key=lambda c: (abs(W - (M + c * S)), c % 2)))
+        ambiguous.append(_near_tie((W - M) / S, 2.0 ** -22))
+    return codes, s_ref, m_ref, ambiguous
+
+
+def _int4_mismatches(w, q, s, m):
+    bad = []
+    for n in range(w.shape[0]):
+        for g in range(w.shape[1] // 64):
+            blk = w[n, 64 * g:64 * g + 64]
+            codes, s_ref, m_ref, amb = _brute_int4(blk)
+            if float(s[n, g]) != s_ref or float(m[n, g]) != m_ref:
+                bad.append((n, g, "scale/min"))
+            for i in range(64):
+                got = int(q[n, 64 * g + i])
+                if (abs(got - codes[i]) > 1) if amb[i] else (got != codes[i]):
+                    bad.append((n, g, i))
+    return bad
+
 
 def test_int4_brute_force_argmin():
     w = si.weights(20, 4, 128)
     q, s, m = quant.quantize_int4_g64(w)
-    for n in range(4):
-        for g in range(2):
+    assert _int4_mismatches(w, q, s, m) == []
+
+
+def _int4_clamp_events(w):
+    hi = lo = 0
+    for n in range(w.shape[0]):
+        for g in range(w.shape[1] // 64):
             blk = w[n, 64 * g:64 * g + 64]
-            mn, mx = Fraction(float(blk.min())), Fraction(float(blk.max()))
-            s_ref = X.fp16(X.fp32(Fraction(X.fp32(mx - mn)) / 15))
-            m_ref = X.fp16(mn)
-            assert float(s[n, g]) == s_ref and float(m[n, g]) == m_ref
-            S, M = Fraction(s_ref), Fraction(m_ref)
-            for i, v in enumerate(blk):
-                W = Fraction(float(v))
-                best = min(range(16), key=lambda c: (abs(W - (M + c * S)), c % 2))
-                got = int(q[n, 64 * g + i])
-                if _near_tie((W - M) / S, 2.0 ** -22):
-                    assert abs(got - best) <= 1
-                else:
-                    assert got == best, (n, g, i)
+            _, s_ref, m_ref, _ = _brute_int4(blk)
+            if s_ref == 0:
+                continue
+            for v in blk:
+                t = (Fraction(float(v)) - Fraction(m_ref)) / Fraction(s_ref)
+                hi += t > Fraction(31, 2)
+                lo += t < -Fraction(1, 2)
+    return hi, lo
+
+
+def test_int4_clamp_brute_force():
+    """Groups whose fp16 min lands far from the true min compared with the
+    scale reach both clamps (all codes of a group, or only its ends)."""
+    w = hard_weights.int4_clamp_rows(256)
+    hi, lo = _int4_clamp_events(w)
+    assert hi > 0 and lo > 0, (hi, lo)
+    q, s, m = quant.quantize_int4_g64(w)
+    assert _int4_mismatches(w, q, s, m) == []
+    assert int(q.min()) == 0 and int(q.max()) == 15
+
+
+# Planted mistakes in the oracle's clamp: each must fail a pin above.
+_CLAMP_MUTANTS = {
+    "no clamp": lambda qf, lo, hi: qf,
+    "int8 floor -128": lambda qf, lo, hi: np.clip(qf, lo - 1 if lo < 0 else lo, hi),
+    "int4 clamp to 255, masked": lambda qf, lo, hi: (np.clip(qf, lo, 255) % 16 if hi == 15
+                                                    else np.clip(qf, lo, hi)),
+    "int4 floor -1": lambda qf, lo, hi: np.clip(qf, -1 if hi == 15 else lo, hi),
+    "int8 ceiling 126": lambda qf, lo, hi: np.clip(qf, lo, hi - 1 if hi == 127 else hi),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_CLAMP_MUTANTS))
+def test_clamp_mutants_fail_the_pins(monkeypatch, name):
+    monkeypatch.setattr(quant, "_clamp_codes", _CLAMP_MUTANTS[name])
+    w8 = hard_weights.int8_clamp_rows(128)
+    w4 = hard_weights.int4_clamp_rows(128)
+    with np.errstate(invalid="ignore", over="ignore"):
+        q8, s8 = quant.quantize_int8_b32(w8)
+        q4, s4, m4 = quant.quantize_int4_g64(w4)
+    caught = bool(_int8_mismatches(w8, q8, s8)) or bool(_int4_mismatches(w4, q4, s4, m4))
+    assert caught, f"planted mistake '{name}' passes every clamp pin"
+
+
+def _ieee2019_min(vals):
+    """IEEE 754-2019 minimum over a list: the least value, -0 below +0."""
+    return min(vals, key=lambda v: (v, 0 if (v == 0 and math.copysign(1.0, v) < 0) else 1))
+
+
+def test_int4_signed_zero_min():
+    """A group's stored min follows IEEE 754-2019 minimum: -0 (bits 0x8000)
+    when the least value is zero and any zero is -0, whatever the order;
+    zero groups have a zero scale and zero codes."""
+    w = hard_weights.signed_zero_rows(128)
+    q, s, m = quant.quantize_int4_g64(w)
+    mbits = m.view(np.uint16)
+    for n in range(w.shape[0]):
+        for g in range(2):
+            blk = [float(v) for v in w[n, 64 * g:64 * g + 64]]
+            want = np.float16(_ieee2019_min(blk)).view(np.uint16)
+            assert int(mbits[n, g]) == int(want), (n, g, hex(int(mbits[n, g])), hex(int(want)))
+    assert [int(b) for b in mbits[:4, 0]] == [0x0000, 0x8000, 0x8000, 0x8000]
+    assert int(mbits[4, 0]) == 0x8000 and int(mbits[5, 0]) == 0 and int(mbits[6, 0]) == 0x8000
+    assert not s[:4].view(np.uint16).any() and not q[:4].any()
+    assert _int4_mismatches(w, q, s, m) == []
+
+
+def test_int4_order_dependent_min_fails_the_pin(monkeypatch):
+    """A min that keeps whichever zero comes first (plain np.min) is caught."""
+    def first_zero(groups):
+        return groups.min(axis=-1), groups.max(axis=-1)
+    monkeypatch.setattr(quant, "_group_min_max", first_zero)
+    with pytest.raises(AssertionError):
+        test_int4_signed_zero_min()
 
 
 def test_int4_roundtrip_and_degenerate():
