@@ -18,7 +18,10 @@
  *   int4 g64  -- 4-bit codes per group of 64 along K (CoreML-LLM Qwen3-VL
  *                4B/8B handoff page, Architecture paragraph), in affine form:
  *                s = fp16(fl32(fl32(max - min) / 15)), m = fp16(min),
- *                q = clamp(rint(fl32(fl32(w - m) / s)), 0, 15), w^ = m + q s.
+ *                q = clamp(rint(fl32(fl32(w - m) / s)), 0, 15), w^ = m + q s;
+ *                min and max order -0 below +0 (IEEE 754-2019 minimum and
+ *                maximum), so a group whose least value is zero stores the min
+ *                -0 when any of its zeros is -0.
  *   A zero scale gives zero codes.  Rounding is IEEE round-to-nearest-even
  *   throughout.
  *
@@ -213,6 +216,13 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * buffers; the persistent kernel sums each row's tiles in its own fixed order,
  * so its outputs may differ from the launches' in the last bit (and are the
  * same from run to run).
+ * The persistent kernel runs one workgroup per compute unit and needs all of
+ * them resident at once.  Runs use a plain launch, which on a device with no
+ * other work running makes them so; if another kernel holds compute units,
+ * the first device-wide wait of the run times out (waits are bounded, so the
+ * kernel still ends), qd_stack_plan_error reports it, and from then on the
+ * plan uses a cooperative launch, which guarantees co-residency at a cost of
+ * about 30 us per step.
  * qd_stack_plan_create validates `ops` exactly as decode_linear_stack does,
  * copies the descriptors to the device and allocates the plan's scratch
  * (completion stamps, an error word and, at m > 1, copies of the step's
@@ -238,7 +248,8 @@ qd_status qd_stack_plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m
 qd_status qd_stack_plan_run(qd_stack_plan* plan, void* stream);
 /* Device error word of the last completed run (host reads it with a blocking
  * copy): 0 = fine, nonzero = a bounded wait timed out (the step's outputs are
- * incomplete; the plan resets its scratch and can be run again). */
+ * incomplete; the plan resets its scratch, switches to cooperative launches
+ * and can be run again). */
 qd_status qd_stack_plan_error(qd_stack_plan* plan, int32_t* out_error);
 /* *out = 1 if runs use the persistent kernel, 0 if they replay launches. */
 qd_status qd_stack_plan_is_persistent(const qd_stack_plan* plan, int32_t* out);

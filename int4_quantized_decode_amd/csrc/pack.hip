@@ -124,14 +124,23 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const float* __restrict_
       v[4 * i + 2] = f[2];
       v[4 * i + 3] = f[3];
     }
+    // IEEE 754-2019 minimum and maximum: -0 orders below +0 whatever order
+    // the zeros come in, so a group whose least value is zero stores the min
+    // -0 when any of its zeros is -0.  (The sign of a zero max never reaches
+    // a stored bit: mx - mn is then +0.)
     float mn = v[0], mx = v[0];
-    bool finite = true;
+    bool finite = true, neg_zero = false, pos_zero = false;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       finite = finite && __builtin_isfinite(v[i]);
-      mn = __builtin_fminf(mn, v[i]);
-      mx = __builtin_fmaxf(mx, v[i]);
+      mn = v[i] < mn ? v[i] : mn;
+      mx = v[i] > mx ? v[i] : mx;
+      const uint32_t b = __builtin_bit_cast(uint32_t, v[i]);
+      neg_zero = neg_zero || b == 0x80000000u;
+      pos_zero = pos_zero || b == 0u;
     }
+    if (mn == 0.0f) mn = neg_zero ? -0.0f : 0.0f;
+    if (mx == 0.0f) mx = pos_zero ? 0.0f : -0.0f;
     const float range = mx - mn;
     const float s32 = range / 15.0f;
     const half_t s16 = (half_t)s32;

@@ -49,19 +49,22 @@ __device__ __forceinline__ float dot8_int8(uint32_t d0, uint32_t d1, half8_t x, 
   return acc;
 }
 
-// sum_{i<8} (1024 + c_i) x_i for one int4 word (nibble p holds code
-// k0 + (0,2,4,6,1,3,5,7)[p]), so each and-or yields the pair (k0+2t, k0+2t+1).
-__device__ __forceinline__ float dot8_int4_biased(uint32_t w, half8_t x, float acc) {
-  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
-  const half2_t c01 = as_h2((w & m) | e);
-  const half2_t c23 = as_h2(((w >> 4) & m) | e);
-  const half2_t c45 = as_h2(((w >> 8) & m) | e);
-  const half2_t c67 = as_h2(((w >> 12) & m) | e);
-  acc = __builtin_amdgcn_fdot2(c01, (half2_t){x[0], x[1]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c23, (half2_t){x[2], x[3]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c45, (half2_t){x[4], x[5]}, acc, false);
-  acc = __builtin_amdgcn_fdot2(c67, (half2_t){x[6], x[7]}, acc, false);
-  return acc;
+// INT4 codes straight into fp16 operands with one AND per pair and no bias:
+// a half whose exponent field is zero holds mantissa * 2^-24 exactly (an fp16
+// subnormal), so for a word whose nibble p holds code (0,2,4,6,1,3,5,7)[p]
+//   w        & 0x000F000F = half2(c0, c1) * 2^-24
+//   w        & 0x00F000F0 = half2(c2, c3) * 2^-20   (16 times larger)
+//   (w >> 8) & 0x000F000F = half2(c4, c5) * 2^-24
+//   (w >> 8) & 0x00F000F0 = half2(c6, c7) * 2^-20
+// The two kinds of pair accumulate apart (lo, hi); the caller forms
+// lo + hi / 16 = 2^-24 sum c x, exact products summed in fp32.
+__device__ __forceinline__ void dot8_int4_sub(uint32_t w, half8_t x, float& lo, float& hi) {
+  const uint32_t m = 0x000F000Fu, m4 = 0x00F000F0u;
+  const uint32_t w8 = w >> 8;
+  lo = __builtin_amdgcn_fdot2(as_h2(w & m), (half2_t){x[0], x[1]}, lo, false);
+  hi = __builtin_amdgcn_fdot2(as_h2(w & m4), (half2_t){x[2], x[3]}, hi, false);
+  lo = __builtin_amdgcn_fdot2(as_h2(w8 & m), (half2_t){x[4], x[5]}, lo, false);
+  hi = __builtin_amdgcn_fdot2(as_h2(w8 & m4), (half2_t){x[6], x[7]}, hi, false);
 }
 
 // Sum over the four lanes rho, rho+16, rho+32, rho+48 (a row's K quarters);
@@ -119,11 +122,14 @@ __device__ __forceinline__ float tile_dot8(const Tile8& T, const half_t* xs_j, i
 }
 
 // Lane (g, rho)'s share of one int4 tile: 4 groups x 16 codes.
-// y += s * sum (1024 + c) x + (m - 1024 s) * sum x  ==  sum (m + c s) x.
+// y += sum_groups (s sum c x + m sum x); the code sums come out of
+// dot8_int4_sub scaled by 2^-24, so the scale terms collect apart and take
+// the factor 2^24 (exact) once per tile.
 __device__ __forceinline__ float tile_dot4(const Tile4& T, const half_t* xs_j, const float* xsum_j, int g,
                                   float acc) {
   const half8_t meta = __builtin_bit_cast(half8_t, T.meta);
   const float4_t xsum = *reinterpret_cast<const float4_t*>(xsum_j + 4 * g);
+  float acc_s = 0.0f;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -132,14 +138,14 @@ __device__ __forceinline__ float tile_dot4(const Tile4& T, const half_t* xs_j, c
       const half_t* xp = xs_j + 64 * gam + 16 * g;
       const half8_t xa = *reinterpret_cast<const half8_t*>(xp);
       const half8_t xb = *reinterpret_cast<const half8_t*>(xp + 8);
-      float p = dot8_int4_biased(T.c[s][2 * h], xa, 0.0f);
-      p = dot8_int4_biased(T.c[s][2 * h + 1], xb, p);
-      const float sc = (float)meta[gam], mn = (float)meta[4 + gam];
-      acc = __builtin_fmaf(sc, p, acc);
-      acc = __builtin_fmaf(__builtin_fmaf(-1024.0f, sc, mn), xsum[gam], acc);
+      float lo = 0.0f, hi = 0.0f;
+      dot8_int4_sub(T.c[s][2 * h], xa, lo, hi);
+      dot8_int4_sub(T.c[s][2 * h + 1], xb, lo, hi);
+      acc_s = __builtin_fmaf((float)meta[gam], __builtin_fmaf(hi, 0.0625f, lo), acc_s);
+      acc = __builtin_fmaf((float)meta[4 + gam], xsum[gam], acc);
     }
   }
-  return acc;
+  return __builtin_fmaf(acc_s, 16777216.0f, acc);
 }
 
 // fp16 weights (the unquantized head): chunk s holds the 32-wide block s of

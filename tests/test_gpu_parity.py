@@ -8,6 +8,8 @@ import pytest
 
 import synthetic_inputs as si
 from oracle import layout, linear, quant
+from tests import hard_weights
+from tests import test_oracle_pins as pins
 from tests.numerics import check_vector
 
 torch = pytest.importorskip("torch")
@@ -99,6 +101,11 @@ def _adversarial(fmt, n=32, k=512, near_max=True):
     for c in range(16):                                             # near-ties around x.5
         w[7, c] = np.float32((c + 0.5) * 2.0 ** -7 * (1 + (-1) ** c * 2.0 ** -20))
     w[7, 31] = np.float32(127 * 2.0 ** -7)
+    # rows that reach the quantizers' clamps (subnormal int8 scales; INT4
+    # groups whose fp16 min lands far from the true min) and signed zeros
+    w[10:16, :] = hard_weights.int8_clamp_rows(k)
+    w[16:22, :] = hard_weights.int4_clamp_rows(k)
+    w[22:30, :] = hard_weights.signed_zero_rows(k)
     if fmt == "fp16":
         # exact midpoints between fp16 neighbours (ties), both signs, many exponents
         base = (rng.standard_normal(k) * np.exp2(rng.integers(-20, 12, k))).astype(np.float16)
@@ -112,6 +119,14 @@ def _adversarial(fmt, n=32, k=512, near_max=True):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_pack_adversarial_bit_exact(qd, fmt):
     w = _adversarial(fmt)
+    # the oracle takes the clamp branches on these rows (both ends, both formats)
+    if fmt == "int8_b32":
+        hi, lo = pins._int8_clamp_events(w[10:16])
+        assert hi > 0 and lo > 0
+    if fmt == "int4_g64":
+        hi, lo = pins._int4_clamp_events(w[16:22])
+        assert hi > 0 and lo > 0
+        assert (_oracle_parts(fmt, w)[2][22:30].view(np.uint16) == 0x8000).any()
     pw = _pack(qd, fmt, _gpu(w))
     got = _host(pw.blob)
     want = _oracle_blob(fmt, _oracle_parts(fmt, w))
