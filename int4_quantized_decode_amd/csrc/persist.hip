@@ -6,7 +6,7 @@
 // the next kernel starts loading only after the previous one drains.  Here the
 // weight stream keeps going across group boundaries:
 //
-//   * one workgroup per CU (cooperative launch, all co-resident), 16 waves:
+//   * one workgroup per CU (all co-resident), 16 waves:
 //     streaming compute waves, reserve compute waves and 1 control wave.  The
 //     workgroup's share of every group's schedule lives in LDS, so no wave
 //     waits on a memory round trip to find its next tiles;
@@ -1120,6 +1120,7 @@ struct qd_stack_plan {
   qd::PlanArgs args{};
   size_t lds = 0;
   unsigned long long epoch = 0;
+  bool cooperative = false;              // launch cooperatively (after a run whose wait timed out)
 };
 
 namespace qd {
@@ -1729,8 +1730,18 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   }
   plan->args.epoch = ++plan->epoch;
   void* kargs[] = {&plan->args};
-  const hipError_t e = hipLaunchCooperativeKernel(kernel_ptr(plan->fmt, plan->multi, plan->glue), dim3(plan->args.G),
-                                                  dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
+  // One workgroup per CU, each needing a whole CU (1024 threads and most of
+  // its LDS), so on an otherwise idle device a plain launch makes them all
+  // resident at once; it saves the cooperative launch's own cost (about 30
+  // us per step, measured).  Should another kernel hold CUs, some
+  // workgroups would wait for it: the first device-wide wait then times out
+  // (every wait is bounded, so the kernel still ends), the run reports the
+  // timeout, and the plan launches cooperatively from then on.
+  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue);
+  const hipError_t e =
+      plan->cooperative
+          ? hipLaunchCooperativeKernel(kfn, dim3(plan->args.G), dim3(kWaves * 64), kargs, (unsigned)plan->lds, s)
+          : hipLaunchKernel(kfn, dim3(plan->args.G), dim3(kWaves * 64), kargs, (unsigned)plan->lds, s);
   if (e != hipSuccess) {
     --plan->epoch;
     return QD_ELAUNCH;
@@ -1748,11 +1759,14 @@ qd_status plan_error(qd_stack_plan* plan, int32_t* out_error) {
     return QD_ELAUNCH;
   *out_error = (int32_t)e;
   if (e != 0) {
-    // A timed-out wait leaves the counters inconsistent: start over.
+    // A timed-out wait leaves the counters inconsistent: start over.  The
+    // workgroups may not all have been resident (another kernel held CUs):
+    // later runs launch cooperatively, which guarantees they are.
     if (hipMemset(plan->scratch, 0, plan->scratch_bytes) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
       return QD_ELAUNCH;
     plan->epoch = 0;
+    plan->cooperative = true;
   }
   return QD_OK;
 }
