@@ -293,6 +293,32 @@ qd_status qd_stack_plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t
 void qd_stack_plan_destroy(qd_stack_plan* plan);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one step of
+ * `ops` in the persistent kernel, as a plan made from the same ops would run
+ * it, with no plan object and no allocation.  The plan's tables and scratch
+ * live in one static device array of about 4.1 MiB per device (held until
+ * the process ends), whose address is looked up once per device on the first
+ * call; each call rewrites what it uses through small kernels on `stream`
+ * (the tables travel as kernel arguments, so a captured graph replays exactly
+ * the captured call).  Differences from a plan: activations are always read
+ * in place (no copies in matrix-core order, so steps with several token rows
+ * run somewhat slower); the launch is always a plain one (see the plan's
+ * launch above; there is no plan to switch to cooperative launches).
+ * Arguments and validation as decode_linear_stack; additionally QD_ESHAPE if
+ * the step needs more than 512 group records or 1024 member records after
+ * the row-range split at several token rows, QD_EALIGN if err_flag is not
+ * 4-byte aligned.  `err_flag` (device int32, may be NULL) has the run's
+ * error bits OR-ed in (nonzero: a bounded wait timed out; the outputs are
+ * incomplete).  Steps the persistent kernel does not take are replayed as
+ * decode_linear_stack's launches, as a plan would.  All calls on one device
+ * share the array: calls that overlap in time on one device (two streams,
+ * two threads) race and must be serialised by the caller.
+ */
+qd_status qd_stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t* err_flag,
+                               void* stream);
+
+/*
  * Measurement helper (not part of the method): read every byte of the device
  * buffer `buf` (16-byte aligned, `bytes` > 0) once with a plain streaming
  * kernel of `grid` workgroups (1..65535) x 256 threads, so a run can quote

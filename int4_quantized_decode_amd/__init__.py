@@ -20,6 +20,7 @@ from ._lib import (QD_EPI_NONE, QD_EPI_SILU, QD_FMT_FP16, QD_FMT_INT4_G64, QD_FM
 __all__ = [
     "FORMATS", "PackedWeight", "QDError", "packed_bytes", "qpack_int8_b32", "qpack_int4_g64",
     "qpack_fp16", "qgemv_int8_b32", "qgemv_int4_g64", "qgemv_fp16", "qgemm_small_m", "decode_linear_stack", "StackPlan",
+    "stack_run_noalloc",
     "QD_MAX_K", "QD_MAX_M", "LinearOp", "PROLOGUES", "EPILOGUES",
 ]
 
@@ -252,6 +253,17 @@ class StackPlan:
             self.close()
         except Exception:
             pass
+
+
+def stack_run_noalloc(ops, m: int = 1, err: torch.Tensor | None = None) -> None:
+    """One step of `ops` in the persistent kernel without a plan object and
+    without allocating device memory (tables and scratch in the library's
+    static per-device array).  `err`, an int32 CUDA tensor, gets the run's
+    error bits OR-ed in.  Calls overlapping on one device race."""
+    if err is not None and not (err.is_cuda and err.dtype == torch.int32 and err.numel() >= 1):
+        raise ValueError("err must be an int32 CUDA tensor")
+    arr = _op_array(ops)
+    check(lib.qd_stack_run_noalloc(arr, len(ops), m, _ptr(err), _stream()), "qd_stack_run_noalloc")
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int = 512) -> None:

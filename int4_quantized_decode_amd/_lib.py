@@ -73,6 +73,8 @@ SIGNATURES = {
     "qd_read_probe": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p]),
     "qd_stack_plan_destroy": (None, [ctypes.c_void_p]),
+    "qd_stack_run_noalloc": (ctypes.c_int32, [ctypes.POINTER(QDLinearOp), ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 

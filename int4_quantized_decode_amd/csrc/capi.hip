@@ -226,6 +226,11 @@ QD_EXPORT qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t p
 
 QD_EXPORT void qd_stack_plan_destroy(qd_stack_plan* plan) { plan_destroy(plan); }
 
+QD_EXPORT qd_status qd_stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t* err_flag,
+                                         void* stream) {
+  return stack_run_noalloc(ops, n_ops, m, err_flag, static_cast<hipStream_t>(stream));
+}
+
 QD_EXPORT qd_status qd_stack_plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t workgroups,
                                            int64_t* out, int64_t cap, int64_t* out_len) {
   if (!out_len || cap < 0) return QD_EINVAL;

@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1380,7 +1381,11 @@ struct PlanLayout {
   size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
 };
 
-void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanLayout* L) {
+// `copies`: whether steps with several token rows keep activation copies in
+// matrix-core order (plan scratch); without them every activation is read in
+// place.
+void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanLayout* L,
+                 bool copies = true) {
   *L = PlanLayout{};
   L->G = G;
   // Persistent walker: one format, no empty-K groups; one token row (with or
@@ -1437,7 +1442,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   // read in place.
   std::vector<XtJob> jobs;
   int64_t xt_total = 0;
-  if (multi) {
+  if (multi && copies) {
     std::map<std::pair<const void*, int64_t>, int64_t> early_slots;
     std::map<std::pair<size_t, size_t>, int64_t> out_slots;
     auto new_slot = [&](int J) {
@@ -1782,6 +1787,191 @@ void plan_destroy(qd_stack_plan* plan) {
   if (plan->xt) (void)hipFree(plan->xt);
   if (plan->xt_jobs) (void)hipFree(plan->xt_jobs);
   delete plan;
+}
+
+
+// ---------------------------------------------------------------------------
+// The persistent step without a plan object, for callers that cannot
+// allocate device memory (code under graph capture, serving loops, harnesses
+// that forbid hipMalloc).  The plan's tables and scratch live in one static
+// device array per device, `scratch`, resolved once per device with
+// hipGetSymbolAddress; every call rewrites what it uses:
+//   [0, 4096)            completion stamps of up to kMaxWorkgroups workgroups
+//   [4096, 4352)         the error word
+//   groups, members      the step's group and member tables (at most
+//                        kStaticGroups / kStaticMembers records, after the
+//                        row-range split at several token rows)
+//   schedule             [group][workgroup] records, computed on the device
+// The tables reach the device as kernel arguments of small copy kernels, so a
+// captured graph replays exactly the call that was captured; nothing is
+// copied from host memory that could change afterwards.  Activations are read
+// in place (no copies in matrix-core order).  Calls that overlap on one
+// device race on the array.
+
+constexpr int kStaticGroups = 512;
+constexpr int kStaticMembers = 1024;
+constexpr size_t kStaticErrOff = (size_t)kMaxWorkgroups * 8;
+constexpr size_t kStaticGroupsOff = kStaticErrOff + 256;
+constexpr size_t kStaticMembersOff = kStaticGroupsOff + (size_t)kStaticGroups * sizeof(PGroup);
+constexpr size_t kStaticSchedOff = kStaticMembersOff + (size_t)kStaticMembers * sizeof(PMember);
+constexpr size_t kStaticBytes = kStaticSchedOff + (size_t)kStaticGroups * kMaxWorkgroups * sizeof(PSched);
+static_assert(kStaticGroupsOff % 256 == 0 && kStaticMembersOff % 16 == 0 && kStaticSchedOff % 16 == 0,
+              "tables are written in 16-byte units");
+
+// About 4.1 MiB per device, held until the process ends.
+static __device__ __align__(256) uint8_t scratch[kStaticBytes];
+
+namespace {
+
+constexpr int kPutBytes = 3072;   // table bytes per copy launch (kernel arguments stay below 4 KiB)
+struct PutPayload {
+  uint32_t n16;                   // 16-byte units in `data`
+  uint32_t pad[3];
+  u32x4 data[kPutBytes / 16];
+};
+
+__global__ __launch_bounds__(256) void put_kernel(u32x4* __restrict__ dst, PutPayload p) {
+  for (uint32_t i = threadIdx.x; i < p.n16; i += 256) dst[i] = p.data[i];
+}
+
+// Clear the stamps and the error word, and give each workgroup w its part of
+// every group: whole row-groups w R / G .. (w + 1) R / G, in tiles (at several
+// token rows, in units of `unit` row-groups), with its running offset in the
+// workgroup's sequence (the host's layout_plan computes the same records).
+__global__ __launch_bounds__(kMaxWorkgroups) void static_setup_kernel(uint8_t* __restrict__ base, int ngroups,
+                                                                      int G, int unit) {
+  const int w = threadIdx.x;
+  reinterpret_cast<unsigned long long*>(base)[w] = 0ull;
+  if (w == 0) *reinterpret_cast<uint32_t*>(base + kStaticErrOff) = 0u;
+  if (w >= G) return;
+  const PGroup* gs = reinterpret_cast<const PGroup*>(base + kStaticGroupsOff);
+  PSched* sched = reinterpret_cast<PSched*>(base + kStaticSchedOff);
+  int32_t off = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t R = gs[g].R, J = gs[g].J;
+    const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
+    const int64_t n = (unit > 1 ? (nrg + unit - 1) / unit : nrg) * J;
+    sched[(size_t)g * G + w] = PSched{(int32_t)n, off, (int32_t)r0, (int32_t)nrg};
+    if (nrg != 0) off += (int32_t)n;
+  }
+}
+
+__global__ void static_report_kernel(const uint32_t* __restrict__ err, int32_t* __restrict__ out) {
+  if (threadIdx.x == 0 && *err != 0u) atomicOr(out, (int32_t)*err);
+}
+
+struct StaticDevice {
+  bool ready = false;
+  hipError_t status = hipSuccess;
+  uint8_t* base = nullptr;        // device address of `scratch` on this device
+  int cus = 0;
+  size_t lds_max = 0;
+};
+
+constexpr int kStaticDevices = 64;
+std::mutex g_static_mu;
+StaticDevice g_static[kStaticDevices];
+
+// Set-up, once per device (with that device current): the array's device
+// address and the device's compute units and LDS.
+const StaticDevice* static_device(int dev) {
+  if (dev < 0 || dev >= kStaticDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& d = g_static[dev];
+  if (!d.ready) {
+    d.ready = true;
+    void* ptr = nullptr;
+    d.status = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    hipDeviceProp_t prop;
+    if (d.status == hipSuccess) d.status = hipGetDeviceProperties(&prop, dev);
+    if (d.status == hipSuccess) {
+      d.base = static_cast<uint8_t*>(ptr);
+      d.cus = prop.multiProcessorCount;
+      d.lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return d.status == hipSuccess ? &d : nullptr;
+}
+
+hipError_t put_table(uint8_t* dst, const void* src, size_t bytes, hipStream_t s) {
+  const uint8_t* p = static_cast<const uint8_t*>(src);
+  for (size_t done = 0; done < bytes; done += kPutBytes) {
+    PutPayload pl{};
+    const size_t n = std::min<size_t>(kPutBytes, bytes - done);
+    pl.n16 = (uint32_t)((n + 15) / 16);
+    memcpy(pl.data, p + done, n);
+    hipLaunchKernelGGL(put_kernel, dim3(1), dim3(256), 0, s, reinterpret_cast<u32x4*>(dst + done), pl);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32_t* err_flag, hipStream_t s) {
+  std::vector<StackGroup> replay;
+  qd_status st = build_groups(ops, n_ops, m, &replay);
+  if (st != QD_OK) return st;
+  if (err_flag && (uintptr_t)err_flag % 4) return QD_EALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QD_EDEVICE;
+  const StaticDevice* sd = static_device(dev);
+  if (!sd) return QD_EDEVICE;
+  const int G = std::min(sd->cus, kMaxWorkgroups);
+  PlanLayout L;
+  layout_plan(ops, n_ops, m, G, &L, /*copies=*/false);
+  auto replay_all = [&]() { return launch_groups(replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH; };
+  if (!L.persistent) return replay_all();
+  if (L.pg.size() > (size_t)kStaticGroups || L.pm.size() > (size_t)kStaticMembers) return QD_ESHAPE;
+  std::vector<StackGroup> tail;
+  if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) return replay_all();
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue);
+  if (L.lds > sd->lds_max) return replay_all();
+  if (L.lds > 65536 && hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return replay_all();
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kWaves * 64, L.lds) != hipSuccess || per_cu < 1) {
+    (void)hipGetLastError();
+    return replay_all();
+  }
+  uint8_t* const base = sd->base;
+  if (put_table(base + kStaticGroupsOff, L.pg.data(), sizeof(PGroup) * L.pg.size(), s) != hipSuccess ||
+      put_table(base + kStaticMembersOff, L.pm.data(), sizeof(PMember) * L.pm.size(), s) != hipSuccess)
+    return QD_ELAUNCH;
+  hipLaunchKernelGGL(static_setup_kernel, dim3(1), dim3(kMaxWorkgroups), 0, s, base, (int)L.pg.size(), G,
+                     L.multi ? unit16(L.fmt) : 1);
+  if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
+  PlanArgs a{};
+  a.groups = reinterpret_cast<const PGroup*>(base + kStaticGroupsOff);
+  a.members = reinterpret_cast<const PMember*>(base + kStaticMembersOff);
+  a.sched = reinterpret_cast<const PSched*>(base + kStaticSchedOff);
+  a.flags = reinterpret_cast<unsigned long long*>(base);
+  a.err = reinterpret_cast<uint32_t*>(base + kStaticErrOff);
+  a.epoch = 1;                    // stamps were cleared above
+  a.ngroups = (int32_t)L.pg.size();
+  a.nmem = (int32_t)L.pm.size();
+  a.G = G;
+  a.x_bytes = (int32_t)L.x_bytes;
+  a.xsum_bytes = (int32_t)L.xsum_bytes;
+  a.red_bytes = (int32_t)L.red_bytes;
+  a.cnt_bytes = (int32_t)L.cnt_bytes;
+  a.tab_bytes = (int32_t)L.tab_bytes;
+  a.m = (int32_t)m;
+  a.spin_limit = kSpinLimit;
+  void* kargs[] = {&a};
+  // A plain launch, as a plan's: capturable in a graph.
+  if (hipLaunchKernel(kfn, dim3(G), dim3(kWaves * 64), kargs, (unsigned)L.lds, s) != hipSuccess) return QD_ELAUNCH;
+  if (err_flag) {
+    hipLaunchKernelGGL(static_report_kernel, dim3(1), dim3(64), 0, s, a.err, err_flag);
+    if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
+  }
+  if (!tail.empty() && launch_groups(tail, s) != hipSuccess) return QD_ELAUNCH;
+  return QD_OK;
 }
 
 }  // namespace qd
