@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--path", choices=["plan", "launches"], default="plan",
                     help="plan: persistent one-launch step (default); launches: one fused launch per group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="default workload only: skip the chained step measured beside it")
     ap.add_argument("--rotate-mb", type=int, default=1024,
                     help="single-GEMV workload: weight copies cycled to exceed the caches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,54 +251,151 @@ def read_probe_gbs(qd, torch, dev, gib=2, reps=7):
     return best
 
 
-def cpu_baseline(si, workload, alg_bytes_step, dev, torch, min_seconds=10.0):
-    """The oracle as it stands, timed on host cores over a bounded sample:
-    layer 0's projections of the same workload (same weights, regenerated on
-    the device and copied over), repeated until about ten seconds of oracle
-    time have accumulated, then scaled to a full step by bytes."""
-    import numpy as np
-    from oracle import linear, quant
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _synthetic_parts(rng, fmt, n, k):
+    """Canonical quantized arrays of one [n, k] matrix with the format's
+    shapes and value ranges, drawn directly (timing only: the oracle's cost
+    does not depend on the values, and quantizing gigabytes on the host is
+    slower than the products being timed)."""
+    import numpy as np
+    if fmt == "int8_b32":
+        return (rng.integers(-127, 128, (n, k), dtype=np.int8),
+                (rng.standard_normal((n, k // 32)) * 2e-4).astype(np.float16))
+    return (rng.integers(0, 16, (n, k), dtype=np.uint8),
+            (rng.standard_normal((n, k // 64)) * 1e-3).astype(np.float16),
+            (rng.standard_normal((n, k // 64)) * 2e-2).astype(np.float16))
+
+
+def cpu_baseline(si, workload, alg_bytes_step):
+    """The oracle as it stands (fp64 dequantize-then-multiply, matrices
+    streamed in row chunks), timed on this host over every projection of one
+    full step of the workload, with BLAS threads pinned to the cores this
+    process may run on.  Codes and scales are drawn once per distinct matrix
+    shape and reused across layers."""
+    import numpy as np
+    from oracle import linear
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(cores)
     except Exception:
-        cores = 1
+        limiter = None
     wl = si.WORKLOADS[workload]
     if wl.single is not None:
         n, k = wl.single
-        sample = [("gemv", [("W", n, k)])]
-        model = "single"
+        groups, model = [("gemv", [("W", n, k)])], "single"
     else:
-        sample = wl.decoder.groups()[:4]          # layer 0: qkv, o, gate_up, down
-        model = wl.decoder.name
-    qz = quant.quantize_int8_b32 if wl.fmt == "int8_b32" else quant.quantize_int4_g64
-    work, pass_bytes = [], 0
-    for gname, members in sample:
+        groups, model = wl.decoder.groups(), wl.decoder.name
+    rng = np.random.default_rng(20261203)
+    parts_by_shape, xs = {}, {}
+    for gname, members in groups:
         k = members[0][2]
-        x = si.activations(si.activation_seed(workload, gname), wl.m, k)
-        xin = x if wl.m > 1 else x[0]
-        pass_bytes += wl.m * k * 2
+        if k not in xs:
+            x = si.activations(si.activation_seed(workload, "cpu", k), wl.m, k)
+            xs[k] = x if wl.m > 1 else x[0]
         for pname, n, kk in members:
-            w = si.weights_torch(si.matrix_seed(model, pname), n, kk, dev).cpu().numpy()
-            parts = qz(w)                                  # untimed: packing is offline
-            del w
-            work.append((parts, xin))
-            pass_bytes += sum(p.nbytes for p in parts) + wl.m * n * 2
-    t_total, passes = 0.0, 0
-    while t_total < min_seconds:
-        for parts, xin in work:
-            t0 = time.perf_counter()
-            linear.ref_linear(wl.fmt, parts, xin)
-            t_total += time.perf_counter() - t0
-        passes += 1
-    sample_bytes = pass_bytes * passes
-    gbs = sample_bytes / t_total / 1e9
-    us_step = t_total * 1e6 * alg_bytes_step / sample_bytes
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "us_per_step": round(us_step, 1),
-            "sample": f"layer 0 of {workload} ({len(sample)} groups, {pass_bytes / 1e6:.1f} MB of "
-                      f"quantized weights + activations) x {passes} passes, fp64 "
-                      f"dequantize-then-multiply, {t_total:.1f} s; scaled to a full step by bytes"}
+            if (n, kk) not in parts_by_shape:
+                parts_by_shape[(n, kk)] = _synthetic_parts(rng, wl.fmt, n, kk)
+    t0 = time.perf_counter()
+    for gname, members in groups:
+        for pname, n, kk in members:
+            linear.ref_linear(wl.fmt, parts_by_shape[(n, kk)], xs[kk])
+    secs = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
+    return {"value": round(alg_bytes_step / secs / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_step": round(secs * 1e6, 1), "cpu_model": _cpu_model(),
+            "sample": f"one full step of {workload} ({sum(len(m) for _, m in groups)} projections, every one "
+                      f"computed once), fp64 dequantize-then-multiply in row chunks of {linear.ROW_CHUNK}, "
+                      f"{secs:.1f} s; codes and scales drawn per matrix shape, not quantized from the step's weights"}
+
+
+TRIALS = 3
+
+# The pages' whole-model decode rates on an Apple M4 Max (int8hu bundles):
+# Qwen3-VL 4B and 8B Core AI cards, Measured paragraph; Qwen3.8-27B page,
+# Verified table (llm-benchmark -n 3).  Context only: another machine, and a
+# whole decoder rather than its linear layers.
+M4_MAX_DECODE_TOK_S = {"qwen3-vl-4b": 92.2, "qwen3-vl-8b": 54.3, "qwen3.8-27b": 15.7}
+
+
+def time_steps(run, steps, stream, torch):
+    """`steps` steps bracketed by a synchronize on both sides; HIP events on
+    the launch stream around each step.  Returns (wall seconds per step,
+    per-step event milliseconds)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        run(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def measure(qd, si, torch, workload, path, steps, warmup, rotate_mb, dev):
+    """Build a workload, warm up, then TRIALS timed trials of `steps` steps."""
+    log(f"building {workload} (weights generated and packed on the device)")
+    ops, alg_bytes, weight_bytes, m = build_stack(qd, si, torch, workload, dev)
+    log(f"{len(ops)} projections, {weight_bytes / 1e9:.3f} GB packed weights, {alg_bytes / 1e9:.4f} GB per step")
+    wl = si.WORKLOADS[workload]
+    if wl.single is not None:
+        # Cycle copies of the one matrix so successive steps miss the caches.
+        copies = max(1, (rotate_mb << 20) // max(1, weight_bytes))
+        op = ops[0]
+        rot = [op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
+                                  op.x, op.y, 0) for _ in range(copies - 1)]
+        step_ops = [[r] for r in rot]
+    else:
+        step_ops = [ops]
+    plans = []
+    if path == "plan":
+        plans = [qd.StackPlan(o, m) for o in step_ops]
+        runners = [p.run for p in plans]
+    else:
+        runners = [(lambda o=o: qd.decode_linear_stack(o, m)) for o in step_ops]
+    stream = torch.cuda.current_stream()
+    run = lambda i: runners[i % len(runners)]()  # noqa: E731
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    trials = []
+    for t in range(TRIALS):
+        wall, ev_ms = time_steps(run, steps, stream, torch)
+        trials.append((wall, ev_ms))
+        log(f"{workload} trial {t}: wall {wall * 1e6:.1f} us/step, event median "
+            f"{sorted(ev_ms)[len(ev_ms) // 2] * 1e3:.1f} us")
+    for p in plans:
+        if p.error():
+            raise RuntimeError("stack plan reported a timed-out wait")
+    persistent = path == "plan" and all(p.persistent for p in plans)
+    ngroups = len({op.group for op in step_ops[0]})
+    for p in plans:
+        p.close()
+    return {"ops": ops, "n_ops": len(ops), "alg_bytes": alg_bytes, "weight_bytes": weight_bytes, "m": m, "wl": wl,
+            "trials": trials, "persistent": persistent, "ngroups": ngroups}
+
+
+def summarize(res):
+    walls = sorted(w for w, _ in res["trials"])
+    med_wall = walls[len(walls) // 2]
+    all_ev = sorted(e for _, ev in res["trials"] for e in ev)
+    return {"wall_s": med_wall, "trials_us": [round(w * 1e6, 2) for w, _ in res["trials"]],
+            "spread_us": round((walls[-1] - walls[0]) * 1e6, 2),
+            "ev_mean_s": sum(all_ev) / len(all_ev) * 1e-3,
+            "ev_p10_us": all_ev[len(all_ev) // 10] * 1e3, "ev_p50_us": all_ev[len(all_ev) // 2] * 1e3,
+            "ev_p90_us": all_ev[(9 * len(all_ev)) // 10] * 1e3}
 
 
 def main():
@@ -319,69 +418,41 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    log(f"building {args.workload} (weights generated and packed on the device)")
-    ops, alg_bytes, weight_bytes, m = build_stack(qd, si, torch, args.workload, dev)
-    log(f"{len(ops)} projections, {weight_bytes / 1e9:.3f} GB packed weights, "
-        f"{alg_bytes / 1e9:.4f} GB per step")
+    res = measure(qd, si, torch, args.workload, args.path, args.steps, args.warmup, args.rotate_mb, dev)
+    sm = summarize(res)
+    alg_bytes, m, wl = res["alg_bytes"], res["m"], res["wl"]
+    wall_ms = sm["wall_s"] * 1e3
+    value = alg_bytes / sm["wall_s"] / 1e9
+    log(f"wall {wall_ms * 1e3:.1f} us/step (median of {TRIALS} trials {sm['trials_us']}), event median "
+        f"{sm['ev_p50_us']:.1f} us (p10 {sm['ev_p10_us']:.1f}, p90 {sm['ev_p90_us']:.1f})")
 
-    plans = []
-    wl = si.WORKLOADS[args.workload]
-    if wl.single is not None:
-        # Cycle copies of the one matrix so successive steps miss the caches.
-        copies = max(1, (args.rotate_mb << 20) // max(1, weight_bytes))
-        op = ops[0]
-        rot = [op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
-                                  op.x, op.y, 0) for _ in range(copies - 1)]
-        step_ops = [[r] for r in rot]
-    else:
-        step_ops = [ops]
-    if args.path == "plan":
-        plans = [qd.StackPlan(o, m) for o in step_ops]
-        runners = [p.run for p in plans]
-    else:
-        runners = [(lambda o=o: qd.decode_linear_stack(o, m)) for o in step_ops]
+    chained = None
+    if args.workload == "qwen3-8b-int8-m1" and args.path == "plan" and not args.no_chain:
+        # The same step with a true dependency at every boundary (each group
+        # reads an earlier group's output): the decode a real model runs.
+        del res["ops"]
+        torch.cuda.empty_cache()
+        cres = measure(qd, si, torch, "qwen3-8b-int8-chain-m1", "plan", args.steps, args.warmup, 0, dev)
+        csm = summarize(cres)
+        chained = {"workload": "qwen3-8b-int8-chain-m1", "us_per_step": round(csm["wall_s"] * 1e6, 2),
+                   "trials_us": csm["trials_us"], "spread_us": csm["spread_us"],
+                   "gbs": round(cres["alg_bytes"] / csm["wall_s"] / 1e9, 2),
+                   "frac_of_hbm_peak": round(cres["alg_bytes"] / csm["wall_s"] / 1e9 / HBM_PEAK_GBS, 4),
+                   "kernel_us_per_step": round(csm["ev_mean_s"] * 1e6, 2)}
+        log(f"chained step: {chained['us_per_step']:.1f} us ({chained['frac_of_hbm_peak']:.4f} of 8 TB/s)")
+        del cres["ops"]
+        torch.cuda.empty_cache()
 
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        runners[i % len(runners)]()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done; timing {args.steps} steps")
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    step_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        a, b = step_events[i]
-        a.record(stream)
-        runners[i % len(runners)]()
-        b.record(stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    step_ms = sorted(a.elapsed_time(b) for a, b in step_events)
-    med_ms = step_ms[len(step_ms) // 2]
-    for p in plans:
-        if p.error():
-            raise RuntimeError("stack plan reported a timed-out wait")
-    log(f"wall {wall_ms * 1e3:.1f} us/step, event median {med_ms * 1e3:.1f} us "
-        f"(p10 {step_ms[len(step_ms) // 10] * 1e3:.1f}, p90 {step_ms[(9 * len(step_ms)) // 10] * 1e3:.1f})")
-
-    value = alg_bytes / (wall_ms * 1e-3) / 1e9
     probe = read_probe_gbs(qd, torch, dev)
     log(f"read probe {probe:.0f} GB/s")
     # The timed kernel's average launch duration over the timed region: each
     # step's HIP-event pair on the launch stream brackets exactly one launch
     # of the persistent kernel (for the launch path: the step's launches and
     # the gaps between them).
-    ksec = sum(a.elapsed_time(b) for a, b in step_events) / len(step_events) * 1e-3
+    ksec = sm["ev_mean_s"]
     kernel_gbs = alg_bytes / ksec / 1e9
-    ngroups = len({op.group for op in step_ops[0]})
-    persistent = args.path == "plan" and all(p.persistent for p in plans)
+    persistent = res["persistent"]
+    ngroups = res["ngroups"]
     if args.path == "plan" and not persistent:
         log("the plan replays per-group launches for this workload")
     family = ("small_m_int8_kernel" if m > 1 else f"gemv_int{8 if wl.fmt == 'int8_b32' else 4}_kernel")
@@ -406,11 +477,12 @@ def main():
         "dtype": ("int8" if wl.fmt == "int8_b32" else "int4") + ("+fp16 head" if wl.head_fmt else ""),
         "data": "synthetic (W ~ N(0,0.02) fp32 quantized on the device; x ~ N(0,1) fp16)",
         "config": {"workload": args.workload, "m": m, "path": args.path,
-                   "bytes_per_step": alg_bytes, "weight_bytes": weight_bytes,
-                   "projections": len(ops), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "bytes_per_step": alg_bytes, "weight_bytes": res["weight_bytes"],
+                   "projections": res["n_ops"],
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "trials": TRIALS, "trials_us_per_step": sm["trials_us"], "trial_spread_us": sm["spread_us"],
                    "read_probe_gbs": round(probe, 1), "frac_of_read_probe": round(value / probe, 4),
-                   "us_p10": round(step_ms[len(step_ms) // 10] * 1e3, 2),
-                   "us_p90": round(step_ms[(9 * len(step_ms)) // 10] * 1e3, 2),
+                   "us_p10": round(sm["ev_p10_us"], 2), "us_p90": round(sm["ev_p90_us"], 2),
                    "glue": wl.glue, "chained": wl.chain or wl.glue,
                    "tok_per_s_note": ("linear stack with fused RMSNorm and SwiGLU glue; excludes attention, "
                                       "residual adds and embedding" if wl.glue else
@@ -419,12 +491,15 @@ def main():
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname,
                      "kernel_us_per_step": round(ksec * 1e6, 2)},
+        "context": {"m4_max_decode_tok_s": M4_MAX_DECODE_TOK_S,
+                    "note": "the pages' whole-model decode rates on Apple M4 Max (int8hu bundles); "
+                            "another machine and a whole decoder, so context rather than a baseline"},
     }
+    if chained is not None:
+        out["config"]["chained_step"] = chained
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(si, args.workload, alg_bytes, dev, torch)
-    for p in plans:
-        p.close()
+        log("timing the CPU oracle over one full step")
+        out["cpu_baseline"] = cpu_baseline(si, args.workload, alg_bytes)
     print(json.dumps(out), flush=True)
 
 

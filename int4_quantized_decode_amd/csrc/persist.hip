@@ -1283,15 +1283,16 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // SIMD; this was best for the 2B-, 4B- and 8B-shaped steps alike (15 to 50
 // tiles per workgroup per group).  More reserve tiles run several groups
 // ahead and are then not free for the next stall; fewer leave memory idle
-// for part of it.  INT4: no reserve waves, and rings of 2 tiles per
-// streaming wave (8B INT4 step 993-996 us; rings of 1, 3, 4 and 6 took 1098,
-// 1043-1050, 1089-1104 and 1111 us; 2 x 4, 4 x 2 and 7 x 2 reserve tiles with
-// rings of 2 took 1051-1059, 1021-1025 and 1095-1109 us).
+// for part of it.  INT4: rings of 2 tiles per streaming wave and 4 reserve
+// waves of 2 tiles (measured with the one-AND decode and the plain launch,
+// 8B INT4 step, us: reserve 0 914, 2 x 2 915, 3 x 2 902, 4 x 2 900, 5 x 2 924,
+// 6 x 2 965, 3 x 3 924, 4 x 3 925; rings of 3 and 4 without reserve 965 and
+// 1024).
 #ifndef QD_PLAN_RESERVE4
-#define QD_PLAN_RESERVE4 0
+#define QD_PLAN_RESERVE4 4
 #endif
 #ifndef QD_PLAN_RESERVE4_S
-#define QD_PLAN_RESERVE4_S 4
+#define QD_PLAN_RESERVE4_S 2
 #endif
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4, kReserveInt4S = QD_PLAN_RESERVE4_S;
 
