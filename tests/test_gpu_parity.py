@@ -351,6 +351,18 @@ def test_stack_mixed_formats_fp16_head(qd, m):
             plan.close()
 
 
+def _check_chain_on_device_inputs(bufs, parts_list, what):
+    """Op i read bufs[i] and wrote bufs[i + 1]: each output against the
+    oracle on the fp16 input the device actually read, at the acceptance
+    bound.  (Read too early, an input would still hold its NaN poison.)"""
+    vals = [_host(b).copy() for b in bufs]
+    for i, parts in enumerate(parts_list):
+        x_in = vals[i]
+        assert np.all(np.isfinite(x_in.astype(np.float64))), f"{what}: input of op {i}"
+        y_ref = linear.ref_linear("int8_b32", parts, x_in)
+        check_vector(vals[i + 1], y_ref, linear.row_max_abs("int8_b32", parts), x_in, f"{what} op {i}")
+
+
 def test_stack_chain_respects_order(qd):
     """A chain where each op reads the previous op's output: correct only if
     every group starts after the one before it has finished.  Outputs are
@@ -367,18 +379,7 @@ def test_stack_chain_respects_order(qd):
         for b in bufs[1:]:
             b.fill_(float("nan"))
         qd.decode_linear_stack(ops, 1)
-        oracle_ops = [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[0]), "x": x0}]
-        oracle_ops += [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[i]), "x_from": i - 1}
-                       for i in range(1, len(ws))]
-        refs = linear.ref_stack(oracle_ops)
-        x_in = x0.astype(np.float64)
-        for i, ref in enumerate(refs):
-            y = _host(bufs[i + 1])
-            parts = oracle_ops[i]["parts"]
-            rmax = linear.row_max_abs("int8_b32", parts)
-            # depth i inherits the fp16 rounding of i earlier outputs: bound grows linearly
-            check_vector(y, ref, (i + 1) * rmax, x_in, f"chain step {i}")
-            x_in = ref.astype(np.float16)
+        _check_chain_on_device_inputs(bufs, [quant.quantize_int8_b32(w) for w in ws], f"chain rep {rep}")
 
 
 # ------------------------------------------------------------------ full size, sampled
@@ -457,19 +458,15 @@ def test_plan_chain_respects_order(qd):
     oracle_ops = [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[0]), "x": x0}]
     oracle_ops += [{"fmt": "int8_b32", "parts": quant.quantize_int8_b32(ws[i]), "x_from": i - 1}
                    for i in range(1, depth)]
-    refs = linear.ref_stack(oracle_ops)
     for rep in range(3):
         for b in bufs[1:]:
             b.fill_(float("nan"))
         plan.run()
         torch.cuda.synchronize()
         assert plan.error() == 0
-        x_in = x0.astype(np.float64)
-        for i, ref in enumerate(refs):
-            y = _host(bufs[i + 1])
-            rmax = linear.row_max_abs("int8_b32", oracle_ops[i]["parts"])
-            check_vector(y, ref, (i + 1) * rmax, x_in, f"plan chain step {i} rep {rep}")
-            x_in = ref.astype(np.float16)
+        _check_chain_on_device_inputs(bufs, [op_["parts"] for op_ in oracle_ops], f"plan chain rep {rep}")
+        # and the chain as a whole follows the oracle's own chain
+        assert np.all(np.isfinite(_host(bufs[-1]).astype(np.float64)))
     plan.close()
 
 
@@ -988,6 +985,40 @@ def test_plan_multi_token_copy_of_a_split_member(qd):
     plan.close()
 
 
+def _group_slices(ops):
+    """[(first op, end op)] of each group of consecutive equal `group` ids."""
+    out, i = [], 0
+    while i < len(ops):
+        e = i + 1
+        while e < len(ops) and ops[e].group == ops[i].group:
+            e += 1
+        out.append((i, e))
+        i = e
+    return out
+
+
+def _prefix_states(qd, ops, m, restore, snapshot):
+    """The buffers before the step and after each of its groups, from plans of
+    the step's first 1, 2, ... groups, each run from the same initial state.
+    A group's schedule is the same in every plan that holds it (its ranges
+    depend on its own row-groups only), so its outputs are bit-identical
+    across them."""
+    states = []
+    restore()
+    torch.cuda.synchronize()
+    states.append(snapshot())
+    for _, e in _group_slices(ops):
+        sub = qd.StackPlan(ops[:e], m)
+        assert sub.persistent
+        restore()
+        sub.run()
+        torch.cuda.synchronize()
+        assert sub.error() == 0
+        states.append(snapshot())
+        sub.close()
+    return states
+
+
 @pytest.mark.parametrize("m,packed,fmt", [(1, False, "int8_b32"), (1, True, "int8_b32"), (16, False, "int8_b32"),
                                           (16, True, "int8_b32"), (16, False, "int4_g64"), (16, True, "int4_g64")])
 def test_plan_buffer_orderings(qd, m, packed, fmt):
@@ -1026,39 +1057,38 @@ def test_plan_buffer_orderings(qd, m, packed, fmt):
     ops = [LinearOp(pws[g], bufs[xb], bufs[yb], g) for g, (xb, yb) in enumerate(prog)]
     plan = qd.StackPlan(ops, m)
     assert plan.persistent
-    # the sequential model, with each stored output rounded to fp16
-    state = [v.astype(np.float16) for v in init]
-    want, xin = [None] * len(prog), [None] * len(prog)
-    for g, (xb, yb) in enumerate(prog):
-        parts = _oracle_parts(fmt, ws[g])
-        xin[g] = state[xb].copy()
-        want[g] = linear.ref_linear(fmt, parts, xin[g])
-        state[yb] = want[g].astype(np.float16)
-    final_writer = {}
-    for g, (xb, yb) in enumerate(prog):
-        final_writer[yb] = g
-    first = None
-    for rep in range(3):
+
+    def restore():
         for i, b in enumerate(bufs):
             b.copy_(_gpu(init[i]))
+
+    def snapshot():
+        return [_host(b).copy() for b in bufs]
+
+    # Each group against the oracle on the input the device gave it, at the
+    # acceptance bound; every other buffer untouched by it.
+    states = _prefix_states(qd, ops, m, restore, snapshot)
+    for g, (xb, yb) in enumerate(prog):
+        parts = _oracle_parts(fmt, ws[g])
+        xin = states[g][xb].reshape(m, k)
+        assert np.all(np.isfinite(xin.astype(np.float64))), f"group {g} input"
+        ref = linear.ref_linear(fmt, parts, xin)
+        got = states[g + 1][yb].reshape(m, k)
+        rmax = linear.row_max_abs(fmt, parts)
+        for t in range(m):
+            check_vector(got[t], ref[t], rmax, xin[t], f"buffer {yb} (group {g}) token {t}")
+        for b in range(nbuf):
+            if b != yb:
+                assert np.array_equal(states[g + 1][b].view(np.uint16), states[g][b].view(np.uint16)), \
+                    f"group {g} changed buffer {b}"
+    # The whole step in one plan, three runs: exactly the sequence above.
+    for rep in range(3):
+        restore()
         plan.run()
         torch.cuda.synchronize()
         assert plan.error() == 0
-        outs = [_host(b).copy() for b in bufs]
-        if first is None:
-            first = outs
-            for yb, g in final_writer.items():
-                parts = _oracle_parts(fmt, ws[g])
-                # the input the kernel saw was the device's own earlier output: bound the
-                # chain by the rows' magnitudes along the path (at most 3 products deep)
-                got, ref, xs = (outs[yb].reshape(m, k), want[g].reshape(m, k),
-                                xin[g].astype(np.float64).reshape(m, k))
-                for t in range(m):
-                    check_vector(got[t], ref[t], 4 * linear.row_max_abs(fmt, parts),
-                                 xs[t], f"buffer {yb} (group {g}) token {t}")
-        else:
-            for a_, b_ in zip(first, outs):
-                assert np.array_equal(a_.view(np.uint16), b_.view(np.uint16))
+        for b_, (a_, want_) in enumerate(zip(snapshot(), states[-1])):
+            assert np.array_equal(a_.view(np.uint16), want_.view(np.uint16)), f"rep {rep} buffer {b_}"
     plan.close()
 
 
@@ -1067,9 +1097,10 @@ def test_plan_random_steps_against_sequential_model(qd):
     buffers built from the oracle: groups of 1-3 members in one fp16 arena;
     each group reads a fresh region, an earlier op's whole output or (one
     token row) a slice of one; outputs go to fresh regions or overwrite an
-    earlier op's output.  Every region's final value is checked (bound 8x
-    the acceptance bound: inputs chain through up to six groups, and a
-    wrongly ordered read would be off by the whole value)."""
+    earlier op's output.  Plans of the step's first groups give the arena
+    after each group: every group's outputs against the oracle on the input
+    the device gave it, at the acceptance bound, and the one-plan step must
+    reproduce the final arena bit for bit."""
     from int4_quantized_decode_amd import LinearOp
     rng = np.random.default_rng(si.seed_for("random-steps"))
     arena_n = 1 << 21
@@ -1078,7 +1109,6 @@ def test_plan_random_steps_against_sequential_model(qd):
         m = [1, 5, 16][(case // 2) % 3]
         init = si.activations(si.seed_for("random-arena", case), 1, arena_n)[0]
         arena = _gpu(init)
-        model = init.astype(np.float64).copy()
         top = 0
 
         def take(n):
@@ -1113,21 +1143,171 @@ def test_plan_random_steps_against_sequential_model(qd):
             outs.extend((yo, n) for yo, n, _ in members)
         plan = qd.StackPlan(ops, m)
         assert plan.persistent, f"case {case}"
-        plan.run()
-        torch.cuda.synchronize()
-        assert plan.error() == 0
-        got = _host(arena).astype(np.float64)
-        # sequential model: each group reads its input, then writes its outputs
-        final = {}
-        for xo, k, members in prog:
-            X = model[xo:xo + m * k].reshape(m, k).copy()
+        init_g = _gpu(init)
+
+        def restore():
+            arena.copy_(init_g)
+
+        def snapshot():
+            return _host(arena).copy()
+
+        # Each group against the oracle on the input the device gave it, at
+        # the acceptance bound, and nothing outside its outputs changed; then
+        # the whole step in one plan must reproduce the final state exactly.
+        states = _prefix_states(qd, ops, m, restore, snapshot)
+        for g, (xo, k, members) in enumerate(prog):
+            X = states[g][xo:xo + m * k].reshape(m, k)
+            assert np.all(np.isfinite(X.astype(np.float64))), f"case {case} group {g} input"
+            touched = np.zeros(arena_n, bool)
             for yo, n, w in members:
                 parts = _oracle_parts(fmt, w)
                 Y = linear.ref_linear(fmt, parts, X)
-                model[yo:yo + m * n] = Y.astype(np.float16).astype(np.float64).reshape(-1)
-                final[yo] = (n, Y, X, linear.row_max_abs(fmt, parts))
-        for yo, (n, Y, X, rmax) in final.items():
-            G_ = got[yo:yo + m * n].reshape(m, n)
-            for t in range(m):
-                check_vector(G_[t], Y[t], 8 * rmax, X[t], f"case {case} ({fmt}, m={m}) output at {yo} token {t}")
+                G_ = states[g + 1][yo:yo + m * n].reshape(m, n)
+                rmax = linear.row_max_abs(fmt, parts)
+                for t in range(m):
+                    check_vector(G_[t], Y[t], rmax, X[t], f"case {case} ({fmt}, m={m}) group {g} output at {yo} token {t}")
+                touched[yo:yo + m * n] = True
+            assert np.array_equal(states[g + 1][~touched].view(np.uint16), states[g][~touched].view(np.uint16)), \
+                f"case {case} group {g} wrote outside its outputs"
+        restore()
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        assert np.array_equal(snapshot().view(np.uint16), states[-1].view(np.uint16)), f"case {case}"
         plan.close()
+
+
+def _one_row_per_row_group(n, salt):
+    """One row of every 16-row row-group, at a position that moves from
+    row-group to row-group (every row lane is used)."""
+    r = np.arange((n + 15) // 16)
+    return np.minimum(16 * r + (7 * r + salt) % 16, n - 1)
+
+
+@pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int8-chain-m1", "qwen3-8b-int4-m1",
+                                      "qwen3-8b-int8-m16"])
+def test_plan_full_size_every_row_group(qd, workload):
+    """The 8B-shaped step as the bench times it (and its chained, INT4 and
+    16-token variants): one row of every row-group of every projection
+    against the oracle, every token row, on the activations the op read."""
+    import bench
+    ops, alg_bytes, weight_bytes, m = bench.build_stack(qd, si, torch, workload, DEV)
+    plan = qd.StackPlan(ops, m)
+    assert plan.persistent
+    for op in ops:
+        op.y.fill_(float("nan"))
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    wl = si.WORKLOADS[workload]
+    names = [p for _, ms in wl.decoder.groups() for p, _, _ in ms]
+    assert len(names) == len(ops)
+    for i, (name, op) in enumerate(zip(names, ops)):
+        n, k = op.w.n, op.w.k
+        rows = _one_row_per_row_group(n, i)
+        w_full = si.weights_torch(si.matrix_seed(wl.decoder.name, name), n, k, DEV)
+        if wl.chain:                                   # the chained step's weight scale
+            w_full.mul_(1.0 / (si.W_STD * k ** 0.5))
+        w_rows = w_full[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        del w_full
+        x = op.x.cpu().numpy().reshape(m, k)           # the activations the op read
+        parts = _oracle_parts(wl.fmt, w_rows)
+        y_ref = linear.ref_linear(wl.fmt, parts, x).reshape(m, -1)
+        y_got = _host(op.y).reshape(m, n)[:, rows]
+        rmax = linear.row_max_abs(wl.fmt, parts)
+        for t in range(m):
+            check_vector(y_got[t], y_ref[t], rmax, x[t], f"{name} token {t}")
+    plan.close()
+    del ops
+    torch.cuda.empty_cache()
+
+
+# every matrix of every configuration: (model name, format, workload holding it)
+PACK_CONFIGS = [("single", "int8_b32", "gemv-2048x2048-int8"), ("qwen3-2b", "int8_b32", "qwen3-2b-int8-m1"),
+                ("qwen3-4b", "int8_b32", "qwen3-4b-int8-m1"), ("qwen3-8b", "int8_b32", "qwen3-8b-int8-m1"),
+                ("qwen3-8b", "int4_g64", "qwen3-8b-int4-m1"), ("qwen3.8-27b", "int8_b32", "qwen3.8-27b-int8-m1"),
+                ("qwen3-2b", "fp16", "qwen3-2b-int8-fp16head-m1")]
+
+
+@pytest.mark.parametrize("model,fmt,workload", PACK_CONFIGS)
+def test_pack_every_matrix_sampled(qd, model, fmt, workload):
+    """Every matrix of every configuration packed on the device: the first,
+    the last and two random row-groups of each compared byte for byte with
+    the oracle's blob of those rows (a row-group's tiles are contiguous, so
+    its bytes are the blob of its 16 rows).  The fp16 case is the int8lin
+    head."""
+    wl = si.WORKLOADS[workload]
+    if wl.single is not None:
+        mats = [("W", *wl.single)]
+    else:
+        mats = [(p, n, k) for _, ms in wl.decoder.groups() for p, n, k in ms]
+        if fmt == "fp16":
+            mats = [mt for mt in mats if mt[0] == "head"]
+    rng = np.random.default_rng(si.seed_for("pack-every", model, fmt))
+    tile = {"int8_b32": 4352, "int4_g64": 2304, "fp16": 8192}[fmt]
+    for name, n, k in mats:
+        w_full = si.weights_torch(si.matrix_seed(model, name), n, k, DEV)
+        blob = _pack(qd, fmt, w_full).blob
+        R, J = (n + 15) // 16, (k + 255) // 256
+        picks = sorted({0, R - 1, *(int(v) for v in rng.integers(0, R, 2))})
+        for r in picks:
+            rows = torch.arange(16 * r, min(n, 16 * r + 16), device=DEV)
+            w_rows = w_full[rows].cpu().numpy()
+            want = _oracle_blob(fmt, _oracle_parts(fmt, w_rows))
+            got = blob[r * J * tile:(r + 1) * J * tile].cpu().numpy()
+            assert want.size == got.size == J * tile
+            diff = np.flatnonzero(got != want)
+            assert diff.size == 0, f"{model} {fmt} {name} row-group {r}: {diff.size} bytes differ"
+        del w_full, blob
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_plan_new_activations_every_step(qd, m):
+    """One plan run for several decode steps, with fresh activations written
+    into the step's input buffer before each (as a decoder does token after
+    token).  The paths that read activations through the caches must see
+    this step's values, not lines left from the last one: at one token row a
+    chained group read through the caches (order flag 8); at 16 token rows an
+    activation copied into matrix-core order before the step and one written
+    in that order by the op producing it.  The schedule is asserted to take
+    those paths; every op of every step is checked against the oracle on
+    the input the device read, at the acceptance bound."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 1024
+    shape = (lambda n: (m, n) if m > 1 else (n,))
+    ws = [si.weights(si.seed_for("steps-w", m, i), k, k) for i in range(4)]
+    parts = [quant.quantize_int8_b32(w) for w in ws]
+    pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
+    bufs = [torch.zeros(shape(k), dtype=torch.float16, device=DEV) for _ in range(len(ws) + 1)]
+    ops = [LinearOp(pws[i], bufs[i], bufs[i + 1], i) for i in range(len(ws))]
+    v = qd.describe_stack_plan(ops, m)
+    ng, nm, njobs = v[6], v[7], v[10]
+    groups = [v[16 + 10 * i:26 + 10 * i] for i in range(ng)]
+    members = [v[16 + 10 * ng + 7 * i:23 + 10 * ng + 7 * i] for i in range(nm)]
+    assert v[1] == 1 and ng == len(ws)
+    if m == 1:
+        assert all(g[8] & 8 for g in groups[1:]), "chained groups should read through the caches"
+    else:
+        assert njobs >= 1 and groups[0][9] >= 0, "no pre-step copy of the step's input"
+        assert all(g[9] >= 0 for g in groups[1:]), "chained groups should read producer-written copies"
+        assert all(mb[6] >= 0 for mb in members[:-1]), "producers should write their outputs' copies"
+    plan = qd.StackPlan(ops, m)
+    assert plan.persistent
+    for step in range(5):
+        x = si.activations(si.seed_for("steps-x", m, step), m, k).reshape(shape(k))
+        bufs[0].copy_(_gpu(x))
+        for b in bufs[1:]:
+            b.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        vals = [_host(b).reshape(m, k).copy() for b in bufs]
+        assert np.array_equal(vals[0].view(np.uint16), x.reshape(m, k).view(np.uint16))
+        for i in range(len(ws)):
+            assert np.all(np.isfinite(vals[i].astype(np.float64))), f"step {step} op {i} input"
+            y_ref = linear.ref_linear("int8_b32", parts[i], vals[i])
+            rmax = linear.row_max_abs("int8_b32", parts[i])
+            for t in range(m):
+                check_vector(vals[i + 1][t], y_ref[t], rmax, vals[i][t], f"step {step} op {i} token {t}")
+    plan.close()
