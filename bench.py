@@ -350,13 +350,19 @@ def measure(qd, si, torch, workload, path, steps, warmup, rotate_mb, dev):
     ops, alg_bytes, weight_bytes, m = build_stack(qd, si, torch, workload, dev)
     log(f"{len(ops)} projections, {weight_bytes / 1e9:.3f} GB packed weights, {alg_bytes / 1e9:.4f} GB per step")
     wl = si.WORKLOADS[workload]
+    per_step = 1
     if wl.single is not None:
-        # Cycle copies of the one matrix so successive steps miss the caches.
+        # One step is a pass over copies of the one matrix (so that no copy is
+        # still in the caches when it is read again), each GEMV its own
+        # dependent launch, issued by one library call: the GEMVs run back to
+        # back with no host work between them.
         copies = max(1, (rotate_mb << 20) // max(1, weight_bytes))
         op = ops[0]
-        rot = [op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
-                                  op.x, op.y, 0) for _ in range(copies - 1)]
-        step_ops = [[r] for r in rot]
+        step_ops = [[op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
+                                        op.x, op.y, i + 1) for i in range(copies - 1)]]
+        per_step = copies
+        alg_bytes *= copies
+        weight_bytes *= copies
     else:
         step_ops = [ops]
     plans = []
@@ -383,8 +389,8 @@ def measure(qd, si, torch, workload, path, steps, warmup, rotate_mb, dev):
     ngroups = len({op.group for op in step_ops[0]})
     for p in plans:
         p.close()
-    return {"ops": ops, "n_ops": len(ops), "alg_bytes": alg_bytes, "weight_bytes": weight_bytes, "m": m, "wl": wl,
-            "trials": trials, "persistent": persistent, "ngroups": ngroups}
+    return {"ops": ops, "n_ops": len(step_ops[0]), "alg_bytes": alg_bytes, "weight_bytes": weight_bytes, "m": m,
+            "wl": wl, "trials": trials, "persistent": persistent, "ngroups": ngroups, "per_step": per_step}
 
 
 def summarize(res):
@@ -497,9 +503,12 @@ def main():
     }
     if chained is not None:
         out["config"]["chained_step"] = chained
+    if res["per_step"] > 1:
+        out["config"]["gemvs_per_step"] = res["per_step"]
+        out["config"]["us_per_gemv"] = round(wall_ms * 1e3 / res["per_step"], 3)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle over one full step")
-        out["cpu_baseline"] = cpu_baseline(si, args.workload, alg_bytes)
+        out["cpu_baseline"] = cpu_baseline(si, args.workload, alg_bytes // res["per_step"])
     print(json.dumps(out), flush=True)
 
 
