@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -79,21 +80,26 @@ enum : int32_t {
   kNoWait = 4,          // a further row range of the op(s) before: no device-wide wait at the boundary
   kCleanLines = 8,      // x is written earlier in the step, but no cache can hold a stale copy of its
                         // lines: after the barrier it is read through the caches
+  kPaired = 16,         // several token rows: a two-member group whose row-group i of both members
+                        // forms one unit (virtual row-group 2i + b is member b's row-group i); it
+                        // writes the gated product of its two outputs for a later group
 };
 
 struct PGroup {         // 64 bytes
   const uint16_t* x;
   const uint16_t* gamma;  // RMSNorm weight (prologue QD_PRO_RMSNORM)
-  const uint16_t* xt;     // m > 1: x in matrix-core order (plan scratch), or null
-  int64_t k;
+  const uint16_t* xt;     // m > 1: x in matrix-core order (plan scratch), or null; under the
+                          // gated product it holds the product itself
+  int32_t k;
   int32_t J;            // super-blocks per row
   int32_t R;            // row-groups in the group
   int32_t mem0;         // first member in the member table
   int32_t n_mem;
   int32_t pro;          // qd_prologue of the group's input
   float eps;
-  int32_t order;        // kStageEarly | kAckOutputs | kNoWait | kCleanLines
-  int32_t pad;
+  int32_t order;        // kStageEarly | kAckOutputs | kNoWait | kCleanLines | kPaired
+  int32_t ss0;          // m > 1 under RMSNorm: first sum-of-squares record of x
+  int32_t ss_n;         // and the number of records that add up to it
 };
 
 struct PMember {        // 48 bytes
@@ -102,8 +108,11 @@ struct PMember {        // 48 bytes
   int64_t n;
   int32_t rg_begin;     // first row-group of this member within its group
   int32_t epi;          // qd_epilogue of this member's outputs
-  int64_t ld;           // elements between token rows of y (m > 1)
-  uint16_t* yt;         // m > 1: where the outputs also go in matrix-core order, or null
+  int32_t ld;           // elements between token rows of y (m > 1)
+  int32_t ss;           // m > 1: first of the G sum-of-squares records of these outputs (record
+                        // ss + w from workgroup w), or -1
+  uint16_t* yt;         // m > 1: where the outputs also go in matrix-core order, or null (in a
+                        // paired group, the first member's is where the gated product goes)
 };
 
 struct PSched {         // 16 bytes: one workgroup's part of one group
@@ -122,6 +131,7 @@ struct PlanArgs {
   const PSched* sched;        // [ngroups][G]
   unsigned long long* flags;  // [G] completion stamps
   uint32_t* err;
+  float* ss;                  // m > 1: sum-of-squares records, 16 floats (one per token row) each
   unsigned long long epoch;   // runs so far, including this one
   int32_t ngroups;
   int32_t nmem;
@@ -191,7 +201,10 @@ struct Sched {
   __device__ int pro(int gi) const { return uni(g[gi].pro); }
   __device__ int order(int gi) const { return uni(g[gi].order); }
   __device__ float eps(int gi) const { return __builtin_bit_cast(float, uni(__builtin_bit_cast(int, g[gi].eps))); }
-  __device__ int64_t k(int gi) const { return (int64_t)uni((int)g[gi].k); }
+  __device__ int64_t k(int gi) const { return (int64_t)uni(g[gi].k); }
+  __device__ int ss0(int gi) const { return uni(g[gi].ss0); }
+  __device__ int ss_n(int gi) const { return uni(g[gi].ss_n); }
+  __device__ bool paired(int gi) const { return (order(gi) & kPaired) != 0; }
   __device__ int tiles(int gi) const { return uni(s[gi].n); }
   __device__ int off(int gi) const { return uni(s[gi].off); }
   __device__ int rg0(int gi) const { return uni(s[gi].rg0); }
@@ -205,7 +218,9 @@ struct Sched {
   __device__ uint16_t* y_l(int mi) const { return m[mi].y; }
   __device__ int64_t n_l(int mi) const { return m[mi].n; }
   __device__ int epi_l(int mi) const { return m[mi].epi; }
-  __device__ int64_t ld(int mi) const { return (int64_t)uni((int)m[mi].ld); }
+  __device__ int64_t ld(int mi) const { return (int64_t)uni(m[mi].ld); }
+  __device__ int epi(int mi) const { return uni(m[mi].epi); }
+  __device__ int ss(int mi) const { return uni(m[mi].ss); }
   __device__ uint16_t* yt(int mi) const { return uni_ptr(m[mi].yt); }
 };
 
@@ -230,6 +245,7 @@ struct IssueCursor {
                         // (segment, super-block); for units seg counts units
   int J, rg0, nseg;
   int mem, mem_last;
+  bool paired;          // the current group is paired (kPaired)
 };
 
 template <int FMT>
@@ -280,13 +296,15 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
 // Up to 16 token rows: the sequence is made of units, U row-groups at one
 // super-block (unit-row major: units (q, 0), (q, 1), ... (q, J - 1), then
 // q + 1), so that one activation block serves U tiles.  The last unit of a
-// range may hold fewer row-groups; its missing tiles read as zeros.
+// range may hold fewer row-groups; its missing tiles read as zeros.  In a
+// paired group (PAIR instances only) row-group v is row-group v / 2 of
+// member v % 2, so a unit of two holds the same rows of both members.
 template <int FMT, int U>
 struct Unit {
   typename Fmt<FMT>::Tile w[U];
 };
 
-template <int FMT, int U>
+template <int FMT, int U, bool PAIR>
 __device__ __forceinline__ Unit<FMT, U> issue_unit(const Sched& S, int ngroups, int total, uint32_t* next,
                                                    IssueCursor& c, TileRef& ref, int lane, bool take = true) {
   constexpr int T = Fmt<FMT>::kT;
@@ -314,6 +332,7 @@ __device__ __forceinline__ Unit<FMT, U> issue_unit(const Sched& S, int ngroups, 
       c.j = 0;
       c.mem = S.mem0(c.g);
       c.mem_last = c.mem + S.nmem(c.g) - 1;
+      c.paired = PAIR && S.paired(c.g);
     }
     const int u = idx - S.off(c.g);
     c.j += u - c.u;
@@ -324,20 +343,31 @@ __device__ __forceinline__ Unit<FMT, U> issue_unit(const Sched& S, int ngroups, 
     }
     const int seg0 = c.seg * U;
     const int nv = min(U, c.nseg - seg0);
-    // The cursor follows the member of the unit's first row-group, which
-    // only moves forward along the sequence.  A unit's later row-groups may
-    // lie in the next members: each finds its own from there, without
-    // moving the cursor, since the unit's next super-block starts again
-    // from its first row-group.
-    while (c.mem < c.mem_last && c.rg0 + seg0 >= S.rg_begin(c.mem + 1)) ++c.mem;
+    if (PAIR && c.paired) {
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-      if (q < nv) {
-        const int rg = c.rg0 + seg0 + q;
-        int mi = c.mem;
-        while (mi < c.mem_last && rg >= S.rg_begin(mi + 1)) ++mi;
-        base[q] = S.blob(mi) + ((int64_t)(rg - S.rg_begin(mi)) * c.J + c.j) * T;
-        nbytes[q] = T;
+      for (int q = 0; q < U; ++q) {
+        if (q < nv) {
+          const int rg = c.rg0 + seg0 + q;
+          base[q] = S.blob(c.mem + (rg & 1)) + ((int64_t)(rg >> 1) * c.J + c.j) * T;
+          nbytes[q] = T;
+        }
+      }
+    } else {
+      // The cursor follows the member of the unit's first row-group, which
+      // only moves forward along the sequence.  A unit's later row-groups may
+      // lie in the next members: each finds its own from there, without
+      // moving the cursor, since the unit's next super-block starts again
+      // from its first row-group.
+      while (c.mem < c.mem_last && c.rg0 + seg0 >= S.rg_begin(c.mem + 1)) ++c.mem;
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        if (q < nv) {
+          const int rg = c.rg0 + seg0 + q;
+          int mi = c.mem;
+          while (mi < c.mem_last && rg >= S.rg_begin(mi + 1)) ++mi;
+          base[q] = S.blob(mi) + ((int64_t)(rg - S.rg_begin(mi)) * c.J + c.j) * T;
+          nbytes[q] = T;
+        }
       }
     }
     ref.g = c.g;
@@ -497,6 +527,21 @@ __device__ __forceinline__ float4_t tile_mfma(const Tile4& T, const u32x4 (&xa)[
   return acc;
 }
 
+// Up to 16 token rows under RMSNorm: the activation block as read (raw x)
+// becomes u = fp16(gamma * fp16(x * r)), with the group's per-token factors r
+// (lane (gq, rho) holds token rho) and gamma, both staged in LDS by the
+// control wave before the group's barrier.  K positions past K hold x = 0
+// and gamma = 0, so u = 0 there.
+template <int FMT>
+__device__ __forceinline__ void rms_block(u32x4 (&xa)[8], const half_t* gam, const float* rinv, int j,
+                                          int lane) {
+  const int gq = lane >> 4;
+  const float r = rinv[lane & 15];
+#pragma unroll
+  for (int b = 0; b < 8; ++b)
+    xa[b] = rms8(xa[b], r, *reinterpret_cast<const u32x4*>(gam + j * kSuperK + kpos<FMT>(b, gq)));
+}
+
 // Keep a load where it is written: the scheduler may not move code across
 // the barrier, and the memory clobber stops earlier passes from sinking the
 // load towards its first use (which would empty the ring).
@@ -530,19 +575,21 @@ __device__ __forceinline__ float4_t tile_mfma(const Tile4& T, const u32x4 (&xa)[
 template <int FMT, int MT, int U> struct RingOf { using type = typename Fmt<FMT>::Tile; };
 template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>; };
 
-template <int FMT, int D, bool RESERVE, int R, int MT, int U>
+// At up to 16 token rows with glue (GLUE), xs holds the RMSNorm gamma of the
+// current group and xsum its 16 per-token factors.
+template <int FMT, int D, bool RESERVE, int R, int MT, int U, bool GLUE>
 __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint32_t* next,
                              int lane, const half_t* xs, const float* xsum, float* red,
                              uint32_t* cnt, const int* stalled, const int* staged) {
   using Tile = typename RingOf<FMT, MT, U>::type;
   const int ng = p.ngroups;
   const int g4 = lane >> 4;
-  IssueCursor ic{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0};
+  IssueCursor ic{-1, 0, 0, 0, 0, 1, 0, 0, 0, 0, false};
   Tile ring[D];
   TileRef ref[D];
   auto next_tile = [&](TileRef& r, int ln, bool take = true) {
     if constexpr (MT == 1) return issue<FMT>(S, ng, total, next, ic, r, ln, take);
-    else return issue_unit<FMT, U>(S, ng, total, next, ic, r, ln, take);
+    else return issue_unit<FMT, U, GLUE>(S, ng, total, next, ic, r, ln, take);
   };
   // MT > 1: each slot's activation block, loaded with the tile when the
   // block is already readable (nothing in the step writes it, or its group's
@@ -578,6 +625,9 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       if (lane < 16) red[r.rel * 16 + lane] = part;
     } else {
       if (!xl[s]) load_xblock<FMT>(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr[s]);
+      // (A gated product needs nothing here: the group's copy holds it.)
+      if constexpr (GLUE)
+        if (S.pro(r.g) == QD_PRO_RMSNORM) rms_block<FMT>(xr[s], xs, xsum, r.j, lane);
       // Each tile's 16 x 16 partial, one float4 per lane, in the tile's own
       // slot (row-group seg + q: J slots further on).
       const int J = S.J(r.g);
@@ -768,32 +818,89 @@ __device__ __forceinline__ void store_row(const Sched& S, int g, int rg, int row
 }
 
 // Up to 16 token rows of row-group rg: lane (gq, rho) holds tokens 4 gq + i
-// of weight row rho (the MFMA output layout).
-template <int FMT>
-__device__ __forceinline__ void store_rows16(const PlanArgs& p, const Sched& S, int g, int rg,
-                                             int lane, float4_t v) {
-  int mi = S.mem0(g);
-  const int last = mi + S.nmem(g) - 1;
-  while (mi < last && rg >= S.rg_begin(mi + 1)) ++mi;
+// of weight row rho (the MFMA output layout).  With GLUE: the member's
+// epilogue applies, and in a paired group row-group rg is row-group rg / 2 of
+// member rg % 2 (whose own copy is not written: the group writes the gated
+// product instead).  h gets the stored values (0 for rows past the member and
+// tokens past m); mi and n the member and the lane's row within it.
+template <int FMT, bool GLUE>
+__device__ __forceinline__ void store_rows16(const PlanArgs& p, const Sched& S, int g, int rg, int lane,
+                                             float4_t v, bool paired, uint16_t (&h)[4], int& mi,
+                                             int64_t& n) {
+  mi = S.mem0(g);
+  int64_t local;
+  if (GLUE && paired) {
+    mi += rg & 1;
+    local = rg >> 1;
+  } else {
+    const int last = mi + S.nmem(g) - 1;
+    while (mi < last && rg >= S.rg_begin(mi + 1)) ++mi;
+    local = rg - S.rg_begin(mi);
+  }
   const int gq = lane >> 4, rho = lane & 15;
-  const int64_t n = (int64_t)(rg - S.rg_begin(mi)) * kTileRows + rho;
+  n = local * kTileRows + rho;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = 0;
   if (n >= S.n(mi)) return;
   uint16_t* const y = S.y(mi);
-  uint16_t* const yt = S.yt(mi);
+  uint16_t* const yt = GLUE && paired ? nullptr : S.yt(mi);
+  const int epi = GLUE ? S.epi(mi) : (int)QD_EPI_NONE;
   const int64_t ld = S.ld(mi);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = 4 * gq + i;
     if (tok < p.m) {
-      const uint16_t h = __builtin_bit_cast(uint16_t, (half_t)v[i]);
-      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(y + tok * ld + n), h,
+      const uint16_t hv = GLUE ? epilogue_bits(v[i], epi) : __builtin_bit_cast(uint16_t, (half_t)v[i]);
+      h[i] = hv;
+      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(y + tok * ld + n), hv,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // The later group reading these outputs as its x finds them here in
       // matrix-core order too.
       if (yt)
         __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(yt + xt_index<FMT>(n, tok)),
-                           h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                           hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+// A paired group, rows n of its two members stored (a: the first member's
+// values, b: the second's): the gated product fp16(a * b), one correctly
+// rounded fp16 multiply, into the copy the consuming group reads, in
+// matrix-core order.
+template <int FMT>
+__device__ __forceinline__ void store_product16(const PlanArgs& p, const Sched& S, int g, int lane, int64_t n,
+                                                const uint16_t (&a)[4], const uint16_t (&b)[4]) {
+  const int m0 = S.mem0(g);
+  if (n >= S.n(m0)) return;
+  uint16_t* const pt = S.yt(m0);
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = 4 * gq + i;
+    if (tok < p.m) {
+      const half_t u = __builtin_bit_cast(half_t, a[i]) * __builtin_bit_cast(half_t, b[i]);
+      __hip_atomic_store((__attribute__((address_space(1))) uint16_t*)(pt + xt_index<FMT>(n, tok)),
+                         __builtin_bit_cast(uint16_t, u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// This workgroup's sum-of-squares record of a member's outputs (see
+// finish_group): sq holds, per lane (gq, rho), the squares of tokens
+// 4 gq + i summed over the rows rho it stored, in row-group order; the 16
+// lanes of a quarter are added in a fixed butterfly order and one lane per
+// quarter writes its 4 tokens.
+__device__ __forceinline__ void write_record(const PlanArgs& p, int rec, int lane, float4_t sq) {
+#pragma unroll
+  for (int s = 1; s < 16; s <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq[i] += __shfl_xor(sq[i], s);
+  if ((lane & 15) == 0) {
+    float* const dst = p.ss + (int64_t)rec * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __hip_atomic_store((__attribute__((address_space(1))) float*)(dst + i), sq[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -818,17 +925,34 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cn
 // tile (one row: tiles t = q mod 4 per quarter-wave, then the four quarters;
 // up to 16 rows: each lane its float4 over the tiles in order), so results
 // are deterministic.
+//
+// Up to 16 token rows with glue, two more duties.  A member whose outputs a
+// later RMSNorm reads has sum-of-squares records: this workgroup adds the
+// squares of the values it stored, per token, and writes them as record
+// ss + w (zeros if it stored none of them), before its stamp.  A paired group
+// (row-groups alternate between its two members) writes the gated product of
+// the two members' rows as each pair of row-groups completes.
 template <int FMT, bool GLUE, int MT>
-__device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
+__device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, int lane, const float* red,
                              uint32_t* cnt, int* stalled, bool& dead) {
+  int rec_mem = -1;                 // the member with sum-of-squares records, if any
+  if constexpr (GLUE && MT != 1) {
+    const int m0 = S.mem0(g), m1 = m0 + S.nmem(g);
+    for (int mi = m0; mi < m1; ++mi)
+      if (S.ss(mi) >= 0) rec_mem = mi;
+  }
+  float4_t sq = {0.0f, 0.0f, 0.0f, 0.0f};
   const int ntiles = S.tiles(g);
   if (ntiles == 0) {
     if (lane == 0) lds_put(stalled, g);
+    if (GLUE && MT != 1 && rec_mem >= 0) write_record(p, S.ss(rec_mem) + w, lane, sq);
     return;
   }
   const int J = S.J(g);
   const int rg0 = S.rg0(g), nseg = S.nseg(g);
   const int row = lane & 15, q = lane >> 4;
+  const bool paired = GLUE && MT != 1 && S.paired(g);
+  uint16_t first[4] = {0, 0, 0, 0};  // paired: the first member's stored values of the current pair
   for (int s = 0; s < nseg; ++s) {
     wait_count(p, cnt, s, (uint32_t)J, dead);
     if (s == nseg - 1 && lane == 0) lds_put(stalled, g);   // every tile of g is in
@@ -854,7 +978,28 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
         for (int i = 0; i < 4; ++i) sum[i] += v[i];
       }
       if (lane == 0) cnt[s] = 0u;
-      store_rows16<FMT>(p, S, g, rg0 + s, lane, sum);
+      uint16_t h[4];
+      int mi;
+      int64_t n;
+      store_rows16<FMT, GLUE>(p, S, g, rg0 + s, lane, sum, paired, h, mi, n);
+      if constexpr (GLUE) {
+        if (mi == rec_mem) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float f = (float)__builtin_bit_cast(half_t, h[i]);
+            sq[i] = __builtin_fmaf(f, f, sq[i]);
+          }
+        }
+        if (paired) {
+          // Workgroup ranges of a paired group start at even row-groups.
+          if ((s & 1) == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) first[i] = h[i];
+          } else {
+            store_product16<FMT>(p, S, g, lane, n, first, h);
+          }
+        }
+      }
       continue;
     }
     // This runs on the group's critical path for its last row-group: four
@@ -874,6 +1019,7 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int lane,
     if (lane == 0) cnt[s] = 0u;                // ready for the next group
     if (lane < 16) store_row<GLUE>(S, g, rg0 + s, row, sum);
   }
+  if (GLUE && MT != 1 && rec_mem >= 0) write_record(p, S.ss(rec_mem) + w, lane, sq);
 }
 
 // Publish that this workgroup has finished every row it owes group g.
@@ -963,6 +1109,50 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane, int delay) {
   asm volatile("" ::: "memory");
 }
 
+// Up to 16 token rows, a group under RMSNorm: stage gamma into LDS at xs and
+// the 16 per-token factors r = 1 / sqrt(mean + eps) at rinv (0 past m).  Each
+// token's sum of squares over x is the sum of the group's ss_n records (one
+// per producing workgroup and row range, or one made before the step), added
+// in a fixed order: lane l takes float4 l % 4 (tokens 4 (l % 4) .. + 3) of
+// records l / 4, l / 4 + 16, ... in turn, then the lanes of equal l % 4 are
+// added in a butterfly.  Gamma and the records are loaded first, with one
+// wait.  Records are always read device-coherently (other workgroups wrote
+// them in this launch); gamma as POLICY says.
+template <int POLICY>
+__device__ __forceinline__ void stage_rms16(const PlanArgs& p, const Sched& S, int g, int lane, half_t* xs,
+                                            float* rinv) {
+  const int Kp = S.J(g) * kSuperK;
+  const int64_t k = S.k(g);
+  dma_to_lds<POLICY>(make_rsrc(S.gamma(g), (uint32_t)(k * 2)), Kp, lane, xs);
+  const int nrec = S.ss_n(g);
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(p.ss + (int64_t)S.ss0(g) * 16, (uint32_t)nrec * 64u);
+  const int tq = lane & 3, r0 = lane >> 2;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i0 = 0; i0 < nrec; i0 += 128) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = bload16_coherent(rr, (uint32_t)((i0 + 16 * u + r0) * 64 + tq * 16));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4_t f = __builtin_bit_cast(float4_t, v[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += f[i];
+    }
+  }
+#pragma unroll
+  for (int s = 4; s < 64; s <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], s);
+  wait_stores();                  // vmcnt(0): gamma is in LDS
+  if (lane < 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 4 * lane + i;
+      rinv[tok] = tok < p.m ? rms_inverse(acc[i], k, S.eps(g)) : 0.0f;
+    }
+  }
+}
+
 template <int FMT, bool GLUE, int MT>
 __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane, half_t* xs,
                              float* xsum, const float* red, uint32_t* cnt, int* stalled,
@@ -973,10 +1163,12 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
   if constexpr (MT == 1) stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
+  if constexpr (MT != 1 && GLUE)
+    if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
-    finish_group<FMT, GLUE, MT>(p, S, g, lane, red, cnt, stalled, dead);
+    finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead);
     publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
       // Activations no earlier group writes are staged while the stamps are
@@ -984,7 +1176,12 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // compute waves start g + 1 after the barrier either way.
       // (MT > 1: the compute waves read the activations themselves.)
       const bool early = (S.order(g + 1) & kStageEarly) != 0;
+      // Several token rows under RMSNorm: gamma and the per-token factors,
+      // whose records are complete once every workgroup has finished the
+      // producing group (or were made before the step: early).
+      const bool rms16 = GLUE && MT != 1 && S.pro(g + 1) == QD_PRO_RMSNORM;
       if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+      if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
       // and needs what g needed, which g's own boundary already waited for.
       if (!(S.order(g + 1) & kNoWait))
@@ -992,6 +1189,10 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (MT == 1 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
         else stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+      }
+      if (rms16 && !early) {
+        if (S.order(g + 1) & kCleanLines) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
+        else stage_rms16<kPolicyCoherent>(p, S, g + 1, lane, xs, xsum);
       }
       if (lane == 0) lds_put(staged, g + 1);
       wg_barrier();               // activations of g + 1 staged
@@ -1050,9 +1251,9 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
     const int last = p.ngroups - 1;
     const int total = S.off(last) + S.tiles(last);
     if (wave < kCtl - R)
-      compute_wave<FMT, D, false, R, MT, U>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+      compute_wave<FMT, D, false, R, MT, U, GLUE>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
     else
-      compute_wave<FMT, RS, true, R, MT, U>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
+      compute_wave<FMT, RS, true, R, MT, U, GLUE>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -1060,12 +1261,19 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
 // Before a step with up to 16 token rows: copy the activations no group of
 // the step writes into matrix-core order (see load_xblock), 256 chunks of 16
 // bytes per workgroup, chunk-contiguous stores.  Chunks of token rows past m
-// or past K are left as they are (zero since the plan was made).
-struct XtJob {
-  const uint16_t* x;    // [m, k]
-  uint16_t* t;          // the copy
+// or past K are left as they are (zero since the plan was made).  Under a
+// gated product the copy holds fp16(A * B) of the two blocks.  A job with a
+// record instead (one workgroup) writes each token's sum of squares over its
+// K values, for a group under RMSNorm: per token one wave adds its lanes'
+// 8-value chunks in order, then the lanes in a butterfly.
+struct XtJob {          // 48 bytes
+  const uint16_t* x;    // [m, k]; under a gated product [2, m, k]
+  uint16_t* t;          // the copy (copy jobs)
+  float* ss;            // the record, 16 floats (record jobs), or null
   int64_t k;
   int64_t first_block;  // first workgroup of this job
+  int32_t glu;          // copy jobs: 1 = the copy holds the gated product
+  int32_t pad;
 };
 
 template <int FMT>
@@ -1077,12 +1285,25 @@ __global__ __launch_bounds__(256) void xt_copy_kernel(const XtJob* jobs, int njo
     else hi = mid - 1;
   }
   const XtJob jb = jobs[lo];
+  if (jb.ss) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int tok = wave; tok < 16; tok += 4) {
+      float acc = 0.0f;
+      if (tok < m)
+        for (int64_t i = lane * 8; i < jb.k; i += 512)
+          acc = sumsq8(*reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + i), acc);
+      acc = wave_sum(acc);
+      if (lane == 0) jb.ss[tok] = acc;
+    }
+    return;
+  }
   // chunk c = (8 j + q) 64 + lane, lane = 16 gq + t
   const int64_t c = ((int64_t)blockIdx.x - jb.first_block) * 256 + threadIdx.x;
   const int tok = (int)(c & 15), gq = (int)((c >> 4) & 3), q = (int)((c >> 6) & 7);
   const int64_t k = (c >> 9) * kSuperK + kpos<FMT>(q, gq);
   if (tok >= m || k >= jb.k) return;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k);
+  u32x4 v = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k);
+  if (jb.glu) v = glu8(v, *reinterpret_cast<const u32x4*>(jb.x + (m + tok) * jb.k + k));
   *reinterpret_cast<u32x4*>(jb.t + c * 8) = v;
 }
 
@@ -1141,6 +1362,13 @@ struct HostGroup {
   float eps;
   int32_t order = 0;
   int64_t xt_off = -1;         // m > 1: byte offset of the group's x copy, or -1
+  // Several token rows with glue:
+  std::vector<int> rec;        // per member: key of its sum-of-squares records, or -1
+  int ss_key = -1;             // under RMSNorm: key of the records of x
+  bool ss_early = false;       // ... made before the step (x is not written by the step)
+  bool paired = false;         // two members whose gated product a later group reads
+  int64_t glu_src = -1;        // under the gated product: the paired group writing it, or -2 when
+                               // x is not written by the step (the product is copied before it)
 };
 
 bool ranges_overlap(const void* a, uint64_t an, const void* b, uint64_t bn) {
@@ -1232,32 +1460,59 @@ void order_groups(std::vector<HostGroup>& gs, int64_t m, int64_t tbytes) {
   }
 }
 
+// A paired group's row range per piece of the split below, in row-groups:
+// whole pairs, at most tiles / J row-groups per workgroup, and, when the
+// group has to be cut, a multiple of 32 row-groups (256 rows of each member),
+// so that the gated product's copy is addressed by plain offsets.  0 if no
+// such piece exists.
+int64_t paired_piece(int64_t R, int J, int64_t tiles, int G) {
+  const int64_t pairs = tiles / J / 2;
+  if (pairs < 1) return 0;
+  const int64_t full = pairs * 2 * G;
+  return R <= full ? full : full / 32 * 32;
+}
+
 // Split groups into row ranges of at most `tiles` tiles per workgroup (G
 // workgroups), so that one range's 16 x 16 tile partials fit in LDS.  Each
 // range is a group of its own whose members are the slices of the original
-// members it covers; ranges after the first carry kNoWait.  False if a
-// single row-group has more tiles than that.
+// members it covers; ranges after the first carry kNoWait.  A paired group's
+// ranges hold the same rows of both members.  False if a single row-group
+// (a paired group: a pair) has more tiles than that.
 bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G, int64_t tbytes) {
   std::vector<HostGroup> out;
   for (HostGroup& hg : gs) {
     const int64_t per_wg = tiles / hg.J;
     if (per_wg < 1) return false;
-    const int64_t piece = per_wg * G;
+    const int64_t piece = hg.paired ? paired_piece(hg.R, hg.J, tiles, G) : per_wg * G;
+    if (piece < 1) return false;
     if (hg.R <= piece) {
       out.push_back(std::move(hg));
       continue;
     }
     for (int64_t a = 0; a < hg.R; a += piece) {
       const int64_t b = std::min<int64_t>(hg.R, a + piece);
-      HostGroup pg{hg.x, hg.k, hg.J, {}, {}, {}, 0, hg.gamma, hg.pro, hg.eps};
-      pg.order = hg.order;
-      pg.xt_off = hg.xt_off;
+      HostGroup pg = hg;
+      pg.mem.clear();
+      pg.src.clear();
+      pg.yt_off.clear();
+      pg.rec.clear();
+      pg.R = 0;
       for (size_t q = 0; q < hg.mem.size(); ++q) {
         const PMember& mm = hg.mem[q];
-        const int64_t r0 = mm.rg_begin, r1 = r0 + ceil_div(mm.n, kTileRows);
-        const int64_t lo = std::max(a, r0), hi = std::min(b, r1);
+        // Row-groups [lo, hi) of the group that are this member's, and how
+        // many of the member's come before them.
+        int64_t lo, hi, skip;
+        if (hg.paired) {          // a and b are even; both members have R / 2 row-groups
+          lo = a / 2;
+          hi = b / 2;
+          skip = lo;
+        } else {
+          const int64_t r0 = mm.rg_begin, r1 = r0 + ceil_div(mm.n, kTileRows);
+          lo = std::max(a, r0);
+          hi = std::min(b, r1);
+          skip = lo - r0;
+        }
         if (lo >= hi) continue;
-        const int64_t skip = lo - r0;   // row-groups of the member before this range
         PMember slice = mm;
         slice.blob = mm.blob + skip * hg.J * tbytes;
         slice.y = mm.y + skip * kTileRows;
@@ -1266,6 +1521,7 @@ bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G, int64_t tbytes
         pg.mem.push_back(slice);
         pg.src.push_back(hg.src[q]);
         pg.yt_off.push_back(hg.yt_off[q] < 0 ? -1 : hg.yt_off[q] + skip * kTileRows * 16 * 2);
+        pg.rec.push_back(hg.rec[q]);
         pg.R += (int)(hi - lo);
       }
       if (a > 0) pg.order |= kNoWait;
@@ -1344,17 +1600,26 @@ constexpr int unit16(int fmt) { return fmt == QD_FMT_INT8_B32 ? QD_PLAN_UNIT16 :
 #define QD_PLAN_TILES16 96
 #endif
 
-// One token row with glue: the staging applies the prologue in LDS and the
-// row stores apply the epilogue (a separate instance, so steps without glue
-// run the plain kernel).
+// Glue: at one token row the staging applies the prologue in LDS; at several
+// the compute waves apply RMSNorm to each activation block and a gated
+// product is read from a copy that holds it.  The row stores apply the
+// epilogue.  (Separate instances, so steps without glue run the plain
+// kernels.)
+template <int FMT, bool GLUE>
+const void* multi_kernel() {
+  if constexpr (FMT == QD_FMT_INT8_B32)
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
+                                                       QD_PLAN_RESERVE16_S, GLUE, 16, QD_PLAN_UNIT16>);
+  else
+    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16_INT4, QD_PLAN_RESERVE16_INT4_R,
+                                                       QD_PLAN_RESERVE16_INT4_S, GLUE, 16, QD_PLAN_UNIT16_INT4>);
+}
+
 const void* kernel_ptr(int fmt, bool multi, bool glue) {
-  if (multi)
-    return fmt == QD_FMT_INT8_B32
-               ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
-                                                             QD_PLAN_RESERVE16_S, false, 16, QD_PLAN_UNIT16>)
-               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16_INT4,
-                                                             QD_PLAN_RESERVE16_INT4_R, QD_PLAN_RESERVE16_INT4_S,
-                                                             false, 16, QD_PLAN_UNIT16_INT4>);
+  if (multi) {
+    if (fmt == QD_FMT_INT8_B32) return glue ? multi_kernel<QD_FMT_INT8_B32, true>() : multi_kernel<QD_FMT_INT8_B32, false>();
+    return glue ? multi_kernel<QD_FMT_INT4_G64, true>() : multi_kernel<QD_FMT_INT4_G64, false>();
+  }
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
@@ -1362,11 +1627,24 @@ const void* kernel_ptr(int fmt, bool multi, bool glue) {
               : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, kRing4, kReserveInt4, kReserveInt4S, false, 1, 1>);
 }
 
+// A job made before each step at several token rows: a copy of an activation
+// no group of the step writes, in matrix-core order (of x, or of the gated
+// product of its two blocks), or the sum-of-squares record of such an
+// activation under RMSNorm.
+struct HostJob {
+  const uint16_t* x;
+  int64_t k;
+  int64_t copy_off;            // byte offset of the copy in the plan's copies, or -1 (a record job)
+  int64_t rec;                 // the record (record jobs), or -1
+  int32_t glu;                 // copy jobs: the copy holds the gated product of x's two blocks
+  int64_t first_block;
+};
+
 // The persistent step's tables, built on the host alone: the groups in step
 // order with their boundary ordering, their row-range split at several token
-// rows, the activation-copy slots, the per-workgroup schedules and the LDS
-// the kernel needs, for G workgroups.  Copy addresses are byte offsets into
-// the plan's copies until those exist.
+// rows, the activation-copy slots, the sum-of-squares records, the
+// per-workgroup schedules and the LDS the kernel needs, for G workgroups.
+// Copy addresses are byte offsets into the plan's copies until those exist.
 struct PlanLayout {
   bool persistent = false;     // false: the whole step replays per-group launches
   int fmt = 0;
@@ -1377,26 +1655,37 @@ struct PlanLayout {
   std::vector<PMember> pm;
   std::vector<PSched> ps;      // [group][workgroup]
   std::vector<int64_t> xt_fix, yt_fix;   // per group / member: offset of its copy, or -1
-  std::vector<XtJob> jobs;     // copies made before each step (t holds the offset)
+  std::vector<HostJob> jobs;   // made before each step
   int64_t xt_total = 0, xt_blocks = 0;
+  int64_t ss_total = 0;        // sum-of-squares records, 16 floats each
   size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
 };
 
-// `copies`: whether steps with several token rows keep activation copies in
-// matrix-core order (plan scratch); without them every activation is read in
-// place.
+// The last group before g writing any byte of [x, x + xb), or SIZE_MAX.
+size_t last_writer(const std::vector<HostGroup>& gs, size_t g, const void* x, uint64_t xb, int64_t m) {
+  size_t p = SIZE_MAX;
+  for (size_t j = 0; j < g; ++j)
+    for (const PMember& pj : gs[j].mem)
+      if (ranges_overlap(x, xb, pj.y, y_span(pj, m))) p = j;
+  return p;
+}
+
+// `scratch`: whether the plan has scratch of its own (a plan object).  Steps
+// with several token rows then keep activation copies in matrix-core order,
+// and take glue, which needs those copies and sum-of-squares records;
+// without scratch every activation is read in place, and glue at several
+// token rows ends the persistent part of the step.
 void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanLayout* L,
-                 bool copies = true) {
+                 bool scratch = true) {
   *L = PlanLayout{};
   L->G = G;
-  // Persistent walker: one format, no empty-K groups; one token row (with or
-  // without glue), or up to 16 without glue.  The leading
-  // groups that qualify run in the persistent kernel; from the first group
-  // that does not (another format, say an fp16 head), the rest of the step
-  // is replayed as per-group launches after it on the same stream.
+  // Persistent walker: one format, no empty-K groups, up to 16 token rows.
+  // The leading groups that qualify run in the persistent kernel; from the
+  // first group that does not (another format, say an fp16 head, or glue at
+  // several token rows the kernel cannot take), the rest of the step is
+  // replayed as per-group launches after it on the same stream.
   std::vector<HostGroup> groups;
   const bool multi = m > 1;
-  bool glue = false;
   if (m < 1 || m > 16 || G < 1 || G > kMaxWorkgroups) return;
   int fmt = 0;
   int64_t split = n_ops;
@@ -1405,7 +1694,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     while (e < n_ops && ops[e].group == ops[i].group) ++e;
     HostGroup hg{ops[i].x, ops[i].w.k, (int)ceil_div(ops[i].w.k, kSuperK), {}, {}, {}, 0,
                  ops[i].gamma, ops[i].prologue, ops[i].eps};
-    bool gok = true, gglue = false;
+    bool gok = true;
     int gfmt = fmt;
     for (int64_t q = i; q < e; ++q) {
       if (ops[q].w.n == 0) continue;
@@ -1413,15 +1702,12 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       if (gfmt == 0) gfmt = ops[q].w.fmt;
       if (ops[q].w.fmt != gfmt) gok = false;
       if (gfmt != QD_FMT_INT8_B32 && gfmt != QD_FMT_INT4_G64) gok = false;   // fp16: replay
-      // Glue (a prologue or an epilogue): at one token row only.
-      if (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE) {
-        gglue = true;
-        if (multi) gok = false;
-      }
+      if (multi && !scratch && (ops[q].prologue != QD_PRO_NONE || ops[q].epilogue != QD_EPI_NONE)) gok = false;
       hg.mem.push_back(PMember{static_cast<const uint8_t*>(ops[q].w.data), ops[q].y, ops[q].w.n,
-                               hg.R, ops[q].epilogue, ops[q].w.n, nullptr});
+                               hg.R, ops[q].epilogue, (int32_t)ops[q].w.n, -1, nullptr});
       hg.src.push_back(i);
       hg.yt_off.push_back(-1);
+      hg.rec.push_back(-1);
       hg.R += (int)ceil_div(ops[q].w.n, kTileRows);
     }
     if (!gok) {
@@ -1429,38 +1715,129 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       break;
     }
     fmt = gfmt;
-    glue = glue || gglue;
     if (!hg.mem.empty()) groups.push_back(std::move(hg));
     i = e;
   }
   if (groups.empty()) return;
   order_groups(groups, m, tile_bytes(fmt));
 
+  // Several token rows with glue: what each glued group needs.
+  //  * RMSNorm needs each token's sum of squares over x.  When no group of
+  //    the step writes x, it is summed before the step (one record); when x
+  //    is exactly the whole output of one op of its last writer, that op's
+  //    workgroups write one record each as they finish it.  The op must be
+  //    the only one of its group with records, in a group that is not paired.
+  //  * The gated product needs its two blocks as the whole outputs of the two
+  //    members of its last writer, A's first: that group runs paired and
+  //    writes the product into the copy the consumer reads (units of two
+  //    row-groups only).  When no group writes x, the product is copied
+  //    before the step.
+  // The first glued group that fits neither ends the persistent part.
+  int nkeys = 0;
+  if (multi) {
+    std::map<std::pair<const void*, int64_t>, int> early_keys;
+    size_t cut = groups.size();
+    for (size_t g = 0; g < groups.size() && cut == groups.size(); ++g) {
+      HostGroup& hg = groups[g];
+      if (hg.pro == QD_PRO_NONE) continue;
+      const uint64_t xb = (uint64_t)m * hg.k * 2 * (hg.pro == QD_PRO_GLU ? 2 : 1);
+      const size_t p = (hg.order & kStageEarly) ? SIZE_MAX : last_writer(groups, g, hg.x, xb, m);
+      bool ok = true;
+      if (p == SIZE_MAX) {          // no group of the step writes x
+        if (hg.pro == QD_PRO_RMSNORM) {
+          auto it = early_keys.emplace(std::make_pair((const void*)hg.x, hg.k), nkeys).first;
+          if (it->second == nkeys) ++nkeys;
+          hg.ss_key = it->second;
+          hg.ss_early = true;
+        } else {
+          hg.glu_src = -2;
+        }
+      } else if (hg.pro == QD_PRO_RMSNORM) {
+        HostGroup& pg = groups[p];
+        int q = -1, hits = 0;
+        for (size_t b = 0; b < pg.mem.size(); ++b)
+          if (ranges_overlap(hg.x, xb, pg.mem[b].y, y_span(pg.mem[b], m))) {
+            q = (int)b;
+            ++hits;
+          }
+        ok = hits == 1 && !pg.paired && (const void*)pg.mem[q].y == (const void*)hg.x &&
+             pg.mem[q].n == hg.k && pg.mem[q].ld == hg.k;
+        for (size_t b = 0; ok && b < pg.mem.size(); ++b)
+          if ((int)b != q && pg.rec[b] >= 0) ok = false;
+        if (ok) {
+          if (pg.rec[q] < 0) pg.rec[q] = nkeys++;
+          hg.ss_key = pg.rec[q];
+        }
+      } else {
+        HostGroup& pg = groups[p];
+        ok = unit16(fmt) == 2 && pg.mem.size() == 2 && pg.rec[0] < 0 && pg.rec[1] < 0 &&
+             (const void*)pg.mem[0].y == (const void*)hg.x &&
+             (const void*)pg.mem[1].y == (const void*)(hg.x + m * hg.k) &&
+             pg.mem[0].n == hg.k && pg.mem[1].n == hg.k && pg.mem[0].ld == hg.k && pg.mem[1].ld == hg.k &&
+             paired_piece(pg.R, pg.J, QD_PLAN_TILES16, G) > 0;
+        if (ok) {
+          pg.paired = true;
+          hg.glu_src = (int64_t)p;
+        }
+      }
+      if (!ok) cut = g;
+    }
+    if (cut < groups.size()) {
+      // The boundary ordering is redone for the groups kept: what the
+      // replayed ops read needs no ordering inside the kernel.
+      split = groups[cut].src[0];
+      groups.resize(cut);
+      for (HostGroup& hg : groups) hg.order = 0;
+      order_groups(groups, m, tile_bytes(fmt));
+    }
+  }
+  bool glue = false;
+  for (const HostGroup& hg : groups) {
+    glue = glue || hg.pro != QD_PRO_NONE;
+    for (const PMember& pm : hg.mem) glue = glue || pm.epi != QD_EPI_NONE;
+  }
+
   // Several token rows: copies of the activations in matrix-core order.  An
   // activation no group writes is copied before the step; one that is
   // exactly an earlier op's whole output (the last write to any of its
-  // bytes) is written in that order by the op itself.  Other activations are
-  // read in place.
-  std::vector<XtJob> jobs;
+  // bytes) is written in that order by the op itself.  A gated product's copy
+  // holds the product (written by the paired group, or made before the
+  // step).  Other activations are read in place.
+  std::vector<HostJob> jobs;
   int64_t xt_total = 0;
-  if (multi && copies) {
-    std::map<std::pair<const void*, int64_t>, int64_t> early_slots;
+  if (multi && scratch) {
+    std::map<std::tuple<const void*, int64_t, int>, int64_t> early_slots;
     std::map<std::pair<size_t, size_t>, int64_t> out_slots;
     auto new_slot = [&](int J) {
       const int64_t off = xt_total;
       xt_total += (int64_t)align_up((size_t)J * 8192, 256);
       return off;
     };
+    auto early_slot = [&](const HostGroup& hg, int glu) {
+      const auto key = std::make_tuple((const void*)hg.x, hg.k, glu);
+      auto it = early_slots.find(key);
+      if (it == early_slots.end()) {
+        it = early_slots.emplace(key, new_slot(hg.J)).first;
+        jobs.push_back(HostJob{hg.x, hg.k, it->second, -1, glu, 0});
+      }
+      return it->second;
+    };
     for (size_t g = 0; g < groups.size(); ++g) {
       HostGroup& hg = groups[g];
-      if (hg.order & kStageEarly) {
-        const auto key = std::make_pair((const void*)hg.x, hg.k);
-        auto it = early_slots.find(key);
-        if (it == early_slots.end()) {
-          it = early_slots.emplace(key, new_slot(hg.J)).first;
-          jobs.push_back(XtJob{hg.x, reinterpret_cast<uint16_t*>((uintptr_t)it->second), hg.k, 0});
+      if (hg.pro == QD_PRO_GLU) {
+        if (hg.glu_src == -2) {
+          hg.xt_off = early_slot(hg, 1);
+        } else {
+          const size_t p = (size_t)hg.glu_src;
+          auto it = out_slots.find(std::make_pair(p, (size_t)0));
+          if (it == out_slots.end()) it = out_slots.emplace(std::make_pair(p, (size_t)0), new_slot(hg.J)).first;
+          groups[p].yt_off[0] = it->second;
+          hg.xt_off = it->second;
         }
-        hg.xt_off = it->second;
+        continue;
+      }
+      if (hg.order & kStageEarly) {
+        hg.xt_off = early_slot(hg, 0);
         continue;
       }
       size_t p = SIZE_MAX, q = 0;
@@ -1470,7 +1847,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
             p = j;
             q = b;
           }
-      if (p == SIZE_MAX) continue;
+      if (p == SIZE_MAX || groups[p].paired) continue;   // a paired group's copy slot holds its product
       const PMember& pq = groups[p].mem[q];
       if ((const void*)pq.y != (const void*)hg.x || pq.n != hg.k || pq.ld != hg.k) continue;
       // The copy's order repeats every 256 rows, and a row range cut out of
@@ -1490,19 +1867,48 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     }
   }
   if (multi && !split_rows(groups, QD_PLAN_TILES16, G, tile_bytes(fmt))) return;
+
+  // Sum-of-squares records: G per member slice with records (one per
+  // workgroup), in plan order, so that the slices of one op are contiguous;
+  // then one per activation summed before the step.
+  std::map<int, std::pair<int64_t, int64_t>> recs;   // key -> first record, records
+  int64_t ss_total = 0;
+  for (HostGroup& hg : groups)
+    for (size_t b = 0; b < hg.mem.size(); ++b)
+      if (hg.rec[b] >= 0) {
+        auto& e = recs[hg.rec[b]];
+        if (e.second == 0) e.first = ss_total;
+        e.second += G;
+        hg.mem[b].ss = (int32_t)ss_total;
+        ss_total += G;
+      }
+  for (HostGroup& hg : groups)
+    if (hg.ss_early && !recs.count(hg.ss_key)) {
+      recs[hg.ss_key] = std::make_pair(ss_total, (int64_t)1);
+      jobs.push_back(HostJob{hg.x, hg.k, -1, ss_total, 0, 0});
+      ++ss_total;
+    }
+
   const int ng = (int)groups.size();
   L->pg.resize(ng);
   L->ps.resize((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
-  int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1;
+  int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1, maxGamma = 0;
   for (int g = 0; g < ng; ++g) {
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
     // A step the persistent walker cannot hold (tile counts past int32)
     // replays per-group launches instead.
     if (T > (int64_t)INT32_MAX / 2) return;
-    L->pg[g] = PGroup{hg.x, hg.gamma, nullptr, hg.k, hg.J, hg.R, (int32_t)L->pm.size(), (int32_t)hg.mem.size(),
-                      hg.pro, hg.eps, hg.order, 0};
+    int32_t ss0 = 0, ss_n = 0;
+    if (multi && hg.pro == QD_PRO_RMSNORM) {
+      const auto& e = recs.at(hg.ss_key);
+      ss0 = (int32_t)e.first;
+      ss_n = (int32_t)e.second;
+      maxGamma = std::max(maxGamma, x_span(hg.J * kSuperK));
+    }
+    L->pg[g] = PGroup{hg.x, hg.gamma, nullptr, (int32_t)hg.k, hg.J, hg.R, (int32_t)L->pm.size(),
+                      (int32_t)hg.mem.size(), hg.pro, hg.eps, hg.order | (hg.paired ? kPaired : 0), ss0, ss_n};
     L->xt_fix.push_back(hg.xt_off);
     for (size_t b = 0; b < hg.mem.size(); ++b) {
       L->pm.push_back(hg.mem[b]);
@@ -1516,13 +1922,21 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // go on prefetching the next groups).  Splitting a row-group across
     // workgroups would put a cross-workgroup combine, one more device-wide
     // round trip, on the group's critical path; measured, that costs more
-    // than the uneven split.
+    // than the uneven split.  A paired group is spread in whole pairs.
     for (int w = 0; w < G; ++w) {
       // Contiguous row-groups: each workgroup streams one contiguous range.
       // (Interleaving them, row-group w + i G to workgroup w, measured 2-11%
       // slower: the contiguous streams keep DRAM pages open.)
       // Several token rows: the sequence holds units of unit16(fmt) row-groups.
-      const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
+      int64_t r0, nrg;
+      if (hg.paired) {
+        const int64_t P = R / 2;
+        r0 = 2 * ((int64_t)w * P / G);
+        nrg = 2 * ((int64_t)(w + 1) * P / G) - r0;
+      } else {
+        r0 = (int64_t)w * R / G;
+        nrg = (int64_t)(w + 1) * R / G - r0;
+      }
       const int64_t n = (multi ? ceil_div(nrg, (int64_t)unit16(fmt)) : nrg) * J;
       L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
       if (nrg == 0) continue;
@@ -1531,21 +1945,25 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       maxSeg = std::max<int>(maxSeg, (int)nrg);
     }
   }
-  // Several token rows: no staged activations, and 16 x 16 partials per tile.
-  L->x_bytes = multi ? 0 : (size_t)maxXH * 2;      // a multiple of 1024
-  L->xsum_bytes = fmt == QD_FMT_INT4_G64 && !multi ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
+  // One token row: staged activations (and their run sums for INT4).
+  // Several: no staged activations, 16 x 16 partials per tile, and under
+  // RMSNorm gamma and the 16 per-token factors.
+  L->x_bytes = multi ? (size_t)maxGamma * 2 : (size_t)maxXH * 2;      // a multiple of 1024
+  L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0)
+                        : fmt == QD_FMT_INT4_G64 ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
   L->lds = L->x_bytes + L->xsum_bytes + L->red_bytes + L->cnt_bytes + L->tab_bytes + 16;   // + counter, stall flag
   int64_t blocks = 0;
-  for (XtJob& jb : jobs) {
+  for (HostJob& jb : jobs) {
     jb.first_block = blocks;
-    blocks += 2 * ceil_div(jb.k, kSuperK);         // 512 chunks per super-block
+    blocks += jb.copy_off >= 0 ? 2 * ceil_div(jb.k, kSuperK) : 1;   // 512 chunks per super-block; a record: 1
   }
   L->jobs = std::move(jobs);
   L->xt_total = xt_total;
   L->xt_blocks = blocks;
+  L->ss_total = ss_total;
   L->fmt = fmt;
   L->multi = multi;
   L->glue = glue;
@@ -1605,66 +2023,70 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return fallback();
   }
 
-  // The activation copies (zeroed once: token rows past m and K positions
-  // past K stay zero) and the table of copies made before each step.
-  if (L.xt_total > 0) {
-    void* dj = nullptr;
-    if (hipMalloc(&plan->xt, (size_t)L.xt_total) != hipSuccess ||
-        hipMemset(plan->xt, 0, (size_t)L.xt_total) != hipSuccess ||
-        (!L.jobs.empty() && hipMalloc(&dj, sizeof(XtJob) * L.jobs.size()) != hipSuccess)) {
-      if (plan->xt) (void)hipFree(plan->xt);
-      delete plan;
-      return QD_ELAUNCH;
-    }
-    uint8_t* const xb = static_cast<uint8_t*>(plan->xt);
-    for (XtJob& jb : L.jobs) jb.t = reinterpret_cast<uint16_t*>(xb + reinterpret_cast<uintptr_t>(jb.t));
-    if (!L.jobs.empty() &&
-        hipMemcpy(dj, L.jobs.data(), sizeof(XtJob) * L.jobs.size(), hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(plan->xt);
-      (void)hipFree(dj);
-      delete plan;
-      return QD_ELAUNCH;
-    }
-    plan->xt_jobs = dj;
-    plan->xt_njobs = (int)L.jobs.size();
-    plan->xt_blocks = L.xt_blocks;
-    for (int g = 0; g < ng; ++g)
-      if (L.xt_fix[g] >= 0) pg[g].xt = reinterpret_cast<const uint16_t*>(xb + L.xt_fix[g]);
-    for (size_t i = 0; i < pm.size(); ++i)
-      if (L.yt_fix[i] >= 0) pm[i].yt = reinterpret_cast<uint16_t*>(xb + L.yt_fix[i]);
-  }
-
-  // Device tables, then scratch.
-  const size_t o_groups = 0;
-  const size_t o_mem = align_up(o_groups + sizeof(PGroup) * ng, 256);
-  const size_t o_sched = align_up(o_mem + sizeof(PMember) * pm.size(), 256);
-  const size_t t_bytes = align_up(o_sched + sizeof(PSched) * L.ps.size(), 256);
-  const size_t s_flags = 0;
-  const size_t s_err = align_up(sizeof(unsigned long long) * G, 256);
-  const size_t s_bytes = s_err + 256;
-  std::vector<uint8_t> host(t_bytes, 0);
-  memcpy(host.data() + o_groups, pg.data(), sizeof(PGroup) * ng);
-  memcpy(host.data() + o_mem, pm.data(), sizeof(PMember) * pm.size());
-  memcpy(host.data() + o_sched, L.ps.data(), sizeof(PSched) * L.ps.size());
-  if (hipMalloc(&plan->tables, t_bytes) != hipSuccess ||
-      hipMalloc(&plan->scratch, s_bytes) != hipSuccess ||
-      hipMemcpy(plan->tables, host.data(), t_bytes, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(plan->scratch, 0, s_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+  auto fail = [&]() {
     if (plan->tables) (void)hipFree(plan->tables);
     if (plan->scratch) (void)hipFree(plan->scratch);
     if (plan->xt) (void)hipFree(plan->xt);
     if (plan->xt_jobs) (void)hipFree(plan->xt_jobs);
     delete plan;
     return QD_ELAUNCH;
-  }
-  uint8_t* tb = static_cast<uint8_t*>(plan->tables);
+  };
+  // Scratch: the completion stamps, the error word and the sum-of-squares
+  // records (zeroed here; every run rewrites the records it reads).
+  const size_t s_flags = 0;
+  const size_t s_err = align_up(sizeof(unsigned long long) * G, 256);
+  const size_t s_ss = s_err + 256;
+  const size_t s_bytes = s_ss + align_up((size_t)L.ss_total * 64, 256);
+  if (hipMalloc(&plan->scratch, s_bytes) != hipSuccess || hipMemset(plan->scratch, 0, s_bytes) != hipSuccess)
+    return fail();
   uint8_t* sb = static_cast<uint8_t*>(plan->scratch);
+  float* const ss = L.ss_total > 0 ? reinterpret_cast<float*>(sb + s_ss) : nullptr;
+
+  // The activation copies (zeroed once: token rows past m and K positions
+  // past K stay zero) and the table of jobs made before each step.
+  if (L.xt_total > 0 &&
+      (hipMalloc(&plan->xt, (size_t)L.xt_total) != hipSuccess ||
+       hipMemset(plan->xt, 0, (size_t)L.xt_total) != hipSuccess))
+    return fail();
+  uint8_t* const xb = static_cast<uint8_t*>(plan->xt);
+  if (!L.jobs.empty()) {
+    std::vector<XtJob> dev_jobs;
+    for (const HostJob& jb : L.jobs)
+      dev_jobs.push_back(XtJob{jb.x, jb.copy_off >= 0 ? reinterpret_cast<uint16_t*>(xb + jb.copy_off) : nullptr,
+                               jb.rec >= 0 ? ss + jb.rec * 16 : nullptr, jb.k, jb.first_block, jb.glu, 0});
+    if (hipMalloc(&plan->xt_jobs, sizeof(XtJob) * dev_jobs.size()) != hipSuccess ||
+        hipMemcpy(plan->xt_jobs, dev_jobs.data(), sizeof(XtJob) * dev_jobs.size(), hipMemcpyHostToDevice) !=
+            hipSuccess)
+      return fail();
+    plan->xt_njobs = (int)dev_jobs.size();
+    plan->xt_blocks = L.xt_blocks;
+  }
+  for (int g = 0; g < ng; ++g)
+    if (L.xt_fix[g] >= 0) pg[g].xt = reinterpret_cast<const uint16_t*>(xb + L.xt_fix[g]);
+  for (size_t i = 0; i < pm.size(); ++i)
+    if (L.yt_fix[i] >= 0) pm[i].yt = reinterpret_cast<uint16_t*>(xb + L.yt_fix[i]);
+
+  // Device tables.
+  const size_t o_groups = 0;
+  const size_t o_mem = align_up(o_groups + sizeof(PGroup) * ng, 256);
+  const size_t o_sched = align_up(o_mem + sizeof(PMember) * pm.size(), 256);
+  const size_t t_bytes = align_up(o_sched + sizeof(PSched) * L.ps.size(), 256);
+  std::vector<uint8_t> host(t_bytes, 0);
+  memcpy(host.data() + o_groups, pg.data(), sizeof(PGroup) * ng);
+  memcpy(host.data() + o_mem, pm.data(), sizeof(PMember) * pm.size());
+  memcpy(host.data() + o_sched, L.ps.data(), sizeof(PSched) * L.ps.size());
+  if (hipMalloc(&plan->tables, t_bytes) != hipSuccess ||
+      hipMemcpy(plan->tables, host.data(), t_bytes, hipMemcpyHostToDevice) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    return fail();
+  uint8_t* tb = static_cast<uint8_t*>(plan->tables);
   PlanArgs& a = plan->args;
   a.groups = reinterpret_cast<const PGroup*>(tb + o_groups);
   a.members = reinterpret_cast<const PMember*>(tb + o_mem);
   a.sched = reinterpret_cast<const PSched*>(tb + o_sched);
   a.flags = reinterpret_cast<unsigned long long*>(sb + s_flags);
   a.err = reinterpret_cast<uint32_t*>(sb + s_err);
+  a.ss = ss;
   a.ngroups = ng;
   a.nmem = (int32_t)pm.size();
   a.G = G;
@@ -1698,22 +2120,22 @@ qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32
     std::vector<StackGroup> tail;
     if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) L = PlanLayout{};
   }
-  std::vector<int64_t> v = {1, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
+  std::vector<int64_t> v = {2, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
                             (int64_t)L.pg.size(), (int64_t)L.pm.size(), L.G, L.xt_total,
                             (int64_t)L.jobs.size(), (int64_t)L.lds, (int64_t)L.x_bytes,
-                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes};
+                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes, L.ss_total};
   auto addr = [](const void* p) { return (int64_t)(uintptr_t)p; };
   for (size_t g = 0; g < L.pg.size(); ++g) {
     const PGroup& p = L.pg[g];
-    v.insert(v.end(), {addr(p.x), addr(p.gamma), p.k, p.J, p.R, p.mem0, p.n_mem, p.pro, p.order, L.xt_fix[g]});
+    v.insert(v.end(), {addr(p.x), addr(p.gamma), p.k, p.J, p.R, p.mem0, p.n_mem, p.pro, p.order, L.xt_fix[g],
+                       p.ss0, p.ss_n});
   }
   for (size_t i = 0; i < L.pm.size(); ++i) {
     const PMember& p = L.pm[i];
-    v.insert(v.end(), {addr(p.blob), addr(p.y), p.n, p.rg_begin, p.epi, p.ld, L.yt_fix[i]});
+    v.insert(v.end(), {addr(p.blob), addr(p.y), p.n, p.rg_begin, p.epi, p.ld, L.yt_fix[i], p.ss});
   }
   for (const PSched& s : L.ps) v.insert(v.end(), {s.n, s.off, s.rg0, s.nseg});
-  for (const XtJob& j : L.jobs)
-    v.insert(v.end(), {addr(j.x), (int64_t)reinterpret_cast<uintptr_t>(j.t), j.k, j.first_block});
+  for (const HostJob& j : L.jobs) v.insert(v.end(), {addr(j.x), j.copy_off, j.k, j.first_block, j.glu, j.rec});
   *out_len = (int64_t)v.size();
   if (!out) return QD_OK;                           // a size query
   if (cap < (int64_t)v.size()) return QD_ESHAPE;
@@ -1923,7 +2345,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   if (!sd) return QD_EDEVICE;
   const int G = std::min(sd->cus, kMaxWorkgroups);
   PlanLayout L;
-  layout_plan(ops, n_ops, m, G, &L, /*copies=*/false);
+  layout_plan(ops, n_ops, m, G, &L, /*scratch=*/false);
   auto replay_all = [&]() { return launch_groups(replay, s) == hipSuccess ? QD_OK : QD_ELAUNCH; };
   if (!L.persistent) return replay_all();
   if (L.pg.size() > (size_t)kStaticGroups || L.pm.size() > (size_t)kStaticMembers) return QD_ESHAPE;

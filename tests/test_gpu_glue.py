@@ -10,7 +10,7 @@ import pytest
 
 import synthetic_inputs as si
 from oracle import glue, linear, quant
-from tests.test_gpu_parity import _prefix_states
+from tests.test_gpu_parity import _plan_tables, _prefix_states
 from tests.numerics import MAX_ERR_COEF, REL_L2, check_vector
 
 torch = pytest.importorskip("torch")
@@ -90,8 +90,11 @@ def test_prologues_and_epilogue_exact(qd, fmt, m, path):
            qd.LinearOp(pw, as_, ys[2], 2, epilogue="silu")]
     if path == "plan":
         plan = qd.StackPlan(ops, m)
-        # the persistent kernel takes glue at one token row (int8; fp16 steps replay)
-        assert plan.persistent == (m == 1 and fmt != "fp16")
+        # the persistent kernel takes the three glued groups (fp16 steps replay): at
+        # several token rows the RMSNorm factors and the gated product's copy
+        # are made before the step, since no group of it writes their inputs
+        assert plan.persistent == (fmt != "fp16")
+        assert qd.describe_stack_plan(ops, m)[5] == (3 if fmt != "fp16" else 0)
         plan.run()
         torch.cuda.synchronize()
         assert plan.error() == 0
@@ -265,14 +268,35 @@ def test_glue_stack_launches(qd, fmt, m):
     _check_glue_stack(fmt, m, ops, meta, f"launches {fmt} m={m}")
 
 
-@pytest.mark.parametrize("fmt,m", [("int8_b32", 16), ("int4_g64", 16), ("fp16", 5)])
+@pytest.mark.parametrize("fmt,m", [("int8_b32", 16), ("int4_g64", 16), ("int8_b32", 5), ("int4_g64", 2),
+                                   ("fp16", 5)])
 def test_glue_stack_plan_multi_token(qd, fmt, m):
-    """A plan of the glued step at m > 1 (it replays the glued launches)."""
+    """A plan of the glued step at m > 1: the persistent kernel runs all of
+    it (int8, INT4; fp16 replays launches).  Each op against the oracle on
+    the activations it read, and bit-identical repeated runs with the outputs
+    poisoned in between: the RMSNorm factors come from per-workgroup records
+    added in a fixed order, gate|up runs paired and writes down's gated
+    product."""
     ops, meta, keep = _glue_stack(qd, fmt, m, _tiny())
     plan = qd.StackPlan(ops, m)
-    plan.run()
-    torch.cuda.synchronize()
-    _check_glue_stack(fmt, m, ops, meta, f"plan {fmt} m={m}")
+    assert plan.persistent == (fmt != "fp16")
+    if fmt != "fp16":
+        d = qd.describe_stack_plan(ops, m)
+        assert d[4] == 1 and d[5] == len(ops), "the whole glued step runs in the persistent kernel"
+    first = None
+    for rep in range(3):
+        for op in ops:
+            op.y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        outs = [_host(op.y).copy() for op in ops]
+        if first is None:
+            first = outs
+            _check_glue_stack(fmt, m, ops, meta, f"plan {fmt} m={m}")
+        else:
+            for a, b in zip(first, outs):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
     plan.close()
 
 
@@ -317,10 +341,11 @@ def test_glue_stack_persistent(qd, fmt):
 
 @pytest.mark.parametrize("workload,path", [("qwen3-8b-int8-glue-m1", "launches"),
                                            ("qwen3-8b-int8-glue-m1", "plan"),
-                                           ("qwen3-8b-int8-glue-m16", "launches")])
+                                           ("qwen3-8b-int8-glue-m16", "launches"),
+                                           ("qwen3-8b-int8-glue-m16", "plan")])
 def test_glue_full_size_sampled(qd, workload, path):
     """The full 8B-shaped step chained through the glue, as the bench times it
-    (the persistent plan at one token row, per-group launches): every output
+    (the persistent plan, per-group launches): every output
     finite; sampled rows of sampled projections (RMSNorm-fed q and head,
     silu-stored gate, up, gated-product-fed down, plain o) match the oracle on
     the activations each op read."""
@@ -463,3 +488,113 @@ def test_plan_random_glued_steps_against_sequential_model(qd):
         assert plan.error() == 0
         assert np.array_equal(snapshot().view(np.uint16), states[-1].view(np.uint16)), f"case {case}"
         plan.close()
+
+
+def test_plan_random_glued_steps_multi_token(qd):
+    """Random glued steps at 2, 5 and 16 token rows against a sequential
+    model of the buffers built from the oracle.  Groups take no prologue,
+    RMSNorm or the gated product; inputs are fresh, an earlier op's whole
+    output (so RMSNorm's factors come from the producing op's per-workgroup
+    records) or the two outputs of an earlier two-op group written one after
+    the other (so that group runs paired and writes the product); ops store
+    with or without silu.  Where a glued group falls outside what the
+    persistent kernel takes, the rest of the step replays launches.  Every
+    group is checked on the input the device gave it, at the acceptance
+    bound, nothing else may change, and the one-plan step must reproduce the
+    final buffers bit for bit."""
+    from int4_quantized_decode_amd import LinearOp
+    rng = np.random.default_rng(si.seed_for("random-glued-steps-multi"))
+    arena_n = 1 << 21
+    seen_paired = seen_records = 0
+    for case in range(12):
+        fmt = ["int8_b32", "int4_g64"][case % 2]
+        m = [2, 5, 16][case % 3]
+        init = si.activations(si.seed_for("random-glued-arena-multi", case), 1, arena_n)[0]
+        arena = _gpu(init)
+        top = 0
+
+        def take(n):
+            nonlocal top
+            off = top
+            top += (n + 63) // 64 * 64
+            assert top <= arena_n
+            return off
+
+        ops, prog, outs, pairs = [], [], [], []
+        for g in range(int(rng.integers(2, 7))):
+            pro = ["none", "rmsnorm", "glu"][int(rng.integers(3))]
+            k = int(rng.choice([256, 512, 1088]))
+            if pro == "glu" and pairs and rng.random() < 0.7:
+                xo, k = pairs[int(rng.integers(len(pairs)))]
+            elif pro != "glu" and any(n % 64 == 0 for _, n in outs) and rng.random() < 0.6:
+                cands = [(o, n) for o, n in outs if n % 64 == 0]      # a K both formats take
+                xo, k = cands[int(rng.integers(len(cands)))]
+            else:
+                xo = take(m * k * (2 if pro == "glu" else 1))
+            span = m * k * (2 if pro == "glu" else 1)
+            gamma = None
+            if pro == "rmsnorm":
+                gamma = _gpu((1.0 + 0.25 * rng.standard_normal(k)).astype(np.float16))
+            members = []
+            if rng.random() < 0.4:
+                n = int(rng.choice([256, 512, 1088]))
+                go = take(2 * m * n)
+                for j in range(2):
+                    epi = "silu" if (j == 0 and rng.random() < 0.7) else "none"
+                    w = si.weights(si.seed_for("random-glued-multi-w", case, g, j), n, k)
+                    members.append((go + j * m * n, n, w, epi))
+                pairs.append((go, n))
+            else:
+                for j in range(int(rng.integers(1, 4))):
+                    n = int(rng.choice([16, 48, 256, 1000, 1088]))
+                    epi = "silu" if rng.random() < 0.4 else "none"
+                    w = si.weights(si.seed_for("random-glued-multi-w", case, g, j), n, k)
+                    members.append((take(m * n), n, w, epi))
+            for yo, n, w, epi in members:
+                ops.append(LinearOp(_pack(qd, fmt, w), arena[xo:xo + span].view(-1, k) if pro != "glu"
+                                    else arena[xo:xo + span], arena[yo:yo + m * n].view(m, n), g,
+                                    prologue=pro, gamma=gamma, eps=EPS if pro == "rmsnorm" else 0.0,
+                                    epilogue=epi))
+            prog.append((xo, k, span, pro, None if gamma is None else _host(gamma), members))
+            outs.extend((yo, n) for yo, n, _, _ in members)
+        v, groups, _, _ = _plan_tables(qd, ops, m)
+        assert v[1] == 1, f"case {case}"
+        seen_paired += any(g[8] & 16 for g in groups)          # a paired group writes a gated product
+        seen_records += v[16] > 0                               # sum-of-squares records
+        init_g = _gpu(init)
+
+        def restore():
+            arena.copy_(init_g)
+
+        def snapshot():
+            return _host(arena).copy()
+
+        states = _prefix_states(qd, ops, m, restore, snapshot)
+        for g, (xo, k, span, pro, gam, members) in enumerate(prog):
+            raw = states[g][xo:xo + span]
+            assert np.all(np.isfinite(raw.astype(np.float64))), f"case {case} group {g} input"
+            raw = raw.reshape(2, m, k) if pro == "glu" else raw.reshape(m, k)
+            X = glue.apply_prologue(pro, raw, gam, EPS).astype(np.float64)
+            touched = np.zeros(arena_n, bool)
+            for yo, n, w, epi in members:
+                parts = _parts(fmt, w)
+                Y = linear.ref_linear(fmt, parts, X)
+                got = states[g + 1][yo:yo + m * n].reshape(m, n)
+                rmax = linear.row_max_abs(fmt, parts)
+                for t in range(m):
+                    what = f"case {case} ({fmt}, m={m}) group {g} {pro} output at {yo} token {t}"
+                    if epi == "silu":
+                        _check_silu(got[t], Y[t], rmax, X[t], what)
+                    else:
+                        check_vector(got[t], Y[t], rmax, X[t], what)
+                touched[yo:yo + m * n] = True
+            assert np.array_equal(states[g + 1][~touched].view(np.uint16), states[g][~touched].view(np.uint16)), \
+                f"case {case} group {g} wrote outside its outputs"
+        plan = qd.StackPlan(ops, m)
+        restore()
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        assert np.array_equal(snapshot().view(np.uint16), states[-1].view(np.uint16)), f"case {case}"
+        plan.close()
+    assert seen_paired >= 2 and seen_records >= 2

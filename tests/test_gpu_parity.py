@@ -895,11 +895,11 @@ def test_plan_multi_token_unit_across_members(qd, fmt):
         x_g = _gpu(x)
         ys = [torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV) for n, _ in shapes]
         ops = [LinearOp(pw, x_g, y, 0) for pw, y in zip(pws, ys)]
-        v = qd.describe_stack_plan(ops, m)
+        v, groups, members, sched = _plan_tables(qd, ops, m)
         G, ng, nm = v[8], v[6], v[7]
         assert v[1] == 1 and ng == 1 and nm == 3
-        starts = {v[16 + 10 * ng + 7 * i + 3] for i in range(1, nm)}     # members' first row-groups
-        sched = [v[16 + 10 * ng + 7 * nm + 4 * w:16 + 10 * ng + 7 * nm + 4 * w + 4] for w in range(G)]
+        starts = {mb[3] for mb in members[1:]}                          # members' first row-groups
+        sched = sched[:G]
         crossing = sum(1 for _, _, rg0, nseg in sched for u in range(0, nseg - 1, 2) if rg0 + u + 1 in starts)
         assert crossing >= 1, "no unit holds row-groups of two members"
         plan = qd.StackPlan(ops, m)
@@ -944,10 +944,8 @@ def test_plan_multi_token_copy_of_a_split_member(qd):
            LinearOp(pws["d"], x_g, y["d"], 2), LinearOp(pws["e"], x_g, y["e"], 2),
            LinearOp(pws["f"], y["d"], y["f"], 3)]
     # The schedule this device gets: b's slices carry no copy, d's do.
-    v = qd.describe_stack_plan(ops, m)
+    v, groups, members, _ = _plan_tables(qd, ops, m)
     ng, nm = v[6], v[7]
-    groups = [v[16 + 10 * i:26 + 10 * i] for i in range(ng)]
-    members = [v[16 + 10 * ng + 7 * i:23 + 10 * ng + 7 * i] for i in range(nm)]
     yptr = {name: t.data_ptr() for name, t in y.items()}
     if v[8] != 256:
         pytest.skip("the cuts are laid out for 256 compute units")
@@ -995,6 +993,21 @@ def _group_slices(ops):
         out.append((i, e))
         i = e
     return out
+
+
+def _plan_tables(qd, ops, m):
+    """qd_stack_plan_describe's words for `ops` on this device, cut into the
+    header, the group records (12 words), the member records (8 words) and
+    the per-workgroup schedule entries (4 words, group-major)."""
+    v = qd.describe_stack_plan(ops, m)
+    assert v[0] == 2
+    ng, nm, G = v[6], v[7], v[8]
+    groups = [v[17 + 12 * i:29 + 12 * i] for i in range(ng)]
+    mo = 17 + 12 * ng
+    members = [v[mo + 8 * i:mo + 8 * i + 8] for i in range(nm)]
+    so = mo + 8 * nm
+    sched = [v[so + 4 * i:so + 4 * i + 4] for i in range(ng * G)]
+    return v, groups, members, sched
 
 
 def _prefix_states(qd, ops, m, restore, snapshot):
@@ -1281,10 +1294,8 @@ def test_plan_new_activations_every_step(qd, m):
     pws = [qd.qpack_int8_b32(_gpu(w)) for w in ws]
     bufs = [torch.zeros(shape(k), dtype=torch.float16, device=DEV) for _ in range(len(ws) + 1)]
     ops = [LinearOp(pws[i], bufs[i], bufs[i + 1], i) for i in range(len(ws))]
-    v = qd.describe_stack_plan(ops, m)
+    v, groups, members, _ = _plan_tables(qd, ops, m)
     ng, nm, njobs = v[6], v[7], v[10]
-    groups = [v[16 + 10 * i:26 + 10 * i] for i in range(ng)]
-    members = [v[16 + 10 * ng + 7 * i:23 + 10 * ng + 7 * i] for i in range(nm)]
     assert v[1] == 1 and ng == len(ws)
     if m == 1:
         assert all(g[8] & 8 for g in groups[1:]), "chained groups should read through the caches"

@@ -31,7 +31,7 @@ from synthetic_inputs import QWEN3_2B, QWEN3_8B, QWEN38_27B, Decoder
 FMT = {"int8_b32": 1, "int4_g64": 2, "fp16": 3}
 PRO_NONE, PRO_RMSNORM, PRO_GLU = 0, 1, 2
 EPI_NONE, EPI_SILU = 0, 1
-EARLY, ACK, NOWAIT, CLEAN = 1, 2, 4, 8
+EARLY, ACK, NOWAIT, CLEAN, PAIRED = 1, 2, 4, 8, 16
 TILE_BYTES = {1: 4352, 2: 2304}
 LDS_MAX = 160 * 1024
 
@@ -102,8 +102,8 @@ class StepBuilder:
 def step_ops(L, dec: Decoder, m, fmt, layers=None, chain=False, glue=False, head_fmt=None):
     """One decode step's op list: q|k|v -> o -> gate|up -> down per layer,
     then the head.  Plain: every group reads an activation of its own.
-    Chained: each group reads an earlier group's output.  Glued (one token
-    row): RMSNorm before q|k|v, gate|up and the head, silu on gate, the
+    Chained: each group reads an earlier group's output.  Glued:
+    RMSNorm before q|k|v, gate|up and the head, silu on gate, the
     gated product before down."""
     b = StepBuilder(L, m)
     H, Q, KV, I = dec.hidden, dec.q_dim, dec.kv_dim, dec.mlp
@@ -148,9 +148,9 @@ def describe(L, b, workgroups=256):
                                         ctypes.byref(n)) == 0
     v = list(buf)
     keys = ["version", "persistent", "fmt", "m", "glue", "prefix", "ngroups", "nmem", "G",
-            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes"]
-    d = dict(zip(keys, v[:16]))
-    pos = 16
+            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes", "ss_total"]
+    d = dict(zip(keys, v[:17]))
+    pos = 17
 
     def take(count, width, names):
         nonlocal pos
@@ -160,11 +160,11 @@ def describe(L, b, workgroups=256):
             pos += width
         return out
 
-    d["groups"] = take(d["ngroups"], 10, ["x", "gamma", "k", "J", "R", "mem0", "nmem", "pro", "order",
-                                          "xt"])
-    d["members"] = take(d["nmem"], 7, ["blob", "y", "n", "rg_begin", "epi", "ld", "yt"])
+    d["groups"] = take(d["ngroups"], 12, ["x", "gamma", "k", "J", "R", "mem0", "nmem", "pro", "order",
+                                          "xt", "ss0", "ss_n"])
+    d["members"] = take(d["nmem"], 8, ["blob", "y", "n", "rg_begin", "epi", "ld", "yt", "ss"])
     d["sched"] = take(d["ngroups"] * d["G"], 4, ["n", "off", "rg0", "nseg"])
-    d["jobs"] = take(d["njobs"], 4, ["x", "t", "k", "first_block"])
+    d["jobs"] = take(d["njobs"], 6, ["x", "t", "k", "first_block", "glu", "rec"])
     assert pos == len(v)
     return d
 
@@ -203,7 +203,7 @@ def attach_sources(b, d):
 def check_layout(b, d, lds_fits=True):
     m, ops = b.m, b.ops
     G, gs, ms = d["G"], d["groups"], d["members"]
-    assert d["version"] == 1 and d["persistent"] == 1 and d["m"] == m
+    assert d["version"] == 2 and d["persistent"] == 1 and d["m"] == m
     src = attach_sources(b, d)
 
     # Rows: every op of the prefix is covered exactly once by its slices.
@@ -232,7 +232,14 @@ def check_layout(b, d, lds_fits=True):
         assert sch[0]["rg0"] == 0
         assert all(sch[w]["rg0"] + sch[w]["nseg"] == sch[w + 1]["rg0"] for w in range(G - 1))
         assert sch[-1]["rg0"] + sch[-1]["nseg"] == g["R"]
-        assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 1
+        if g["order"] & PAIRED:
+            # Paired (several token rows, its two members' gated product read
+            # later): ranges of whole pairs of row-groups, balanced in pairs.
+            assert m > 1 and g["nmem"] == 2 and g["R"] % 2 == 0
+            assert all(s["rg0"] % 2 == 0 and s["nseg"] % 2 == 0 for s in sch)
+            assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 2
+        else:
+            assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 1
         unit = 2 if m > 1 else 1
         assert all(s["n"] == -(-s["nseg"] // unit) * g["J"] for s in sch)
     # Tile offsets: running sums over the groups a workgroup has work in.
@@ -306,11 +313,14 @@ def check_layout(b, d, lds_fits=True):
             assert bool(o & ACK) == ack, f"group {gi} acknowledge flag"
             assert bool(o & CLEAN) == clean, f"group {gi} cache-read flag"
 
-    # Activation copies (several token rows).
+    # Activation copies and sum-of-squares records (several token rows).
     if m == 1:
-        assert d["xt_total"] == 0 and d["njobs"] == 0
-        assert all(g["xt"] == -1 for g in gs) and all(mb["yt"] == -1 for mb in ms)
+        assert d["xt_total"] == 0 and d["njobs"] == 0 and d["ss_total"] == 0
+        assert all(g["xt"] == -1 and g["ss_n"] == 0 for g in gs)
+        assert all(mb["yt"] == -1 and mb["ss"] == -1 for mb in ms)
+        assert not any(g["order"] & PAIRED for g in gs)
     else:
+        check_records(b, d, src, sg)
         slots = {}
         for g in gs:
             if g["xt"] >= 0:
@@ -319,15 +329,22 @@ def check_layout(b, d, lds_fits=True):
         spans = sorted(slots.items())
         assert all(a + s <= b2 for (a, s), (b2, _) in zip(spans, spans[1:]))
         assert not spans or spans[-1][0] + spans[-1][1] <= d["xt_total"]
-        job_keys = {(jb["x"], jb["k"]): jb["t"] for jb in d["jobs"]}
-        assert len(job_keys) == d["njobs"]
+        # Jobs made before the step: copies (of x, or of the gated product of
+        # its two blocks) and sum-of-squares records, one of each per key.
+        for jb in d["jobs"]:
+            assert (jb["t"] >= 0) != (jb["rec"] >= 0) and (jb["glu"] == 0 or jb["t"] >= 0)
+        copy_jobs = {(jb["x"], jb["k"], jb["glu"]): jb["t"] for jb in d["jobs"] if jb["t"] >= 0}
+        rec_jobs = {(jb["x"], jb["k"]): jb["rec"] for jb in d["jobs"] if jb["t"] < 0}
+        assert len(copy_jobs) + len(rec_jobs) == d["njobs"]
         blocks = 0
         for jb in d["jobs"]:
             assert jb["first_block"] == blocks
-            blocks += 2 * -(-jb["k"] // 256)
+            blocks += 2 * -(-jb["k"] // 256) if jb["t"] >= 0 else 1
         for gi, g in enumerate(gs):
             if g["order"] & EARLY:
-                assert g["xt"] == job_keys[(g["x"], g["k"])]
+                assert g["xt"] == copy_jobs[(g["x"], g["k"], int(g["pro"] == PRO_GLU))]
+            if g["pro"] == PRO_GLU:
+                assert g["xt"] >= 0, "a gated product at several token rows is read from its copy"
         # Output copies: member slices of one op share the op's copy, at
         # 512 bytes per row-group of skip, with skip whole 256-row blocks.
         base = {}
@@ -338,11 +355,19 @@ def check_layout(b, d, lds_fits=True):
             assert r0 % 256 == 0, "copy offset cut inside a 256-row block"
             b0 = base.setdefault(op_i, mb["yt"] - r0 * 32)
             assert mb["yt"] == b0 + r0 * 32
+        paired_op = {src[j][0]: bool(g["order"] & PAIRED) for g in gs
+                     for j in range(g["mem0"], g["mem0"] + g["nmem"])}
+        for g in gs:
+            if g["order"] & PAIRED:   # the first member's copy slot holds the product, the second has none
+                assert ms[g["mem0"] + 1]["yt"] == -1
         for op_i, b0 in base.items():
             o = ops[op_i]
             consumers = [g for g in gs if g["xt"] == b0]
-            assert consumers and all(g["x"] == o.y and g["k"] == o.n and g["pro"] == PRO_NONE
-                                     for g in consumers)
+            assert consumers and all(g["x"] == o.y and g["k"] == o.n for g in consumers)
+            if paired_op[op_i]:
+                assert all(g["pro"] == PRO_GLU for g in consumers)
+            else:
+                assert all(g["pro"] in (PRO_NONE, PRO_RMSNORM) for g in consumers)
             assert all(not (g["order"] & EARLY) for g in consumers)
         for g in gs:
             if g["xt"] >= 0 and not g["order"] & EARLY:
@@ -351,6 +376,48 @@ def check_layout(b, d, lds_fits=True):
     # then replays launches, which the device check in plan creation decides.)
     assert d["lds"] <= LDS_MAX or not lds_fits
     assert d["lds"] >= d["x_bytes"] + d["red_bytes"] + d["cnt_bytes"] + d["tab_bytes"]
+
+
+def check_records(b, d, src, sg):
+    """Several token rows: each RMSNorm group's ss_n records add up to its
+    activation's per-token sums of squares.  Either no group of the step
+    writes the activation and one record is made before the step (a record
+    job on (x, K)), or the activation is exactly the whole output of one op
+    that its last writer ran, and the records are that op's: G per member
+    slice (one per workgroup), contiguous in slice order.  Records are
+    disjoint and within ss_total; records nobody reads are never written."""
+    m, ops, G, gs, ms = b.m, b.ops, d["G"], d["groups"], d["members"]
+    rec_jobs = {(jb["x"], jb["k"]): jb["rec"] for jb in d["jobs"] if jb["t"] < 0}
+    spans = sorted([(mb["ss"], G) for mb in ms if mb["ss"] >= 0] + [(r, 1) for r in rec_jobs.values()])
+    assert all(a + n <= b2 for (a, n), (b2, _) in zip(spans, spans[1:]))
+    assert sum(n for _, n in spans) == d["ss_total"]
+    step_of = {}                                # plan group -> index into sg
+    for i, (gl, _) in enumerate(sg):
+        for gi in gl:
+            step_of[gi] = i
+    readers = set()
+    for gi, g in enumerate(gs):
+        if g["pro"] != PRO_RMSNORM:
+            assert g["ss_n"] == 0
+            continue
+        writers = [t for t in range(step_of[gi]) for j in sg[t][1]
+                   if overlap(g["x"], m * g["k"] * 2, ms[j]["y"], ((m - 1) * ms[j]["ld"] + ms[j]["n"]) * 2)]
+        if not writers:
+            assert (g["ss0"], g["ss_n"]) == (rec_jobs[(g["x"], g["k"])], 1)
+            continue
+        last = max(writers)
+        mine = [j for j in sg[last][1] if ops[src[j][0]].y == g["x"]]
+        assert mine, "RMSNorm records from an op that is not x's last writer"
+        op_i = src[mine[0]][0]
+        assert ops[op_i].n == g["k"] and all(src[j][0] == op_i for j in mine)
+        assert [ms[j]["ss"] for j in mine] == [g["ss0"] + G * t for t in range(len(mine))]
+        assert g["ss_n"] == G * len(mine)
+        readers.update(mine)
+    assert readers == {j for j, mb in enumerate(ms) if mb["ss"] >= 0}, "records nobody reads"
+    for gl, mj in sg:
+        assert len({src[j][0] for j in mj if ms[j]["ss"] >= 0}) <= 1, "two ops of one group with records"
+        if gs[gl[0]]["order"] & PAIRED:
+            assert all(ms[j]["ss"] < 0 for j in mj)
 
 
 CASES = [
@@ -363,6 +430,10 @@ CASES = [
     ("qwen3-8b int8 chain m1", QWEN3_8B, 1, "int8_b32", {"chain": True}),
     ("qwen3-8b int8 chain m16", QWEN3_8B, 16, "int8_b32", {"chain": True}),
     ("qwen3-8b int8 glue m1", QWEN3_8B, 1, "int8_b32", {"glue": True}),
+    ("qwen3-8b int8 glue m16", QWEN3_8B, 16, "int8_b32", {"glue": True}),
+    ("qwen3-8b int4 glue m16", QWEN3_8B, 16, "int4_g64", {"glue": True}),
+    ("qwen3-2b int8 glue m5", QWEN3_2B, 5, "int8_b32", {"glue": True}),
+    ("qwen3.8-27b int8 glue m16 (3 layers)", QWEN38_27B, 16, "int8_b32", {"glue": True, "layers": 3}),
     ("qwen3.8-27b int8 m16 (4 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 4}),
     ("qwen3.8-27b int8 chain m16 (3 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 3, "chain": True}),
     ("qwen3-8b int8 chain m5", QWEN3_8B, 5, "int8_b32", {"chain": True, "layers": 4}),
@@ -393,11 +464,11 @@ def test_plan_layout_fp16_head_is_replayed_tail(L):
     check_layout(b, d)
 
 
-@pytest.mark.parametrize("m,fmt,kw", [(16, "int8_b32", {"glue": True}), (1, "fp16", {}), (16, "fp16", {})])
+@pytest.mark.parametrize("m,fmt,kw", [(1, "fp16", {}), (16, "fp16", {})])
 def test_plan_layout_replays_whole(L, m, fmt, kw):
     b = step_ops(L, QWEN3_8B, m, fmt, layers=1, **kw)
     d = describe(L, b)
-    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 16 + 4
+    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 17 + 4
 
 
 def test_plan_layout_copy_not_cut_inside_a_block(L):
@@ -518,3 +589,113 @@ def test_plan_layout_random_steps(L):
         check_layout(b, d, lds_fits=G >= 80)
         checked += 1
     assert checked >= 100
+
+
+def _glue_prefix(b):
+    """The first op the persistent kernel cannot take in a glued step at
+    several token rows, by the rules the plan states: an RMSNorm group needs
+    its activation unwritten by the step, or exactly the whole output of one
+    op of its last writer (an op that is then the only one of its group with
+    sum-of-squares records, in a group that is not paired); a gated product
+    needs its two blocks unwritten by the step, or exactly the whole outputs
+    of the two ops of its last writer, A's first (a group that then runs
+    paired and has no records)."""
+    m, ops = b.m, b.ops
+    groups = []                                   # [(first op, [op indices])]
+    for i, o in enumerate(ops):
+        if groups and ops[groups[-1][1][0]].group == o.group:
+            groups[-1][1].append(i)
+        else:
+            groups.append((i, [i]))
+    paired, recs = set(), {}                      # group index; group index -> op with records
+    for g, (first, mem) in enumerate(groups):
+        o = ops[first]
+        if o.pro == PRO_NONE:
+            continue
+        span = m * o.k * 2 * (2 if o.pro == PRO_GLU else 1)
+        last = max((h for h in range(g) for j in groups[h][1]
+                    if overlap(o.x, span, ops[j].y, m * ops[j].n * 2)), default=None)
+        if last is None:
+            continue
+        lm = groups[last][1]
+        if o.pro == PRO_RMSNORM:
+            hit = [j for j in lm if overlap(o.x, span, ops[j].y, m * ops[j].n * 2)]
+            ok = (len(hit) == 1 and ops[hit[0]].y == o.x and ops[hit[0]].n == o.k and last not in paired
+                  and recs.get(last, hit[0]) == hit[0])
+            if ok:
+                recs[last] = hit[0]
+        else:
+            ok = (len(lm) == 2 and last not in recs and ops[lm[0]].y == o.x and
+                  ops[lm[1]].y == o.x + m * o.k * 2 and ops[lm[0]].n == o.k and ops[lm[1]].n == o.k)
+            if ok:
+                paired.add(last)
+        if not ok:
+            return first
+    return len(ops)
+
+
+def _random_glued_step(L, rng):
+    """A random glued step at several token rows: groups take no prologue,
+    RMSNorm or the gated product; activations are fresh, an earlier op's
+    whole output, the start of a longer one, or (gated product) the two
+    outputs of an earlier two-op group written A then B, B then A, or with
+    a third op beside them; ops store with or without silu."""
+    fmt = int(rng.choice([1, 2]))
+    m = int(rng.choice([2, 5, 16]))
+    b = StepBuilder(L, m)
+    outs, pairs = [], []                          # (y, n); (A address, n) of two-op groups
+    for _ in range(int(rng.integers(2, 8))):
+        pro = int(rng.choice([PRO_NONE, PRO_RMSNORM, PRO_GLU]))
+        k = int(rng.choice([256, 512, 1024, 2048]))
+        r = rng.random()
+        if pro == PRO_GLU and pairs and r < 0.6:
+            x, k = pairs[int(rng.integers(len(pairs)))]
+        elif pro != PRO_GLU and outs and r < 0.6:
+            y, n = outs[int(rng.integers(len(outs)))]
+            x, k = y, (n if rng.random() < 0.7 or n < 256 else 256)
+        else:
+            x = b.heap.take(m * k * 2 * (2 if pro == PRO_GLU else 1))
+        gamma = b.heap.take(k * 2) if pro == PRO_RMSNORM else 0
+        shape = rng.random()
+        if shape < 0.35:                          # a gate|up-like pair writing one buffer
+            n = int(rng.choice([256, 512, 1024]))
+            gu = b.heap.take(2 * m * n * 2)
+            ys = [gu, gu + m * n * 2] if rng.random() < 0.8 else [gu + m * n * 2, gu]
+            members = [(n, k), (n, k)]
+            if rng.random() < 0.15:
+                members.append((64, k))
+                ys.append(b.heap.take(m * 64 * 2))
+            epis = [int(rng.choice([EPI_NONE, EPI_SILU])) for _ in members]
+            got = b.group(members, x, fmt, pro, gamma, epis=epis, ys=ys)
+            if len(members) == 2 and ys[0] < ys[1]:
+                pairs.append((gu, n))
+        else:
+            members = [(int(rng.choice([64, 256, 512, 1024, 2048])), k) for _ in range(int(rng.integers(1, 4)))]
+            epis = [int(rng.choice([EPI_NONE, EPI_SILU])) for _ in members]
+            got = b.group(members, x, fmt, pro, gamma, epis=epis)
+        outs.extend(zip(got, [n for n, _ in members]))
+    return b
+
+
+def test_plan_layout_random_glued_steps(L):
+    """300 random glued steps at several token rows: the persistent part ends
+    exactly where the rules say, and its tables pass every invariant above
+    (records, paired groups, product copies included)."""
+    import numpy as np
+    rng = np.random.default_rng(20261204)
+    checked = cut = 0
+    for _ in range(300):
+        b = _random_glued_step(L, rng)
+        arr, n = b.array(), ctypes.c_int64(0)
+        if L.lib.qd_stack_plan_describe(arr, len(b.ops), b.m, 256, None, 0, ctypes.byref(n)) != 0:
+            continue
+        d = describe(L, b, 256)
+        want = _glue_prefix(b)
+        if want == 0:
+            assert d["persistent"] == 0
+            continue
+        assert d["persistent"] == 1 and d["prefix"] == want
+        check_layout(b, d)
+        checked += 1
+        cut += want < len(b.ops)
+    assert checked >= 150 and 20 <= cut <= checked - 20
