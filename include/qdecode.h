@@ -227,20 +227,31 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * copies the descriptors to the device and allocates the plan's scratch
  * (completion stamps, an error word and, at m > 1, copies of the step's
  * activations in the order the matrix cores read them: 8 KiB per 256 input
- * features per group, about 28 MB for an 8B-shaped step) once; the pointers
- * in `ops` must stay valid while the plan lives.  qd_stack_plan_run enqueues
- * one step on `stream` (at m > 1 a small copy kernel for the activations no
- * op of the step writes, then the persistent kernel) and allocates nothing.  A plan may be run repeatedly but not
+ * features per group, about 28 MB for an 8B-shaped step, and 64 bytes of
+ * RMSNorm statistics per workgroup per op that feeds an RMSNorm) once; the
+ * pointers in `ops` must stay valid while the plan lives.
+ * qd_stack_plan_run enqueues one step on `stream` (at m > 1 a small kernel
+ * for what the step needs of the activations no op of it writes: their
+ * copies, gated products and RMSNorm statistics; then the persistent kernel)
+ * and allocates nothing.  A plan may be run repeatedly but not
  * concurrently.  The persistent kernel takes groups of one format, int8
- * b32 or INT4 g64, at m = 1 with or without glue and at m = 2..16 without
- * glue.  It runs the step's leading groups that qualify; from the first
+ * b32 or INT4 g64, at m = 1..16, with or without glue.  At m > 1 a glued
+ * group qualifies when its input is one the kernel can prepare: under
+ * QD_PRO_RMSNORM, x is not written by the step, or is exactly the whole
+ * output of one op of the last group writing it (that op's workgroups then
+ * write per-token sums of squares of what they store, added in a fixed order
+ * by the consumer; such an op must be the only one of its group feeding an
+ * RMSNorm); under QD_PRO_GLU, x is not written by the step, or its two
+ * blocks are exactly the whole outputs of the two ops of the last group
+ * writing it, A's first (that group then computes row-group i of both ops
+ * together and writes the product itself; it may not also feed an RMSNorm).
+ * The plan runs the step's leading groups that qualify; from the first
  * group that does not (say an fp16 head), the rest of the step is replayed
  * after it as the same per-group launches decode_linear_stack makes.  A
- * step whose first group does not qualify (fp16 weights, glue at m > 1), or
- * whose schedule is larger than one CU's LDS or has
- * a row-group too long for it at m > 1, is replayed whole, with the same
- * results as decode_linear_stack; qd_stack_plan_is_persistent tells whether
- * the persistent kernel runs.
+ * step whose first group does not qualify (fp16 weights), or whose schedule
+ * is larger than one CU's LDS or has a row-group too long for it at m > 1,
+ * is replayed whole, with the same results as decode_linear_stack;
+ * qd_stack_plan_is_persistent tells whether the persistent kernel runs.
  */
 typedef struct qd_stack_plan qd_stack_plan;
 
@@ -265,24 +276,32 @@ qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
  * and offset, never dereferenced, so any values that pass the validation of
  * decode_linear_stack will do).  Writes int64 words to `out` (host memory,
  * caller-owned) and their count to *out_len:
- *   header, 16 words: version (1), persistent (0/1), format, m, glue (0/1),
+ *   header, 17 words: version (2), persistent (0/1), format, m, glue (0/1),
  *     prefix ops (ops [0, prefix) run in the persistent kernel, the rest are
  *     replayed after it), groups G_n, members M_n, workgroups W, bytes of the
- *     activation copies, copy jobs J_n, dynamic LDS bytes, then LDS bytes of
- *     the staged activations, the tile partials, the row-group counters and
- *     the schedule tables;
- *   G_n groups of 10 words, in the order the kernel runs them: x, gamma, K,
+ *     activation copies, pre-step jobs J_n, dynamic LDS bytes, then LDS bytes
+ *     of the staged activations (at m > 1: RMSNorm gamma), the tile partials,
+ *     the row-group counters and the schedule tables, and the number of
+ *     RMSNorm statistics records (16 floats each);
+ *   G_n groups of 12 words, in the order the kernel runs them: x, gamma, K,
  *     super-blocks J, row-groups R, first member, members, prologue, order
  *     flags (1 = may stage early, 2 = acknowledges its stores before its
  *     stamp, 4 = waits for nothing (a later row range of a split group),
- *     8 = reads its activations through the caches), offset of its activation
- *     copy in the plan's copies or -1;
- *   M_n members of 7 words: weight blob, y, rows N, first row-group within
+ *     8 = reads its activations through the caches, 16 = paired: row-group
+ *     2i + b is row-group i of member b, and the group writes the gated
+ *     product of its two members' outputs), offset of its activation copy in
+ *     the plan's copies or -1 (under QD_PRO_GLU at m > 1: of the product),
+ *     first statistics record of its RMSNorm input and their count (0, 0
+ *     when none);
+ *   M_n members of 8 words: weight blob, y, rows N, first row-group within
  *     the group, epilogue, elements between token rows of y, offset of the
- *     copy of its outputs or -1;
+ *     copy of its outputs or -1 (a paired group's first member: where it
+ *     writes the product), first of its W statistics records or -1;
  *   G_n x W schedule entries of 4 words, group-major: tiles, tiles of this
  *     workgroup in earlier groups, first row-group, row-groups;
- *   J_n copy jobs of 4 words: x, offset of its copy, K, first block.
+ *   J_n pre-step jobs of 6 words: x, offset of its copy or -1, K, first
+ *     block, 1 if the copy holds the gated product of x's two blocks, the
+ *     statistics record it writes or -1.
  * A step that replays whole gives the header alone.  With out NULL only
  * *out_len is set (a size query, QD_OK); with cap below the count *out_len is
  * set, nothing is written and the result is QD_ESHAPE.  QD_EINVAL for a null out_len, a
@@ -303,8 +322,10 @@ void qd_stack_plan_destroy(qd_stack_plan* plan);
  * (the tables travel as kernel arguments, so a captured graph replays exactly
  * the captured call).  Differences from a plan: activations are always read
  * in place (no copies in matrix-core order, so steps with several token rows
- * run somewhat slower); the launch is always a plain one (see the plan's
- * launch above; there is no plan to switch to cooperative launches).
+ * run somewhat slower), and at m > 1 the first group with glue ends the
+ * persistent part (glue there needs the plan's copies and statistics); the
+ * launch is always a plain one (see the plan's launch above; there is no
+ * plan to switch to cooperative launches).
  * Arguments and validation as decode_linear_stack; additionally QD_ESHAPE if
  * the step needs more than 512 group records or 1024 member records after
  * the row-range split at several token rows, QD_EALIGN if err_flag is not
