@@ -206,8 +206,11 @@ qd_status decode_linear_stack(const qd_linear_op* ops, int64_t n_ops, int64_t m,
  * The same step as a persistent plan: one kernel launch per step that walks
  * every group in order, keeping the weight stream going across group
  * boundaries (weights of later groups are fetched while a group completes).
- * Every group's products start only after every workgroup has finished the
- * group before it.  The plan orders each boundary from the step's buffers:
+ * A group that reads an earlier group's output, or writes what an earlier
+ * group reads or writes, starts its products only after every workgroup has
+ * finished the group before it; a group independent of every earlier one
+ * does not wait for them (outputs are the same either way).  The plan orders
+ * each boundary from the step's buffers:
  * a group's activations are read ahead of that barrier only when no earlier
  * group writes any byte of them, and a group's outputs are made visible
  * before its completion is signalled only when a later group reads or
@@ -276,18 +279,22 @@ qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
  * and offset, never dereferenced, so any values that pass the validation of
  * decode_linear_stack will do).  Writes int64 words to `out` (host memory,
  * caller-owned) and their count to *out_len:
- *   header, 17 words: version (2), persistent (0/1), format, m, glue (0/1),
+ *   header, 18 words: version (3), persistent (0/1), format, m, glue (0/1),
  *     prefix ops (ops [0, prefix) run in the persistent kernel, the rest are
  *     replayed after it), groups G_n, members M_n, workgroups W, bytes of the
  *     activation copies, pre-step jobs J_n, dynamic LDS bytes, then LDS bytes
  *     of the staged activations (at m > 1: RMSNorm gamma), the tile partials,
- *     the row-group counters and the schedule tables, and the number of
- *     RMSNorm statistics records (16 floats each);
+ *     the row-group counters and the schedule tables, the number of
+ *     RMSNorm statistics records (16 floats each), and the drift bound: before
+ *     a group independent of every earlier one, how many groups the slowest
+ *     workgroup may trail (0: unbounded);
  *   G_n groups of 12 words, in the order the kernel runs them: x, gamma, K,
  *     super-blocks J, row-groups R, first member, members, prologue, order
  *     flags (1 = may stage early, 2 = acknowledges its stores before its
  *     stamp, 4 = waits for nothing (a later row range of a split group),
- *     8 = reads its activations through the caches, 16 = paired: row-group
+ *     8 = reads its activations through the caches, 32 = independent of
+ *     every earlier group (reads nothing an earlier group writes, writes
+ *     nothing an earlier group reads or writes; also carries 4), 16 = paired: row-group
  *     2i + b is row-group i of member b, and the group writes the gated
  *     product of its two members' outputs), offset of its activation copy in
  *     the plan's copies or -1 (under QD_PRO_GLU at m > 1: of the product),

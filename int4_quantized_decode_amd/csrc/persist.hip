@@ -77,12 +77,15 @@ constexpr uint32_t kSpinLimit = 1u << 20;   // default wait bound, polls (each a
 enum : int32_t {
   kStageEarly = 1,      // no earlier group writes any byte of x: it may be staged before the barrier
   kAckOutputs = 2,      // a later group reads or rewrites an output: stores complete before the stamp
-  kNoWait = 4,          // a further row range of the op(s) before: no device-wide wait at the boundary
+  kNoWait = 4,          // no device-wide wait at the boundary: a further row range of the op(s)
+                        // before, or a group independent of every earlier group
   kCleanLines = 8,      // x is written earlier in the step, but no cache can hold a stale copy of its
                         // lines: after the barrier it is read through the caches
   kPaired = 16,         // several token rows: a two-member group whose row-group i of both members
                         // forms one unit (virtual row-group 2i + b is member b's row-group i); it
                         // writes the gated product of its two outputs for a later group
+  kIndependent = 32,    // independent of every earlier group (with kNoWait): at most the plan's
+                        // lag bounds how far the workgroups drift apart (see control_wave)
 };
 
 struct PGroup {         // 64 bytes
@@ -143,6 +146,9 @@ struct PlanArgs {
   int32_t tab_bytes;
   int32_t m;                  // token rows (1 .. 16)
   uint32_t spin_limit;        // bound of every wait, in polls
+  int32_t lag;                // before an independent group: how many groups behind may the slowest
+                              // workgroup be (0: unbounded); see control_wave
+  int32_t pad;
 };
 
 template <int FMT> struct Fmt;
@@ -1168,6 +1174,14 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   wg_barrier();                   // activations of group 0 staged
   bool dead = false;
   for (int g = 0; g < p.ngroups; ++g) {
+    // The boundary before an independent group g + 1 does not wait.  With a
+    // lag L, this workgroup instead waits, while it streams g, for every
+    // workgroup to have finished group g - L, so none runs more than about L
+    // groups ahead of the slowest.  (Measured: on the larger steps, workgroups
+    // left to drift apart end the step later than with a wait at every
+    // boundary; on the smaller ones they end it earliest.)
+    if (p.lag > 0 && g + 1 < p.ngroups && (S.order(g + 1) & kIndependent) && g >= p.lag)
+      wait_group(p, g - p.lag, lane, 0);
     finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead);
     publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
@@ -1183,7 +1197,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
       if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
-      // and needs what g needed, which g's own boundary already waited for.
+      // and needs what g needed, which g's own boundary already waited for;
+      // a group independent of every earlier group needs nothing of them.
       if (!(S.order(g + 1) & kNoWait))
         wait_group(p, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
@@ -1416,6 +1431,24 @@ void order_groups(std::vector<HostGroup>& gs, int64_t m, int64_t tbytes) {
       }
     }
     if (early) gs[i].order |= kStageEarly;
+    // A group that reads nothing an earlier group writes, and writes nothing
+    // an earlier group reads or writes, needs no earlier group to have
+    // finished: the device-wide wait before it is skipped.  (A later group
+    // that does depend on an earlier one waits for every workgroup to finish
+    // the group before it, and a workgroup finishes its groups in order.)
+    bool independent = early;
+    for (size_t j = 0; independent && j < i; ++j) {
+      const uint64_t xbj = (uint64_t)m * gs[j].k * 2 * (gs[j].pro == QD_PRO_GLU ? 2 : 1);
+      for (const PMember& pa : gs[i].mem) {
+        const uint64_t ya = y_span(pa, m);
+        if (ranges_overlap(pa.y, ya, gs[j].x, xbj) ||
+            (gs[j].pro == QD_PRO_RMSNORM && ranges_overlap(pa.y, ya, gs[j].gamma, (uint64_t)gs[j].k * 2)))
+          independent = false;
+        for (const PMember& pj : gs[j].mem)
+          if (ranges_overlap(pa.y, ya, pj.y, y_span(pj, m))) independent = false;
+      }
+    }
+    if (independent && i > 0) gs[i].order |= kNoWait | kIndependent;
   }
   // A group whose x an earlier group writes may still read it through the
   // caches when no cache can hold a stale copy of its lines.  The caches
@@ -1659,6 +1692,7 @@ struct PlanLayout {
   int64_t xt_total = 0, xt_blocks = 0;
   int64_t ss_total = 0;        // sum-of-squares records, 16 floats each
   size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
+  int lag = 0;                 // drift bound across independent groups, in groups (0: none)
 };
 
 // The last group before g writing any byte of [x, x + xb), or SIZE_MAX.
@@ -1668,6 +1702,24 @@ size_t last_writer(const std::vector<HostGroup>& gs, size_t g, const void* x, ui
     for (const PMember& pj : gs[j].mem)
       if (ranges_overlap(x, xb, pj.y, y_span(pj, m))) p = j;
   return p;
+}
+
+// How many groups the slowest workgroup may trail before a workgroup starting
+// an independent group waits for it (0: no bound), by the step's weight bytes
+// and token rows.  Measured on the persistent steps here (HIP-event medians,
+// us; a wait at every boundary / none / lags of 1, 3 and 6 groups):
+//   2B int8, 1.8 GB, one row:          561 /  451 /  520 /  535 /  516
+//   4B int8, 3.9 GB, one row:          926 /  777 /  850 /  857 /  888
+//   8B INT4, 4.3 GB, one row:          896 /  816 /  818 /  857 /  865
+//   8B INT4, 4.3 GB, 16 rows:         1599 / 1299 / 1375 / 1396 / 1321
+//   8B int8, 8.0 GB, one row:         1330 / 1348 / 1267 / 1298 / 1317
+//   8B int8, 8.0 GB, 16 rows:         1997 / 1855 / 1979 / 1889 / 1856
+//   27B-shaped int8, 24.5 GB, one row: 4250 / 4718 / 4011 / 3940 / 3989
+//   27B-shaped int8, 24.5 GB, 16 rows: 6432 / 6516 / 6419 / 6225 / 6267
+int drift_lag(int64_t weight_bytes, bool multi) {
+  if (weight_bytes >= ((int64_t)12 << 30)) return 3;
+  if (weight_bytes >= ((int64_t)6 << 30) && !multi) return 1;
+  return 0;
 }
 
 // `scratch`: whether the plan has scratch of its own (a plan object).  Steps
@@ -1894,12 +1946,14 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->ps.resize((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1, maxGamma = 0;
+  int64_t weight_bytes = 0;
   for (int g = 0; g < ng; ++g) {
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
     // A step the persistent walker cannot hold (tile counts past int32)
     // replays per-group launches instead.
     if (T > (int64_t)INT32_MAX / 2) return;
+    weight_bytes += T * tile_bytes(fmt);
     int32_t ss0 = 0, ss_n = 0;
     if (multi && hg.pro == QD_PRO_RMSNORM) {
       const auto& e = recs.at(hg.ss_key);
@@ -1964,6 +2018,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->xt_total = xt_total;
   L->xt_blocks = blocks;
   L->ss_total = ss_total;
+  L->lag = drift_lag(weight_bytes, multi);
   L->fmt = fmt;
   L->multi = multi;
   L->glue = glue;
@@ -2097,6 +2152,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.tab_bytes = (int32_t)L.tab_bytes;
   a.m = (int32_t)m;
   a.spin_limit = kSpinLimit;
+  a.lag = L.lag;
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = L.fmt;
@@ -2120,10 +2176,10 @@ qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32
     std::vector<StackGroup> tail;
     if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) L = PlanLayout{};
   }
-  std::vector<int64_t> v = {2, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
+  std::vector<int64_t> v = {3, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
                             (int64_t)L.pg.size(), (int64_t)L.pm.size(), L.G, L.xt_total,
                             (int64_t)L.jobs.size(), (int64_t)L.lds, (int64_t)L.x_bytes,
-                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes, L.ss_total};
+                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes, L.ss_total, L.lag};
   auto addr = [](const void* p) { return (int64_t)(uintptr_t)p; };
   for (size_t g = 0; g < L.pg.size(); ++g) {
     const PGroup& p = L.pg[g];
@@ -2386,6 +2442,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   a.tab_bytes = (int32_t)L.tab_bytes;
   a.m = (int32_t)m;
   a.spin_limit = kSpinLimit;
+  a.lag = L.lag;
   void* kargs[] = {&a};
   // A plain launch, as a plan's: capturable in a graph.
   if (hipLaunchKernel(kfn, dim3(G), dim3(kWaves * 64), kargs, (unsigned)L.lds, s) != hipSuccess) return QD_ELAUNCH;

@@ -1000,10 +1000,10 @@ def _plan_tables(qd, ops, m):
     header, the group records (12 words), the member records (8 words) and
     the per-workgroup schedule entries (4 words, group-major)."""
     v = qd.describe_stack_plan(ops, m)
-    assert v[0] == 2
+    assert v[0] == 3
     ng, nm, G = v[6], v[7], v[8]
-    groups = [v[17 + 12 * i:29 + 12 * i] for i in range(ng)]
-    mo = 17 + 12 * ng
+    groups = [v[18 + 12 * i:30 + 12 * i] for i in range(ng)]
+    mo = 18 + 12 * ng
     members = [v[mo + 8 * i:mo + 8 * i + 8] for i in range(nm)]
     so = mo + 8 * nm
     sched = [v[so + 4 * i:so + 4 * i + 4] for i in range(ng * G)]

@@ -31,7 +31,7 @@ from synthetic_inputs import QWEN3_2B, QWEN3_8B, QWEN38_27B, Decoder
 FMT = {"int8_b32": 1, "int4_g64": 2, "fp16": 3}
 PRO_NONE, PRO_RMSNORM, PRO_GLU = 0, 1, 2
 EPI_NONE, EPI_SILU = 0, 1
-EARLY, ACK, NOWAIT, CLEAN, PAIRED = 1, 2, 4, 8, 16
+EARLY, ACK, NOWAIT, CLEAN, PAIRED, INDEPENDENT = 1, 2, 4, 8, 16, 32
 TILE_BYTES = {1: 4352, 2: 2304}
 LDS_MAX = 160 * 1024
 
@@ -148,9 +148,9 @@ def describe(L, b, workgroups=256):
                                         ctypes.byref(n)) == 0
     v = list(buf)
     keys = ["version", "persistent", "fmt", "m", "glue", "prefix", "ngroups", "nmem", "G",
-            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes", "ss_total"]
-    d = dict(zip(keys, v[:17]))
-    pos = 17
+            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes", "ss_total", "lag"]
+    d = dict(zip(keys, v[:18]))
+    pos = 18
 
     def take(count, width, names):
         nonlocal pos
@@ -203,7 +203,7 @@ def attach_sources(b, d):
 def check_layout(b, d, lds_fits=True):
     m, ops = b.m, b.ops
     G, gs, ms = d["G"], d["groups"], d["members"]
-    assert d["version"] == 2 and d["persistent"] == 1 and d["m"] == m
+    assert d["version"] == 3 and d["persistent"] == 1 and d["m"] == m
     src = attach_sources(b, d)
 
     # Rows: every op of the prefix is covered exactly once by its slices.
@@ -259,9 +259,10 @@ def check_layout(b, d, lds_fits=True):
 
     step_group = [ops[s[0]].group for s in src]
     sg = []                                   # [(group indices, member indices)]
+    later = []                                # per plan group: a later row range of a split group
     for gi, g in enumerate(gs):
         later_range = gi > 0 and step_group[gs[gi - 1]["mem0"]] == step_group[g["mem0"]]
-        assert bool(g["order"] & NOWAIT) == later_range, f"group {gi} no-wait flag"
+        later.append(later_range)
         if not later_range:
             sg.append(([], []))
         sg[-1][0].append(gi)
@@ -282,6 +283,22 @@ def check_layout(b, d, lds_fits=True):
                 lines(g["gamma"], g["k"] * 2) if g["pro"] == PRO_RMSNORM else (0, 0)]
 
     early = [not any(reads(gs[gl[0]], j) for _, mj in sg[:i] for j in mj) for i, (gl, _) in enumerate(sg)]
+
+    # No device-wide wait before a later row range, nor before a step group
+    # that reads nothing an earlier group writes and writes nothing an
+    # earlier group reads or writes.
+    def writes_into(mine, t):
+        h = gs[sg[t][0][0]]
+        return any(overlap(*out_span(a), h["x"], x_bytes(h, m)) or
+                   (h["pro"] == PRO_RMSNORM and overlap(*out_span(a), h["gamma"], h["k"] * 2)) or
+                   any(overlap(*out_span(a), *out_span(j)) for j in sg[t][1])
+                   for a in mine)
+
+    for i, (gi_list, mem) in enumerate(sg):
+        independent = i > 0 and early[i] and not any(writes_into(mem, t) for t in range(i))
+        for gi in gi_list:
+            assert bool(gs[gi]["order"] & NOWAIT) == (later[gi] or independent), f"group {gi} no-wait flag"
+            assert bool(gs[gi]["order"] & INDEPENDENT) == independent, f"group {gi} independent flag"
     for i, (gi_list, mem) in enumerate(sg):
         g = gs[gi_list[0]]
         e = early[i]
@@ -440,12 +457,33 @@ CASES = [
 ]
 
 
+def expected_lag(b, d):
+    """The drift bound the plan states: 3 groups from 12 GiB of weights in
+    the persistent part, 1 from 6 GiB at one token row, else none."""
+    wbytes = sum(-(-o.n // 16) * -(-o.k // 256) * TILE_BYTES[o.fmt] for o in b.ops[:d["prefix"]])
+    if wbytes >= 12 << 30:
+        return 3
+    return 1 if wbytes >= 6 << 30 and b.m == 1 else 0
+
+
 @pytest.mark.parametrize("name,dec,m,fmt,kw", CASES, ids=[c[0] for c in CASES])
 def test_plan_layout_invariants(L, name, dec, m, fmt, kw):
     b = step_ops(L, dec, m, fmt, **kw)
     d = describe(L, b)
     assert d["prefix"] == len(b.ops) and d["glue"] == int(bool(kw.get("glue")))
+    assert d["lag"] == expected_lag(b, d)
     check_layout(b, d)
+
+
+def test_plan_layout_independent_groups(L):
+    """The metric's workload (every group reads an activation of its own and
+    writes fresh outputs): every group after the first is independent and
+    waits for nothing; in the chained step none is."""
+    d = describe(L, step_ops(L, QWEN3_8B, 1, "int8_b32"))
+    assert all(g["order"] & INDEPENDENT and g["order"] & NOWAIT for g in d["groups"][1:])
+    assert not d["groups"][0]["order"] & (INDEPENDENT | NOWAIT) and d["lag"] == 1
+    d = describe(L, step_ops(L, QWEN3_8B, 1, "int8_b32", chain=True))
+    assert not any(g["order"] & (INDEPENDENT | NOWAIT) for g in d["groups"])
 
 
 @pytest.mark.parametrize("workgroups", [1, 7, 80, 255, 304, 512])
@@ -468,7 +506,7 @@ def test_plan_layout_fp16_head_is_replayed_tail(L):
 def test_plan_layout_replays_whole(L, m, fmt, kw):
     b = step_ops(L, QWEN3_8B, m, fmt, layers=1, **kw)
     d = describe(L, b)
-    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 17 + 4
+    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 18 + 4
 
 
 def test_plan_layout_copy_not_cut_inside_a_block(L):
