@@ -1344,7 +1344,8 @@ struct qd_stack_plan {
   bool persistent = false;
   int fmt = 0;
   bool multi = false;                    // m > 1
-  bool glue = false;                     // one token row with a prologue or an epilogue
+  bool glue = false;                     // a prologue or an epilogue in the persistent part
+  bool light = false;                    // one token row, few stalls: the lighter reserve (kernel_ptr)
   std::vector<qd::StackGroup> tail;      // groups replayed after the persistent kernel
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (K = 0, mixed formats, glue, ...)
   void* tables = nullptr;
@@ -1648,11 +1649,31 @@ const void* multi_kernel() {
                                                        QD_PLAN_RESERVE16_INT4_S, GLUE, 16, QD_PLAN_UNIT16_INT4>);
 }
 
-const void* kernel_ptr(int fmt, bool multi, bool glue) {
+//
+// `light`: one token row, no glue, and few stalls to cover (no group waits for
+// the one before it, and the drift bound is not 1 group): fewer reserve waves
+// (int8 3 x 2, INT4 none), measured on those steps (HIP-event medians, us,
+// reserve 7 x 2 / 3 x 2 / none for int8, 4 x 2 / none for INT4): 4B int8
+// 781 / 741 / 770, 27B-shaped int8 3954 / 3866 / 3879, 8B INT4 813 / 772.
+// Steps with stalls keep the deeper reserve (8B int8 at a drift bound of 1:
+// 1276 / 1358 / 1384; the chained 8B step 1471 / 1599 / 1631).
+#ifndef QD_PLAN_RESERVE8_LIGHT
+#define QD_PLAN_RESERVE8_LIGHT 3
+#endif
+#ifndef QD_PLAN_RESERVE4_LIGHT
+#define QD_PLAN_RESERVE4_LIGHT 0
+#endif
+const void* kernel_ptr(int fmt, bool multi, bool glue, bool light) {
   if (multi) {
     if (fmt == QD_FMT_INT8_B32) return glue ? multi_kernel<QD_FMT_INT8_B32, true>() : multi_kernel<QD_FMT_INT8_B32, false>();
     return glue ? multi_kernel<QD_FMT_INT4_G64, true>() : multi_kernel<QD_FMT_INT4_G64, false>();
   }
+  if (light && !glue)
+    return fmt == QD_FMT_INT8_B32
+               ? reinterpret_cast<const void*>(
+                     &stack_kernel<QD_FMT_INT8_B32, kRing8, QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
+               : reinterpret_cast<const void*>(
+                     &stack_kernel<QD_FMT_INT4_G64, kRing4, QD_PLAN_RESERVE4_LIGHT, kReserveInt4S, false, 1, 1>);
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
@@ -1693,6 +1714,7 @@ struct PlanLayout {
   int64_t ss_total = 0;        // sum-of-squares records, 16 floats each
   size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
   int lag = 0;                 // drift bound across independent groups, in groups (0: none)
+  bool light = false;          // see kernel_ptr
 };
 
 // The last group before g writing any byte of [x, x + xb), or SIZE_MAX.
@@ -2019,6 +2041,9 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->xt_blocks = blocks;
   L->ss_total = ss_total;
   L->lag = drift_lag(weight_bytes, multi);
+  bool waits = false;          // a group that waits for the one before it
+  for (size_t g = 1; g < L->pg.size(); ++g) waits = waits || !(L->pg[g].order & kNoWait);
+  L->light = !multi && !waits && L->lag != 1;
   L->fmt = fmt;
   L->multi = multi;
   L->glue = glue;
@@ -2062,7 +2087,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return QD_EDEVICE;
   }
   // LDS beyond one CU's: replay.
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light);
   const size_t lds = L.lds;
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
@@ -2158,6 +2183,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   plan->fmt = L.fmt;
   plan->multi = L.multi;
   plan->glue = L.glue;
+  plan->light = L.light;
   plan->tail = std::move(tail);
   plan->persistent = true;
   *out = plan;
@@ -2221,7 +2247,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   // workgroups would wait for it: the first device-wide wait then times out
   // (every wait is bounded, so the kernel still ends), the run reports the
   // timeout, and the plan launches cooperatively from then on.
-  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue);
+  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue, plan->light);
   const hipError_t e =
       plan->cooperative
           ? hipLaunchCooperativeKernel(kfn, dim3(plan->args.G), dim3(kWaves * 64), kargs, (unsigned)plan->lds, s)
@@ -2407,7 +2433,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   if (L.pg.size() > (size_t)kStaticGroups || L.pm.size() > (size_t)kStaticMembers) return QD_ESHAPE;
   std::vector<StackGroup> tail;
   if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) return replay_all();
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light);
   if (L.lds > sd->lds_max) return replay_all();
   if (L.lds > 65536 && hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds) != hipSuccess) {
     (void)hipGetLastError();
