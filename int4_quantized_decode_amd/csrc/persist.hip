@@ -1599,8 +1599,14 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #ifndef QD_PLAN_RING16
 #define QD_PLAN_RING16 1
 #endif
+// Reserve waves at several token rows: 3 of one unit (int8) and 1 (INT4)
+// since independent groups stopped waiting; measured (HIP-event medians, us,
+// 7 / 3 / 0 reserve waves for int8, 3 / 1 / 0 for INT4): 8B int8 1863 / 1809
+// / 1842, 8B INT4 1300 / 1273 / 1289, 27B-shaped int8 6303 / 6119 / 6280,
+// glued 8B int8 2253 / 2188 / 2294.  (Before, with a wait at every boundary,
+// 7 and 3 were best; see below.)
 #ifndef QD_PLAN_RESERVE16_R
-#define QD_PLAN_RESERVE16_R 7
+#define QD_PLAN_RESERVE16_R 3
 #endif
 #ifndef QD_PLAN_UNIT16
 #define QD_PLAN_UNIT16 2
@@ -1609,7 +1615,8 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #define QD_PLAN_RESERVE16_S 1
 #endif
 // INT4 at up to 16 token rows: its own shape (tiles of 2304 rather than 4352
-// bytes), measured on the 8B INT4 step (us): reserve waves of one unit
+// bytes), measured on the 8B INT4 step with a wait at every boundary (us):
+// reserve waves of one unit
 // 0 / 2 / 3 / 4 / 5 / 6 / 7 / 10 gave 1671 / 1608 / 1607 / 1621-1634 / 1630 /
 // 1650 / 1709 / 2038 (from two boxes); units of 3 row-groups 1636 with 4
 // reserve waves.  A ring of 2 units, two units per reserve wave and units of
@@ -1618,7 +1625,7 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #define QD_PLAN_RING16_INT4 QD_PLAN_RING16
 #endif
 #ifndef QD_PLAN_RESERVE16_INT4_R
-#define QD_PLAN_RESERVE16_INT4_R 3
+#define QD_PLAN_RESERVE16_INT4_R 1
 #endif
 #ifndef QD_PLAN_RESERVE16_INT4_S
 #define QD_PLAN_RESERVE16_INT4_S QD_PLAN_RESERVE16_S
