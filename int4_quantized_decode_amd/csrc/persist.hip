@@ -25,8 +25,13 @@
 //     stores each row-group as soon as it is complete (fixed-order sums:
 //     deterministic), publishes that the workgroup has finished the group
 //     (one completion stamp per workgroup), waits until every workgroup has
-//     published it, and releases the compute waves (one barrier per group),
-//     so an op may consume an earlier op's output;
+//     published it, and releases the compute waves (one workgroup barrier
+//     per group), so an op may consume an earlier op's output;
+//   * a group that depends on no earlier group (reads nothing one writes,
+//     writes nothing one reads or writes) skips that device-wide wait; a
+//     bound on how far the workgroups may drift apart is kept instead (a
+//     wait, overlapped with the streaming, for the group a plan-chosen lag
+//     before);
 //   * one token row: the control wave stages each group's activation vector
 //     (and, with glue, gamma or the gated product's second block) straight
 //     into LDS and applies the prologue there;
@@ -35,7 +40,10 @@
 //     (made before the step, or written by the op producing them), and the
 //     partials are 16 x 16 per tile; groups too large for the partials in
 //     LDS are split into row ranges that need no device-wide wait between
-//     them;
+//     them; with glue, RMSNorm is applied to each block from per-token
+//     factors the producing op's workgroups prepare (sum-of-squares
+//     records), and a gate|up group run paired writes the gated product
+//     into the copy its consumer reads;
 //   * compute waves issue no global stores or atomics.
 //
 // Ordering around each boundary is decided from the step's buffers when the
