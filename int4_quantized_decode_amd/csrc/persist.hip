@@ -605,29 +605,17 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
     if constexpr (MT == 1) return issue<FMT>(S, ng, total, next, ic, r, ln, take);
     else return issue_unit<FMT, U, GLUE>(S, ng, total, next, ic, r, ln, take);
   };
-  // MT > 1: each slot's activation block, loaded with the tile when the
-  // block is already readable (nothing in the step writes it, or its group's
-  // boundary has passed), else when the tile is computed.
-  u32x4 xr[MT > 1 ? D : 1][8];
-  bool xl[MT > 1 ? D : 1];
+  // MT > 1: the unit's activation block is loaded when the unit is computed,
+  // not with its tiles (measured on the 8B steps at 16 token rows, us: int8
+  // 1810 -> 1734, INT4 1287 -> 1259 against loading it with the tiles when it
+  // is already readable; the block is read from L2 and the unit's weights are
+  // long in flight by then).  One block's registers serve every ring slot.
+  u32x4 xr[8];
   int cg = -1;                      // last group whose activations this wave has waited for
   auto settle_to = [&](int g) {
     while (cg < g) {
       ++cg;
       if (cg < ng) wg_barrier();
-    }
-  };
-  auto early_x = [&](int s) {
-    if constexpr (MT > 1) {
-      xl[s] = false;
-      if (ref[s].g < ng) {
-        const int ord = S.order(ref[s].g);
-        const bool early = (ord & kStageEarly) != 0;
-        if (early || uni(lds_get(staged)) >= ref[s].g) {
-          load_xblock<FMT>(S, ref[s].g, ref[s].j, p.m, lane, !(ord & (kStageEarly | kCleanLines)), xr[s]);
-          xl[s] = true;
-        }
-      }
     }
   };
   auto compute = [&](int s) {
@@ -638,18 +626,18 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       const float part = quad_reduce(tile_dot<FMT>(t, xs, xsum, r.j, g4, 0.0f));
       if (lane < 16) red[r.rel * 16 + lane] = part;
     } else {
-      if (!xl[s]) load_xblock<FMT>(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr[s]);
+      load_xblock<FMT>(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr);
       // (A gated product needs nothing here: the group's copy holds it.)
       if constexpr (GLUE)
-        if (S.pro(r.g) == QD_PRO_RMSNORM) rms_block<FMT>(xr[s], xs, xsum, r.j, lane);
+        if (S.pro(r.g) == QD_PRO_RMSNORM) rms_block<FMT>(xr, xs, xsum, r.j, lane);
       // Each tile's 16 x 16 partial, one float4 per lane, in the tile's own
       // slot (row-group seg + q: J slots further on).
       const int J = S.J(r.g);
       float4_t xs4[4];
-      if constexpr (FMT == QD_FMT_INT4_G64) group_sums(xr[s], xs4);
+      if constexpr (FMT == QD_FMT_INT4_G64) group_sums(xr, xs4);
 #pragma unroll
       for (int q = 0; q < U; ++q)
-        if (q < r.nv) reinterpret_cast<float4_t*>(red)[(r.rel + q * J) * 64 + lane] = tile_mfma(t.w[q], xr[s], xs4);
+        if (q < r.nv) reinterpret_cast<float4_t*>(red)[(r.rel + q * J) * 64 + lane] = tile_mfma(t.w[q], xr, xs4);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) {
@@ -667,7 +655,6 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       ring[s] = next_tile(ref[s], lane);
-      early_x(s);
       QD_PIN_ISSUE();
     }
     // The ring is consumed and refilled in slot order with a single loop
@@ -677,8 +664,7 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       for (int s = 0; s < D; ++s) {
         if (ref[s].g < ng) compute(s);
         ring[s] = next_tile(ref[s], lane);
-        early_x(s);
-        QD_PIN_ISSUE();
+          QD_PIN_ISSUE();
       }
       if (ref[0].g >= ng) break;   // slot 0 was refilled first: nothing left for later slots
     }
@@ -710,8 +696,7 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
         }
         stop = stop || lds_get(staged) > trig;
         ring[s] = next_tile(ref[s], lane, !stop);
-        early_x(s);
-        exhausted = exhausted || (!stop && ref[s].g >= ng);
+          exhausted = exhausted || (!stop && ref[s].g >= ng);
         QD_PIN_ISSUE();
       }
 #pragma unroll
