@@ -163,13 +163,32 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<QD_FMT_INT8_B32> {
   using Tile = Tile8;
   static constexpr int kT = kTileBytes8;
-  __device__ static Tile load(__amdgpu_buffer_rsrc_t r, int lane) { return load_tile8(r, 0, lane); }
+  __device__ static Tile load(__amdgpu_buffer_rsrc_t r, int lane, int j = 0) { return load_tile8(r, j, lane); }
 };
 template <> struct Fmt<QD_FMT_INT4_G64> {
   using Tile = Tile4;
   static constexpr int kT = kTileBytes4;
-  __device__ static Tile load(__amdgpu_buffer_rsrc_t r, int lane) { return load_tile4(r, 0, lane); }
+  __device__ static Tile load(__amdgpu_buffer_rsrc_t r, int lane, int j = 0) { return load_tile4(r, j, lane); }
 };
+
+// At one token row a hand-out covers ku1(fmt) consecutive super-blocks of one
+// row-group (consecutive tiles in the blob).  INT4 tiles are half the bytes
+// of int8 ones for the same hand-out work (the LDS counter, the address
+// arithmetic, one partial, one count): two per hand-out put INT4 at about
+// int8's bytes per hand-out.  A row-group's last hand-out may hold fewer.
+#ifndef QD_PLAN_KU4
+#define QD_PLAN_KU4 2
+#endif
+__host__ __device__ constexpr int ku1(int fmt) { return fmt == QD_FMT_INT4_G64 ? QD_PLAN_KU4 : 1; }
+
+template <int FMT, int KU> struct KTiles {
+  typename Fmt<FMT>::Tile t[KU];
+};
+template <bool C, typename A, typename B> struct Pick { using type = A; };
+template <typename A, typename B> struct Pick<false, A, B> { using type = B; };
+// What one hand-out at one token row loads.
+template <int FMT>
+using Hand1 = typename Pick<ku1(FMT) == 1, typename Fmt<FMT>::Tile, KTiles<FMT, ku1(FMT)>>::type;
 
 __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -256,17 +275,19 @@ struct IssueCursor {
   int g;                // current group (-1 before the first)
   int off_next;         // sequence index where the next group starts
   int u, seg, j;        // last issued tile (or unit): index within the workgroup's part,
-                        // (segment, super-block); for units seg counts units
+                        // (segment, super-block); for units seg counts units, and at one
+                        // token row j counts hand-outs of ku1 super-blocks
   int J, rg0, nseg;
   int mem, mem_last;
   bool paired;          // the current group is paired (kPaired)
 };
 
 template <int FMT>
-__device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngroups, int total,
-                                                         uint32_t* next, IssueCursor& c,
-                                                         TileRef& ref, int lane, bool take = true) {
+__device__ __forceinline__ Hand1<FMT> issue(const Sched& S, int ngroups, int total,
+                                            uint32_t* next, IssueCursor& c,
+                                            TileRef& ref, int lane, bool take = true) {
   constexpr int T = Fmt<FMT>::kT;
+  constexpr int KU = ku1(FMT);
   // take == false: claim nothing; the load below then reads an empty buffer
   // (zeros, no memory traffic), which keeps the caller's control flow uniform.
   uint32_t got = (uint32_t)total;
@@ -289,22 +310,34 @@ __device__ __forceinline__ typename Fmt<FMT>::Tile issue(const Sched& S, int ngr
       c.mem_last = c.mem + S.nmem(c.g) - 1;
     }
     const int u = idx - S.off(c.g);
+    const int Ju = (c.J + KU - 1) / KU;                 // hand-outs per row-group
     c.j += u - c.u;
     c.u = u;
-    while (c.j >= c.J) {
-      c.j -= c.J;
+    while (c.j >= Ju) {
+      c.j -= Ju;
       ++c.seg;
     }
     const int rg = c.rg0 + c.seg;
     while (c.mem < c.mem_last && rg >= S.rg_begin(c.mem + 1)) ++c.mem;
-    base = S.blob(c.mem) + ((int64_t)(rg - S.rg_begin(c.mem)) * c.J + c.j) * T;
-    nbytes = T;
+    const int j0 = c.j * KU;
+    const int nv = min(KU, c.J - j0);
+    base = S.blob(c.mem) + ((int64_t)(rg - S.rg_begin(c.mem)) * c.J + j0) * T;
+    nbytes = (uint32_t)(nv * T);                        // a missing last tile reads as zeros
     ref.g = c.g;
-    ref.j = c.j;
+    ref.j = j0;
     ref.rel = u;
     ref.seg = c.seg;
+    ref.nv = nv;
   }
-  return Fmt<FMT>::load(make_rsrc(base, nbytes), lane);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, nbytes);
+  if constexpr (KU == 1) {
+    return Fmt<FMT>::load(r, lane);
+  } else {
+    KTiles<FMT, KU> t;
+#pragma unroll
+    for (int q = 0; q < KU; ++q) t.t[q] = Fmt<FMT>::load(r, lane, q);
+    return t;
+  }
 }
 
 // Up to 16 token rows: the sequence is made of units, U row-groups at one
@@ -407,18 +440,66 @@ __device__ __forceinline__ uint32_t pace_ticks(int k) {
   return (uint32_t)(((int64_t)k * Fmt<FMT>::kT * 100) / (256 * QD_PLAN_PACE_PCT));
 }
 
+// INT4 g64 at one token row on the matrix cores.  The codes become fp16
+// subnormals with one AND per pair, as in the GEMV: for a word whose nibble p
+// holds code (0,2,4,6,1,3,5,7)[p], w & 0x000F000F and (w >> 8) & 0x000F000F
+// are codes (0,1) and (4,5) times 2^-24, w & 0x00F000F0 and
+// (w >> 8) & 0x00F000F0 codes (2,3) and (6,7) times 2^-20.  Per group of 64
+// codes, one 16x16x32 product takes the lane's eight 2^-24 codes (from its two
+// words) and another the eight 2^-20 ones, each against the matching x pairs;
+// the matrix core also sums the group's four K quarters, which the VALU dot
+// products left to a cross-lane reduction.  With the same x in every A row,
+// every output row of the product is the weight row's dot product, so lane
+// (g, rho) ends with row rho's total.  Products are exact (a 4-bit code times
+// an fp16 value, scaled by a power of two) and sums are fp32, as in the
+// GEMV; y = 2^24 sum_a s_a (lo_a + hi_a / 16) + sum_a min_a X_a, X_a being
+// the group's activation sum (staged in LDS, 4 per super-block).
+__device__ __forceinline__ float tile_row4(const Tile4& T, const half_t* xs_j, const float* gsum_j, int g) {
+  const half8_t mt = __builtin_bit_cast(half8_t, T.meta);
+  const float4_t gs = *reinterpret_cast<const float4_t*>(gsum_j);
+  const uint32_t m = 0x000F000Fu, m4 = 0x00F000F0u;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc_s = 0.0f, acc = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int s = a >> 1, h = a & 1;
+    // x pairs (0,1), (4,5), (8,9), (12,13) of the lane's 16 values against
+    // the 2^-24 codes, (2,3), (6,7), (10,11), (14,15) against the 2^-20 ones:
+    // read as dword pairs two apart, straight into operand order (the empty
+    // asm keeps the two halves from being merged into contiguous loads that
+    // would then need register moves).
+    const uint32_t* x32 = reinterpret_cast<const uint32_t*>(xs_j + 64 * a + 16 * g);
+    const u32x4 alo = {x32[0], x32[2], x32[4], x32[6]};
+    asm volatile("" ::: "memory");
+    const u32x4 ahi = {x32[1], x32[3], x32[5], x32[7]};
+    const uint32_t w0 = T.c[s][2 * h], w1 = T.c[s][2 * h + 1];
+    const uint32_t w08 = w0 >> 8, w18 = w1 >> 8;
+    const u32x4 blo = {w0 & m, w08 & m, w1 & m, w18 & m};
+    const u32x4 bhi = {w0 & m4, w08 & m4, w1 & m4, w18 & m4};
+    const float4_t lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(half8_t, alo), __builtin_bit_cast(half8_t, blo), zero, 0, 0, 0);
+    const float4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(half8_t, ahi), __builtin_bit_cast(half8_t, bhi), zero, 0, 0, 0);
+    acc_s = __builtin_fmaf((float)mt[a], __builtin_fmaf(hi[0], 0.0625f, lo[0]), acc_s);
+    acc = __builtin_fmaf((float)mt[4 + a], gs[a], acc);
+  }
+  return __builtin_fmaf(acc_s, 16777216.0f, acc);
+}
+
+// One tile at one token row: lanes 0..15 get the 16 rows' sums (INT4: every
+// lane gets its row's).
 template <int FMT>
-__device__ __forceinline__ float tile_dot(const typename Fmt<FMT>::Tile& T, const half_t* xs,
-                                          const float* xsum, int j, int g, float acc);
+__device__ __forceinline__ float tile_row(const typename Fmt<FMT>::Tile& T, const half_t* xs,
+                                          const float* xsum, int j, int g);
 template <>
-__device__ __forceinline__ float tile_dot<QD_FMT_INT8_B32>(const Tile8& T, const half_t* xs,
-                                                           const float*, int j, int g, float acc) {
-  return tile_dot8(T, xs + j * kSuperK, g, acc);
+__device__ __forceinline__ float tile_row<QD_FMT_INT8_B32>(const Tile8& T, const half_t* xs,
+                                                           const float*, int j, int g) {
+  return quad_reduce(tile_dot8(T, xs + j * kSuperK, g, 0.0f));
 }
 template <>
-__device__ __forceinline__ float tile_dot<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs,
-                                                           const float* xsum, int j, int g, float acc) {
-  return tile_dot4(T, xs + j * kSuperK, xsum + 16 * j, g, acc);
+__device__ __forceinline__ float tile_row<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs,
+                                                           const float* xsum, int j, int g) {
+  return tile_row4(T, xs + j * kSuperK, xsum + 4 * j, g);
 }
 
 // Up to 16 token rows (MT = 16).  The activation block of super-block j,
@@ -586,7 +667,7 @@ __device__ __forceinline__ void rms_block(u32x4 (&xa)[8], const half_t* gam, con
 // 16 x 16 at up to 16 token rows) to their own LDS slot and counts the tile
 // against its row-group, so the control wave can finish a row-group as soon
 // as its last tile is in.
-template <int FMT, int MT, int U> struct RingOf { using type = typename Fmt<FMT>::Tile; };
+template <int FMT, int MT, int U> struct RingOf { using type = Hand1<FMT>; };
 template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>; };
 
 // At up to 16 token rows with glue (GLUE), xs holds the RMSNorm gamma of the
@@ -623,7 +704,17 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
     const TileRef& r = ref[s];
     settle_to(r.g);
     if constexpr (MT == 1) {
-      const float part = quad_reduce(tile_dot<FMT>(t, xs, xsum, r.j, g4, 0.0f));
+      float part;
+      if constexpr (ku1(FMT) == 1) {
+        part = tile_row<FMT>(t, xs, xsum, r.j, g4);
+      } else {
+        // The tiles' sums in tile order.  A missing last tile (J odd) holds
+        // zero codes, scales and mins, and reads zero activations and sums
+        // (the staging clears them), so it adds exactly zero.
+        part = tile_row<FMT>(t.t[0], xs, xsum, r.j, g4);
+#pragma unroll
+        for (int q = 1; q < ku1(FMT); ++q) part += tile_row<FMT>(t.t[q], xs, xsum, r.j + q, g4);
+      }
       if (lane < 16) red[r.rel * 16 + lane] = part;
     } else {
       load_xblock<FMT>(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr);
@@ -689,7 +780,7 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       bool stop = false, exhausted = false;
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        const uint32_t due = t0 + pace_ticks<FMT>((s * R + r) * (MT == 1 ? 1 : U));
+        const uint32_t due = t0 + pace_ticks<FMT>((s * R + r) * (MT == 1 ? ku1(FMT) : U));
         while (!stop && (int32_t)((uint32_t)__builtin_amdgcn_s_memrealtime() - due) < 0) {
           stop = lds_get(staged) > trig;
           if (!stop) __builtin_amdgcn_s_sleep(2);
@@ -731,7 +822,7 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
         0, POLICY);
 }
 
-// Stage a group's multiplied vector (and, for int4, its 16-value run sums) in
+// Stage a group's multiplied vector (and, for int4, its 64-value group sums) in
 // LDS.  All loads, and under a prologue the second operand's (gamma, or the
 // gated product's B block) into xs + x_span(Kp), are issued before the single wait,
 // so staging costs one memory round trip whatever K is.  The prologue then
@@ -770,8 +861,11 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
     wait_stores();                                 // vmcnt(0): the data is in LDS
   }
   if (FMT == QD_FMT_INT4_G64) {
-    // One 16-value run per lane, four runs' reads in flight before any sum:
-    // this runs on the group boundary's critical path.
+    // Each group's activation sum, X[4 j + a] for group a of super-block j.
+    // One 16-value run per lane, four runs' reads in flight before any sum
+    // (this runs on the group boundary's critical path); the four runs of a
+    // group sit in four adjacent lanes and are added across them,
+    // (q0 + q1) + (q2 + q3).
     const int runs = Kp / 16;
     const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
     for (int t0 = 0; t0 < runs; t0 += 256) {
@@ -791,12 +885,17 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
           sum = __builtin_amdgcn_fdot2((half2_t){va[u][e], va[u][e + 1]}, one2, sum, false);
           sum = __builtin_amdgcn_fdot2((half2_t){vb[u][e], vb[u][e + 1]}, one2, sum, false);
         }
-        if (t < runs) {
-          const int jj = t >> 4, within = t & 15;
-          xsum[16 * jj + 4 * (within & 3) + (within >> 2)] = sum;
-        }
+        const int su = __builtin_bit_cast(int, sum);
+        const float s2 = sum + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(su, su, 0xB1, 0xF, 0xF, false));
+        const int s2u = __builtin_bit_cast(int, s2);
+        const float s4 = s2 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(s2u, s2u, 0x4E, 0xF, 0xF, false));
+        if (t < runs && (t & 3) == 0) xsum[t >> 2] = s4;
       }
     }
+    // The sums a hand-out's missing last tile reads (J not a multiple of
+    // ku1): zero.
+    for (int t = runs / 4 + lane; t < (Kp / kSuperK + ku1(FMT) - 1) / ku1(FMT) * ku1(FMT) * 4; t += 64)
+      xsum[t] = 0.0f;
   }
 }
 
@@ -947,7 +1046,9 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, in
     if (GLUE && MT != 1 && rec_mem >= 0) write_record(p, S.ss(rec_mem) + w, lane, sq);
     return;
   }
-  const int J = S.J(g);
+  // Partials per row-group: one per tile at several token rows, one per
+  // hand-out of ku1 tiles at one.
+  const int J = MT == 1 ? (S.J(g) + ku1(FMT) - 1) / ku1(FMT) : S.J(g);
   const int rg0 = S.rg0(g), nseg = S.nseg(g);
   const int row = lane & 15, q = lane >> 4;
   const bool paired = GLUE && MT != 1 && S.paired(g);
@@ -1575,7 +1676,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 #define QD_PLAN_RESERVE4 4
 #endif
 #ifndef QD_PLAN_RESERVE4_S
-#define QD_PLAN_RESERVE4_S 2
+#define QD_PLAN_RESERVE4_S 1
 #endif
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4, kReserveInt4S = QD_PLAN_RESERVE4_S;
 
@@ -2013,20 +2114,20 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
         r0 = (int64_t)w * R / G;
         nrg = (int64_t)(w + 1) * R / G - r0;
       }
-      const int64_t n = (multi ? ceil_div(nrg, (int64_t)unit16(fmt)) : nrg) * J;
+      const int64_t n = multi ? ceil_div(nrg, (int64_t)unit16(fmt)) * J : nrg * ceil_div(J, (int64_t)ku1(fmt));
       L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
       if (nrg == 0) continue;
       off[w] += (int32_t)n;
-      maxRel = std::max<int>(maxRel, (int)(nrg * J));
+      maxRel = std::max<int>(maxRel, (int)(multi ? nrg * J : n));
       maxSeg = std::max<int>(maxSeg, (int)nrg);
     }
   }
-  // One token row: staged activations (and their run sums for INT4).
+  // One token row: staged activations (and their group sums for INT4).
   // Several: no staged activations, 16 x 16 partials per tile, and under
   // RMSNorm gamma and the 16 per-token factors.
   L->x_bytes = multi ? (size_t)maxGamma * 2 : (size_t)maxXH * 2;      // a multiple of 1024
   L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0)
-                        : fmt == QD_FMT_INT4_G64 ? align_up((size_t)maxJ * 16 * 4, 16) : 0;
+                        : fmt == QD_FMT_INT4_G64 ? align_up((size_t)ceil_div(maxJ, ku1(fmt)) * ku1(fmt) * 4 * 4, 16) : 0;
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
@@ -2344,7 +2445,7 @@ __global__ __launch_bounds__(256) void put_kernel(u32x4* __restrict__ dst, PutPa
 // token rows, in units of `unit` row-groups), with its running offset in the
 // workgroup's sequence (the host's layout_plan computes the same records).
 __global__ __launch_bounds__(kMaxWorkgroups) void static_setup_kernel(uint8_t* __restrict__ base, int ngroups,
-                                                                      int G, int unit) {
+                                                                      int G, int unit, int ku) {
   const int w = threadIdx.x;
   reinterpret_cast<unsigned long long*>(base)[w] = 0ull;
   if (w == 0) *reinterpret_cast<uint32_t*>(base + kStaticErrOff) = 0u;
@@ -2355,7 +2456,7 @@ __global__ __launch_bounds__(kMaxWorkgroups) void static_setup_kernel(uint8_t* _
   for (int g = 0; g < ngroups; ++g) {
     const int64_t R = gs[g].R, J = gs[g].J;
     const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
-    const int64_t n = (unit > 1 ? (nrg + unit - 1) / unit : nrg) * J;
+    const int64_t n = unit > 1 ? (nrg + unit - 1) / unit * J : nrg * ((J + ku - 1) / ku);
     sched[(size_t)g * G + w] = PSched{(int32_t)n, off, (int32_t)r0, (int32_t)nrg};
     if (nrg != 0) off += (int32_t)n;
   }
@@ -2449,7 +2550,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
       put_table(base + kStaticMembersOff, L.pm.data(), sizeof(PMember) * L.pm.size(), s) != hipSuccess)
     return QD_ELAUNCH;
   hipLaunchKernelGGL(static_setup_kernel, dim3(1), dim3(kMaxWorkgroups), 0, s, base, (int)L.pg.size(), G,
-                     L.multi ? unit16(L.fmt) : 1);
+                     L.multi ? unit16(L.fmt) : 1, L.multi ? 1 : ku1(L.fmt));
   if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
   PlanArgs a{};
   a.groups = reinterpret_cast<const PGroup*>(base + kStaticGroupsOff);

@@ -240,8 +240,11 @@ def check_layout(b, d, lds_fits=True):
             assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 2
         else:
             assert max(s["nseg"] for s in sch) - min(s["nseg"] for s in sch) <= 1
-        unit = 2 if m > 1 else 1
-        assert all(s["n"] == -(-s["nseg"] // unit) * g["J"] for s in sch)
+        if m > 1:      # units of two row-groups at one super-block
+            assert all(s["n"] == -(-s["nseg"] // 2) * g["J"] for s in sch)
+        else:          # one token row: INT4 hands out two super-blocks at a time
+            ku = 2 if d["fmt"] == FMT["int4_g64"] else 1
+            assert all(s["n"] == s["nseg"] * -(-g["J"] // ku) for s in sch)
     # Tile offsets: running sums over the groups a workgroup has work in.
     for w in range(G):
         acc = 0
