@@ -494,7 +494,24 @@ __device__ __forceinline__ float tile_row(const typename Fmt<FMT>::Tile& T, cons
 template <>
 __device__ __forceinline__ float tile_row<QD_FMT_INT8_B32>(const Tile8& T, const half_t* xs,
                                                            const float*, int j, int g) {
-  return quad_reduce(tile_dot8(T, xs + j * kSuperK, g, 0.0f));
+  // Per 32-block one 16x16x32 product of the lane's 8 codes (exact fp16
+  // integers) against its 8 activations; with the same x in every A row each
+  // output row is the weight row's block sum, so lane (g, rho) gets row rho's.
+  const half_t* xs_j = xs + j * kSuperK;
+  const half8_t scales = __builtin_bit_cast(half8_t, T.sc);
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8_t xv = *reinterpret_cast<const half8_t*>(xs_j + 64 * s + 32 * h + 8 * g);
+      const half8_t bq = codes_to_half8(T.c[s][2 * h], T.c[s][2 * h + 1]);
+      const float4_t pr = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv, bq, zero, 0, 0, 0);
+      acc = __builtin_fmaf((float)scales[2 * s + h], pr[0], acc);
+    }
+  }
+  return acc;
 }
 template <>
 __device__ __forceinline__ float tile_row<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs,
