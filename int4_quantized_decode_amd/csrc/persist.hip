@@ -2085,6 +2085,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->pg.resize(ng);
   L->ps.resize((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
+  std::vector<int64_t> given(G, 0);  // one token row: hand-outs each workgroup has so far
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1, maxGamma = 0;
   int64_t weight_bytes = 0;
   for (int g = 0; g < ng; ++g) {
@@ -2117,6 +2118,31 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // workgroups would put a cross-workgroup combine, one more device-wide
     // round trip, on the group's critical path; measured, that costs more
     // than the uneven split.  A paired group is spread in whole pairs.
+    //
+    // One token row: a group whose row-groups do not divide evenly starts
+    // its run of ranges at the workgroup (rot) that leaves the lowest
+    // largest total of hand-outs so far (the first such).  With the ranges
+    // always in the same place, the same workgroups would take the extra
+    // row-groups of every layer (8B-shaped step: q|k|v has 384 row-groups
+    // for 256 workgroups, so every other workgroup would carry 16 tiles a
+    // layer more, 4% above the mean over the step), and with independent
+    // groups the step ends when the most loaded workgroup does.
+    int rot = 0;
+    if (!multi && !hg.paired && R % G != 0) {
+      const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
+      int64_t best = INT64_MAX;
+      for (int p = 0; p < G; ++p) {
+        int64_t top = 0;
+        for (int w = 0; w < G; ++w) {
+          const int64_t i = (w - p + G) % G;
+          top = std::max(top, given[w] + ((i + 1) * R / G - i * R / G) * Ju);
+        }
+        if (top < best) {
+          best = top;
+          rot = p;
+        }
+      }
+    }
     for (int w = 0; w < G; ++w) {
       // Contiguous row-groups: each workgroup streams one contiguous range.
       // (Interleaving them, row-group w + i G to workgroup w, measured 2-11%
@@ -2128,11 +2154,13 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
         r0 = 2 * ((int64_t)w * P / G);
         nrg = 2 * ((int64_t)(w + 1) * P / G) - r0;
       } else {
-        r0 = (int64_t)w * R / G;
-        nrg = (int64_t)(w + 1) * R / G - r0;
+        const int64_t i = (w - rot + G) % G;
+        r0 = i * R / G;
+        nrg = (i + 1) * R / G - r0;
       }
       const int64_t n = multi ? ceil_div(nrg, (int64_t)unit16(fmt)) * J : nrg * ceil_div(J, (int64_t)ku1(fmt));
       L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
+      if (!multi) given[w] += n;
       if (nrg == 0) continue;
       off[w] += (int32_t)n;
       maxRel = std::max<int>(maxRel, (int)(multi ? nrg * J : n));
