@@ -1769,12 +1769,12 @@ const void* multi_kernel() {
 
 //
 // `light`: one token row, no glue, and few stalls to cover (no group waits for
-// the one before it, and the drift bound is not 1 group): fewer reserve waves
-// (int8 3 x 2, INT4 none), measured on those steps (HIP-event medians, us,
-// reserve 7 x 2 / 3 x 2 / none for int8, 4 x 2 / none for INT4): 4B int8
-// 781 / 741 / 770, 27B-shaped int8 3954 / 3866 / 3879, 8B INT4 813 / 772.
-// Steps with stalls keep the deeper reserve (8B int8 at a drift bound of 1:
-// 1276 / 1358 / 1384; the chained 8B step 1471 / 1599 / 1631).
+// the one before it): fewer reserve waves (int8 3 x 2, INT4 none), measured
+// on those steps (HIP-event medians, us, reserve 7 x 2 / 3 x 2 / none for
+// int8, 4 x 2 / none for INT4): 4B int8 781 / 741 / 770, 27B-shaped int8
+// 3954 / 3866 / 3879, 8B INT4 813 / 772; with the rotated ranges, 8B int8
+// without a drift bound 1283 / 1246 (7 x 2 / 3 x 2).  Steps with stalls keep
+// the deeper reserve (the chained 8B step 1471 / 1599 / 1631).
 #ifndef QD_PLAN_RESERVE8_LIGHT
 #define QD_PLAN_RESERVE8_LIGHT 3
 #endif
@@ -1856,9 +1856,19 @@ size_t last_writer(const std::vector<HostGroup>& gs, size_t g, const void* x, ui
 //   8B int8, 8.0 GB, 16 rows:         1997 / 1855 / 1979 / 1889 / 1856
 //   27B-shaped int8, 24.5 GB, one row: 4250 / 4718 / 4011 / 3940 / 3989
 //   27B-shaped int8, 24.5 GB, 16 rows: 6432 / 6516 / 6419 / 6225 / 6267
+// Those one-row figures were taken before the one-row ranges of unevenly
+// divided groups rotated (layout_plan), when the same workgroups carried the
+// extra row-groups of every layer.  With the rotation (no bound / lags of 1,
+// 2 and 3 groups; reserve as `light` chooses, except where marked):
+//   2B int8, one row:            357 /  486 /  501 /  501
+//   4B int8, one row:            725 /  892 /  859 /  867
+//   8B INT4, one row:            758 /  957 /  927 /  885
+//   8B int8, one row:           1246 / 1340 / 1322 / 1304  (7 x 2 reserve: no bound 1283,
+//                                                          lag 1 1259, lag 2 1294)
+//   27B-shaped int8, one row:   3767 / 3964 / 3757 / 3668
 int drift_lag(int64_t weight_bytes, bool multi) {
+  (void)multi;
   if (weight_bytes >= ((int64_t)12 << 30)) return 3;
-  if (weight_bytes >= ((int64_t)6 << 30) && !multi) return 1;
   return 0;
 }
 
@@ -2189,7 +2199,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->lag = drift_lag(weight_bytes, multi);
   bool waits = false;          // a group that waits for the one before it
   for (size_t g = 1; g < L->pg.size(); ++g) waits = waits || !(L->pg[g].order & kNoWait);
-  L->light = !multi && !waits && L->lag != 1;
+  L->light = !multi && !waits;
   L->fmt = fmt;
   L->multi = multi;
   L->glue = glue;

@@ -468,11 +468,9 @@ CASES = [
 
 def expected_lag(b, d):
     """The drift bound the plan states: 3 groups from 12 GiB of weights in
-    the persistent part, 1 from 6 GiB at one token row, else none."""
+    the persistent part, else none."""
     wbytes = sum(-(-o.n // 16) * -(-o.k // 256) * TILE_BYTES[o.fmt] for o in b.ops[:d["prefix"]])
-    if wbytes >= 12 << 30:
-        return 3
-    return 1 if wbytes >= 6 << 30 and b.m == 1 else 0
+    return 3 if wbytes >= 12 << 30 else 0
 
 
 @pytest.mark.parametrize("name,dec,m,fmt,kw", CASES, ids=[c[0] for c in CASES])
@@ -490,7 +488,7 @@ def test_plan_layout_independent_groups(L):
     waits for nothing; in the chained step none is."""
     d = describe(L, step_ops(L, QWEN3_8B, 1, "int8_b32"))
     assert all(g["order"] & INDEPENDENT and g["order"] & NOWAIT for g in d["groups"][1:])
-    assert not d["groups"][0]["order"] & (INDEPENDENT | NOWAIT) and d["lag"] == 1
+    assert not d["groups"][0]["order"] & (INDEPENDENT | NOWAIT) and d["lag"] == 0
     d = describe(L, step_ops(L, QWEN3_8B, 1, "int8_b32", chain=True))
     assert not any(g["order"] & (INDEPENDENT | NOWAIT) for g in d["groups"])
 
