@@ -2095,7 +2095,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->pg.resize(ng);
   L->ps.resize((size_t)ng * G);
   std::vector<int32_t> off(G, 0);
-  std::vector<int64_t> given(G, 0);  // one token row: hand-outs each workgroup has so far
+  std::vector<int64_t> given(G, 0);  // tiles each workgroup has so far
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1, maxGamma = 0;
   int64_t weight_bytes = 0;
   for (int g = 0; g < ng; ++g) {
@@ -2129,23 +2129,25 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // round trip, on the group's critical path; measured, that costs more
     // than the uneven split.  A paired group is spread in whole pairs.
     //
-    // One token row: a group whose row-groups do not divide evenly starts
-    // its run of ranges at the workgroup (rot) that leaves the lowest
-    // largest total of hand-outs so far (the first such).  With the ranges
-    // always in the same place, the same workgroups would take the extra
-    // row-groups of every layer (8B-shaped step: q|k|v has 384 row-groups
-    // for 256 workgroups, so every other workgroup would carry 16 tiles a
-    // layer more, 4% above the mean over the step), and with independent
-    // groups the step ends when the most loaded workgroup does.
+    // A group whose row-groups do not divide evenly starts its run of
+    // ranges at the workgroup (rot) that leaves the lowest largest total of
+    // tiles so far (the first such).  With the ranges always in the same
+    // place, the same workgroups would take the extra row-groups of every
+    // layer (8B-shaped step: q|k|v has 384 row-groups for 256 workgroups, so
+    // every other workgroup would carry 16 tiles a layer more, 4% above the
+    // mean over the step), and with independent groups the step ends when
+    // the most loaded workgroup does.  A group that waits for the one
+    // before it starts the totals afresh (every workgroup is level there),
+    // so it keeps workgroup order, as paired groups do.
+    if (!(hg.order & kNoWait)) std::fill(given.begin(), given.end(), (int64_t)0);
     int rot = 0;
-    if (!multi && !hg.paired && R % G != 0) {
-      const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
+    if (!hg.paired && R % G != 0) {
       int64_t best = INT64_MAX;
       for (int p = 0; p < G; ++p) {
         int64_t top = 0;
         for (int w = 0; w < G; ++w) {
           const int64_t i = (w - p + G) % G;
-          top = std::max(top, given[w] + ((i + 1) * R / G - i * R / G) * Ju);
+          top = std::max(top, given[w] + ((i + 1) * R / G - i * R / G) * J);
         }
         if (top < best) {
           best = top;
@@ -2170,7 +2172,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       }
       const int64_t n = multi ? ceil_div(nrg, (int64_t)unit16(fmt)) * J : nrg * ceil_div(J, (int64_t)ku1(fmt));
       L->ps[(size_t)g * G + w] = PSched{(int32_t)n, off[w], (int32_t)r0, (int32_t)nrg};
-      if (!multi) given[w] += n;
+      given[w] += nrg * J;
       if (nrg == 0) continue;
       off[w] += (int32_t)n;
       maxRel = std::max<int>(maxRel, (int)(multi ? nrg * J : n));

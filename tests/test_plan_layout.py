@@ -227,16 +227,16 @@ def check_layout(b, d, lds_fits=True):
             rg += -(-ms[j]["n"] // 16)
         assert rg == g["R"]
         # Each workgroup one contiguous range; ranges cover [0, R) in
-        # workgroup order, balanced within one row-group.  At one token row
-        # the order may start at any workgroup (cyclically), where the
-        # row-groups do not divide evenly; otherwise at workgroup 0.
+        # workgroup order, balanced within one row-group.  The order may
+        # start at any workgroup (cyclically) where the row-groups do not
+        # divide evenly, except in a paired group; otherwise at workgroup 0.
         sch = d["sched"][gi * G:(gi + 1) * G]
 
         def chain_from(rot):
             seq = [sch[(rot + i) % G] for i in range(G)]
             return (seq[0]["rg0"] == 0 and seq[-1]["rg0"] + seq[-1]["nseg"] == g["R"]
                     and all(seq[i]["rg0"] + seq[i]["nseg"] == seq[i + 1]["rg0"] for i in range(G - 1)))
-        rots = [0] if (m > 1 or g["R"] % G == 0) else range(G)
+        rots = [0] if (g["order"] & PAIRED or g["R"] % G == 0) else range(G)
         assert any(chain_from(r) for r in rots), f"group {gi}: ranges not in (cyclic) workgroup order"
         if g["order"] & PAIRED:
             # Paired (several token rows, its two members' gated product read
