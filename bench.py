@@ -353,13 +353,14 @@ def measure(qd, si, torch, workload, path, steps, warmup, rotate_mb, dev):
     per_step = 1
     if wl.single is not None:
         # One step is a pass over copies of the one matrix (so that no copy is
-        # still in the caches when it is read again), each GEMV its own
-        # dependent launch, issued by one library call: the GEMVs run back to
-        # back with no host work between them.
+        # still in the caches when it is read again), each GEMV its own group
+        # with its own output, issued by one library call: the GEMVs run back
+        # to back with no host work between them (launches: one per GEMV;
+        # plan: one persistent launch, the GEMVs independent of each other).
         copies = max(1, (rotate_mb << 20) // max(1, weight_bytes))
         op = ops[0]
         step_ops = [[op] + [qd.LinearOp(qd.PackedWeight(op.w.fmt, op.w.n, op.w.k, op.w.blob.clone()),
-                                        op.x, op.y, i + 1) for i in range(copies - 1)]]
+                                        op.x, torch.empty_like(op.y), i + 1) for i in range(copies - 1)]]
         per_step = copies
         alg_bytes *= copies
         weight_bytes *= copies

@@ -279,15 +279,18 @@ qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
  * and offset, never dereferenced, so any values that pass the validation of
  * decode_linear_stack will do).  Writes int64 words to `out` (host memory,
  * caller-owned) and their count to *out_len:
- *   header, 18 words: version (3), persistent (0/1), format, m, glue (0/1),
+ *   header, 22 words: version (4), persistent (0/1), format, m, glue (0/1),
  *     prefix ops (ops [0, prefix) run in the persistent kernel, the rest are
  *     replayed after it), groups G_n, members M_n, workgroups W, bytes of the
  *     activation copies, pre-step jobs J_n, dynamic LDS bytes, then LDS bytes
  *     of the staged activations (at m > 1: RMSNorm gamma), the tile partials,
  *     the row-group counters and the schedule tables, the number of
- *     RMSNorm statistics records (16 floats each), and the drift bound: before
+ *     RMSNorm statistics records (16 floats each), the drift bound: before
  *     a group independent of every earlier one, how many groups the slowest
- *     workgroup may trail (0: unbounded);
+ *     workgroup may trail (0: unbounded), and for a last group split at run
+ *     time (flag 64 below; else zeros): row-groups per claimed chunk, chunks
+ *     claimed ahead of the tile hand-out, chunks in the group and the most
+ *     one workgroup may claim;
  *   G_n groups of 12 words, in the order the kernel runs them: x, gamma, K,
  *     super-blocks J, row-groups R, first member, members, prologue, order
  *     flags (1 = may stage early, 2 = acknowledges its stores before its
@@ -296,7 +299,10 @@ qd_status qd_stack_plan_set_spin_limit(qd_stack_plan* plan, uint32_t polls);
  *     every earlier group (reads nothing an earlier group writes, writes
  *     nothing an earlier group reads or writes; also carries 4), 16 = paired: row-group
  *     2i + b is row-group i of member b, and the group writes the gated
- *     product of its two members' outputs), offset of its activation copy in
+ *     product of its two members' outputs, 64 = m = 1, the step's last group
+ *     with at least 4 W row-groups: not split in advance (its schedule
+ *     entries are zeros); workgroups claim chunks of its row-groups from a
+ *     device counter as they reach it), offset of its activation copy in
  *     the plan's copies or -1 (under QD_PRO_GLU at m > 1: of the product),
  *     first statistics record of its RMSNorm input and their count (0, 0
  *     when none);

@@ -94,6 +94,9 @@ enum : int32_t {
                         // writes the gated product of its two outputs for a later group
   kIndependent = 32,    // independent of every earlier group (with kNoWait): at most the plan's
                         // lag bounds how far the workgroups drift apart (see control_wave)
+  kDynamic = 64,        // one token row, the last group: its row-groups are not split in advance;
+                        // workgroups claim them a chunk at a time as they get there (see
+                        // finish_dynamic)
 };
 
 struct PGroup {         // 64 bytes
@@ -156,6 +159,18 @@ struct PlanArgs {
   uint32_t spin_limit;        // bound of every wait, in polls
   int32_t lag;                // before an independent group: how many groups behind may the slowest
                               // workgroup be (0: unbounded); see control_wave
+  // The dynamic last group (kDynamic), if dyn_c > 0: chunks of dyn_c row-groups are claimed
+  // from dyn_ctr[epoch & 1] (the other counter is cleared for the next run); dyn_nch chunks in
+  // all, at most dyn_max per workgroup, dyn_q claimed ahead of the tile hand-out; partial
+  // slots and row-group counts reused modulo dyn_rcap and dyn_scap (powers of two).
+  uint32_t* dyn_ctr;
+  int32_t dyn_c;
+  int32_t dyn_q;
+  int32_t dyn_nch;
+  int32_t dyn_max;
+  int32_t dyn_rcap;
+  int32_t dyn_scap;
+  int32_t dyn_win;            // row-groups compute waves may run ahead of the reduction
   int32_t pad;
 };
 
@@ -219,11 +234,28 @@ __device__ __forceinline__ T* uni_ptr(T* ptr) {
   return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
+// A workgroup's claims on the dynamic last group, in LDS (after the tile
+// counter and the flags).  The control wave appends chunk ids in claim order;
+// compute waves map their hand-outs in the group onto them.
+struct DynCtl {
+  int32_t claimed;      // chunks held (valid entries of chunk[])
+  int32_t ended;        // no further chunk for this workgroup (the group is used up, or the cap)
+  int32_t reduced;      // the group's row-groups reduced so far, in this workgroup's order
+  int32_t pad;
+  int32_t chunk[1];     // [dyn_max]
+};
+
 // The workgroup's schedule, resident in LDS.  Reads are wave-uniform.
 struct Sched {
   const PGroup* g;
   const PMember* m;
   const PSched* s;
+  // The dynamic last group (dyn_c > 0): claims, partial-slot and count masks,
+  // and the row-groups compute waves may run ahead of the reduction.
+  DynCtl* dyn;
+  int dyn_c, dyn_rmask, dyn_smask, dyn_win;
+  uint32_t spin;
+  uint32_t* err;
   __device__ int J(int gi) const { return uni(g[gi].J); }
   __device__ int R(int gi) const { return uni(g[gi].R); }
   __device__ int mem0(int gi) const { return uni(g[gi].mem0); }
@@ -269,6 +301,8 @@ struct TileRef {
               // (row-group major; a unit's: its first tile's)
   int seg;    // row-group within the range (a unit's: its first)
   int nv;     // units: row-groups the unit holds
+  int lseg;   // the dynamic group: row-group in this workgroup's claim order (rel and seg
+              // are then that modulo the slot and count capacities); else -1
 };
 
 struct IssueCursor {
@@ -296,6 +330,7 @@ __device__ __forceinline__ Hand1<FMT> issue(const Sched& S, int ngroups, int tot
   const uint8_t* base = nullptr;
   uint32_t nbytes = 0;
   ref.g = ngroups;
+  ref.lseg = -1;
   if (idx < total) {
     while (idx >= c.off_next) {                       // enter the group holding idx
       ++c.g;
@@ -311,6 +346,68 @@ __device__ __forceinline__ Hand1<FMT> issue(const Sched& S, int ngroups, int tot
     }
     const int u = idx - S.off(c.g);
     const int Ju = (c.J + KU - 1) / KU;                 // hand-outs per row-group
+    if (S.dyn_c > 0 && c.g == ngroups - 1) {
+      // The dynamic last group: hand-out u is hand-out t of the k-th chunk
+      // this workgroup claimed (the control wave claims ahead of the
+      // hand-outs; it never reuses an entry).
+      // (The cursor moves forward by the hand-outs since the wave's last one,
+      // as in a fixed range: c.seg counts chunks, c.j hand-outs within one.)
+      const int per = S.dyn_c * Ju;
+      c.j += u - c.u;
+      c.u = u;
+      while (c.j >= per) {
+        c.j -= per;
+        ++c.seg;
+      }
+      const int k = c.seg;
+      int jh = c.j, sq = 0;
+      while (jh >= Ju) {
+        jh -= Ju;
+        ++sq;
+      }
+      int ch = -1;
+      for (uint32_t spins = 0;; ++spins) {
+        const bool ended = lds_get(&S.dyn->ended) != 0;
+        if (k < lds_get(&S.dyn->claimed)) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+          ch = uni(S.dyn->chunk[k]);
+          break;
+        }
+        if (ended) break;                             // no chunk k: the sequence ends here
+        if (spins > S.spin) {
+          if (lane == 0) atomicOr(S.err, 2u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (ch >= 0) {
+        const int lseg = k * S.dyn_c + sq;
+        const int rg = ch * S.dyn_c + sq;            // past the group (its last chunk): zeros
+        const int j0 = jh * KU;
+        const int nv = min(KU, c.J - j0);
+        if (rg < S.R(c.g)) {
+          int mi = c.mem;                             // members in row-group order; any may hold rg
+          while (mi < c.mem_last && rg >= S.rg_begin(mi + 1)) ++mi;
+          base = S.blob(mi) + ((int64_t)(rg - S.rg_begin(mi)) * c.J + j0) * T;
+          nbytes = (uint32_t)(nv * T);
+        }
+        ref.g = c.g;
+        ref.j = j0;
+        ref.rel = u & S.dyn_rmask;
+        ref.seg = lseg & S.dyn_smask;
+        ref.nv = nv;
+        ref.lseg = lseg;
+      }
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(base, nbytes);
+      if constexpr (KU == 1) {
+        return Fmt<FMT>::load(rd, lane);
+      } else {
+        KTiles<FMT, KU> t2;
+#pragma unroll
+        for (int q = 0; q < KU; ++q) t2.t[q] = Fmt<FMT>::load(rd, lane, q);
+        return t2;
+      }
+    }
     c.j += u - c.u;
     c.u = u;
     while (c.j >= Ju) {
@@ -367,6 +464,7 @@ __device__ __forceinline__ Unit<FMT, U> issue_unit(const Sched& S, int ngroups, 
   }
   ref.g = ngroups;
   ref.nv = 0;
+  ref.lseg = -1;
   if (idx < total) {
     while (idx >= c.off_next) {                       // enter the group holding idx
       ++c.g;
@@ -732,6 +830,17 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
 #pragma unroll
         for (int q = 1; q < ku1(FMT); ++q) part += tile_row<FMT>(t.t[q], xs, xsum, r.j + q, g4);
       }
+      if (r.lseg >= 0) {
+        // The dynamic group reuses partial slots and counts: row-group lseg
+        // may start only when the row-group dyn_w before it is reduced.
+        for (uint32_t spins = 0; r.lseg >= lds_get(&S.dyn->reduced) + S.dyn_win; ++spins) {
+          if (spins > S.spin) {
+            if (lane == 0) atomicOr(S.err, 2u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
       if (lane < 16) red[r.rel * 16 + lane] = part;
     } else {
       load_xblock<FMT>(S, r.g, r.j, p.m, lane, !(S.order(r.g) & (kStageEarly | kCleanLines)), xr);
@@ -1022,13 +1131,80 @@ __device__ __forceinline__ void write_record(const PlanArgs& p, int rec, int lan
 // Spin (bounded) until the compute waves have counted `want` tiles against
 // row-group slot `seg`.  After one timed-out wait (an error) later waits are
 // skipped.
-__device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cnt, int seg,
-                                           uint32_t want, bool& dead) {
+// The dynamic last group: claim chunks until this workgroup holds `want`
+// (control wave only, one device-scope atomic per chunk, in order).  A claim
+// past the last chunk, or the per-workgroup cap, ends the workgroup's part.
+__device__ void dyn_claim(const PlanArgs& p, DynCtl* d, int want, int lane) {
+  if (p.dyn_c <= 0 || lds_get(&d->ended)) return;
+  int have = lds_get(&d->claimed);
+  bool used_up = false;
+  while (have < min(want, p.dyn_max)) {
+    uint32_t c = 0;
+    if (lane == 0)
+      c = __hip_atomic_fetch_add(p.dyn_ctr + (p.epoch & 1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    c = (uint32_t)uni((int)c);
+    if (c >= (uint32_t)p.dyn_nch) {
+      used_up = true;
+      break;
+    }
+    if (lane == 0) {
+      d->chunk[have] = (int32_t)c;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      lds_put(&d->claimed, have + 1);
+    }
+    ++have;
+  }
+  if ((used_up || have >= p.dyn_max) && lane == 0) {   // no further chunk for this workgroup
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    lds_put(&d->ended, 1);
+  }
+}
+
+// Record chunks first, first + 1, ... (n of them, claimed with one atomic) as
+// this workgroup's next; those past the group end its part.
+__device__ void dyn_take(const PlanArgs& p, DynCtl* d, uint32_t first, int n, int lane) {
+  int have = lds_get(&d->claimed);
+  bool used_up = false;
+  for (int i = 0; i < n; ++i) {
+    if (first + (uint32_t)i >= (uint32_t)p.dyn_nch || have >= p.dyn_max) {
+      used_up = true;
+      break;
+    }
+    if (lane == 0) d->chunk[have] = (int32_t)(first + (uint32_t)i);
+    ++have;
+  }
+  if (lane == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    lds_put(&d->claimed, have);
+    if (used_up || have >= p.dyn_max) lds_put(&d->ended, 1);
+  }
+}
+
+// Keep the claims dyn_q chunks ahead of the compute waves' hand-outs in the
+// dynamic group (`handed`: the workgroup's tile counter).  Called from the
+// control wave's waits, so a compute wave never waits on a claim for long.
+template <int FMT>
+__device__ __forceinline__ void dyn_service(const PlanArgs& p, const Sched& S, const uint32_t* handed,
+                                            int lane) {
+  if (p.dyn_c <= 0) return;
+  const int last = p.ngroups - 1;
+  const int h = (int)lds_get(handed) - S.off(last);   // hand-outs taken in the group
+  if (h <= 0) return;
+  const int per = p.dyn_c * ((S.J(last) + ku1(FMT) - 1) / ku1(FMT));
+  const int want = (h - 1) / per + 1 + p.dyn_q;
+  if (want > lds_get(&S.dyn->claimed)) dyn_claim(p, S.dyn, want, lane);
+}
+
+template <int FMT>
+__device__ __forceinline__ void wait_count(const PlanArgs& p, const Sched& S, const uint32_t* handed,
+                                           const uint32_t* cnt, int seg, uint32_t want, bool& dead,
+                                           int lane) {
   for (uint32_t spins = 0; !dead && lds_get(cnt + seg) < want; ++spins) {
     if (spins > p.spin_limit) {
       atomicOr(p.err, 2u);
       dead = true;
     }
+    dyn_service<FMT>(p, S, handed, lane);
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -1049,7 +1225,7 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const uint32_t* cn
 // the two members' rows as each pair of row-groups completes.
 template <int FMT, bool GLUE, int MT>
 __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, int lane, const float* red,
-                             uint32_t* cnt, int* stalled, bool& dead) {
+                             uint32_t* cnt, int* stalled, bool& dead, const uint32_t* handed) {
   int rec_mem = -1;                 // the member with sum-of-squares records, if any
   if constexpr (GLUE && MT != 1) {
     const int m0 = S.mem0(g), m1 = m0 + S.nmem(g);
@@ -1071,7 +1247,7 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, in
   const bool paired = GLUE && MT != 1 && S.paired(g);
   uint16_t first[4] = {0, 0, 0, 0};  // paired: the first member's stored values of the current pair
   for (int s = 0; s < nseg; ++s) {
-    wait_count(p, cnt, s, (uint32_t)J, dead);
+    wait_count<FMT>(p, S, handed, cnt, s, (uint32_t)J, dead, lane);
     if (s == nseg - 1 && lane == 0) lds_put(stalled, g);   // every tile of g is in
     if constexpr (MT != 1) {
       // Each lane sums its float4 over the row-group's tiles in tile order.
@@ -1139,6 +1315,40 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, in
   if (GLUE && MT != 1 && rec_mem >= 0) write_record(p, S.ss(rec_mem) + w, lane, sq);
 }
 
+// The dynamic last group (one token row): this workgroup's row-groups are
+// those of the chunks it claimed, in claim order (local row-group s is
+// row-group s mod C of chunk s / C).  Each is reduced, as in finish_group,
+// once its hand-outs are counted; partial slots and counts are reused modulo
+// their capacities (the compute waves wait before running that far ahead).
+// Claims for the next chunks are made here, ahead of the hand-outs, until one
+// finds the group used up.
+template <int FMT, bool GLUE>
+__device__ void finish_dynamic(const PlanArgs& p, const Sched& S, int g, int lane, const float* red,
+                               uint32_t* cnt, int* stalled, bool& dead, const uint32_t* handed) {
+  const int Ju = (S.J(g) + ku1(FMT) - 1) / ku1(FMT);
+  const int C = p.dyn_c, R = S.R(g);
+  const int rmask = p.dyn_rcap - 1, smask = p.dyn_scap - 1;
+  const int row = lane & 15, q = lane >> 4;
+  DynCtl* d = S.dyn;
+  for (int s = 0; !dead; ++s) {
+    const int k = s / C;
+    dyn_claim(p, d, k + 1, lane);                     // chunk k, if there is one
+    if (k >= lds_get(&d->claimed)) break;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const int ch = uni(d->chunk[k]);
+    wait_count<FMT>(p, S, handed, cnt, s & smask, (uint32_t)Ju, dead, lane);
+    float part = 0.0f;
+    for (int t = q; t < Ju; t += 4) part += red[((s * Ju + t) & rmask) * 16 + row];
+    const float sum = quad_reduce(part);
+    if (lane == 0) cnt[s & smask] = 0u;
+    const int rg = ch * C + (s - k * C);
+    if (lane < 16 && rg < R) store_row<GLUE>(S, g, rg, row, sum);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) lds_put(&d->reduced, s + 1);
+  }
+  if (lane == 0) lds_put(stalled, g);
+}
+
 // Publish that this workgroup has finished every row it owes group g.
 // When no later group of the step reads or rewrites the outputs, they need
 // only be visible when the kernel ends, and the stamp goes out without
@@ -1194,7 +1404,9 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
 #ifndef QD_POLL_DELAY16
 #define QD_POLL_DELAY16 6
 #endif
-__device__ void wait_group(const PlanArgs& p, int g, int lane, int delay) {
+template <int FMT>
+__device__ void wait_group(const PlanArgs& p, const Sched& S, const uint32_t* handed, int g, int lane,
+                           int delay) {
   if (__hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return;
   const unsigned long long target = stamp(p, g);
   // Past the G stamps the buffer reads zeros, which the check ignores.
@@ -1221,6 +1433,7 @@ __device__ void wait_group(const PlanArgs& p, int g, int lane, int delay) {
       if (lane == 0) atomicOr(p.err, 1u);
       break;
     }
+    if (!done && kPollDepth == 1) dyn_service<FMT>(p, S, handed, lane);
   }
   wait_stores();                  // no poll left in flight
   asm volatile("" ::: "memory");
@@ -1273,13 +1486,24 @@ __device__ __forceinline__ void stage_rms16(const PlanArgs& p, const Sched& S, i
 template <int FMT, bool GLUE, int MT>
 __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane, half_t* xs,
                              float* xsum, const float* red, uint32_t* cnt, int* stalled,
-                             int* staged) {
+                             int* staged, const uint32_t* handed) {
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
+  // The dynamic last group: the first dyn_q chunks are claimed now, with one
+  // atomic whose round trip overlaps group 0's staging.  Until the group's
+  // barrier the compute waves can take no more of its tiles than their rings
+  // hold, fewer than those chunks have, so none of them can wait on a claim
+  // while the control wave waits at a barrier; from the barrier on the
+  // control wave claims ahead of them in its waits.
+  uint32_t first = 0;
+  if (MT == 1 && p.dyn_c > 0 && lane == 0)
+    first = __hip_atomic_fetch_add(p.dyn_ctr + (p.epoch & 1), (uint32_t)p.dyn_q, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
   if constexpr (MT == 1) stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
+  if (MT == 1 && p.dyn_c > 0) dyn_take(p, S.dyn, (uint32_t)uni((int)first), p.dyn_q, lane);
   if constexpr (MT != 1 && GLUE)
     if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
@@ -1292,8 +1516,15 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
     // left to drift apart end the step later than with a wait at every
     // boundary; on the smaller ones they end it earliest.)
     if (p.lag > 0 && g + 1 < p.ngroups && (S.order(g + 1) & kIndependent) && g >= p.lag)
-      wait_group(p, g - p.lag, lane, 0);
-    finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead);
+      wait_group<FMT>(p, S, handed, g - p.lag, lane, 0);
+    bool dynamic = false;
+    if constexpr (MT == 1) {
+      if (p.dyn_c > 0 && g == p.ngroups - 1) {
+        finish_dynamic<FMT, GLUE>(p, S, g, lane, red, cnt, stalled, dead, handed);
+        dynamic = true;
+      }
+    }
+    if (!dynamic) finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead, handed);
     publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
       // Activations no earlier group writes are staged while the stamps are
@@ -1311,7 +1542,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // and needs what g needed, which g's own boundary already waited for;
       // a group independent of every earlier group needs nothing of them.
       if (!(S.order(g + 1) & kNoWait))
-        wait_group(p, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
+        wait_group<FMT>(p, S, handed, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
         else stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
@@ -1349,6 +1580,14 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
   S.m = reinterpret_cast<const PMember*>(tab + (size_t)p.ngroups * sizeof(PGroup));
   S.s = reinterpret_cast<const PSched*>(tab + (size_t)p.ngroups * sizeof(PGroup) +
                                         (size_t)p.nmem * sizeof(PMember));
+  // The dynamic last group's claims follow the counter and the flags.
+  S.dyn = reinterpret_cast<DynCtl*>(next + 4);
+  S.dyn_c = p.dyn_c;
+  S.dyn_rmask = p.dyn_rcap - 1;
+  S.dyn_smask = p.dyn_scap - 1;
+  S.dyn_win = p.dyn_win;
+  S.spin = p.spin_limit;
+  S.err = p.err;
   {
     u32x4* dst = reinterpret_cast<u32x4*>(tab);
     const u32x4* gsrc = reinterpret_cast<const u32x4*>(p.groups);
@@ -1366,16 +1605,24 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
       *next = 0u;
       *stalled = -1;
       *staged = 0;
+      S.dyn->claimed = 0;
+      S.dyn->ended = 0;
+      S.dyn->reduced = 0;
+      // The next run's claim counter (this run uses the other one).
+      if (p.dyn_c > 0 && w == 0)
+        __hip_atomic_store(p.dyn_ctr + ((p.epoch + 1) & 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     for (int i = threadIdx.x; i < p.cnt_bytes / 4; i += kWaves * 64) cnt[i] = 0u;
   }
   __syncthreads();
 
   if (wave == kCtl) {
-    control_wave<FMT, GLUE, MT>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged);
+    control_wave<FMT, GLUE, MT>(p, S, w, lane, xs, xsum, red, cnt, stalled, staged, next);
   } else {
     const int last = p.ngroups - 1;
-    const int total = S.off(last) + S.tiles(last);
+    // The dynamic last group has no set length: its hand-outs end where the
+    // claims do.
+    const int total = p.dyn_c > 0 ? 0x3fffffff : S.off(last) + S.tiles(last);
     if (wave < kCtl - R)
       compute_wave<FMT, D, false, R, MT, U, GLUE>(p, S, total, next, lane, xs, xsum, red, cnt, stalled, staged);
     else
@@ -1833,7 +2080,15 @@ struct PlanLayout {
   size_t x_bytes = 0, xsum_bytes = 0, red_bytes = 0, cnt_bytes = 0, tab_bytes = 0, lds = 0;
   int lag = 0;                 // drift bound across independent groups, in groups (0: none)
   bool light = false;          // see kernel_ptr
+  // The dynamic last group (one token row; see PlanArgs), dyn_c = 0 if none.
+  int dyn_c = 0, dyn_q = 0, dyn_nch = 0, dyn_max = 0, dyn_rcap = 0, dyn_scap = 0, dyn_win = 0;
 };
+
+int pow2_at_least(int64_t v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
 
 // The last group before g writing any byte of [x, x + xb), or SIZE_MAX.
 size_t last_writer(const std::vector<HostGroup>& gs, size_t g, const void* x, uint64_t xb, int64_t m) {
@@ -2140,6 +2395,38 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // before it starts the totals afresh (every workgroup is level there),
     // so it keeps workgroup order, as paired groups do.
     if (!(hg.order & kNoWait)) std::fill(given.begin(), given.end(), (int64_t)0);
+    // One token row, 6 GiB of weights or more: the step's last group, when
+    // it has at least four row-groups per workgroup, is split at run time
+    // instead (kDynamic).  The workgroups reach it at different times: each
+    // streams at its own rate (on the 8B-shaped step the workgroups of some
+    // XCDs finish their share 5-8% later than others', the lag adding up
+    // over the step), so with a fixed split the early ones would idle while
+    // the late ones finish.  Each claims chunks of C row-groups from a device
+    // counter as it goes, about 16 per workgroup in all.  Measured, same
+    // boxes, wall us/step, fixed / dynamic: 8B int8 1259 / 1243, 1302 / 1288,
+    // 1298 / 1289 (the last workgroups' finishing times spread 4 us instead
+    // of 110); 27B-shaped 3676 / 3672, 3648-3660 / 3652; but the smaller
+    // steps lose what they gain (2B 370 / 383, 4B 734-741 / 735-744, 8B INT4
+    // 756-764 / 762-777), so they keep the fixed split.  (Claims of 8 or 4
+    // chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.)
+    if (!multi && !hg.paired && g == ng - 1 && R >= 4 * (int64_t)G && weight_bytes >= ((int64_t)6 << 30)) {
+      const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
+      L->dyn_c = (int)std::max<int64_t>(1, R / (16 * (int64_t)G));
+      L->dyn_nch = (int)ceil_div(R, (int64_t)L->dyn_c);
+      // Claims run dyn_q chunks ahead of the hand-outs, at least 64 tiles: more
+      // than the compute waves' rings hold, so that until the group's barrier
+      // no wave can reach an unclaimed chunk.
+      L->dyn_q = (int)ceil_div(64, L->dyn_c * Ju) + 1;
+      L->dyn_max = (int)(4 * ceil_div(L->dyn_nch, (int64_t)G)) + L->dyn_q + 8;
+      L->dyn_rcap = pow2_at_least(std::max<int64_t>(256, 16 * Ju));
+      L->dyn_scap = pow2_at_least(std::max<int64_t>(32, L->dyn_rcap / Ju + 1));
+      L->dyn_win = (int)std::min<int64_t>(L->dyn_scap, L->dyn_rcap / Ju);
+      L->pg[g].order |= kDynamic;
+      for (int w = 0; w < G; ++w) L->ps[(size_t)g * G + w] = PSched{0, off[w], 0, 0};
+      maxRel = std::max(maxRel, L->dyn_rcap);
+      maxSeg = std::max(maxSeg, L->dyn_scap);
+      continue;
+    }
     int rot = 0;
     if (!hg.paired && R % G != 0) {
       int64_t best = INT64_MAX;
@@ -2188,7 +2475,9 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
-  L->lds = L->x_bytes + L->xsum_bytes + L->red_bytes + L->cnt_bytes + L->tab_bytes + 16;   // + counter, stall flag
+  // + the tile counter and the flags, then the dynamic group's claims
+  L->lds = L->x_bytes + L->xsum_bytes + L->red_bytes + L->cnt_bytes + L->tab_bytes + 16 + 16 +
+           4 * (size_t)std::max(1, L->dyn_max);
   int64_t blocks = 0;
   for (HostJob& jb : jobs) {
     jb.first_block = blocks;
@@ -2210,6 +2499,18 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
 }
 
 }  // namespace
+
+// The dynamic last group's kernel arguments; `ctr`: two zeroed counters.
+void set_dynamic(PlanArgs& a, const PlanLayout& L, uint32_t* ctr) {
+  a.dyn_ctr = ctr;
+  a.dyn_c = L.dyn_c;
+  a.dyn_q = L.dyn_q;
+  a.dyn_nch = L.dyn_nch;
+  a.dyn_max = L.dyn_max;
+  a.dyn_rcap = std::max(1, L.dyn_rcap);
+  a.dyn_scap = std::max(1, L.dyn_scap);
+  a.dyn_win = L.dyn_win;
+}
 
 qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out) {
   std::vector<StackGroup> replay;
@@ -2336,6 +2637,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
   a.m = (int32_t)m;
   a.spin_limit = kSpinLimit;
   a.lag = L.lag;
+  set_dynamic(a, L, reinterpret_cast<uint32_t*>(sb + s_err + 64));   // two counters beside the error word
   plan->scratch_bytes = s_bytes;
   plan->lds = lds;
   plan->fmt = L.fmt;
@@ -2360,10 +2662,11 @@ qd_status plan_describe(const qd_linear_op* ops, int64_t n_ops, int64_t m, int32
     std::vector<StackGroup> tail;
     if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) L = PlanLayout{};
   }
-  std::vector<int64_t> v = {3, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
+  std::vector<int64_t> v = {4, L.persistent, L.fmt, m, L.glue, L.persistent ? L.split : 0,
                             (int64_t)L.pg.size(), (int64_t)L.pm.size(), L.G, L.xt_total,
                             (int64_t)L.jobs.size(), (int64_t)L.lds, (int64_t)L.x_bytes,
-                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes, L.ss_total, L.lag};
+                            (int64_t)L.red_bytes, (int64_t)L.cnt_bytes, (int64_t)L.tab_bytes, L.ss_total, L.lag,
+                            L.dyn_c, L.dyn_q, L.dyn_nch, L.dyn_max};
   auto addr = [](const void* p) { return (int64_t)(uintptr_t)p; };
   for (size_t g = 0; g < L.pg.size(); ++g) {
     const PGroup& p = L.pg[g];
@@ -2506,6 +2809,7 @@ __global__ __launch_bounds__(kMaxWorkgroups) void static_setup_kernel(uint8_t* _
   const int w = threadIdx.x;
   reinterpret_cast<unsigned long long*>(base)[w] = 0ull;
   if (w == 0) *reinterpret_cast<uint32_t*>(base + kStaticErrOff) = 0u;
+  if (w < 2) reinterpret_cast<uint32_t*>(base + kStaticErrOff + 64)[w] = 0u;   // the claim counters
   if (w >= G) return;
   const PGroup* gs = reinterpret_cast<const PGroup*>(base + kStaticGroupsOff);
   PSched* sched = reinterpret_cast<PSched*>(base + kStaticSchedOff);
@@ -2513,6 +2817,10 @@ __global__ __launch_bounds__(kMaxWorkgroups) void static_setup_kernel(uint8_t* _
   for (int g = 0; g < ngroups; ++g) {
     const int64_t R = gs[g].R, J = gs[g].J;
     const int64_t r0 = (int64_t)w * R / G, nrg = (int64_t)(w + 1) * R / G - r0;
+    if (gs[g].order & kDynamic) {                   // split at run time
+      sched[(size_t)g * G + w] = PSched{0, off, 0, 0};
+      continue;
+    }
     const int64_t n = unit > 1 ? (nrg + unit - 1) / unit * J : nrg * ((J + ku - 1) / ku);
     sched[(size_t)g * G + w] = PSched{(int32_t)n, off, (int32_t)r0, (int32_t)nrg};
     if (nrg != 0) off += (int32_t)n;
@@ -2627,6 +2935,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   a.m = (int32_t)m;
   a.spin_limit = kSpinLimit;
   a.lag = L.lag;
+  set_dynamic(a, L, reinterpret_cast<uint32_t*>(base + kStaticErrOff + 64));
   void* kargs[] = {&a};
   // A plain launch, as a plan's: capturable in a graph.
   if (hipLaunchKernel(kfn, dim3(G), dim3(kWaves * 64), kargs, (unsigned)L.lds, s) != hipSuccess) return QD_ELAUNCH;

@@ -1000,10 +1000,10 @@ def _plan_tables(qd, ops, m):
     header, the group records (12 words), the member records (8 words) and
     the per-workgroup schedule entries (4 words, group-major)."""
     v = qd.describe_stack_plan(ops, m)
-    assert v[0] == 3
+    assert v[0] == 4
     ng, nm, G = v[6], v[7], v[8]
-    groups = [v[18 + 12 * i:30 + 12 * i] for i in range(ng)]
-    mo = 18 + 12 * ng
+    groups = [v[22 + 12 * i:34 + 12 * i] for i in range(ng)]
+    mo = 22 + 12 * ng
     members = [v[mo + 8 * i:mo + 8 * i + 8] for i in range(nm)]
     so = mo + 8 * nm
     sched = [v[so + 4 * i:so + 4 * i + 4] for i in range(ng * G)]
@@ -1198,7 +1198,7 @@ def _one_row_per_row_group(n, salt):
 
 
 @pytest.mark.parametrize("workload", ["qwen3-8b-int8-m1", "qwen3-8b-int8-chain-m1", "qwen3-8b-int4-m1",
-                                      "qwen3-8b-int8-m16"])
+                                      "qwen3-8b-int8-m16", "qwen3.8-27b-int8-m1"])
 def test_plan_full_size_every_row_group(qd, workload):
     """The 8B-shaped step as the bench times it (and its chained, INT4 and
     16-token variants): one row of every row-group of every projection
@@ -1322,3 +1322,100 @@ def test_plan_new_activations_every_step(qd, m):
             for t in range(m):
                 check_vector(vals[i + 1][t], y_ref[t], rmax, vals[i][t], f"step {step} op {i} token {t}")
     plan.close()
+
+
+DYNAMIC = 64          # qd_stack_plan_describe order flag: the last group is split at run time
+
+
+@pytest.mark.parametrize("fmt", ["int8_b32", "int4_g64"])
+@pytest.mark.parametrize("chained", [False, True])
+def test_plan_dynamic_last_group(qd, fmt, chained):
+    """The step's last group split at run time (workgroups claim chunks of
+    row-groups from a device counter), which a plan does from 6 GiB of
+    weights: groups of copies of one 32768 x 16384 matrix make up the
+    bytes.  The last group has two members with ragged row tails
+    (100003 and 31220 rows, 8203 row-groups: chunks of 2, the last one half
+    past the group) and K = 2304 (9 super-blocks: an INT4 hand-out of two
+    holds a missing tile at the end of each row-group); it reads the output
+    of the group before it (chained) or an activation of its own.  Three
+    runs with fresh activations (the claim counter alternates between runs):
+    one row of every row-group and every row of the members' last two
+    row-groups against the oracle on the inputs the device read; a rerun on
+    the same input bit-identical; the no-allocation entry point
+    bit-identical too."""
+    from int4_quantized_decode_amd import LinearOp
+    k = 2304
+    pack = _pack_fn(qd, fmt)
+    nf, kf = 32768, 16384
+    wf = si.weights_torch(si.seed_for("dyn-filler", fmt), nf, kf, DEV)
+    pf = pack(wf)
+    frows = np.sort(np.random.default_rng(si.seed_for("dyn-filler-rows", fmt)).choice(nf, 48, replace=False))
+    parts_f = _oracle_parts(fmt, wf[torch.from_numpy(frows).to(DEV)].cpu().numpy())
+    del wf
+    copies = -(-(6 << 30) // pf.blob.numel())
+    xf = _gpu(si.activations(si.seed_for("dyn-xf", fmt), 1, kf)[0])
+    ops = [LinearOp(pf, xf, torch.zeros(nf, dtype=torch.float16, device=DEV), i) for i in range(copies)]
+    w0 = si.weights(si.seed_for("dyn-w0", fmt), k, k)
+    parts0 = _oracle_parts(fmt, w0)
+    x0 = torch.zeros(k, dtype=torch.float16, device=DEV)
+    y0 = torch.zeros(k, dtype=torch.float16, device=DEV)
+    x1 = y0 if chained else torch.zeros(k, dtype=torch.float16, device=DEV)
+    ops.append(LinearOp(pack(_gpu(w0)), x0, y0, copies))
+    heads = []
+    for i, n in enumerate((100003, 31220)):
+        w = si.weights_torch(si.seed_for("dyn-w", fmt, i), n, k, DEV)
+        y = torch.zeros(n, dtype=torch.float16, device=DEV)
+        ops.append(LinearOp(pack(w), x1, y, copies + 1))
+        rows = _one_row_per_row_group(n, i)
+        rows = np.unique(np.concatenate([rows, np.arange(max(0, n - 32), n)]))
+        w_rows = w[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        del w
+        heads.append((n, y, rows, _oracle_parts(fmt, w_rows)))
+    v, groups, _, sched = _plan_tables(qd, ops, 1)
+    G = v[8]
+    assert v[1] == 1 and len(groups) == copies + 2 and groups[-1][8] & DYNAMIC
+    assert not any(g[8] & DYNAMIC for g in groups[:-1])
+    assert v[18] == 2 and v[20] == -(-8203 // 2), "chunk size / chunk count"
+    assert all(sc[0] == 0 and sc[3] == 0 for sc in sched[(copies + 1) * G:])
+    plan = qd.StackPlan(ops, 1)
+    assert plan.persistent
+    xfh = _host(xf)
+    outs = []
+    for step in range(3):
+        x = si.activations(si.seed_for("dyn-x", fmt, chained, step), 1, k)[0]
+        x0.copy_(_gpu(x))
+        if not chained:
+            x1.copy_(_gpu(si.activations(si.seed_for("dyn-x1", fmt, step), 1, k)[0]))
+        for op in ops:
+            op.y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert plan.error() == 0
+        yf = [_host(op.y) for op in ops[:copies]]
+        assert all(np.array_equal(yf[0].view(np.uint16), a.view(np.uint16)) for a in yf[1:])
+        check_vector(yf[0][frows], linear.ref_linear(fmt, parts_f, xfh), linear.row_max_abs(fmt, parts_f), xfh,
+                     f"step {step} filler")
+        y0h, x1h = _host(y0).copy(), _host(x1).copy()
+        check_vector(y0h, linear.ref_linear(fmt, parts0, x), linear.row_max_abs(fmt, parts0), x, f"step {step} A")
+        for i, (n, y, rows, parts) in enumerate(heads):
+            yh = _host(y)
+            assert np.all(np.isfinite(yh.astype(np.float64))), f"step {step} member {i}: unwritten rows"
+            check_vector(yh[rows], linear.ref_linear(fmt, parts, x1h), linear.row_max_abs(fmt, parts), x1h,
+                         f"step {step} member {i}")
+        outs = [_host(op.y).copy() for op in ops[copies:]]
+    plan.run()                                     # the same input again: the same bits
+    torch.cuda.synchronize()
+    assert plan.error() == 0
+    for a, op in zip(outs, ops[copies:]):
+        assert np.array_equal(a.view(np.uint16), _host(op.y).view(np.uint16))
+    plan.close()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for op in ops:
+        op.y.fill_(float("nan"))
+    qd.stack_run_noalloc(ops, 1, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for a, op in zip(outs, ops[copies:]):
+        assert np.array_equal(a.view(np.uint16), _host(op.y).view(np.uint16)), "no-allocation step differs"
+    del ops, heads, pf
+    torch.cuda.empty_cache()

@@ -31,7 +31,7 @@ from synthetic_inputs import QWEN3_2B, QWEN3_8B, QWEN38_27B, Decoder
 FMT = {"int8_b32": 1, "int4_g64": 2, "fp16": 3}
 PRO_NONE, PRO_RMSNORM, PRO_GLU = 0, 1, 2
 EPI_NONE, EPI_SILU = 0, 1
-EARLY, ACK, NOWAIT, CLEAN, PAIRED, INDEPENDENT = 1, 2, 4, 8, 16, 32
+EARLY, ACK, NOWAIT, CLEAN, PAIRED, INDEPENDENT, DYNAMIC = 1, 2, 4, 8, 16, 32, 64
 TILE_BYTES = {1: 4352, 2: 2304}
 LDS_MAX = 160 * 1024
 
@@ -148,9 +148,10 @@ def describe(L, b, workgroups=256):
                                         ctypes.byref(n)) == 0
     v = list(buf)
     keys = ["version", "persistent", "fmt", "m", "glue", "prefix", "ngroups", "nmem", "G",
-            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes", "ss_total", "lag"]
-    d = dict(zip(keys, v[:18]))
-    pos = 18
+            "xt_total", "njobs", "lds", "x_bytes", "red_bytes", "cnt_bytes", "tab_bytes", "ss_total", "lag",
+            "dyn_c", "dyn_q", "dyn_nch", "dyn_max"]
+    d = dict(zip(keys, v[:len(keys)]))
+    pos = len(keys)
 
     def take(count, width, names):
         nonlocal pos
@@ -200,10 +201,34 @@ def attach_sources(b, d):
     return src
 
 
+def check_dynamic(d, gi, g, m):
+    """One token row, 6 GiB of weights or more: the step's last group, with
+    at least four row-groups per workgroup, is split at run time (DYNAMIC): no workgroup has a range
+    in it, and workgroups claim chunks of C row-groups (about 16 per
+    workgroup), dyn_q chunks ahead of their hand-outs (at least 64 tiles), at
+    most dyn_max each.  Returns whether group gi is that group."""
+    G = d["G"]
+    dynamic = bool(g["order"] & DYNAMIC)
+    expect = (m == 1 and gi == d["ngroups"] - 1 and g["R"] >= 4 * G and not g["order"] & PAIRED
+              and d["weight_bytes"] >= 6 << 30)
+    assert dynamic == expect, f"group {gi}: dynamic flag"
+    if not dynamic:
+        return False
+    sch = d["sched"][gi * G:(gi + 1) * G]
+    assert all(s["n"] == 0 and s["nseg"] == 0 for s in sch)
+    ju = -(-g["J"] // (2 if d["fmt"] == FMT["int4_g64"] else 1))
+    c = max(1, g["R"] // (16 * G))
+    nch = -(-g["R"] // c)
+    q = -(-64 // (c * ju)) + 1
+    assert (d["dyn_c"], d["dyn_nch"], d["dyn_q"]) == (c, nch, q)
+    assert d["dyn_max"] == 4 * -(-nch // G) + q + 8 and d["dyn_max"] * G >= 4 * nch
+    return True
+
+
 def check_layout(b, d, lds_fits=True):
     m, ops = b.m, b.ops
     G, gs, ms = d["G"], d["groups"], d["members"]
-    assert d["version"] == 3 and d["persistent"] == 1 and d["m"] == m
+    assert d["version"] == 4 and d["persistent"] == 1 and d["m"] == m
     src = attach_sources(b, d)
 
     # Rows: every op of the prefix is covered exactly once by its slices.
@@ -226,6 +251,9 @@ def check_layout(b, d, lds_fits=True):
             assert g["J"] == -(-o.k // 256) and g["gamma"] == o.gamma
             rg += -(-ms[j]["n"] // 16)
         assert rg == g["R"]
+        d["weight_bytes"] = sum(-(-o.n // 16) * -(-o.k // 256) * TILE_BYTES[o.fmt] for o in ops[:d["prefix"]])
+        if check_dynamic(d, gi, g, m):
+            continue
         # Each workgroup one contiguous range; ranges cover [0, R) in
         # workgroup order, balanced within one row-group.  The order may
         # start at any workgroup (cyclically) where the row-groups do not
@@ -463,6 +491,7 @@ CASES = [
     ("qwen3.8-27b int8 m16 (4 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 4}),
     ("qwen3.8-27b int8 chain m16 (3 layers)", QWEN38_27B, 16, "int8_b32", {"layers": 3, "chain": True}),
     ("qwen3-8b int8 chain m5", QWEN3_8B, 5, "int8_b32", {"chain": True, "layers": 4}),
+    ("qwen3.8-27b int8 m1", QWEN38_27B, 1, "int8_b32", {}),
 ]
 
 
@@ -513,7 +542,7 @@ def test_plan_layout_fp16_head_is_replayed_tail(L):
 def test_plan_layout_replays_whole(L, m, fmt, kw):
     b = step_ops(L, QWEN3_8B, m, fmt, layers=1, **kw)
     d = describe(L, b)
-    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 18 + 4
+    assert d["persistent"] == 0 and d["ngroups"] == 0 and len(d) == 22 + 4
 
 
 def test_plan_layout_copy_not_cut_inside_a_block(L):
