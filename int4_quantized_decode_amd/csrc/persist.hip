@@ -1134,30 +1134,20 @@ __device__ __forceinline__ void write_record(const PlanArgs& p, int rec, int lan
 // The dynamic last group: claim chunks until this workgroup holds `want`
 // (control wave only, one device-scope atomic per chunk, in order).  A claim
 // past the last chunk, or the per-workgroup cap, ends the workgroup's part.
+__device__ void dyn_take(const PlanArgs& p, DynCtl* d, uint32_t first, int n, int lane);
+
+// The dynamic last group: claim chunks until this workgroup holds `want` (or
+// the group is used up), all of them with one device-scope atomic: they are
+// consecutive chunks (control wave only).
 __device__ void dyn_claim(const PlanArgs& p, DynCtl* d, int want, int lane) {
   if (p.dyn_c <= 0 || lds_get(&d->ended)) return;
-  int have = lds_get(&d->claimed);
-  bool used_up = false;
-  while (have < min(want, p.dyn_max)) {
-    uint32_t c = 0;
-    if (lane == 0)
-      c = __hip_atomic_fetch_add(p.dyn_ctr + (p.epoch & 1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    c = (uint32_t)uni((int)c);
-    if (c >= (uint32_t)p.dyn_nch) {
-      used_up = true;
-      break;
-    }
-    if (lane == 0) {
-      d->chunk[have] = (int32_t)c;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      lds_put(&d->claimed, have + 1);
-    }
-    ++have;
-  }
-  if ((used_up || have >= p.dyn_max) && lane == 0) {   // no further chunk for this workgroup
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    lds_put(&d->ended, 1);
-  }
+  const int n = min(want, p.dyn_max) - lds_get(&d->claimed);
+  if (n <= 0) return;
+  uint32_t first = 0;
+  if (lane == 0)
+    first = __hip_atomic_fetch_add(p.dyn_ctr + (p.epoch & 1), (uint32_t)n, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  dyn_take(p, d, (uint32_t)uni((int)first), n, lane);
 }
 
 // Record chunks first, first + 1, ... (n of them, claimed with one atomic) as
@@ -1193,6 +1183,20 @@ __device__ __forceinline__ void dyn_service(const PlanArgs& p, const Sched& S, c
   const int per = p.dyn_c * ((S.J(last) + ku1(FMT) - 1) / ku1(FMT));
   const int want = (h - 1) / per + 1 + p.dyn_q;
   if (want > lds_get(&S.dyn->claimed)) dyn_claim(p, S.dyn, want, lane);
+}
+
+// Before the control wave waits at a barrier: the compute waves may take up
+// to 64 more hand-outs before they all arrive (their rings and the reserve
+// waves' hold fewer), and none may then wait on a claim; claim what those
+// would need in the dynamic group.
+template <int FMT>
+__device__ __forceinline__ void dyn_ahead(const PlanArgs& p, const Sched& S, const uint32_t* handed, int lane) {
+  if (p.dyn_c <= 0) return;
+  const int last = p.ngroups - 1;
+  const int h = (int)lds_get(handed) + 64 - S.off(last);
+  if (h <= 0) return;
+  const int per = p.dyn_c * ((S.J(last) + ku1(FMT) - 1) / ku1(FMT));
+  dyn_claim(p, S.dyn, (h - 1) / per + 1 + p.dyn_q, lane);
 }
 
 template <int FMT>
@@ -1490,20 +1494,14 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
-  // The dynamic last group: the first dyn_q chunks are claimed now, with one
-  // atomic whose round trip overlaps group 0's staging.  Until the group's
-  // barrier the compute waves can take no more of its tiles than their rings
-  // hold, fewer than those chunks have, so none of them can wait on a claim
-  // while the control wave waits at a barrier; from the barrier on the
-  // control wave claims ahead of them in its waits.
-  uint32_t first = 0;
-  if (MT == 1 && p.dyn_c > 0 && lane == 0)
-    first = __hip_atomic_fetch_add(p.dyn_ctr + (p.epoch & 1), (uint32_t)p.dyn_q, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+  // The dynamic last group's chunks are claimed ahead of the hand-outs: in
+  // the control wave's waits, and before each of its barriers for what the
+  // compute waves could take while it waits there (dyn_ahead), so that no
+  // compute wave waits on a claim while the control wave waits at a barrier.
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
   if constexpr (MT == 1) stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
-  if (MT == 1 && p.dyn_c > 0) dyn_take(p, S.dyn, (uint32_t)uni((int)first), p.dyn_q, lane);
+  if constexpr (MT == 1) dyn_ahead<FMT>(p, S, handed, lane);
   if constexpr (MT != 1 && GLUE)
     if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
   wg_barrier();                   // activations of group 0 staged
@@ -1552,6 +1550,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
         else stage_rms16<kPolicyCoherent>(p, S, g + 1, lane, xs, xsum);
       }
       if (lane == 0) lds_put(staged, g + 1);
+      if constexpr (MT == 1) dyn_ahead<FMT>(p, S, handed, lane);
       wg_barrier();               // activations of g + 1 staged
     }
   }
@@ -2413,9 +2412,8 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
       L->dyn_c = (int)std::max<int64_t>(1, R / (16 * (int64_t)G));
       L->dyn_nch = (int)ceil_div(R, (int64_t)L->dyn_c);
-      // Claims run dyn_q chunks ahead of the hand-outs, at least 64 tiles: more
-      // than the compute waves' rings hold, so that until the group's barrier
-      // no wave can reach an unclaimed chunk.
+      // Claims run dyn_q chunks ahead of the hand-outs, at least 64 tiles (a
+      // claim's round trip is a few tiles' time).
       L->dyn_q = (int)ceil_div(64, L->dyn_c * Ju) + 1;
       L->dyn_max = (int)(4 * ceil_div(L->dyn_nch, (int64_t)G)) + L->dyn_q + 8;
       L->dyn_rcap = pow2_at_least(std::max<int64_t>(256, 16 * Ju));
