@@ -2015,14 +2015,23 @@ const void* multi_kernel() {
 
 //
 // `light`: one token row, no glue, and few stalls to cover (no group waits for
-// the one before it): fewer reserve waves (int8 3 x 2, INT4 none), measured
-// on those steps (HIP-event medians, us, reserve 7 x 2 / 3 x 2 / none for
-// int8, 4 x 2 / none for INT4): 4B int8 781 / 741 / 770, 27B-shaped int8
-// 3954 / 3866 / 3879, 8B INT4 813 / 772; with the rotated ranges, 8B int8
-// without a drift bound 1283 / 1246 (7 x 2 / 3 x 2).  Steps with stalls keep
-// the deeper reserve (the chained 8B step 1471 / 1599 / 1631).
+// the one before it): no reserve waves, every compute wave streaming (int8
+// with rings of 2 tiles).  Measured on those steps (HIP-event medians, us):
+// first, reserve 7 x 2 / 3 x 2 / none for int8, 4 x 2 / none for INT4: 4B
+// int8 781 / 741 / 770, 27B-shaped int8 3954 / 3866 / 3879, 8B INT4 813 /
+// 772; with the rotated ranges, 8B int8 without a drift bound 1283 / 1246
+// (7 x 2 / 3 x 2).  Then, with the matrix-core tiles and the dynamic head,
+// int8 reserve 3 x 2 on rings of 3 / none on rings of 3 / none on rings of 2:
+// 8B 1266 / 1220 / 1216, 2B 365 / 349 / 341, 4B 727 / 740 / 728, 27B-shaped
+// 3651-3663 / 3661-3664 / 3653 (and 2 x 2 reserve 1239, 4 x 2 1285 on the 8B
+// step).  Steps with stalls keep the deeper reserve and rings of 3 (the
+// chained 8B step, reserve 7 / 5 / 3 / 0 waves of 2: 1485 / 1575 / 1596 /
+// 1644; the glued one 1640 / 1718 / 1741 / 1791).
 #ifndef QD_PLAN_RESERVE8_LIGHT
-#define QD_PLAN_RESERVE8_LIGHT 3
+#define QD_PLAN_RESERVE8_LIGHT 0
+#endif
+#ifndef QD_PLAN_RING8_LIGHT
+#define QD_PLAN_RING8_LIGHT 2
 #endif
 #ifndef QD_PLAN_RESERVE4_LIGHT
 #define QD_PLAN_RESERVE4_LIGHT 0
@@ -2035,7 +2044,7 @@ const void* kernel_ptr(int fmt, bool multi, bool glue, bool light) {
   if (light && !glue)
     return fmt == QD_FMT_INT8_B32
                ? reinterpret_cast<const void*>(
-                     &stack_kernel<QD_FMT_INT8_B32, kRing8, QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
+                     &stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT, QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
                : reinterpret_cast<const void*>(
                      &stack_kernel<QD_FMT_INT4_G64, kRing4, QD_PLAN_RESERVE4_LIGHT, kReserveInt4S, false, 1, 1>);
   if (fmt == QD_FMT_INT8_B32)
