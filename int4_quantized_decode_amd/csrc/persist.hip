@@ -1227,9 +1227,13 @@ __device__ __forceinline__ void wait_count(const PlanArgs& p, const Sched& S, co
 // ss + w (zeros if it stored none of them), before its stamp.  A paired group
 // (row-groups alternate between its two members) writes the gated product of
 // the two members' rows as each pair of row-groups completes.
+//
+// One token row, defer_last: the last row-group's rows are left in held /
+// held_rg (-1: none) for the caller to store, rather than stored here.
 template <int FMT, bool GLUE, int MT>
 __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, int lane, const float* red,
-                             uint32_t* cnt, int* stalled, bool& dead, const uint32_t* handed) {
+                             uint32_t* cnt, int* stalled, bool& dead, const uint32_t* handed,
+                             bool defer_last, float& held, int& held_rg) {
   int rec_mem = -1;                 // the member with sum-of-squares records, if any
   if constexpr (GLUE && MT != 1) {
     const int m0 = S.mem0(g), m1 = m0 + S.nmem(g);
@@ -1314,7 +1318,12 @@ __device__ void finish_group(const PlanArgs& p, const Sched& S, int g, int w, in
     for (; r < rend; r += 4) part += red[r * 16 + row];
     const float sum = quad_reduce(part);
     if (lane == 0) cnt[s] = 0u;                // ready for the next group
-    if (lane < 16) store_row<GLUE>(S, g, rg0 + s, row, sum);
+    if (defer_last && s == nseg - 1) {
+      held = sum;
+      held_rg = rg0 + s;
+    } else if (lane < 16) {
+      store_row<GLUE>(S, g, rg0 + s, row, sum);
+    }
   }
   if (GLUE && MT != 1 && rec_mem >= 0) write_record(p, S.ss(rec_mem) + w, lane, sq);
 }
@@ -1522,7 +1531,25 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
         dynamic = true;
       }
     }
-    if (!dynamic) finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead, handed);
+    // One token row, a step with a dynamic last group and no drift bound
+    // (6 to 12 GiB of weights), before a group whose activations no earlier
+    // group writes and that waits for no other workgroup, g's outputs needing
+    // no acknowledgement: the last row-group's rows are stored after the next
+    // activations are staged, so the staging's wait (vmcnt(0)) covers its own
+    // loads and not those stores.  Measured, wall us per step, stores before /
+    // after the staging, on three devices: 8B int8 1202 / 1192, 1221 / 1195,
+    // 1203 / 1190.  Elsewhere it was slower: 27B-shaped int8 (drift bound 3)
+    // 3672 / 3700, 8B INT4 759 / 804, 4B int8 735 / 761, 2B int8 344 / 375
+    // (and, with the staging issued before the last row-group's reduction
+    // instead, 8B int8 1205 / 1202, INT4 760 / 850, 4B 733 / 770, 2B 344 /
+    // 381).
+    const bool defer = MT == 1 && p.dyn_c > 0 && p.lag == 0 && g + 1 < p.ngroups &&
+                       !(S.order(g) & kAckOutputs) &&
+                       (S.order(g + 1) & (kStageEarly | kNoWait)) == (kStageEarly | kNoWait);
+    float held = 0.0f;
+    int held_rg = -1;
+    if (!dynamic)
+      finish_group<FMT, GLUE, MT>(p, S, g, w, lane, red, cnt, stalled, dead, handed, defer, held, held_rg);
     publish(p, S, g, w, lane);
     if (g + 1 < p.ngroups) {
       // Activations no earlier group writes are staged while the stamps are
@@ -1535,6 +1562,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // producing group (or were made before the step: early).
       const bool rms16 = GLUE && MT != 1 && S.pro(g + 1) == QD_PRO_RMSNORM;
       if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+      if (defer && held_rg >= 0 && lane < 16) store_row<GLUE>(S, g, held_rg, lane, held);
       if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
       // and needs what g needed, which g's own boundary already waited for;
@@ -1975,7 +2003,7 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 // bytes), measured on the 8B INT4 step with a wait at every boundary (us):
 // reserve waves of one unit
 // 0 / 2 / 3 / 4 / 5 / 6 / 7 / 10 gave 1671 / 1608 / 1607 / 1621-1634 / 1630 /
-// 1650 / 1709 / 2038 (from two boxes); units of 3 row-groups 1636 with 4
+// 1650 / 1709 / 2038 (from two devices); units of 3 row-groups 1636 with 4
 // reserve waves.  A ring of 2 units, two units per reserve wave and units of
 // 4 spill registers.
 #ifndef QD_PLAN_RING16_INT4
@@ -2411,7 +2439,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // over the step), so with a fixed split the early ones would idle while
     // the late ones finish.  Each claims chunks of C row-groups from a device
     // counter as it goes, about 16 per workgroup in all.  Measured, same
-    // boxes, wall us/step, fixed / dynamic: 8B int8 1259 / 1243, 1302 / 1288,
+    // devices, wall us/step, fixed / dynamic: 8B int8 1259 / 1243, 1302 / 1288,
     // 1298 / 1289 (the last workgroups' finishing times spread 4 us instead
     // of 110); 27B-shaped 3676 / 3672, 3648-3660 / 3652; but the smaller
     // steps lose what they gain (2B 370 / 383, 4B 734-741 / 735-744, 8B INT4
