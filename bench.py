@@ -502,6 +502,8 @@ def main():
                     "note": "the pages' whole-model decode rates on Apple M4 Max (int8hu bundles); "
                             "another machine and a whole decoder, so context rather than a baseline"},
     }
+    if wl.notes:
+        out["config"]["note"] = wl.notes
     if chained is not None:
         out["config"]["chained_step"] = chained
     if res["per_step"] > 1:
