@@ -1730,7 +1730,7 @@ struct qd_stack_plan {
   int fmt = 0;
   bool multi = false;                    // m > 1
   bool glue = false;                     // a prologue or an epilogue in the persistent part
-  bool light = false;                    // one token row, few stalls: the lighter reserve (kernel_ptr)
+  bool light = false;                    // no group waits for the one before it: the lighter reserve (kernel_ptr)
   std::vector<qd::StackGroup> tail;      // groups replayed after the persistent kernel
   std::vector<qd::StackGroup> replay;    // launch-per-group fallback (K = 0, mixed formats, glue, ...)
   void* tables = nullptr;
@@ -1993,6 +1993,16 @@ constexpr int kReserve8R = QD_PLAN_RESERVE8_R, kReserve8S = QD_PLAN_RESERVE8_S;
 #ifndef QD_PLAN_RESERVE16_R
 #define QD_PLAN_RESERVE16_R 3
 #endif
+// int8 at several token rows, a step in which some group waits for the one
+// before it (more stalls to cover): 4 reserve waves.  Measured, wall us per
+// step, 3 / 4 / 5 reserve waves: chained 8B 2070-2082 / 2034-2049 /
+// 2031-2046, glued 8B 2211-2213 / 2194-2197 / 2213-2214 (on another device
+// 3 / 4: chained 2080 / 2043-2048, glued 2227-2230 / 2228-2230); the steps without
+// waits kept 3 (8B 1711-1717 / 1722-1724 / 1747-1752, 27B-shaped 5420-5423 /
+// 5444 / 5473-5477; 2 reserve waves: 8B 1712-1720, chained 2122).
+#ifndef QD_PLAN_RESERVE16_WAITS_R
+#define QD_PLAN_RESERVE16_WAITS_R 4
+#endif
 #ifndef QD_PLAN_UNIT16
 #define QD_PLAN_UNIT16 2
 #endif
@@ -2032,19 +2042,23 @@ constexpr int unit16(int fmt) { return fmt == QD_FMT_INT8_B32 ? QD_PLAN_UNIT16 :
 // epilogue.  (Separate instances, so steps without glue run the plain
 // kernels.)
 template <int FMT, bool GLUE>
-const void* multi_kernel() {
+const void* multi_kernel(bool light) {
   if constexpr (FMT == QD_FMT_INT8_B32)
-    return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
-                                                       QD_PLAN_RESERVE16_S, GLUE, 16, QD_PLAN_UNIT16>);
+    return light ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16, QD_PLAN_RESERVE16_R,
+                                                               QD_PLAN_RESERVE16_S, GLUE, 16, QD_PLAN_UNIT16>)
+                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING16,
+                                                               QD_PLAN_RESERVE16_WAITS_R, QD_PLAN_RESERVE16_S,
+                                                               GLUE, 16, QD_PLAN_UNIT16>);
   else
     return reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT4_G64, QD_PLAN_RING16_INT4, QD_PLAN_RESERVE16_INT4_R,
                                                        QD_PLAN_RESERVE16_INT4_S, GLUE, 16, QD_PLAN_UNIT16_INT4>);
 }
 
 //
-// `light`: one token row, no glue, and few stalls to cover (no group waits for
-// the one before it): no reserve waves, every compute wave streaming (int8
-// with rings of 2 tiles).  Measured on those steps (HIP-event medians, us):
+// `light`: no group waits for the one before it (few stalls to cover).  At
+// several token rows it picks the int8 reserve (above).  At one token row
+// without glue: no reserve waves, every compute wave streaming (int8 with
+// rings of 2 tiles).  Measured on those steps (HIP-event medians, us):
 // first, reserve 7 x 2 / 3 x 2 / none for int8, 4 x 2 / none for INT4: 4B
 // int8 781 / 741 / 770, 27B-shaped int8 3954 / 3866 / 3879, 8B INT4 813 /
 // 772; with the rotated ranges, 8B int8 without a drift bound 1283 / 1246
@@ -2066,8 +2080,9 @@ const void* multi_kernel() {
 #endif
 const void* kernel_ptr(int fmt, bool multi, bool glue, bool light) {
   if (multi) {
-    if (fmt == QD_FMT_INT8_B32) return glue ? multi_kernel<QD_FMT_INT8_B32, true>() : multi_kernel<QD_FMT_INT8_B32, false>();
-    return glue ? multi_kernel<QD_FMT_INT4_G64, true>() : multi_kernel<QD_FMT_INT4_G64, false>();
+    if (fmt == QD_FMT_INT8_B32)
+      return glue ? multi_kernel<QD_FMT_INT8_B32, true>(light) : multi_kernel<QD_FMT_INT8_B32, false>(light);
+    return glue ? multi_kernel<QD_FMT_INT4_G64, true>(light) : multi_kernel<QD_FMT_INT4_G64, false>(light);
   }
   if (light && !glue)
     return fmt == QD_FMT_INT8_B32
@@ -2525,7 +2540,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   L->lag = drift_lag(weight_bytes, multi);
   bool waits = false;          // a group that waits for the one before it
   for (size_t g = 1; g < L->pg.size(); ++g) waits = waits || !(L->pg[g].order & kNoWait);
-  L->light = !multi && !waits;
+  L->light = !waits;
   L->fmt = fmt;
   L->multi = multi;
   L->glue = glue;
