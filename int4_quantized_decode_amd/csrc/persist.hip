@@ -1410,7 +1410,13 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
 // measured: one token row, before a dependent group (8B chained step 1505
 // with 2, 1543 with none; 1 and 4 took 1513 and 1516 us), and up to 16 token
 // rows (8B step 2025 with 6, 2118 with none; 2, 4 and 8 took 2063, 2037 and
-// 2023, the chained step 2065 with 6 and 2085 with 8).
+// 2023, the chained step 2065 with 6 and 2085 with 8).  Re-measured once
+// independent groups stopped waiting (only steps with dependent groups wait),
+// wall us per step: one token row, 1 / 2 / 3 / 4 sleeps: chained 8B 1498 /
+// 1489 / 1491 / 1497, glued 1670 / 1658 / 1654 / 1656; 16 token rows, 4 / 6
+// / 8: chained 2029 / 2044 / 2075, glued 2214 / 2213 / 2223; on another
+// device, 4 / 6: chained 2045 / 2056, glued 2207 / 2197 (6 kept: the two
+// steps move in opposite directions by less than the spread between devices).
 #ifndef QD_POLL_DELAY
 #define QD_POLL_DELAY 2
 #endif
