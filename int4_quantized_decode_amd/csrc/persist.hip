@@ -619,14 +619,37 @@ __device__ __forceinline__ float tile_row<QD_FMT_INT4_G64>(const Tile4& T, const
 
 // Up to 16 token rows (MT = 16).  The activation block of super-block j,
 // X[0..15][256 j .. 256 j + 255], as the eight A operands of the tile's
-// 16x16x32 products: operand q of lane (gq, rho) holds token rho's 8 values
-// at K position kpos(q, gq) within the super-block:
-//   int8 b32: 32 q + 8 gq                       (operand q = 32-block q)
-//   INT4 g64: 64 (q / 2) + 16 gq + 8 (q % 2)    (operands 2a, 2a + 1 = group a;
-//                                                the lane's 16 consecutive codes)
+// 16x16x32 products: operand q of lane (gq, rho) holds 8 of token rho's
+// values.
+//   int8 b32: the 8 at K position kpos(q, gq) = 32 q + 8 gq within the
+//             super-block (operand q = 32-block q).
+//   INT4 g64: operands 2a, 2a + 1 cover the lane's 16 consecutive values of
+//             group a, at 64 a + 16 gq: its halves start at kpos(2a, gq) and
+//             kpos(2a + 1, gq) = kpos(2a, gq) + 8.  Operand 2a holds value
+//             pairs 0, 2, 4, 6 of the 16 (against codes taken as 2^-24
+//             subnormals) and operand 2a + 1 pairs 1, 3, 5, 7 (against codes
+//             times 2^-20): int4_lo / int4_hi of the two halves.
 template <int FMT>
 __host__ __device__ constexpr int kpos(int q, int gq) {
   return FMT == QD_FMT_INT8_B32 ? 32 * q + 8 * gq : 64 * (q >> 1) + 16 * gq + 8 * (q & 1);
+}
+__device__ __forceinline__ u32x4 int4_lo(const u32x4& h0, const u32x4& h1) {
+  return (u32x4){h0[0], h0[2], h1[0], h1[2]};
+}
+__device__ __forceinline__ u32x4 int4_hi(const u32x4& h0, const u32x4& h1) {
+  return (u32x4){h0[1], h0[3], h1[1], h1[3]};
+}
+// The eight operands from the natural halves (INT4: in place).
+template <int FMT>
+__device__ __forceinline__ void to_operand_order(u32x4 (&xa)[8]) {
+  if constexpr (FMT == QD_FMT_INT4_G64) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const u32x4 h0 = xa[2 * a], h1 = xa[2 * a + 1];
+      xa[2 * a] = int4_lo(h0, h1);
+      xa[2 * a + 1] = int4_hi(h0, h1);
+    }
+  }
 }
 
 // The blocks are read from memory, not staged (16 x K does not fit in LDS for
@@ -661,6 +684,7 @@ __device__ __forceinline__ void load_xblock(const Sched& S, int g, int j, int m,
     const uint32_t off = kk < K ? (uint32_t)((rho * K + kk) * 2) : 0x80000000u;
     xa[b] = coherent ? bload16_coherent(rx, off) : bload16(rx, off);
   }
+  to_operand_order<FMT>(xa);
 }
 
 // Where output row n (of a K-long input row of a later group) goes in that
@@ -669,9 +693,12 @@ template <int FMT>
 __device__ __forceinline__ int64_t xt_index(int64_t n, int t) {
   const int64_t j = n >> 8;
   const int w = (int)(n & 255);
-  const int q = FMT == QD_FMT_INT8_B32 ? w >> 5 : 2 * (w >> 6) + ((w >> 3) & 1);
+  // INT4: value r = w & 15 of the lane's run, pair (r & 7) / 2 of half r / 8
+  // (see kpos): odd pairs go to operand 2a + 1; slot half * 2 + pair / 2.
+  const int q = FMT == QD_FMT_INT8_B32 ? w >> 5 : 2 * (w >> 6) + ((w >> 1) & 1);
   const int gq = FMT == QD_FMT_INT8_B32 ? (w >> 3) & 3 : (w >> 4) & 3;
-  return (((j * 8 + q) * 64 + gq * 16 + t) << 3) + (w & 7);
+  const int pos = FMT == QD_FMT_INT8_B32 ? (w & 7) : ((w >> 3) & 1) * 4 + ((w >> 2) & 1) * 2 + (w & 1);
+  return (((j * 8 + q) * 64 + gq * 16 + t) << 3) + pos;
 }
 
 // The tile's 16 x 16 product with the activation block on the matrix cores
@@ -696,8 +723,12 @@ __device__ __forceinline__ float4_t tile_mfma(const Tile8& T, const u32x4 (&xa)[
   return acc;
 }
 
-// INT4 g64, per group a: codes as exact fp16 integers (nibble p of a word
-// holds code (0,2,4,6,1,3,5,7)[p]) through two MFMAs, then
+// INT4 g64, per group a: the codes as fp16 subnormals with one AND per pair,
+// as at one token row (nibble p of a word holds code (0,2,4,6,1,3,5,7)[p], so
+// w & 0x000F000F and (w >> 8) & 0x000F000F are codes (0,1) and (4,5) times
+// 2^-24, w & 0x00F000F0 and (w >> 8) & 0x00F000F0 codes (2,3) and (6,7) times
+// 2^-20): one product per kind against the operand holding the matching value
+// pairs (see kpos), sums in fp32 apart, sum(c x) = 2^24 (lo + hi / 16).  Then
 // y += scale * sum(c x) + min * sum(x), the group's activation sums coming
 // from the same operands against an all-ones B (group_sums, once per unit).
 __device__ __forceinline__ void group_sums(const u32x4 (&xa)[8], float4_t (&xs)[4]) {
@@ -713,26 +744,24 @@ __device__ __forceinline__ void group_sums(const u32x4 (&xa)[8], float4_t (&xs)[
 
 __device__ __forceinline__ float4_t tile_mfma(const Tile4& T, const u32x4 (&xa)[8], const float4_t* xs) {
   const half8_t mt = __builtin_bit_cast(half8_t, T.meta);
-  const half2_t minus1024 = {(half_t)-1024.0f, (half_t)-1024.0f};
+  const uint32_t m = 0x000F000Fu, m4 = 0x00F000F0u;
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int s = a >> 1, h = a & 1;
-    float4_t pc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t w0 = T.c[s][2 * h], w1 = T.c[s][2 * h + 1];
+    const uint32_t w08 = w0 >> 8, w18 = w1 >> 8;
+    const u32x4 blo = {w0 & m, w08 & m, w1 & m, w18 & m};
+    const u32x4 bhi = {w0 & m4, w08 & m4, w1 & m4, w18 & m4};
+    const float4_t lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(half8_t, xa[2 * a]), __builtin_bit_cast(half8_t, blo), zero, 0, 0, 0);
+    const float4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(half8_t, xa[2 * a + 1]), __builtin_bit_cast(half8_t, bhi), zero, 0, 0, 0);
+    const float sc = (float)mt[a] * 16777216.0f, mn = (float)mt[4 + a];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t wd = T.c[s][2 * h + half];
-      const uint32_t mk = 0x000F000Fu, e = 0x64006400u;
-      const half2_t c01 = as_h2((wd & mk) | e) + minus1024;
-      const half2_t c23 = as_h2(((wd >> 4) & mk) | e) + minus1024;
-      const half2_t c45 = as_h2(((wd >> 8) & mk) | e) + minus1024;
-      const half2_t c67 = as_h2(((wd >> 12) & mk) | e) + minus1024;
-      const half8_t bq = {c01[0], c01[1], c23[0], c23[1], c45[0], c45[1], c67[0], c67[1]};
-      pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xa[2 * a + half]), bq, pc, 0, 0, 0);
-    }
-    const float sc = (float)mt[a], mn = (float)mt[4 + a];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, pc[i], __builtin_fmaf(mn, xs[a][i], acc[i]));
+    for (int i = 0; i < 4; ++i)
+      acc[i] = __builtin_fmaf(sc, __builtin_fmaf(hi[i], 0.0625f, lo[i]), __builtin_fmaf(mn, xs[a][i], acc[i]));
   }
   return acc;
 }
@@ -747,9 +776,12 @@ __device__ __forceinline__ void rms_block(u32x4 (&xa)[8], const half_t* gam, con
                                           int lane) {
   const int gq = lane >> 4;
   const float r = rinv[lane & 15];
+  u32x4 ga[8];
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
-    xa[b] = rms8(xa[b], r, *reinterpret_cast<const u32x4*>(gam + j * kSuperK + kpos<FMT>(b, gq)));
+  for (int b = 0; b < 8; ++b) ga[b] = *reinterpret_cast<const u32x4*>(gam + j * kSuperK + kpos<FMT>(b, gq));
+  to_operand_order<FMT>(ga);            // gamma in the activations' order
+#pragma unroll
+  for (int b = 0; b < 8; ++b) xa[b] = rms8(xa[b], r, ga[b]);
 }
 
 // Keep a load where it is written: the scheduler may not move code across
@@ -1706,11 +1738,25 @@ __global__ __launch_bounds__(256) void xt_copy_kernel(const XtJob* jobs, int njo
   // chunk c = (8 j + q) 64 + lane, lane = 16 gq + t
   const int64_t c = ((int64_t)blockIdx.x - jb.first_block) * 256 + threadIdx.x;
   const int tok = (int)(c & 15), gq = (int)((c >> 4) & 3), q = (int)((c >> 6) & 7);
-  const int64_t k = (c >> 9) * kSuperK + kpos<FMT>(q, gq);
-  if (tok >= m || k >= jb.k) return;
-  u32x4 v = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k);
-  if (jb.glu) v = glu8(v, *reinterpret_cast<const u32x4*>(jb.x + (m + tok) * jb.k + k));
-  *reinterpret_cast<u32x4*>(jb.t + c * 8) = v;
+  if constexpr (FMT == QD_FMT_INT8_B32) {
+    const int64_t k = (c >> 9) * kSuperK + kpos<FMT>(q, gq);
+    if (tok >= m || k >= jb.k) return;
+    u32x4 v = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k);
+    if (jb.glu) v = glu8(v, *reinterpret_cast<const u32x4*>(jb.x + (m + tok) * jb.k + k));
+    *reinterpret_cast<u32x4*>(jb.t + c * 8) = v;
+  } else {
+    // Both halves of the lane's 16 values (K is a multiple of 64, so the
+    // second half is in range with the first), then the operand's pairs.
+    const int64_t k = (c >> 9) * kSuperK + kpos<FMT>(q & ~1, gq);
+    if (tok >= m || k >= jb.k) return;
+    u32x4 h0 = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k);
+    u32x4 h1 = *reinterpret_cast<const u32x4*>(jb.x + tok * jb.k + k + 8);
+    if (jb.glu) {
+      h0 = glu8(h0, *reinterpret_cast<const u32x4*>(jb.x + (m + tok) * jb.k + k));
+      h1 = glu8(h1, *reinterpret_cast<const u32x4*>(jb.x + (m + tok) * jb.k + k + 8));
+    }
+    *reinterpret_cast<u32x4*>(jb.t + c * 8) = (q & 1) ? int4_hi(h0, h1) : int4_lo(h0, h1);
+  }
 }
 
 // Streaming ring depth per format (tiles per streaming wave), measured.
