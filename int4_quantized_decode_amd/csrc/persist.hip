@@ -548,15 +548,21 @@ __device__ __forceinline__ uint32_t pace_ticks(int k) {
 // the matrix core also sums the group's four K quarters, which the VALU dot
 // products left to a cross-lane reduction.  With the same x in every A row,
 // every output row of the product is the weight row's dot product, so lane
-// (g, rho) ends with row rho's total.  Products are exact (a 4-bit code times
-// an fp16 value, scaled by a power of two) and sums are fp32, as in the
-// GEMV; y = 2^24 sum_a s_a (lo_a + hi_a / 16) + sum_a min_a X_a, X_a being
-// the group's activation sum (staged in LDS, 4 per super-block).
-__device__ __forceinline__ float tile_row4(const Tile4& T, const half_t* xs_j, const float* gsum_j, int g) {
+// (g, rho) ends with row rho's total.  The group's activation sum X comes
+// from the same two x operands against an all-ones B (every output is the sum
+// over the group), so nothing beyond x itself is staged.  Products are exact
+// (a 4-bit code times an fp16 value, scaled by a power of two) and sums are
+// fp32, as in the GEMV; y = 2^24 sum_a s_a (lo_a + hi_a / 16) + sum_a min_a X_a.
+// (Measured against group sums added up by the control wave as it stages x,
+// wall us per step on three devices: 8B INT4 762 -> 722-724, 762-764 ->
+// 736-738, 765 -> 753-757; that staging is on every boundary's critical
+// path.)
+__device__ __forceinline__ float tile_row4(const Tile4& T, const half_t* xs_j, int g) {
   const half8_t mt = __builtin_bit_cast(half8_t, T.meta);
-  const float4_t gs = *reinterpret_cast<const float4_t*>(gsum_j);
   const uint32_t m = 0x000F000Fu, m4 = 0x00F000F0u;
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const half_t one = (half_t)1.0f;
+  const half8_t ones = {one, one, one, one, one, one, one, one};
   float acc_s = 0.0f, acc = 0.0f;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -578,8 +584,10 @@ __device__ __forceinline__ float tile_row4(const Tile4& T, const half_t* xs_j, c
         __builtin_bit_cast(half8_t, alo), __builtin_bit_cast(half8_t, blo), zero, 0, 0, 0);
     const float4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(
         __builtin_bit_cast(half8_t, ahi), __builtin_bit_cast(half8_t, bhi), zero, 0, 0, 0);
+    float4_t xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo), ones, zero, 0, 0, 0);
+    xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi), ones, xsum, 0, 0, 0);
     acc_s = __builtin_fmaf((float)mt[a], __builtin_fmaf(hi[0], 0.0625f, lo[0]), acc_s);
-    acc = __builtin_fmaf((float)mt[4 + a], gs[a], acc);
+    acc = __builtin_fmaf((float)mt[4 + a], xsum[0], acc);
   }
   return __builtin_fmaf(acc_s, 16777216.0f, acc);
 }
@@ -587,11 +595,9 @@ __device__ __forceinline__ float tile_row4(const Tile4& T, const half_t* xs_j, c
 // One tile at one token row: lanes 0..15 get the 16 rows' sums (INT4: every
 // lane gets its row's).
 template <int FMT>
-__device__ __forceinline__ float tile_row(const typename Fmt<FMT>::Tile& T, const half_t* xs,
-                                          const float* xsum, int j, int g);
+__device__ __forceinline__ float tile_row(const typename Fmt<FMT>::Tile& T, const half_t* xs, int j, int g);
 template <>
-__device__ __forceinline__ float tile_row<QD_FMT_INT8_B32>(const Tile8& T, const half_t* xs,
-                                                           const float*, int j, int g) {
+__device__ __forceinline__ float tile_row<QD_FMT_INT8_B32>(const Tile8& T, const half_t* xs, int j, int g) {
   // Per 32-block one 16x16x32 product of the lane's 8 codes (exact fp16
   // integers) against its 8 activations; with the same x in every A row each
   // output row is the weight row's block sum, so lane (g, rho) gets row rho's.
@@ -612,9 +618,8 @@ __device__ __forceinline__ float tile_row<QD_FMT_INT8_B32>(const Tile8& T, const
   return acc;
 }
 template <>
-__device__ __forceinline__ float tile_row<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs,
-                                                           const float* xsum, int j, int g) {
-  return tile_row4(T, xs + j * kSuperK, xsum + 4 * j, g);
+__device__ __forceinline__ float tile_row<QD_FMT_INT4_G64>(const Tile4& T, const half_t* xs, int j, int g) {
+  return tile_row4(T, xs + j * kSuperK, g);
 }
 
 // Up to 16 token rows (MT = 16).  The activation block of super-block j,
@@ -853,14 +858,14 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
     if constexpr (MT == 1) {
       float part;
       if constexpr (ku1(FMT) == 1) {
-        part = tile_row<FMT>(t, xs, xsum, r.j, g4);
+        part = tile_row<FMT>(t, xs, r.j, g4);
       } else {
         // The tiles' sums in tile order.  A missing last tile (J odd) holds
-        // zero codes, scales and mins, and reads zero activations and sums
-        // (the staging clears them), so it adds exactly zero.
-        part = tile_row<FMT>(t.t[0], xs, xsum, r.j, g4);
+        // zero codes, scales and mins, and reads zero activations (the
+        // staging's loads past x return zeros), so it adds exactly zero.
+        part = tile_row<FMT>(t.t[0], xs, r.j, g4);
 #pragma unroll
-        for (int q = 1; q < ku1(FMT); ++q) part += tile_row<FMT>(t.t[q], xs, xsum, r.j + q, g4);
+        for (int q = 1; q < ku1(FMT); ++q) part += tile_row<FMT>(t.t[q], xs, r.j + q, g4);
       }
       if (r.lseg >= 0) {
         // The dynamic group reuses partial slots and counts: row-group lseg
@@ -980,8 +985,7 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
         0, POLICY);
 }
 
-// Stage a group's multiplied vector (and, for int4, its 64-value group sums) in
-// LDS.  All loads, and under a prologue the second operand's (gamma, or the
+// Stage a group's multiplied vector in LDS.  All loads, and under a prologue the second operand's (gamma, or the
 // gated product's B block) into xs + x_span(Kp), are issued before the single wait,
 // so staging costs one memory round trip whatever K is.  The prologue then
 // runs in place: each lane rewrites the 8-value chunks its own loads brought.
@@ -1017,43 +1021,6 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
     }
   } else {
     wait_stores();                                 // vmcnt(0): the data is in LDS
-  }
-  if (FMT == QD_FMT_INT4_G64) {
-    // Each group's activation sum, X[4 j + a] for group a of super-block j.
-    // One 16-value run per lane, four runs' reads in flight before any sum
-    // (this runs on the group boundary's critical path); the four runs of a
-    // group sit in four adjacent lanes and are added across them,
-    // (q0 + q1) + (q2 + q3).
-    const int runs = Kp / 16;
-    const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
-    for (int t0 = 0; t0 < runs; t0 += 256) {
-      half8_t va[4], vb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = min(t0 + 64 * u + lane, runs - 1);   // clamped read; result kept only if in range
-        va[u] = *reinterpret_cast<const half8_t*>(xs + 16 * t);
-        vb[u] = *reinterpret_cast<const half8_t*>(xs + 16 * t + 8);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = t0 + 64 * u + lane;
-        float sum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          sum = __builtin_amdgcn_fdot2((half2_t){va[u][e], va[u][e + 1]}, one2, sum, false);
-          sum = __builtin_amdgcn_fdot2((half2_t){vb[u][e], vb[u][e + 1]}, one2, sum, false);
-        }
-        const int su = __builtin_bit_cast(int, sum);
-        const float s2 = sum + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(su, su, 0xB1, 0xF, 0xF, false));
-        const int s2u = __builtin_bit_cast(int, s2);
-        const float s4 = s2 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(s2u, s2u, 0x4E, 0xF, 0xF, false));
-        if (t < runs && (t & 3) == 0) xsum[t >> 2] = s4;
-      }
-    }
-    // The sums a hand-out's missing last tile reads (J not a multiple of
-    // ku1): zero.
-    for (int t = runs / 4 + lane; t < (Kp / kSuperK + ku1(FMT) - 1) / ku1(FMT) * ku1(FMT) * 4; t += 64)
-      xsum[t] = 0.0f;
   }
 }
 
@@ -2568,12 +2535,11 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       maxSeg = std::max<int>(maxSeg, (int)nrg);
     }
   }
-  // One token row: staged activations (and their group sums for INT4).
-  // Several: no staged activations, 16 x 16 partials per tile, and under
-  // RMSNorm gamma and the 16 per-token factors.
+  // One token row: staged activations.  Several: no staged activations,
+  // 16 x 16 partials per tile, and under RMSNorm gamma and the 16 per-token
+  // factors.
   L->x_bytes = multi ? (size_t)maxGamma * 2 : (size_t)maxXH * 2;      // a multiple of 1024
-  L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0)
-                        : fmt == QD_FMT_INT4_G64 ? align_up((size_t)ceil_div(maxJ, ku1(fmt)) * ku1(fmt) * 4 * 4, 16) : 0;
+  L->xsum_bytes = multi && maxGamma > 0 ? 64 : 0;
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
