@@ -2423,6 +2423,8 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   std::vector<int64_t> given(G, 0);  // tiles each workgroup has so far
   int maxJ = 1, maxXH = 512, maxRel = 1, maxSeg = 1, maxGamma = 0;
   int64_t weight_bytes = 0;
+  bool any_wait = false;       // some group waits for the one before it
+  for (int g = 1; g < ng; ++g) any_wait = any_wait || !(groups[g].order & kNoWait);
   for (int g = 0; g < ng; ++g) {
     HostGroup& hg = groups[g];
     const int64_t J = hg.J, R = hg.R, T = R * J;
@@ -2479,7 +2481,12 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // steps lose what they gain (2B 370 / 383, 4B 734-741 / 735-744, 8B INT4
     // 756-764 / 762-777), so they keep the fixed split.  (Claims of 8 or 4
     // chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.)
-    if (!multi && !hg.paired && g == ng - 1 && R >= 4 * (int64_t)G && weight_bytes >= ((int64_t)6 << 30)) {
+    // A step in which some group waits for the one before it keeps the fixed
+    // split too: every such wait brings the workgroups level again, so no lag
+    // builds up for the claims to absorb, and their upkeep in the waits is
+    // pure cost (8B chained 1483-1485 -> 1470, glued 1650-1652 -> 1620-1621).
+    if (!any_wait && !multi && !hg.paired && g == ng - 1 && R >= 4 * (int64_t)G &&
+        weight_bytes >= ((int64_t)6 << 30)) {
       const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
       L->dyn_c = (int)std::max<int64_t>(1, R / (16 * (int64_t)G));
       L->dyn_nch = (int)ceil_div(R, (int64_t)L->dyn_c);
