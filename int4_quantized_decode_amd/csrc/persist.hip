@@ -985,17 +985,17 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
         0, POLICY);
 }
 
-// Stage a group's multiplied vector in LDS.  All loads, and under a prologue the second operand's (gamma, or the
-// gated product's B block) into xs + x_span(Kp), are issued before the single wait,
-// so staging costs one memory round trip whatever K is.  The prologue then
+// Stage a group's multiplied vector in LDS.  All loads, and under a prologue
+// the second operand's (gamma, or the gated product's B block) into
+// xs + x_span(Kp), are issued before the single wait, so staging costs one
+// memory round trip whatever K is.  The prologue then
 // runs in place: each lane rewrites the 8-value chunks its own loads brought.
 // POLICY: device-coherent for activations an earlier group of the step may
 // have written (unless no cache can hold a stale copy of their lines); cached
 // for the others, so the workgroups of an XCD share one L2 copy (8B step
 // 1367-1372 vs 1375-1378 us coherent).
-template <int FMT, bool GLUE, int POLICY = kPolicyCoherent>
-__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs,
-                                              float* xsum) {
+template <bool GLUE, int POLICY = kPolicyCoherent>
+__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs) {
   const int Kp = S.J(g) * kSuperK;
   const int64_t k = S.k(g);
   const uint32_t xbytes = (uint32_t)(k * 2);
@@ -1514,7 +1514,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // compute wave waits on a claim while the control wave waits at a barrier.
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
-  if constexpr (MT == 1) stage_group_x<FMT, GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
+  if constexpr (MT == 1) stage_group_x<GLUE, kPolicyDefault>(S, 0, lane, xs);
   if constexpr (MT == 1) dyn_ahead<FMT>(p, S, handed, lane);
   if constexpr (MT != 1 && GLUE)
     if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
@@ -1566,7 +1566,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // whose records are complete once every workgroup has finished the
       // producing group (or were made before the step: early).
       const bool rms16 = GLUE && MT != 1 && S.pro(g + 1) == QD_PRO_RMSNORM;
-      if (MT == 1 && early) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+      if (MT == 1 && early) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs);
       if (defer && held_rg >= 0 && lane < 16) store_row<GLUE>(S, g, held_rg, lane, held);
       if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
@@ -1575,8 +1575,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (!(S.order(g + 1) & kNoWait))
         wait_group<FMT>(p, S, handed, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
-        if (S.order(g + 1) & kCleanLines) stage_group_x<FMT, GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
-        else stage_group_x<FMT, GLUE>(S, g + 1, lane, xs, xsum);
+        if (S.order(g + 1) & kCleanLines) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs);
+        else stage_group_x<GLUE>(S, g + 1, lane, xs);
       }
       if (rms16 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
