@@ -819,6 +819,7 @@ __device__ __forceinline__ void rms_block(u32x4 (&xa)[8], const half_t* gam, con
 // 16 x 16 at up to 16 token rows) to their own LDS slot and counts the tile
 // against its row-group, so the control wave can finish a row-group as soon
 // as its last tile is in.
+__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float r);
 template <int FMT, int MT, int U> struct RingOf { using type = Hand1<FMT>; };
 template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>; };
 
@@ -826,7 +827,7 @@ template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>;
 // current group and xsum its 16 per-token factors.
 template <int FMT, int D, bool RESERVE, int R, int MT, int U, bool GLUE>
 __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint32_t* next,
-                             int lane, const half_t* xs, const float* xsum, float* red,
+                             int lane, half_t* xs, float* xsum, float* red,
                              uint32_t* cnt, const int* stalled, const int* staged) {
   using Tile = typename RingOf<FMT, MT, U>::type;
   const int ng = p.ngroups;
@@ -848,7 +849,24 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
   auto settle_to = [&](int g) {
     while (cg < g) {
       ++cg;
-      if (cg < ng) wg_barrier();
+      if (cg >= ng) continue;
+      if constexpr (GLUE && MT == 1) {
+        if (S.pro(cg) != QD_PRO_NONE) {
+          // This wave's share of the group's prologue pass, once the control
+          // wave has staged the data (bounded wait; a timeout is reported).
+          const int* flag = reinterpret_cast<const int*>(xsum) + 1;
+          for (uint32_t spins = 0; lds_get(flag) < cg + 1; ++spins) {
+            if (spins > S.spin) {
+              if (lane == 0) atomicOr(S.err, 2u);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+          prologue_share(S, cg, uni((int)(threadIdx.x >> 6)), lane, xs, xsum[0]);
+        }
+      }
+      wg_barrier();
     }
   };
   auto compute = [&](int s) {
@@ -994,8 +1012,29 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
 // have written (unless no cache can hold a stale copy of their lines); cached
 // for the others, so the workgroups of an XCD share one L2 copy (8B step
 // 1367-1372 vs 1375-1378 us coherent).
+// One token row under a prologue, the element-wise pass (the gated product,
+// or RMSNorm's normalisation once its factor r is known) is shared by all 16
+// waves of the workgroup: chunk c (16 bytes) goes to wave (c / 64) % 16.
+// Every wave does its share before the group's barrier, so the pass is
+// complete when the barrier releases the products.  The control wave stages
+// the data (and, for RMSNorm, forms r alone), then publishes the group in
+// pf[1] (r in pf[0], the LDS words after x); the compute waves wait for that
+// in settle_to.
+// Element by element the arithmetic is the one the staging did alone.
+__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float r) {
+  const int Kp = S.J(g) * kSuperK;
+  const int n4 = Kp / 8;                          // 16-byte chunks of x
+  u32x4* x4 = reinterpret_cast<u32x4*>(xs);
+  const u32x4* y4 = reinterpret_cast<const u32x4*>(xs + x_span(Kp));
+  if (S.pro(g) == QD_PRO_GLU) {
+    for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) x4[c] = glu8(x4[c], y4[c]);
+  } else {
+    for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) x4[c] = rms8(x4[c], r, y4[c]);
+  }
+}
+
 template <bool GLUE, int POLICY = kPolicyCoherent>
-__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs) {
+__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs, float* pf) {
   const int Kp = S.J(g) * kSuperK;
   const int64_t k = S.k(g);
   const uint32_t xbytes = (uint32_t)(k * 2);
@@ -1007,17 +1046,18 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
     if (pro == QD_PRO_GLU) dma_to_lds<POLICY>(make_rsrc(S.x(g) + k, xbytes), Kp, lane, xs2);
     if (pro == QD_PRO_RMSNORM) dma_to_lds<POLICY>(make_rsrc(S.gamma(g), xbytes), Kp, lane, xs2);
     wait_stores();                                 // vmcnt(0): the data is in LDS
-    if (pro == QD_PRO_GLU) {
-      for (int i = lane * 8; i < Kp; i += 512)
-        *reinterpret_cast<u32x4*>(xs + i) =
-            glu8(*reinterpret_cast<const u32x4*>(xs + i), *reinterpret_cast<const u32x4*>(xs2 + i));
-    } else if (pro == QD_PRO_RMSNORM) {
-      float ss = 0.0f;
-      for (int i = lane * 8; i < Kp; i += 512) ss = sumsq8(*reinterpret_cast<const u32x4*>(xs + i), ss);
-      const float r = rms_inverse(wave_sum(ss), k, S.eps(g));
-      for (int i = lane * 8; i < Kp; i += 512)
-        *reinterpret_cast<u32x4*>(xs + i) =
-            rms8(*reinterpret_cast<const u32x4*>(xs + i), r, *reinterpret_cast<const u32x4*>(xs2 + i));
+    if (pro != QD_PRO_NONE) {
+      float r = 0.0f;
+      if (pro == QD_PRO_RMSNORM) {
+        float ss = 0.0f;
+        for (int i = lane * 8; i < Kp; i += 512) ss = sumsq8(*reinterpret_cast<const u32x4*>(xs + i), ss);
+        r = rms_inverse(wave_sum(ss), k, S.eps(g));
+        if (lane == 0) pf[0] = r;
+      }
+      // The data and r before the flag; the compute waves read both after it.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) lds_put(reinterpret_cast<int*>(pf) + 1, g + 1);
+      prologue_share(S, g, kCtl, lane, xs, r);
     }
   } else {
     wait_stores();                                 // vmcnt(0): the data is in LDS
@@ -1514,7 +1554,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // compute wave waits on a claim while the control wave waits at a barrier.
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
-  if constexpr (MT == 1) stage_group_x<GLUE, kPolicyDefault>(S, 0, lane, xs);
+  if constexpr (MT == 1) stage_group_x<GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
   if constexpr (MT == 1) dyn_ahead<FMT>(p, S, handed, lane);
   if constexpr (MT != 1 && GLUE)
     if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
@@ -1566,7 +1606,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // whose records are complete once every workgroup has finished the
       // producing group (or were made before the step: early).
       const bool rms16 = GLUE && MT != 1 && S.pro(g + 1) == QD_PRO_RMSNORM;
-      if (MT == 1 && early) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs);
+      if (MT == 1 && early) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
       if (defer && held_rg >= 0 && lane < 16) store_row<GLUE>(S, g, held_rg, lane, held);
       if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
@@ -1575,8 +1615,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (!(S.order(g + 1) & kNoWait))
         wait_group<FMT>(p, S, handed, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
-        if (S.order(g + 1) & kCleanLines) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs);
-        else stage_group_x<GLUE>(S, g + 1, lane, xs);
+        if (S.order(g + 1) & kCleanLines) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+        else stage_group_x<GLUE>(S, g + 1, lane, xs, xsum);
       }
       if (rms16 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
@@ -1637,6 +1677,7 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
       *next = 0u;
       *stalled = -1;
       *staged = 0;
+      if (MT == 1 && GLUE) reinterpret_cast<int*>(xsum)[1] = 0;   // no prologue staged yet
       S.dyn->claimed = 0;
       S.dyn->ended = 0;
       S.dyn->reduced = 0;
@@ -2546,7 +2587,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   // 16 x 16 partials per tile, and under RMSNorm gamma and the 16 per-token
   // factors.
   L->x_bytes = multi ? (size_t)maxGamma * 2 : (size_t)maxXH * 2;      // a multiple of 1024
-  L->xsum_bytes = multi && maxGamma > 0 ? 64 : 0;
+  L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0) : (glue ? 16 : 0);
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
