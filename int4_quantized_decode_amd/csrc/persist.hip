@@ -819,7 +819,7 @@ __device__ __forceinline__ void rms_block(u32x4 (&xa)[8], const half_t* gam, con
 // 16 x 16 at up to 16 token rows) to their own LDS slot and counts the tile
 // against its row-group, so the control wave can finish a row-group as soon
 // as its last tile is in.
-__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float r);
+__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float* pf, int nrms);
 template <int FMT, int MT, int U> struct RingOf { using type = Hand1<FMT>; };
 template <int FMT, int U> struct RingOf<FMT, 16, U> { using type = Unit<FMT, U>; };
 
@@ -846,6 +846,7 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
   // long in flight by then).  One block's registers serve every ring slot.
   u32x4 xr[8];
   int cg = -1;                      // last group whose activations this wave has waited for
+  int nrms = 0;                     // RMSNorm prologues passed (one token row, glue)
   auto settle_to = [&](int g) {
     while (cg < g) {
       ++cg;
@@ -863,7 +864,8 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
             __builtin_amdgcn_s_sleep(1);
           }
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-          prologue_share(S, cg, uni((int)(threadIdx.x >> 6)), lane, xs, xsum[0]);
+          if (S.pro(cg) == QD_PRO_RMSNORM) ++nrms;
+          prologue_share(S, cg, uni((int)(threadIdx.x >> 6)), lane, xs, xsum, nrms);
         }
       }
       wg_barrier();
@@ -942,6 +944,14 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
     }
   } else {
     const int r = uni((int)(threadIdx.x >> 6)) - (kCtl - R);   // rank among reserve waves
+    // The activations after group t are staged (one token row under glue:
+    // their data has landed and the prologue pass, which every wave shares,
+    // is starting).
+    auto next_staged = [&](int t) {
+      if constexpr (GLUE && MT == 1)
+        if (lds_get(reinterpret_cast<const int*>(xsum) + 1) > t + 1) return true;
+      return lds_get(staged) > t;
+    };
     int trig = 0;                   // issue at the stall that ends group `trig`
     for (;;) {
       // Pass the barrier of group `trig` first: the control wave reaches the
@@ -963,10 +973,10 @@ __device__ void compute_wave(const PlanArgs& p, const Sched& S, int total, uint3
       for (int s = 0; s < D; ++s) {
         const uint32_t due = t0 + pace_ticks<FMT>((s * R + r) * (MT == 1 ? ku1(FMT) : U));
         while (!stop && (int32_t)((uint32_t)__builtin_amdgcn_s_memrealtime() - due) < 0) {
-          stop = lds_get(staged) > trig;
+          stop = next_staged(trig);
           if (!stop) __builtin_amdgcn_s_sleep(2);
         }
-        stop = stop || lds_get(staged) > trig;
+        stop = stop || next_staged(trig);
         ring[s] = next_tile(ref[s], lane, !stop);
           exhausted = exhausted || (!stop && ref[s].g >= ng);
         QD_PIN_ISSUE();
@@ -1014,27 +1024,50 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, int Kp, int
 // 1367-1372 vs 1375-1378 us coherent).
 // One token row under a prologue, the element-wise pass (the gated product,
 // or RMSNorm's normalisation once its factor r is known) is shared by all 16
-// waves of the workgroup: chunk c (16 bytes) goes to wave (c / 64) % 16.
-// Every wave does its share before the group's barrier, so the pass is
-// complete when the barrier releases the products.  The control wave stages
-// the data (and, for RMSNorm, forms r alone), then publishes the group in
-// pf[1] (r in pf[0], the LDS words after x); the compute waves wait for that
-// in settle_to.
-// Element by element the arithmetic is the one the staging did alone.
-__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float r) {
+// waves of the workgroup: chunk c (16 bytes) goes to wave (c / 64) % 16, and
+// so is RMSNorm's sum of squares.  Every wave does its share before the
+// group's barrier, so the pass is complete when the barrier releases the
+// products.  The control wave stages the data, then publishes the group in
+// pf[1] (pf: the LDS words after x); the compute waves wait for that in
+// settle_to.
+__device__ void prologue_share(const Sched& S, int g, int wave, int lane, half_t* xs, float* pf, int nrms) {
   const int Kp = S.J(g) * kSuperK;
   const int n4 = Kp / 8;                          // 16-byte chunks of x
   u32x4* x4 = reinterpret_cast<u32x4*>(xs);
   const u32x4* y4 = reinterpret_cast<const u32x4*>(xs + x_span(Kp));
   if (S.pro(g) == QD_PRO_GLU) {
     for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) x4[c] = glu8(x4[c], y4[c]);
-  } else {
-    for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) x4[c] = rms8(x4[c], r, y4[c]);
+    return;
   }
+  // RMSNorm: each wave's sum of squares over its chunks (pf[4 + wave]), then,
+  // once all 16 are in (pf[2] counts them, 16 per RMSNorm group so far),
+  // their total in wave order.  The slots are reused by the next RMSNorm
+  // group only after this group's barrier, which every wave reaches after
+  // reading them.
+  float ss = 0.0f;
+  for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) ss = sumsq8(x4[c], ss);
+  ss = wave_sum(ss);
+  if (lane == 0) pf[4 + wave] = ss;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  int* const count = reinterpret_cast<int*>(pf) + 2;
+  if (lane == 0) __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (uint32_t spins = 0; lds_get(count) < kWaves * nrms; ++spins) {
+    if (spins > S.spin) {
+      if (lane == 0) atomicOr(S.err, 2u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += pf[4 + w];
+  const float r = rms_inverse(tot, S.k(g), S.eps(g));
+  for (int c = 64 * wave + lane; c < n4; c += 64 * kWaves) x4[c] = rms8(x4[c], r, y4[c]);
 }
 
 template <bool GLUE, int POLICY = kPolicyCoherent>
-__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs, float* pf) {
+__device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, half_t* xs, float* pf, int& nrms) {
   const int Kp = S.J(g) * kSuperK;
   const int64_t k = S.k(g);
   const uint32_t xbytes = (uint32_t)(k * 2);
@@ -1047,17 +1080,11 @@ __device__ __forceinline__ void stage_group_x(const Sched& S, int g, int lane, h
     if (pro == QD_PRO_RMSNORM) dma_to_lds<POLICY>(make_rsrc(S.gamma(g), xbytes), Kp, lane, xs2);
     wait_stores();                                 // vmcnt(0): the data is in LDS
     if (pro != QD_PRO_NONE) {
-      float r = 0.0f;
-      if (pro == QD_PRO_RMSNORM) {
-        float ss = 0.0f;
-        for (int i = lane * 8; i < Kp; i += 512) ss = sumsq8(*reinterpret_cast<const u32x4*>(xs + i), ss);
-        r = rms_inverse(wave_sum(ss), k, S.eps(g));
-        if (lane == 0) pf[0] = r;
-      }
-      // The data and r before the flag; the compute waves read both after it.
+      // The data before the flag; the compute waves read it after.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
       if (lane == 0) lds_put(reinterpret_cast<int*>(pf) + 1, g + 1);
-      prologue_share(S, g, kCtl, lane, xs, r);
+      if (pro == QD_PRO_RMSNORM) ++nrms;
+      prologue_share(S, g, kCtl, lane, xs, pf, nrms);
     }
   } else {
     wait_stores();                                 // vmcnt(0): the data is in LDS
@@ -1548,13 +1575,14 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
   // The control wave is on every group's critical path: let it issue ahead of
   // the compute waves that share its SIMD.
   __builtin_amdgcn_s_setprio(3);
+  int nrms = 0;                   // RMSNorm prologues staged (one token row, glue)
   // The dynamic last group's chunks are claimed ahead of the hand-outs: in
   // the control wave's waits, and before each of its barriers for what the
   // compute waves could take while it waits there (dyn_ahead), so that no
   // compute wave waits on a claim while the control wave waits at a barrier.
   // Group 0's activations: nothing of this launch has written anything yet
   // (earlier launches' writes are visible at kernel start).
-  if constexpr (MT == 1) stage_group_x<GLUE, kPolicyDefault>(S, 0, lane, xs, xsum);
+  if constexpr (MT == 1) stage_group_x<GLUE, kPolicyDefault>(S, 0, lane, xs, xsum, nrms);
   if constexpr (MT == 1) dyn_ahead<FMT>(p, S, handed, lane);
   if constexpr (MT != 1 && GLUE)
     if (S.pro(0) == QD_PRO_RMSNORM) stage_rms16<kPolicyDefault>(p, S, 0, lane, xs, xsum);
@@ -1606,7 +1634,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       // whose records are complete once every workgroup has finished the
       // producing group (or were made before the step: early).
       const bool rms16 = GLUE && MT != 1 && S.pro(g + 1) == QD_PRO_RMSNORM;
-      if (MT == 1 && early) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
+      if (MT == 1 && early) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum, nrms);
       if (defer && held_rg >= 0 && lane < 16) store_row<GLUE>(S, g, held_rg, lane, held);
       if (rms16 && early) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
       // A further row range of the same op(s) reads nothing group g writes,
@@ -1615,8 +1643,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
       if (!(S.order(g + 1) & kNoWait))
         wait_group<FMT>(p, S, handed, g, lane, MT > 1 ? QD_POLL_DELAY16 : early ? 0 : QD_POLL_DELAY);
       if (MT == 1 && !early) {
-        if (S.order(g + 1) & kCleanLines) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum);
-        else stage_group_x<GLUE>(S, g + 1, lane, xs, xsum);
+        if (S.order(g + 1) & kCleanLines) stage_group_x<GLUE, kPolicyDefault>(S, g + 1, lane, xs, xsum, nrms);
+        else stage_group_x<GLUE>(S, g + 1, lane, xs, xsum, nrms);
       }
       if (rms16 && !early) {
         if (S.order(g + 1) & kCleanLines) stage_rms16<kPolicyDefault>(p, S, g + 1, lane, xs, xsum);
@@ -1677,7 +1705,10 @@ __global__ __launch_bounds__(kWaves * 64) void stack_kernel(PlanArgs p) {
       *next = 0u;
       *stalled = -1;
       *staged = 0;
-      if (MT == 1 && GLUE) reinterpret_cast<int*>(xsum)[1] = 0;   // no prologue staged yet
+      if (MT == 1 && GLUE) {
+        reinterpret_cast<int*>(xsum)[1] = 0;      // no prologue staged yet
+        reinterpret_cast<int*>(xsum)[2] = 0;      // no RMSNorm shares counted
+      }
       S.dyn->claimed = 0;
       S.dyn->ended = 0;
       S.dyn->reduced = 0;
@@ -2587,7 +2618,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
   // 16 x 16 partials per tile, and under RMSNorm gamma and the 16 per-token
   // factors.
   L->x_bytes = multi ? (size_t)maxGamma * 2 : (size_t)maxXH * 2;      // a multiple of 1024
-  L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0) : (glue ? 16 : 0);
+  L->xsum_bytes = multi ? (maxGamma > 0 ? 64 : 0) : (glue ? 80 : 0);
   L->red_bytes = align_up((size_t)maxRel * 16 * 4 * (multi ? 16 : 1), 16);
   L->cnt_bytes = align_up((size_t)maxSeg * 4, 16);
   L->tab_bytes = (size_t)ng * sizeof(PGroup) + L->pm.size() * sizeof(PMember) + (size_t)ng * sizeof(PSched);
