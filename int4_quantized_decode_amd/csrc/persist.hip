@@ -2044,10 +2044,14 @@ bool split_rows(std::vector<HostGroup>& gs, int64_t tiles, int G, int64_t tbytes
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Reserve waves (and tiles each) per format, as measured on MI355X.  int8:
-// 7 reserve waves of 2 tiles, the 8 streaming waves then sitting two to a
-// SIMD; this was best for the 2B-, 4B- and 8B-shaped steps alike (15 to 50
-// tiles per workgroup per group).  More reserve tiles run several groups
+// Reserve waves (and tiles each) per format, as measured on MI355X.  int8
+// (the steps with stalls: some group waits for the one before it): 9 reserve
+// waves of 2 tiles.  Re-measured with the current kernel on two devices,
+// wall us per step, reserve waves 3 / 5 / 7 / 8 / 9 / 10 / 11: chained 8B
+// 1578 / 1562 / 1470-1477 / 1469-1470 / 1433-1439 / 1553-1556 / 1719, glued
+// 1690 / 1652-1657 / 1560-1568 / 1562 / 1552-1555 / 1684 / 1842.  Before,
+// 7 of 2 tiles (8 streaming waves, two to a SIMD) was best for the 2B-, 4B-
+// and 8B-shaped steps alike (15 to 50 tiles per workgroup per group).  More reserve tiles run several groups
 // ahead and are then not free for the next stall; fewer leave memory idle
 // for part of it.  INT4: rings of 2 tiles per streaming wave and 4 reserve
 // waves of 2 tiles (measured with the one-AND decode and the plain launch,
@@ -2063,7 +2067,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kReserveInt4 = QD_PLAN_RESERVE4, kReserveInt4S = QD_PLAN_RESERVE4_S;
 
 #ifndef QD_PLAN_RESERVE8_R
-#define QD_PLAN_RESERVE8_R 7
+#define QD_PLAN_RESERVE8_R 9
 #endif
 #ifndef QD_PLAN_RESERVE8_S
 #define QD_PLAN_RESERVE8_S 2
