@@ -2163,28 +2163,39 @@ const void* multi_kernel(bool light) {
 // 3651-3663 / 3661-3664 / 3653 (and 2 x 2 reserve 1239, 4 x 2 1285 on the 8B
 // step).  Steps with stalls keep the deeper reserve and rings of 3 (the
 // chained 8B step, reserve 7 / 5 / 3 / 0 waves of 2: 1485 / 1575 / 1596 /
-// 1644; the glued one 1640 / 1718 / 1741 / 1791).
+// 1644; the glued one 1640 / 1718 / 1741 / 1791).  Later, with the stores
+// after the staging: int8 rings of 1 / 2 / 3 without reserve (2 x 2 reserve
+// on rings of 2): 2B 342-343 / 349-350 / 357 (355), 4B 721-722 / 730-731 /
+// 749-750 (718), 8B 1215-1217 / 1192-1193 / 1192-1193 (1206-1207); so steps
+// with a dynamic last group (6 GiB of weights or more) keep rings of 2 and
+// the others take rings of 1.
 #ifndef QD_PLAN_RESERVE8_LIGHT
 #define QD_PLAN_RESERVE8_LIGHT 0
 #endif
 #ifndef QD_PLAN_RING8_LIGHT
 #define QD_PLAN_RING8_LIGHT 2
 #endif
+#ifndef QD_PLAN_RING8_LIGHT_SMALL
+#define QD_PLAN_RING8_LIGHT_SMALL 1
+#endif
 #ifndef QD_PLAN_RESERVE4_LIGHT
 #define QD_PLAN_RESERVE4_LIGHT 0
 #endif
-const void* kernel_ptr(int fmt, bool multi, bool glue, bool light) {
+const void* kernel_ptr(int fmt, bool multi, bool glue, bool light, bool dyn) {
   if (multi) {
     if (fmt == QD_FMT_INT8_B32)
       return glue ? multi_kernel<QD_FMT_INT8_B32, true>(light) : multi_kernel<QD_FMT_INT8_B32, false>(light);
     return glue ? multi_kernel<QD_FMT_INT4_G64, true>(light) : multi_kernel<QD_FMT_INT4_G64, false>(light);
   }
-  if (light && !glue)
-    return fmt == QD_FMT_INT8_B32
-               ? reinterpret_cast<const void*>(
-                     &stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT, QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
-               : reinterpret_cast<const void*>(
-                     &stack_kernel<QD_FMT_INT4_G64, kRing4, QD_PLAN_RESERVE4_LIGHT, kReserveInt4S, false, 1, 1>);
+  if (light && !glue) {
+    if (fmt == QD_FMT_INT8_B32)
+      return dyn ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT,
+                                                               QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
+                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT_SMALL,
+                                                               QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>);
+    return reinterpret_cast<const void*>(
+        &stack_kernel<QD_FMT_INT4_G64, kRing4, QD_PLAN_RESERVE4_LIGHT, kReserveInt4S, false, 1, 1>);
+  }
   if (fmt == QD_FMT_INT8_B32)
     return glue ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, true, 1, 1>)
                 : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, kRing8, kReserve8R, kReserve8S, false, 1, 1>);
@@ -2697,7 +2708,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return QD_EDEVICE;
   }
   // LDS beyond one CU's: replay.
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.dyn_c > 0);
   const size_t lds = L.lds;
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
@@ -2859,7 +2870,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   // workgroups would wait for it: the first device-wide wait then times out
   // (every wait is bounded, so the kernel still ends), the run reports the
   // timeout, and the plan launches cooperatively from then on.
-  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue, plan->light);
+  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue, plan->light, plan->args.dyn_c > 0);
   const hipError_t e =
       plan->cooperative
           ? hipLaunchCooperativeKernel(kfn, dim3(plan->args.G), dim3(kWaves * 64), kargs, (unsigned)plan->lds, s)
@@ -3050,7 +3061,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   if (L.pg.size() > (size_t)kStaticGroups || L.pm.size() > (size_t)kStaticMembers) return QD_ESHAPE;
   std::vector<StackGroup> tail;
   if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) return replay_all();
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.dyn_c > 0);
   if (L.lds > sd->lds_max) return replay_all();
   if (L.lds > 65536 && hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds) != hipSuccess) {
     (void)hipGetLastError();
