@@ -2278,9 +2278,16 @@ size_t last_writer(const std::vector<HostGroup>& gs, size_t g, const void* x, ui
 //   8B int8, one row:           1246 / 1340 / 1322 / 1304  (7 x 2 reserve: no bound 1283,
 //                                                          lag 1 1259, lag 2 1294)
 //   27B-shaped int8, one row:   3767 / 3964 / 3757 / 3668
+// With the stores after the staging, the fixed head for steps with waits and
+// rings of 1 for the small steps (wall us per step; lags of 2 / 3 / 5 / 8 /
+// 12 / 16 / 24 groups): 27B-shaped int8, one row, 3815 / 3668-3685 / 3686-
+// 3707 / 3613-3623 / 3594-3599 / 3583-3591 / 3611-3654; at 16 rows lag 3 /
+// 16: 5417-5422 / 5342.  The smaller steps still do best without a bound
+// (no bound / lags of 16 / 32: 8B int8 1195 / 1232 / 1222, 8B INT4 746-748 /
+// 835 / 821-824, 4B 741 / 841 / 824, 2B 343 / 460 / 442).
 int drift_lag(int64_t weight_bytes, bool multi) {
   (void)multi;
-  if (weight_bytes >= ((int64_t)12 << 30)) return 3;
+  if (weight_bytes >= ((int64_t)12 << 30)) return 16;
   return 0;
 }
 
