@@ -1799,8 +1799,11 @@ __global__ __launch_bounds__(256) void xt_copy_kernel(const XtJob* jobs, int njo
 }
 
 // Streaming ring depth per format (tiles per streaming wave), measured.
+// int8 steps with stalls: rings of 2 with 9 reserve waves (wall us per step,
+// rings of 3 / 2 and reserve tiles 1 / 3 on rings of 3: chained 8B 1441 /
+// 1429 / 1497 / 1463-1468, glued 1554 / 1546 / 1611-1615 / 1545).
 #ifndef QD_PLAN_RING8
-#define QD_PLAN_RING8 3
+#define QD_PLAN_RING8 2
 #endif
 #ifndef QD_PLAN_RING4
 #define QD_PLAN_RING4 2
