@@ -1483,8 +1483,11 @@ __device__ __forceinline__ bool stamps_reached(const u32x4 (&v)[4], int G, int l
 // / 8: chained 2029 / 2044 / 2075, glued 2214 / 2213 / 2223; on another
 // device, 4 / 6: chained 2045 / 2056, glued 2207 / 2197 (6 kept: the two
 // steps move in opposite directions by less than the spread between devices).
+// One token row again with 9 reserve waves on rings of 2 and the glue passes
+// shared, 1 / 2 / 3 / 4 sleeps: chained 1458-1460 / 1430-1433 / 1428-1430 /
+// 1431-1436, glued 1576-1577 / 1548-1550 / 1538-1540 / 1541: 3 taken.
 #ifndef QD_POLL_DELAY
-#define QD_POLL_DELAY 2
+#define QD_POLL_DELAY 3
 #endif
 #ifndef QD_POLL_DELAY16
 #define QD_POLL_DELAY16 6
