@@ -498,10 +498,10 @@ CASES = [
 
 
 def expected_lag(b, d):
-    """The drift bound the plan states: 3 groups from 12 GiB of weights in
+    """The drift bound the plan states: 16 groups from 12 GiB of weights in
     the persistent part, else none."""
     wbytes = sum(-(-o.n // 16) * -(-o.k // 256) * TILE_BYTES[o.fmt] for o in b.ops[:d["prefix"]])
-    return 3 if wbytes >= 12 << 30 else 0
+    return 16 if wbytes >= 12 << 30 else 0
 
 
 @pytest.mark.parametrize("name,dec,m,fmt,kw", CASES, ids=[c[0] for c in CASES])
