@@ -48,9 +48,12 @@ def _pack(qd, fmt, w):
 
 
 def _ulps(a, b):
-    """|a - b| in units of the fp16 spacing at the larger magnitude."""
+    """|a - b| in units of the fp16 spacing at the larger magnitude.  From
+    2^15 up to the largest finite value (65504) the spacing is 32; the step
+    above 65504 itself would be to infinity, so the magnitude is capped at
+    2^15 before taking it."""
     a64, b64 = a.astype(np.float64), b.astype(np.float64)
-    big = np.maximum(np.abs(a64), np.abs(b64)).astype(np.float16)
+    big = np.minimum(np.maximum(np.abs(a64), np.abs(b64)), 32768.0).astype(np.float16)
     return np.abs(a64 - b64) / np.spacing(big).astype(np.float64)
 
 
@@ -120,6 +123,7 @@ def test_prologues_and_epilogue_exact(qd, fmt, m, path):
         assert np.mean(d == 0) >= 0.99, (name, np.mean(d == 0))
     # signs of zeros and the large-argument limits of silu
     assert float(got[2][0, 2]) == 0.0 and float(got[2][0, 3]) == float(want_silu[0, 3])
+    assert float(got[2][0, 4]) == float(want_silu[0, 4]) and float(got[2][0, 0]) == float(want_silu[0, 0])
 
 
 @pytest.mark.parametrize("m", [1, 16])
