@@ -2574,13 +2574,16 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // XCDs finish their share 5-8% later than others', the lag adding up
     // over the step), so with a fixed split the early ones would idle while
     // the late ones finish.  Each claims chunks of C row-groups from a device
-    // counter as it goes, about 16 per workgroup in all.  Measured, same
+    // counter as it goes, about 32 per workgroup in all (C = 1 for the 8B
+    // and 27B-shaped heads).  Measured, same
     // devices, wall us/step, fixed / dynamic: 8B int8 1259 / 1243, 1302 / 1288,
     // 1298 / 1289 (the last workgroups' finishing times spread 4 us instead
     // of 110); 27B-shaped 3676 / 3672, 3648-3660 / 3652; but the smaller
     // steps lose what they gain (2B 370 / 383, 4B 734-741 / 735-744, 8B INT4
     // 756-764 / 762-777), so they keep the fixed split.  (Claims of 8 or 4
-    // chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.)
+    // chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.
+    // About 32 instead of 16, so single row-groups: 8B 1192-1193 -> 1190,
+    // 27B-shaped 3617-3619 -> 3605-3606.)
     // A step in which some group waits for the one before it keeps the fixed
     // split too: every such wait brings the workgroups level again, so no lag
     // builds up for the claims to absorb, and their upkeep in the waits is
@@ -2588,7 +2591,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     if (!any_wait && !multi && !hg.paired && g == ng - 1 && R >= 4 * (int64_t)G &&
         weight_bytes >= ((int64_t)6 << 30)) {
       const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
-      L->dyn_c = (int)std::max<int64_t>(1, R / (16 * (int64_t)G));
+      L->dyn_c = (int)std::max<int64_t>(1, R / (32 * (int64_t)G));
       L->dyn_nch = (int)ceil_div(R, (int64_t)L->dyn_c);
       // Claims run dyn_q chunks ahead of the hand-outs, at least 64 tiles (a
       // claim's round trip is a few tiles' time).

@@ -205,7 +205,7 @@ def check_dynamic(d, gi, g, m):
     """One token row, 6 GiB of weights or more, no group waiting for the one
     before it: the step's last group, with
     at least four row-groups per workgroup, is split at run time (DYNAMIC): no workgroup has a range
-    in it, and workgroups claim chunks of C row-groups (about 16 per
+    in it, and workgroups claim chunks of C row-groups (about 32 per
     workgroup), dyn_q chunks ahead of their hand-outs (at least 64 tiles), at
     most dyn_max each.  Returns whether group gi is that group."""
     G = d["G"]
@@ -219,7 +219,7 @@ def check_dynamic(d, gi, g, m):
     sch = d["sched"][gi * G:(gi + 1) * G]
     assert all(s["n"] == 0 and s["nseg"] == 0 for s in sch)
     ju = -(-g["J"] // (2 if d["fmt"] == FMT["int4_g64"] else 1))
-    c = max(1, g["R"] // (16 * G))
+    c = max(1, g["R"] // (32 * G))
     nch = -(-g["R"] // c)
     q = -(-64 // (c * ju)) + 1
     assert (d["dyn_c"], d["dyn_nch"], d["dyn_q"]) == (c, nch, q)
