@@ -1334,7 +1334,7 @@ def test_plan_dynamic_last_group(qd, fmt, chained):
     row-groups from a device counter), which a plan does from 6 GiB of
     weights: groups of copies of one 32768 x 16384 matrix make up the
     bytes.  The last group has two members with ragged row tails
-    (100003 and 31220 rows, 8203 row-groups: chunks of 2, the last one half
+    (200003 and 62424 rows, 16403 row-groups: chunks of 2, the last one half
     past the group) and K = 2304 (9 super-blocks: an INT4 hand-out of two
     holds a missing tile at the end of each row-group); it reads an
     activation of its own, or the output of the group before it (chained):
@@ -1364,7 +1364,7 @@ def test_plan_dynamic_last_group(qd, fmt, chained):
     x1 = y0 if chained else torch.zeros(k, dtype=torch.float16, device=DEV)
     ops.append(LinearOp(pack(_gpu(w0)), x0, y0, copies))
     heads = []
-    for i, n in enumerate((100003, 31220)):
+    for i, n in enumerate((200003, 62424)):
         w = si.weights_torch(si.seed_for("dyn-w", fmt, i), n, k, DEV)
         y = torch.zeros(n, dtype=torch.float16, device=DEV)
         ops.append(LinearOp(pack(w), x1, y, copies + 1))
@@ -1379,7 +1379,9 @@ def test_plan_dynamic_last_group(qd, fmt, chained):
     assert bool(groups[-1][8] & DYNAMIC) == (not chained)
     assert not any(g[8] & DYNAMIC for g in groups[:-1])
     if not chained:
-        assert v[18] == 2 and v[20] == -(-8203 // 2), "chunk size / chunk count"
+        R = -(-200003 // 16) + -(-62424 // 16)
+        assert G == 256 and R == 16403
+        assert v[18] == max(1, R // (32 * G)) == 2 and v[20] == -(-R // 2), "chunk size / chunk count"
         assert all(sc[0] == 0 and sc[3] == 0 for sc in sched[(copies + 1) * G:])
     plan = qd.StackPlan(ops, 1)
     assert plan.persistent
