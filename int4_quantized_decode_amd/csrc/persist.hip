@@ -171,7 +171,7 @@ struct PlanArgs {
   int32_t dyn_rcap;
   int32_t dyn_scap;
   int32_t dyn_win;            // row-groups compute waves may run ahead of the reduction
-  int32_t pad;
+  int32_t defer;              // a dynamic last group and 6 GiB of weights or more: stores may follow the staging
 };
 
 template <int FMT> struct Fmt;
@@ -1607,8 +1607,8 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
         dynamic = true;
       }
     }
-    // One token row, a step with a dynamic last group and no drift bound
-    // (6 to 12 GiB of weights), before a group whose activations no earlier
+    // One token row, a step with a dynamic last group, 6 GiB of weights or
+    // more and no drift bound (so below 12 GiB; p.defer), before a group whose activations no earlier
     // group writes and that waits for no other workgroup, g's outputs needing
     // no acknowledgement: the last row-group's rows are stored after the next
     // activations are staged, so the staging's wait (vmcnt(0)) covers its own
@@ -1619,7 +1619,7 @@ __device__ void control_wave(const PlanArgs& p, const Sched& S, int w, int lane,
     // (and, with the staging issued before the last row-group's reduction
     // instead, 8B int8 1205 / 1202, INT4 760 / 850, 4B 733 / 770, 2B 344 /
     // 381).
-    const bool defer = MT == 1 && p.dyn_c > 0 && p.lag == 0 && g + 1 < p.ngroups &&
+    const bool defer = MT == 1 && p.defer && p.lag == 0 && g + 1 < p.ngroups &&
                        !(S.order(g) & kAckOutputs) &&
                        (S.order(g + 1) & (kStageEarly | kNoWait)) == (kStageEarly | kNoWait);
     float held = 0.0f;
@@ -2173,8 +2173,8 @@ const void* multi_kernel(bool light) {
 // after the staging: int8 rings of 1 / 2 / 3 without reserve (2 x 2 reserve
 // on rings of 2): 2B 342-343 / 349-350 / 357 (355), 4B 721-722 / 730-731 /
 // 749-750 (718), 8B 1215-1217 / 1192-1193 / 1192-1193 (1206-1207); so steps
-// with a dynamic last group (6 GiB of weights or more) keep rings of 2 and
-// the others take rings of 1.
+// with a dynamic last group and 6 GiB of weights or more (`big`, the plan's
+// defer) keep rings of 2 and the others take rings of 1.
 #ifndef QD_PLAN_RESERVE8_LIGHT
 #define QD_PLAN_RESERVE8_LIGHT 0
 #endif
@@ -2187,7 +2187,7 @@ const void* multi_kernel(bool light) {
 #ifndef QD_PLAN_RESERVE4_LIGHT
 #define QD_PLAN_RESERVE4_LIGHT 0
 #endif
-const void* kernel_ptr(int fmt, bool multi, bool glue, bool light, bool dyn) {
+const void* kernel_ptr(int fmt, bool multi, bool glue, bool light, bool big) {
   if (multi) {
     if (fmt == QD_FMT_INT8_B32)
       return glue ? multi_kernel<QD_FMT_INT8_B32, true>(light) : multi_kernel<QD_FMT_INT8_B32, false>(light);
@@ -2195,7 +2195,7 @@ const void* kernel_ptr(int fmt, bool multi, bool glue, bool light, bool dyn) {
   }
   if (light && !glue) {
     if (fmt == QD_FMT_INT8_B32)
-      return dyn ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT,
+      return big ? reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT,
                                                                QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>)
                  : reinterpret_cast<const void*>(&stack_kernel<QD_FMT_INT8_B32, QD_PLAN_RING8_LIGHT_SMALL,
                                                                QD_PLAN_RESERVE8_LIGHT, kReserve8S, false, 1, 1>);
@@ -2245,6 +2245,9 @@ struct PlanLayout {
   bool light = false;          // see kernel_ptr
   // The dynamic last group (one token row; see PlanArgs), dyn_c = 0 if none.
   int dyn_c = 0, dyn_q = 0, dyn_nch = 0, dyn_max = 0, dyn_rcap = 0, dyn_scap = 0, dyn_win = 0;
+  // A dynamic last group and 6 GiB of weights or more: stores after the
+  // staging (control_wave) and rings of 2 for the light int8 step (kernel_ptr).
+  bool defer = false;
 };
 
 int pow2_at_least(int64_t v) {
@@ -2567,7 +2570,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // before it starts the totals afresh (every workgroup is level there),
     // so it keeps workgroup order, as paired groups do.
     if (!(hg.order & kNoWait)) std::fill(given.begin(), given.end(), (int64_t)0);
-    // One token row, 6 GiB of weights or more: the step's last group, when
+    // One token row, 3 GiB of weights or more: the step's last group, when
     // it has at least four row-groups per workgroup, is split at run time
     // instead (kDynamic).  The workgroups reach it at different times: each
     // streams at its own rate (on the 8B-shaped step the workgroups of some
@@ -2578,18 +2581,21 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
     // and 27B-shaped heads).  Measured, same
     // devices, wall us/step, fixed / dynamic: 8B int8 1259 / 1243, 1302 / 1288,
     // 1298 / 1289 (the last workgroups' finishing times spread 4 us instead
-    // of 110); 27B-shaped 3676 / 3672, 3648-3660 / 3652; but the smaller
-    // steps lose what they gain (2B 370 / 383, 4B 734-741 / 735-744, 8B INT4
-    // 756-764 / 762-777), so they keep the fixed split.  (Claims of 8 or 4
-    // chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.
-    // About 32 instead of 16, so single row-groups: 8B 1192-1193 -> 1190,
-    // 27B-shaped 3617-3619 -> 3605-3606.)
+    // of 110); 27B-shaped 3676 / 3672, 3648-3660 / 3652.  With claims of
+    // about 16 per workgroup the smaller steps lost what they gained (2B 370
+    // / 383, 4B 734-741 / 735-744, 8B INT4 756-764 / 762-777).  (Claims of 8
+    // or 4 chunks per workgroup did no better: 8B 1298 / 1304, 2B 374 / 376.)
+    // With about 32, single row-groups: 8B 1192-1193 -> 1190, 27B-shaped
+    // 3617-3619 -> 3605-3606; and without the stores after the staging and
+    // the rings of 2 that go with it for the larger steps (defer), 4B
+    // 731-733 -> 725-726 and 8B INT4 739-741 -> 737-740, while the 2B step
+    // (1.8 GB) still loses (343-344 -> 345-346), hence 3 GiB.
     // A step in which some group waits for the one before it keeps the fixed
     // split too: every such wait brings the workgroups level again, so no lag
     // builds up for the claims to absorb, and their upkeep in the waits is
     // pure cost (8B chained 1483-1485 -> 1470, glued 1650-1652 -> 1620-1621).
     if (!any_wait && !multi && !hg.paired && g == ng - 1 && R >= 4 * (int64_t)G &&
-        weight_bytes >= ((int64_t)6 << 30)) {
+        weight_bytes >= ((int64_t)3 << 30)) {
       const int64_t Ju = ceil_div(J, (int64_t)ku1(fmt));
       L->dyn_c = (int)std::max<int64_t>(1, R / (32 * (int64_t)G));
       L->dyn_nch = (int)ceil_div(R, (int64_t)L->dyn_c);
@@ -2601,6 +2607,7 @@ void layout_plan(const qd_linear_op* ops, int64_t n_ops, int64_t m, int G, PlanL
       L->dyn_scap = pow2_at_least(std::max<int64_t>(32, L->dyn_rcap / Ju + 1));
       L->dyn_win = (int)std::min<int64_t>(L->dyn_scap, L->dyn_rcap / Ju);
       L->pg[g].order |= kDynamic;
+      L->defer = weight_bytes >= ((int64_t)6 << 30);
       for (int w = 0; w < G; ++w) L->ps[(size_t)g * G + w] = PSched{0, off[w], 0, 0};
       maxRel = std::max(maxRel, L->dyn_rcap);
       maxSeg = std::max(maxSeg, L->dyn_scap);
@@ -2688,6 +2695,7 @@ void set_dynamic(PlanArgs& a, const PlanLayout& L, uint32_t* ctr) {
   a.dyn_rcap = std::max(1, L.dyn_rcap);
   a.dyn_scap = std::max(1, L.dyn_scap);
   a.dyn_win = L.dyn_win;
+  a.defer = L.defer ? 1 : 0;
 }
 
 qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stack_plan** out) {
@@ -2724,7 +2732,7 @@ qd_status plan_create(const qd_linear_op* ops, int64_t n_ops, int64_t m, qd_stac
     return QD_EDEVICE;
   }
   // LDS beyond one CU's: replay.
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.dyn_c > 0);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.defer);
   const size_t lds = L.lds;
   const size_t lds_max = std::max<size_t>(prop.sharedMemPerBlock, prop.maxSharedMemoryPerMultiProcessor);
   if (lds > lds_max) return fallback();
@@ -2886,7 +2894,7 @@ qd_status plan_run(qd_stack_plan* plan, hipStream_t s) {
   // workgroups would wait for it: the first device-wide wait then times out
   // (every wait is bounded, so the kernel still ends), the run reports the
   // timeout, and the plan launches cooperatively from then on.
-  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue, plan->light, plan->args.dyn_c > 0);
+  const void* kfn = kernel_ptr(plan->fmt, plan->multi, plan->glue, plan->light, plan->args.defer != 0);
   const hipError_t e =
       plan->cooperative
           ? hipLaunchCooperativeKernel(kfn, dim3(plan->args.G), dim3(kWaves * 64), kargs, (unsigned)plan->lds, s)
@@ -3077,7 +3085,7 @@ qd_status stack_run_noalloc(const qd_linear_op* ops, int64_t n_ops, int64_t m, i
   if (L.pg.size() > (size_t)kStaticGroups || L.pm.size() > (size_t)kStaticMembers) return QD_ESHAPE;
   std::vector<StackGroup> tail;
   if (L.split < n_ops && build_groups(ops + L.split, n_ops - L.split, m, &tail) != QD_OK) return replay_all();
-  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.dyn_c > 0);
+  const void* kfn = kernel_ptr(L.fmt, L.multi, L.glue, L.light, L.defer);
   if (L.lds > sd->lds_max) return replay_all();
   if (L.lds > 65536 && hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds) != hipSuccess) {
     (void)hipGetLastError();

@@ -1331,7 +1331,7 @@ DYNAMIC = 64          # qd_stack_plan_describe order flag: the last group is spl
 @pytest.mark.parametrize("chained", [False, True])
 def test_plan_dynamic_last_group(qd, fmt, chained):
     """The step's last group split at run time (workgroups claim chunks of
-    row-groups from a device counter), which a plan does from 6 GiB of
+    row-groups from a device counter), which a plan does from 3 GiB of
     weights: groups of copies of one 32768 x 16384 matrix make up the
     bytes.  The last group has two members with ragged row tails
     (200003 and 62424 rows, 16403 row-groups: chunks of 2, the last one half

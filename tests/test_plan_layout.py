@@ -202,7 +202,7 @@ def attach_sources(b, d):
 
 
 def check_dynamic(d, gi, g, m):
-    """One token row, 6 GiB of weights or more, no group waiting for the one
+    """One token row, 3 GiB of weights or more, no group waiting for the one
     before it: the step's last group, with
     at least four row-groups per workgroup, is split at run time (DYNAMIC): no workgroup has a range
     in it, and workgroups claim chunks of C row-groups (about 32 per
@@ -212,7 +212,7 @@ def check_dynamic(d, gi, g, m):
     dynamic = bool(g["order"] & DYNAMIC)
     waits = any(not h["order"] & NOWAIT for h in d["groups"][1:])
     expect = (m == 1 and gi == d["ngroups"] - 1 and g["R"] >= 4 * G and not g["order"] & PAIRED
-              and d["weight_bytes"] >= 6 << 30 and not waits)
+              and d["weight_bytes"] >= 3 << 30 and not waits)
     assert dynamic == expect, f"group {gi}: dynamic flag"
     if not dynamic:
         return False
